@@ -1,0 +1,255 @@
+"""Pins of the oracle's attention paths: the pages' worked examples, their
+frozen tolerance, the ablations they ask for, textbook reductions and a
+pure-Python brute force.  CPU only."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import kvq_oracle as O
+from workloads import SEEDS, WORKLOADS, Workload, make_qkv
+
+
+def _num(tok: str) -> float:
+    if tok.startswith("ln"):
+        return math.log(float(tok[2:]))
+    return float(Fraction(tok))
+
+
+def brute_attention(q, k, v, scale):
+    """Pure-Python loops with math.exp: out[b,h,r] = sum_j e^{s_j} v_j / sum_j e^{s_j}
+    with s_j = scale * q.k_j and KV head h // (Hq/Hkv); no max shift, so only
+    for small, well-scaled inputs."""
+    B, Hq, R, D = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    rep = Hq // Hkv
+    out = np.zeros(q.shape)
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // rep
+            for r in range(R):
+                ws, acc = 0.0, [0.0] * D
+                for j in range(N):
+                    s = scale * sum(float(q[b, h, r, d]) * float(k[b, kv, j, d]) for d in range(D))
+                    w = math.exp(s)
+                    ws += w
+                    for d in range(D):
+                        acc[d] += w * float(v[b, kv, j, d])
+                out[b, h, r] = [a / ws for a in acc]
+    return out
+
+
+# --- the worked example of the two stops ----------------------------------------
+
+def test_two_stops_17_over_3(golden):
+    g = golden("online_softmax_two_stops.json")
+    s = np.array([_num(t) for t in g["scores"]])
+    v = np.array(g["values"], dtype=np.float64)[:, None]
+    cut = np.cumsum([0] + g["blocks"])
+    sb = [s[cut[i]:cut[i + 1]] for i in range(len(g["blocks"]))]
+    vb = [v[cut[i]:cut[i + 1]] for i in range(len(g["blocks"]))]
+    out, states = O.merge_blocks(sb, vb)
+    for (m, z, u), key in zip(states, ("after_block_1", "after_block_2")):
+        want = g[key]
+        assert m == pytest.approx(_num(want["m"]), abs=1e-15)
+        assert z == pytest.approx(_num(want["l"]), abs=1e-14)
+        assert u[0] == pytest.approx(_num(want["u"]), abs=1e-14)
+        assert u[0] / z == pytest.approx(_num(want["out"]), abs=1e-14)
+    assert math.exp(states[0][0] - states[1][0]) == pytest.approx(_num(g["rescale_factor_at_block_2"]))
+    assert out[0] == pytest.approx(_num(g["dense_out"]), abs=1e-14)
+    # dense: weights (1/6, 2/6, 3/6)
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    assert w == pytest.approx([_num(t) for t in g["dense_weights"]], abs=1e-15)
+    q = np.ones((1, 1, 1, 1))
+    dense = O.attend_dense(q, s.reshape(1, 1, 3, 1), v.reshape(1, 1, 3, 1), sm_scale=1.0)
+    assert dense[0, 0, 0, 0] == pytest.approx(17 / 3, abs=1e-14)
+    # the page's caveat: the plain average coincides here
+    assert O.block_average(sb, vb)[0] == pytest.approx(17 / 3, abs=1e-14)
+    # dropping the u rescale does not (6.5 instead of 17/3)
+    bad, _ = O.merge_blocks(sb, vb, rescale_u=False)
+    assert bad[0] == pytest.approx(6.5, abs=1e-12)
+
+
+def test_block_average_deviates(golden):
+    g = golden("block_average_counterexample.json")
+    s = np.array(g["scores"], dtype=np.float64)
+    v = np.array(g["values"], dtype=np.float64)[:, None]
+    sb, vb = [s[:2], s[2:]], [v[:2], v[2:]]
+    dense, _ = O.merge_blocks([s], [v])
+    assert abs(dense[0] - 5.0) < 1e-3          # picks almost only the last value
+    avg = O.block_average(sb, vb)
+    assert avg[0] < dense[0] - 0.5             # visibly shifted towards smaller values
+    merged, _ = O.merge_blocks(sb, vb)
+    assert merged[0] == pytest.approx(dense[0], abs=1e-14)
+    # ablations: each dropped rescale breaks the 1e-10 check
+    for kw in ({"rescale_u": False}, {"rescale_z": False}):
+        bad, _ = O.merge_blocks(sb, vb, **kw)
+        assert abs(bad[0] - dense[0]) > 1e-10
+
+
+# --- frozen tolerance: blocked == dense on the same quantized cache -------------------
+
+def _quantized_case(w, seed, dist, bits, group):
+    q, k, v = make_qkv(w, seed, dist)
+    kc, ks = O.pack_k(k, bits, group)
+    vc, vs = O.pack_v(v, bits, group)
+    kh = O.dequant_k(kc, ks, k.shape, bits, group)
+    vh = O.dequant_v(vc, vs, v.shape, bits, group)
+    return q, k, v, kh, vh
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+@pytest.mark.parametrize("n", [128, 512])
+@pytest.mark.parametrize("dist", ["clean", "early", "late"])
+def test_blocked_equals_dense_18_inputs(seed, n, dist):
+    w = Workload("p", 1, 1, 1, 4, n, 32, ((4, 32),))
+    q, _, _, kh, vh = _quantized_case(w, seed, dist, 4, 32)
+    dense = O.attend_dense(q, kh, vh)
+    blocked = O.attend_blocked(q, kh, vh, 32)
+    assert np.max(np.abs(dense - blocked)) < 1e-10
+
+
+@pytest.mark.parametrize("dist", ["clean", "early", "late"])
+def test_ragged_block_7(dist):
+    w = WORKLOADS["single_n1024"]
+    q, _, _, kh, vh = _quantized_case(w, 0, dist, 4, 8)
+    assert 1024 % 7 == 2  # last block holds 2 tokens
+    dense = O.attend_dense(q, kh, vh)
+    assert np.max(np.abs(dense - O.attend_blocked(q, kh, vh, 7))) < 1e-10
+
+
+def test_biased_distributions_move_attention():
+    w = WORKLOADS["single_n1024"]
+    for dist, idx in (("early", slice(0, 16)), ("late", slice(1008, 1024))):
+        q, k, _ = make_qkv(w, 1, dist)
+        qc, kc, _ = make_qkv(w, 1, "clean")
+        s = (q[0, 0] @ k[0, 0].T) / math.sqrt(32)
+        sc = (qc[0, 0] @ kc[0, 0].T) / math.sqrt(32)
+        shift = (s[:, idx] - sc[:, idx]).mean()
+        assert shift == pytest.approx(4 * sc.std(), rel=1e-3)
+
+
+def test_rescale_removal_fails_on_real_data():
+    w = WORKLOADS["single_n1024"]
+    q, _, _, kh, vh = _quantized_case(w, 2, "late", 4, 8)
+    dense = O.attend_dense(q, kh, vh)
+    for kw in ({"rescale_u": False}, {"rescale_z": False}):
+        assert np.max(np.abs(dense - O.attend_blocked(q, kh, vh, 32, **kw))) > 1e-3
+
+
+def test_large_scores_stay_finite():
+    w = WORKLOADS["single_n128"]
+    q, k, v = make_qkv(w, 0)
+    out = O.attend_dense(q * 1000, k, v)
+    blk = O.attend_blocked(q * 1000, k, v, 32)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(blk))
+    assert np.max(np.abs(out - blk)) < 1e-10
+
+
+def test_work_array_bytes(golden):
+    g = golden("work_array_bytes.json")
+    b = g["blocked"]
+    w = Workload("p", 1, 1, 1, b["queries"], b["n"], b["d"], ((4, 32),))
+    q, k, v = make_qkv(w, 0)
+    t_dense, t_blk = {}, {}
+    O.attend_dense(q, k, v, trace=t_dense)
+    O.attend_blocked(q, k, v, b["block"], trace=t_blk)
+    assert t_dense["decoded_kv_bytes"] == b["decoded_kv_dense"]
+    assert t_blk["decoded_kv_bytes"] == b["decoded_kv_block"]
+    assert t_dense["score_bytes"] == b["score_dense"]
+    assert t_blk["score_bytes"] == b["score_block"]
+    t = g["tiled"]
+    for n, want in t["score_dense"].items():
+        w = Workload("p", 1, 1, 1, t["queries"], int(n), t["d"], ((4, 32),))
+        q, k, v = make_qkv(w, 0)
+        td, tb = {}, {}
+        O.attend_dense(q, k, v, trace=td)
+        O.attend_blocked(q, k, v, t["block"], trace=tb)
+        assert td["score_bytes"] == want
+        assert tb["score_bytes"] == t["score_block"]
+
+
+# --- brute force and textbook reductions ------------------------------------------------
+
+def test_dense_matches_brute_force_gqa():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((2, 4, 2, 5))
+    k = rng.standard_normal((2, 2, 7, 5))
+    v = rng.standard_normal((2, 2, 7, 5))
+    scale = 1 / math.sqrt(5)
+    want = brute_attention(q, k, v, scale)
+    assert np.max(np.abs(O.attend_dense(q, k, v) - want)) < 1e-13
+    assert np.max(np.abs(O.attend_blocked(q, k, v, 3) - want)) < 1e-13
+    for s in (1, 2, 3, 7, 9):
+        assert np.max(np.abs(O.attend_split(q, k, v, s) - want)) < 1e-13
+
+
+def test_gqa_map_is_contiguous():
+    """Query head h reads KV head h // (Hq/Hkv): heads 0,1 -> kv 0, heads 2,3 -> kv 1."""
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((1, 4, 1, 3))
+    k = rng.standard_normal((1, 2, 4, 3))
+    v = np.zeros((1, 2, 4, 3))
+    v[0, 0] = 1.0
+    v[0, 1] = -1.0
+    out = O.attend_dense(q, k, v)
+    assert np.allclose(out[0, :2], 1.0) and np.allclose(out[0, 2:], -1.0)
+
+
+def test_textbook_reductions():
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, 2, 3, 8))
+    k = rng.standard_normal((1, 2, 6, 8))
+    v = rng.standard_normal((1, 2, 6, 8))
+    # N = 1: the output is that one value row
+    out1 = O.attend_dense(q, k[:, :, :1], v[:, :, :1])
+    assert np.allclose(out1, np.broadcast_to(v[:, :, None, 0], out1.shape), atol=1e-15)
+    # q = 0: uniform weights, mean of the value rows
+    out0 = O.attend_dense(np.zeros_like(q), k, v)
+    assert np.allclose(out0, np.broadcast_to(v.mean(axis=2)[:, :, None], out0.shape), atol=1e-14)
+    # one dominant score: that value row
+    k2 = k.copy()
+    k2[0, :, 4] = q[0, :, 0] * 1e3
+    out2 = O.attend_dense(q[:, :, :1], k2, v)
+    assert np.allclose(out2[0, :, 0], v[0, :, 4], atol=1e-12)
+    # Hq == Hkv is multi-head attention: each head alone
+    for h in range(2):
+        solo = O.attend_dense(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1])
+        assert np.allclose(solo[:, 0], O.attend_dense(q, k, v)[:, h], atol=1e-15)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 16, 33, 200])
+def test_split_invariance(splits):
+    w = WORKLOADS["single_n512"]
+    q, _, _, kh, vh = _quantized_case(w, 1, "clean", 4, 32)
+    dense = O.attend_dense(q, kh, vh)
+    assert np.max(np.abs(O.attend_split(q, kh, vh, splits) - dense)) < 1e-12
+
+
+def test_split_bounds_cover_and_empty_tail():
+    b = O.split_bounds(10, 4)
+    assert b == [(0, 3), (3, 6), (6, 9), (9, 10)]
+    b = O.split_bounds(5, 8)
+    assert sum(hi - lo for lo, hi in b) == 5 and b[-1][0] == b[-1][1]
+
+
+# --- quantization error: plausibility only (parity unpinned) -------------------------------
+
+def test_error_table_plausible(golden):
+    g = golden("error_table.json")
+    got = {}
+    for key in g["rel_l2_percent"]:
+        bits, group = map(int, key.split("_"))
+        errs = []
+        for seed in SEEDS:
+            for n in (128, 512):
+                w = Workload("p", 1, 1, 1, 4, n, 32, ((bits, group),))
+                q, k, v, kh, vh = _quantized_case(w, seed, "clean", bits, group)
+                errs.append(O.rel_l2(O.attend_dense(q, kh, vh), O.attend_dense(q, k, v)))
+        got[key] = 100 * float(np.mean(errs))
+    for key, want in g["rel_l2_percent"].items():
+        assert abs(got[key] - want) < 0.15 * want, (key, got[key], want)
+    # the ordering the page reports
+    assert got["8_8"] < got["8_32"] < got["4_8"] < got["4_32"]

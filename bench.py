@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""KV-cache GB/s read by the fused 4-bit attend, on one MI355X.
+
+One step = one ``kvq_attend`` call (the fused path: K/V tile loads, in-register
+decode, scores, online softmax (m, z, u), split combine) over one full
+synthetic packed cache of the chosen workload, with Q, the packed cache, the
+output and the workspace resident in HBM before timing starts.  Packing is
+outside the step, as in the pages' timing scope; it and the decode-all
+baseline (kvq_dequant + kvq_attend_f32) are timed separately and reported
+under "extra".
+
+The timed steps rotate over enough distinct copies of the packed cache that
+their total exceeds the 256 MB Infinity Cache, so every step streams its KV
+bytes from HBM.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from workloads import WORKLOADS, make_qkv  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
+METRIC = "KV-cache GB/s read by fused 4-bit attend (and % of HBM peak) at n=4096, GQA 32/8"
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def kv_bytes(w, bits, group):
+    """Algorithmic bytes one attend reads: every K and V code byte and float32
+    scale once (2 * B * Hkv * N * D * (bits/8 + 4/group))."""
+    npad = -(-w.N // group) * group
+    dpad = -(-w.D // group) * group
+    per_head = (w.D * npad + w.N * dpad) * bits // 8 + 4 * (w.D * npad // group + w.N * dpad // group)
+    return w.B * w.Hkv * per_head
+
+
+def cpu_baseline(w, q, k, v, bits, group, seconds):
+    """Time the float64 oracle (decode the whole packed cache, dense attention)
+    on this host, as it stands, over whole passes of the workload until
+    `seconds` have elapsed (at least 2 passes)."""
+    from oracle import kvq_oracle as O
+    kc, ks = O.pack_k(k, bits, group)
+    vc, vs = O.pack_v(v, bits, group)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 2 or time.perf_counter() - t_start < seconds:
+        t0 = time.perf_counter()
+        O.attend_packed(q, kc, ks, vc, vs, w.N, bits, group)
+        times.append(time.perf_counter() - t0)
+    threads = None
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info())
+    except Exception:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    med = float(np.median(times))
+    return {
+        "value": kv_bytes(w, bits, group) / med / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads or cores),
+        "kind": "oracle",
+        "sample": (f"{len(times)} full passes of {w.name} (decode all {w.B * w.Hkv} KV heads to "
+                   f"float32, dense float64 attention), median {med * 1e3:.1f} ms/pass; "
+                   f"{cores} host cores visible, BLAS threads {threads}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="gqa_n4096", choices=["gqa_n4096", "gqa_n32768"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--splits", type=int, default=-1, help="-1: workload default, 0: auto")
+    ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip pack / decode-all timings")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by (batch, KV head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_kv_cache_attend_amd as kvq
+
+    w = WORKLOADS[args.workload]
+    bits, group = w.formats[0]
+    splits = w.num_splits if args.splits < 0 else args.splits
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} R={w.R} N={w.N} D={w.D} "
+        f"{bits}-bit g{group} splits={splits or kvq.auto_splits(w.B, w.Hkv, w.N)}")
+    q, k, v = make_qkv(w, 0)
+    qd, kd, vd = (torch.from_numpy(a).to(dev) for a in (q, k, v))
+    kc, ks = kvq.pack_k(kd, bits, group)
+    vc, vs = kvq.pack_v(vd, bits, group)
+    torch.cuda.synchronize()
+    nbytes = kv_bytes(w, bits, group)
+    assert nbytes == kc.numel() + vc.numel() + 4 * (ks.numel() + vs.numel())
+
+    copies = args.copies or max(2, math.ceil(3 * MALL_BYTES / nbytes))
+    caches = [(kc, ks, vc, vs)] + [tuple(t.clone() for t in (kc, ks, vc, vs)) for _ in range(copies - 1)]
+    out = torch.empty_like(qd)
+    ws = kvq.new_workspace(w.B, w.Hq, w.Hkv, w.R, w.N, w.D, splits, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    log(f"[bench] {copies} cache copies x {nbytes / 1e6:.1f} MB = {copies * nbytes / 1e6:.0f} MB")
+
+    def step(i):
+        c = caches[i % copies]
+        kvq.attend(qd, *c, w.N, bits, group, num_splits=splits, workspace=ws, out=out,
+                   variant=args.variant)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps back to back, host clock and stream events.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    region_ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] wall {ms_per_step * 1e3:.2f} us/step, stream events {region_ms * 1e3:.2f} us/step")
+
+    # Per-launch duration: an event pair around each call (same stream).
+    n_ev = min(args.steps, 400)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for i in range(n_ev):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]) * 1e3  # us
+    launch_us = float(np.median(per_launch))
+    log(f"[bench] per-launch events: median {launch_us:.2f} us, mean {per_launch.mean():.2f}, "
+        f"min {per_launch.min():.2f}, max {per_launch.max():.2f}")
+
+    kernel_us = min(launch_us, region_ms * 1e3)
+    achieved = nbytes / (kernel_us * 1e-6) / 1e9
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    finite = bool(torch.isfinite(out).all().item())
+
+    extra = {"wall_us_per_step": round(ms_per_step * 1e3, 3),
+             "stream_event_us_per_step": round(region_ms * 1e3, 3),
+             "per_launch_event_us_median": round(launch_us, 3),
+             "cache_copies": copies, "splits": splits or kvq.auto_splits(w.B, w.Hkv, w.N),
+             "variant": args.variant, "output_finite": finite}
+
+    if not args.no_extra:
+        # Pack (outside the step) and the decode-all baseline, same protocol.
+        kf = torch.empty_like(kd)
+        vf = torch.empty_like(vd)
+
+        def timed(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / reps
+
+        reps = 20 if w.N <= 4096 else 3
+        pack_us = timed(lambda: (kvq.pack_k(kd, bits, group), kvq.pack_v(vd, bits, group)), reps)
+
+        def decode_all():
+            kvq.dequant_k(kc, ks, w.N, w.D, bits, group, out=kf)
+            kvq.dequant_v(vc, vs, w.N, w.D, bits, group, out=vf)
+            kvq.attend_f32(qd, kf, vf, num_splits=splits, workspace=ws, out=out)
+        dec_us = timed(decode_all, reps)
+        extra.update({"pack_us": round(pack_us, 1), "decode_all_us": round(dec_us, 1),
+                      "decode_all_kv_gbs": round(nbytes / (dec_us * 1e-6) / 1e9, 1)})
+        log(f"[bench] pack {pack_us:.1f} us, decode-all baseline {dec_us:.1f} us")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host ...")
+        cpu = cpu_baseline(w, q, k, v, bits, group, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value']:.3f} GB/s ({cpu['sample']})")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4+f32",
+        "data": "synthetic (seeded N(0,1) float32 Q/K/V, packed on the GPU)",
+        "config": {"workload": w.name, "batch": w.B, "n_tokens": w.N, "hq": w.Hq, "hkv": w.Hkv,
+                   "queries_per_head": w.R, "head_dim": w.D, "bits": bits, "group": group,
+                   "kv_bytes": nbytes, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

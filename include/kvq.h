@@ -1,0 +1,163 @@
+/*
+ * kvq.h: C ABI of a gfx950 (MI355X) library for attention of a few
+ * non-causal queries over a KV cache stored as symmetric group-quantized,
+ * nibble-packed 4-bit (or byte-wide 8-bit) codes.
+ *
+ * Pages describing the method, cited below by tag:
+ *   [BKD] "Block KV decoding: less workspace, more time"
+ *         (huhohoo.com/en/docs/llm/kv-block-decode-cost)
+ *   [KPG] "KV分组打包：4-bit到底省了多少？" (huhohoo.com/docs/llm/kv-packed-groups)
+ *   [TOS] "注意力分塊：不保存完整分數矩陣，如何保持結果？"
+ *         (huhohoo.com/zh-TW/docs/llm/tiled-online-softmax)
+ *   [RL]  "给长前缀列一张有单位的资源账本" (codingai-lec05.pages.dev, resource-ledger)
+ *
+ * Packed format ([KPG] "what a byte holds", "why grouping needs both
+ * direction and length"):
+ *   - each group of `group` elements has one float32 scale max|x|/qmax
+ *     (qmax = 7 for 4-bit, 127 for 8-bit); a scale that comes out 0 is 1;
+ *   - codes are rint(x/scale) (round half to even, IEEE float32 division)
+ *     clipped to [-qmax, qmax] and stored unsigned as code + qmax;
+ *   - 4-bit: element 2i of a row goes to the low nibble, 2i+1 to the high
+ *     nibble of byte i; 8-bit: one byte per code;
+ *   - K ([B,H,N,D] float32) is grouped along tokens inside each channel:
+ *       K codes  [B][H][D][Npad*bits/8]  uint8,  K scales [B][H][D][Npad/group] float32
+ *   - V ([B,H,N,D] float32) is grouped along features inside each token:
+ *       V codes  [B][H][N][Dpad*bits/8]  uint8,  V scales [B][H][N][Dpad/group] float32
+ *   where Npad, Dpad round N, D up to a multiple of `group`; padding
+ *   elements are zeros before quantization (stored code = qmax).
+ *
+ * Conventions for every call:
+ *   - All array pointers are DEVICE pointers to dense row-major arrays in
+ *     the layouts above; `stream` is a hipStream_t (NULL = the null stream).
+ *     Calls enqueue work on `stream` and return without synchronizing.
+ *   - The caller owns and allocates every buffer, including the attention
+ *     workspace; the library allocates no memory.
+ *   - Arguments are checked before any work is enqueued.  On failure
+ *     nothing is written and a negative kvq_status is returned;
+ *     kvq_last_error() then holds a message for the calling thread.
+ *   - float pointers must be 4-byte aligned.
+ *   - Device faults are not reported by these calls; they surface at the
+ *     caller's next synchronization, as with any HIP launch.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = -1,     /* null pointer, size < 1, bad format, alias, misalignment */
+  KVQ_ERR_UNSUPPORTED = -2, /* valid but not compiled: e.g. attend head dim outside {32,64,128} */
+  KVQ_ERR_HIP = -3,         /* the HIP runtime rejected a launch */
+  KVQ_ERR_WORKSPACE = -4    /* workspace missing or smaller than kvq_attend_workspace_bytes */
+} kvq_status;
+
+/* Attention kernel families for kvq_attend_variant. */
+typedef enum kvq_variant {
+  KVQ_VARIANT_AUTO = 0,  /* what kvq_attend uses */
+  KVQ_VARIANT_VALU = 1,  /* any supported format: decode a tile to float32 in LDS */
+  KVQ_VARIANT_MFMA = 2   /* 4-bit, group 32, D = 128: fp16 matrix cores on exact codes */
+} kvq_variant;
+
+/* ---- host-only sizing (no device work, never fails) ------------------------
+ * Byte / element counts of the packed arrays; 0 if an argument is invalid
+ * (size < 1, bits not 4 or 8, group odd or < 2). */
+size_t kvq_k_code_bytes(int B, int H, int N, int D, int bits, int group);  /* B*H*D*Npad*bits/8 */
+size_t kvq_k_scale_count(int B, int H, int N, int D, int bits, int group); /* B*H*D*Npad/group  */
+size_t kvq_v_code_bytes(int B, int H, int N, int D, int bits, int group);  /* B*H*N*Dpad*bits/8 */
+size_t kvq_v_scale_count(int B, int H, int N, int D, int bits, int group); /* B*H*N*Dpad/group  */
+
+/* Number of KV splits kvq_attend uses when num_splits == 0 ([RL] "two stops
+ * of the online accumulation": per-split (m, z, u) are composable). */
+int kvq_attend_auto_splits(int B, int Hkv, int N);
+
+/* Workspace bytes kvq_attend / kvq_attend_f32 need for `num_splits` splits
+ * (0 = auto: kvq_attend_auto_splits(B, Hkv, N)).  Holds the
+ * per-split partial (m, z, u) of every query row and one arrival counter per
+ * (batch, KV head).  A workspace must be ZERO-FILLED once before its first
+ * use; every completed call leaves the counters at zero again.  Calls that
+ * run at the same time must use different workspaces. */
+size_t kvq_attend_workspace_bytes(int B, int Hq, int Hkv, int R, int N, int D, int num_splits);
+
+/* ---- kvq_pack_k / kvq_pack_v ------------------------------------------------
+ * Quantize and pack float32 K or V [B][H][N][D] into codes + scales in the
+ * layouts above ([KPG] "what a byte holds"; K and V group along different
+ * axes per [KPG] "why grouping needs both direction and length").  Any
+ * N, D >= 1 (ragged final groups are zero-padded).  Bit-exact: the scale is
+ * one IEEE float32 division, codes one float32 division and rint. */
+kvq_status kvq_pack_k(const float* k, int B, int H, int N, int D, int bits, int group,
+                      uint8_t* codes, float* scales, void* stream);
+kvq_status kvq_pack_v(const float* v, int B, int H, int N, int D, int bits, int group,
+                      uint8_t* codes, float* scales, void* stream);
+
+/* ---- kvq_dequant_k / kvq_dequant_v --------------------------------------------
+ * Decode the whole packed cache back to float32 [B][H][N][D], cropping the
+ * padding: out = fl32((stored - qmax) * scale), one float32 multiply ([KPG]
+ * "what a byte holds").  The decode-everything half of the baseline in
+ * [BKD] "Compare equivalent representations first". */
+kvq_status kvq_dequant_k(const uint8_t* codes, const float* scales, int B, int H, int N, int D,
+                         int bits, int group, float* out, void* stream);
+kvq_status kvq_dequant_v(const uint8_t* codes, const float* scales, int B, int H, int N, int D,
+                         int bits, int group, float* out, void* stream);
+
+/* ---- kvq_attend ---------------------------------------------------------------
+ * out[b][hq][r][:] = softmax_j(sm_scale * q[b][hq][r] . k_j) v_j over all N
+ * tokens of KV head hq / (Hq/Hkv), with k_j, v_j decoded from the packed
+ * cache inside the kernel ([RL] "GQA changes the shared interface"; no
+ * causal mask, [TOS] opening section).  The kernel runs the blocked online
+ * softmax of [BKD] "Do not average independently normalized blocks" and
+ * [RL] "why FlashAttention need not keep the whole heat map": per query row
+ * it carries the running max m, exponential sum z and unnormalized value sum
+ * u, rescaling both z and u by exp(m_old - m_new) on every block; KV splits
+ * are merged with the same rescale.
+ *   q      [B][Hq][R][D] float32          out [B][Hq][R][D] float32
+ *   k_codes/k_scales, v_codes/v_scales: the packed layouts above, H = Hkv.
+ *   sm_scale: softmax temperature; 0 means 1/sqrt(D) ([RL] "prefill and decode").
+ *   num_splits: KV splits; 0 = kvq_attend_auto_splits.
+ *   workspace: device buffer of >= kvq_attend_workspace_bytes(...) bytes,
+ *     zero-filled before first use (may be NULL only when one split is used).
+ * Supported: D in {32, 64, 128}; (Hq/Hkv)*R <= 64; any N >= 1.
+ * `out` must not overlap any input.  Accuracy: float32 accumulation, aimed
+ * at 1e-4 absolute of a float64 evaluation over the same decoded cache for
+ * unit-variance inputs. */
+kvq_status kvq_attend(const float* q, const uint8_t* k_codes, const float* k_scales,
+                      const uint8_t* v_codes, const float* v_scales,
+                      int B, int Hq, int Hkv, int R, int N, int D, int bits, int group,
+                      float sm_scale, int num_splits, void* workspace, size_t workspace_bytes,
+                      float* out, void* stream);
+
+/* Same contract as kvq_attend with an explicit kernel family.
+ * KVQ_VARIANT_MFMA returns KVQ_ERR_UNSUPPORTED unless bits == 4,
+ * group == 32, D == 128, (Hq/Hkv)*R <= 32 and the code/scale pointers are
+ * 16-byte aligned. */
+kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,
+                              const uint8_t* v_codes, const float* v_scales,
+                              int B, int Hq, int Hkv, int R, int N, int D, int bits, int group,
+                              float sm_scale, int num_splits, void* workspace,
+                              size_t workspace_bytes, float* out, int variant, void* stream);
+
+/* ---- kvq_attend_f32 -------------------------------------------------------------
+ * The same attention over an unquantized float32 cache k, v [B][Hkv][N][D]:
+ * the float32-cache reference of [BKD] "Compare equivalent representations
+ * first", and, after kvq_dequant_k/_v, the attend half of the decode-all
+ * baseline.  Workspace rules as for kvq_attend. */
+kvq_status kvq_attend_f32(const float* q, const float* k, const float* v,
+                          int B, int Hq, int Hkv, int R, int N, int D, float sm_scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, float* out,
+                          void* stream);
+
+/* ---- diagnostics -------------------------------------------------------------------- */
+const char* kvq_status_string(int status);  /* static string, never NULL */
+const char* kvq_last_error(void);           /* message of this thread's last failed call */
+int kvq_abi_version(void);                  /* bumped on any change of this header */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

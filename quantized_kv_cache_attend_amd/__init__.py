@@ -1,0 +1,208 @@
+"""Python binding of ``libkvq.so``: packed 4/8-bit KV-cache attention on gfx950.
+
+Argument marshalling only: every step of packing, decoding and attention
+runs in the library's HIP kernels.  PyTorch supplies device memory and the
+current stream.  The names follow the C ABI in ``include/kvq.h``.
+
+Importing this package loads ``libkvq.so`` and raises ``ImportError`` if it
+has not been built (``python -m quantized_kv_cache_attend_amd.build``); there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m quantized_kv_cache_attend_amd.build)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_c_int, _c_float, _c_size, _c_vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+# (name, restype, argtypes) of every function in include/kvq.h.
+_SIGNATURES = {
+    "kvq_k_code_bytes": (_c_size, [_c_int] * 6),
+    "kvq_k_scale_count": (_c_size, [_c_int] * 6),
+    "kvq_v_code_bytes": (_c_size, [_c_int] * 6),
+    "kvq_v_scale_count": (_c_size, [_c_int] * 6),
+    "kvq_attend_auto_splits": (_c_int, [_c_int] * 3),
+    "kvq_attend_workspace_bytes": (_c_size, [_c_int] * 7),
+    "kvq_pack_k": (_c_int, [_c_vp] + [_c_int] * 6 + [_c_vp, _c_vp, _c_vp]),
+    "kvq_pack_v": (_c_int, [_c_vp] + [_c_int] * 6 + [_c_vp, _c_vp, _c_vp]),
+    "kvq_dequant_k": (_c_int, [_c_vp, _c_vp] + [_c_int] * 6 + [_c_vp, _c_vp]),
+    "kvq_dequant_v": (_c_int, [_c_vp, _c_vp] + [_c_int] * 6 + [_c_vp, _c_vp]),
+    "kvq_attend": (_c_int, [_c_vp] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_vp, _c_size,
+                                                         _c_vp, _c_vp]),
+    "kvq_attend_variant": (_c_int, [_c_vp] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_vp,
+                                                                 _c_size, _c_vp, _c_int, _c_vp]),
+    "kvq_attend_f32": (_c_int, [_c_vp] * 3 + [_c_int] * 6 + [_c_float, _c_int, _c_vp, _c_size,
+                                                             _c_vp, _c_vp]),
+    "kvq_status_string": (ctypes.c_char_p, [_c_int]),
+    "kvq_last_error": (ctypes.c_char_p, []),
+    "kvq_abi_version": (_c_int, []),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP, KVQ_ERR_WORKSPACE = 0, -1, -2, -3, -4
+VARIANTS = {"auto": 0, "valu": 1, "mfma": 2}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.kvq_last_error().decode() or lib.kvq_status_string(status).decode()
+        super().__init__(f"{where}: {lib.kvq_status_string(status).decode()} ({status}): {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != KVQ_OK:
+        raise KvqError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# --- sizing -------------------------------------------------------------------------
+
+def packed_shapes(B, H, N, D, bits, group):
+    """Shapes of (k_codes, k_scales, v_codes, v_scales) for K/V of [B,H,N,D]."""
+    npad = -(-N // group) * group
+    dpad = -(-D // group) * group
+    return ((B, H, D, npad * bits // 8), (B, H, D, npad // group),
+            (B, H, N, dpad * bits // 8), (B, H, N, dpad // group))
+
+
+def workspace_bytes(B, Hq, Hkv, R, N, D, num_splits=0) -> int:
+    return int(lib.kvq_attend_workspace_bytes(B, Hq, Hkv, R, N, D, num_splits))
+
+
+def auto_splits(B, Hkv, N) -> int:
+    return int(lib.kvq_attend_auto_splits(B, Hkv, N))
+
+
+def new_workspace(B, Hq, Hkv, R, N, D, num_splits=0, device="cuda"):
+    """A zero-filled workspace (the library requires zeros before first use)."""
+    torch = _torch()
+    n = workspace_bytes(B, Hq, Hkv, R, N, D, num_splits)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+# --- calls -----------------------------------------------------------------------------
+
+def _pack(fn, x, bits, group, k_style):
+    torch = _torch()
+    _need(x, torch.float32, "x")
+    B, H, N, D = x.shape
+    ks, kss, vs, vss = packed_shapes(B, H, N, D, bits, group)
+    cshape, sshape = (ks, kss) if k_style else (vs, vss)
+    codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(sshape, dtype=torch.float32, device=x.device)
+    _check(fn(_ptr(x), B, H, N, D, bits, group, _ptr(codes), _ptr(scales), _stream(x.device)),
+           fn.__name__)
+    return codes, scales
+
+
+def pack_k(k, bits=4, group=32):
+    """Pack float32 K [B,H,N,D] -> (codes [B,H,D,Npad*bits/8] u8, scales [B,H,D,Npad/g] f32)."""
+    return _pack(lib.kvq_pack_k, k, bits, group, True)
+
+
+def pack_v(v, bits=4, group=32):
+    """Pack float32 V [B,H,N,D] -> (codes [B,H,N,Dpad*bits/8] u8, scales [B,H,N,Dpad/g] f32)."""
+    return _pack(lib.kvq_pack_v, v, bits, group, False)
+
+
+def _dequant(fn, codes, scales, N, D, bits, group, out):
+    torch = _torch()
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float32, "scales")
+    B, H = codes.shape[:2]
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=torch.float32, device=codes.device)
+    _need(out, torch.float32, "out")
+    if tuple(out.shape) != (B, H, N, D):
+        raise ValueError(f"out must have shape {(B, H, N, D)}")
+    _check(fn(_ptr(codes), _ptr(scales), B, H, N, D, bits, group, _ptr(out),
+              _stream(codes.device)), fn.__name__)
+    return out
+
+
+def dequant_k(codes, scales, N, D, bits=4, group=32, out=None):
+    """Decode packed K to float32 [B,H,N,D]."""
+    return _dequant(lib.kvq_dequant_k, codes, scales, N, D, bits, group, out)
+
+
+def dequant_v(codes, scales, N, D, bits=4, group=32, out=None):
+    """Decode packed V to float32 [B,H,N,D]."""
+    return _dequant(lib.kvq_dequant_v, codes, scales, N, D, bits, group, out)
+
+
+def attend(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scale=0.0,
+           num_splits=0, workspace=None, out=None, variant="auto"):
+    """Fused attention of q [B,Hq,R,D] over the packed cache (KV heads = k_codes.shape[1])."""
+    torch = _torch()
+    _need(q, torch.float32, "q")
+    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (k_scales, "k_scales", torch.float32),
+                     (v_codes, "v_codes", torch.uint8), (v_scales, "v_scales", torch.float32)):
+        _need(t, dt, n)
+    B, Hq, R, D = q.shape
+    Hkv = k_codes.shape[1]
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, R, N, D, num_splits, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.kvq_attend_variant(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                  _ptr(v_scales), B, Hq, Hkv, R, N, D, bits, group,
+                                  float(sm_scale), num_splits, _ptr(workspace),
+                                  workspace.numel(), _ptr(out), VARIANTS[variant],
+                                  _stream(q.device)), "kvq_attend")
+    return out
+
+
+def attend_f32(q, k, v, sm_scale=0.0, num_splits=0, workspace=None, out=None):
+    """Attention of q [B,Hq,R,D] over a float32 cache k, v [B,Hkv,N,D]."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.float32, n)
+    B, Hq, R, D = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, R, N, D, num_splits, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.kvq_attend_f32(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, R, N, D, float(sm_scale),
+                              num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
+                              _stream(q.device)), "kvq_attend_f32")
+    return out

@@ -1,0 +1,314 @@
+// Host side of the C ABI declared in include/kvq.h: argument checks,
+// workspace carving, split and kernel selection, launches.  No allocation,
+// no synchronization, no global mutable state except a thread-local error
+// message.
+#include "kvq.h"
+#include "kvq_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+namespace kvq {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvq_status ok() {
+  g_last_error[0] = '\0';
+  return KVQ_OK;
+}
+
+bool format_ok(int bits, int group) {
+  return (bits == 4 || bits == 8) && group >= 2 && group % 2 == 0;
+}
+
+long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges).
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+kvq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int R, int D, int splits) {
+  (void)Hkv;
+  const size_t rows = static_cast<size_t>(B) * Hq * R;  // every query row once
+  WorkspaceLayout w;
+  w.m_off = 0;
+  w.z_off = round_up(w.m_off + sizeof(float) * splits * rows, 256);
+  w.u_off = round_up(w.z_off + sizeof(float) * splits * rows, 256);
+  w.cnt_off = round_up(w.u_off + sizeof(float) * splits * rows * D, 256);
+  w.total = round_up(w.cnt_off + sizeof(unsigned) * static_cast<size_t>(B) * Hkv, 256);
+  return w;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+namespace {
+
+int auto_splits(int B, int Hkv, int N) {
+  // Enough workgroups to cover the 256 compute units several times over,
+  // but never splits shorter than 256 tokens.
+  const long long heads = static_cast<long long>(B) * Hkv;
+  const long long want = (1024 + heads - 1) / heads;
+  const long long cap = (N + 255) / 256;
+  long long s = want < cap ? want : cap;
+  if (s < 1) s = 1;
+  if (s > 1024) s = 1024;
+  return static_cast<int>(s);
+}
+
+// Shared validation of the attention calls.  `bits` == 32 marks the
+// float32-cache path.
+kvq_status check_attend(const float* q, const void* k, const void* ks, const void* v,
+                        const void* vs, int B, int Hq, int Hkv, int R, int N, int D, int bits,
+                        int group, float sm_scale, int num_splits, void* workspace,
+                        size_t workspace_bytes, float* out, AttendProblem* p) {
+  if (!q || !k || !v || !out || (bits != 32 && (!ks || !vs)))
+    return fail(KVQ_ERR_INVALID, "null pointer argument");
+  if (B < 1 || Hq < 1 || Hkv < 1 || R < 1 || N < 1 || D < 1)
+    return fail(KVQ_ERR_INVALID, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d R=%d N=%d D=%d)", B, Hq,
+                Hkv, R, N, D);
+  if (Hq % Hkv) return fail(KVQ_ERR_INVALID, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (bits != 32 && !format_ok(bits, group))
+    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
+                group);
+  if (num_splits < 0) return fail(KVQ_ERR_INVALID, "num_splits=%d < 0", num_splits);
+  if (!(std::isfinite(sm_scale)) || sm_scale < 0.0f)
+    return fail(KVQ_ERR_INVALID, "sm_scale must be finite and >= 0");
+  if (!aligned(q, 4) || !aligned(out, 4) || (bits != 32 && (!aligned(ks, 4) || !aligned(vs, 4))) ||
+      (bits == 32 && (!aligned(k, 4) || !aligned(v, 4))))
+    return fail(KVQ_ERR_INVALID, "float arrays must be 4-byte aligned");
+  if (D != 32 && D != 64 && D != 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "head dim D=%d not in {32, 64, 128}", D);
+  const int rows = (Hq / Hkv) * R;
+  if (rows > kMaxRows)
+    return fail(KVQ_ERR_UNSUPPORTED, "(Hq/Hkv)*R = %d query rows per KV head > %d", rows,
+                kMaxRows);
+
+  const long long BH = static_cast<long long>(B) * Hkv;
+  const size_t out_bytes = sizeof(float) * static_cast<size_t>(B) * Hq * R * D;
+  size_t kb, vb, ksb = 0, vsb = 0;
+  if (bits == 32) {
+    kb = vb = sizeof(float) * static_cast<size_t>(BH) * N * D;
+  } else {
+    const long long npad = round_up(N, group), dpad = round_up(D, group);
+    kb = static_cast<size_t>(BH * D * npad * bits / 8);
+    vb = static_cast<size_t>(BH * N * dpad * bits / 8);
+    ksb = sizeof(float) * static_cast<size_t>(BH * D * (npad / group));
+    vsb = sizeof(float) * static_cast<size_t>(BH * N * (dpad / group));
+  }
+  if (overlaps(out, out_bytes, q, out_bytes) || overlaps(out, out_bytes, k, kb) ||
+      overlaps(out, out_bytes, v, vb) || (ksb && overlaps(out, out_bytes, ks, ksb)) ||
+      (vsb && overlaps(out, out_bytes, vs, vsb)))
+    return fail(KVQ_ERR_INVALID, "out overlaps an input");
+
+  const int splits = num_splits ? num_splits : auto_splits(B, Hkv, N);
+  if (splits > 65535) return fail(KVQ_ERR_INVALID, "num_splits=%d > 65535", splits);
+  const WorkspaceLayout wl = workspace_layout(B, Hq, Hkv, R, D, splits);
+  if (splits > 1) {
+    if (!workspace) return fail(KVQ_ERR_WORKSPACE, "%d splits need a workspace", splits);
+    if (workspace_bytes < wl.total)
+      return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                  wl.total);
+    if (!aligned(workspace, 16)) return fail(KVQ_ERR_INVALID, "workspace must be 16-byte aligned");
+    if (overlaps(out, out_bytes, workspace, wl.total))
+      return fail(KVQ_ERR_INVALID, "out overlaps the workspace");
+  }
+
+  p->q = q;
+  p->k_codes = static_cast<const uint8_t*>(k);
+  p->k_scales = static_cast<const float*>(ks);
+  p->v_codes = static_cast<const uint8_t*>(v);
+  p->v_scales = static_cast<const float*>(vs);
+  p->k_f32 = static_cast<const float*>(k);
+  p->v_f32 = static_cast<const float*>(v);
+  p->out = out;
+  p->B = B;
+  p->Hq = Hq;
+  p->Hkv = Hkv;
+  p->R = R;
+  p->N = N;
+  p->D = D;
+  p->rows = rows;
+  p->bits = bits;
+  p->group = bits == 32 ? 1 : group;
+  const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(static_cast<float>(D));
+  p->qscale = scale * kLog2e;
+  p->splits = splits;
+  p->tokens_per_split = static_cast<int>((N + splits - 1) / splits);
+  char* ws = static_cast<char*>(workspace);
+  p->part_m = splits > 1 ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
+  p->part_z = splits > 1 ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
+  p->part_u = splits > 1 ? reinterpret_cast<float*>(ws + wl.u_off) : nullptr;
+  p->counters = splits > 1 ? reinterpret_cast<unsigned*>(ws + wl.cnt_off) : nullptr;
+  return KVQ_OK;
+}
+
+bool mfma_eligible(const AttendProblem& p) {
+  (void)p;
+  return false;
+}
+
+kvq_status codec_check(const void* a, const void* b, const void* c, int B, int H, int N, int D,
+                       int bits, int group) {
+  if (!a || !b || !c) return fail(KVQ_ERR_INVALID, "null pointer argument");
+  if (B < 1 || H < 1 || N < 1 || D < 1)
+    return fail(KVQ_ERR_INVALID, "sizes must be >= 1 (B=%d H=%d N=%d D=%d)", B, H, N, D);
+  if (!format_ok(bits, group))
+    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
+                group);
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_k_code_bytes(int B, int H, int N, int D, int bits, int group) {
+  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
+  return static_cast<size_t>(B) * H * D * round_up(N, group) * bits / 8;
+}
+size_t kvq_k_scale_count(int B, int H, int N, int D, int bits, int group) {
+  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
+  return static_cast<size_t>(B) * H * D * (round_up(N, group) / group);
+}
+size_t kvq_v_code_bytes(int B, int H, int N, int D, int bits, int group) {
+  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
+  return static_cast<size_t>(B) * H * N * round_up(D, group) * bits / 8;
+}
+size_t kvq_v_scale_count(int B, int H, int N, int D, int bits, int group) {
+  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
+  return static_cast<size_t>(B) * H * N * (round_up(D, group) / group);
+}
+
+int kvq_attend_auto_splits(int B, int Hkv, int N) {
+  if (B < 1 || Hkv < 1 || N < 1) return 0;
+  return auto_splits(B, Hkv, N);
+}
+
+size_t kvq_attend_workspace_bytes(int B, int Hq, int Hkv, int R, int N, int D, int num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || R < 1 || N < 1 || D < 1 || num_splits < 0) return 0;
+  const int s = num_splits ? num_splits : auto_splits(B, Hkv, N);
+  return workspace_layout(B, Hq, Hkv, R, D, s).total;
+}
+
+kvq_status kvq_pack_k(const float* k, int B, int H, int N, int D, int bits, int group,
+                      uint8_t* codes, float* scales, void* stream) {
+  const kvq_status st = codec_check(k, codes, scales, B, H, N, D, bits, group);
+  if (st != KVQ_OK) return st;
+  return hip_status(launch_pack(k, B, H, N, D, bits, group, true, codes, scales,
+                                static_cast<hipStream_t>(stream)),
+                    "pack_k launch");
+}
+
+kvq_status kvq_pack_v(const float* v, int B, int H, int N, int D, int bits, int group,
+                      uint8_t* codes, float* scales, void* stream) {
+  const kvq_status st = codec_check(v, codes, scales, B, H, N, D, bits, group);
+  if (st != KVQ_OK) return st;
+  return hip_status(launch_pack(v, B, H, N, D, bits, group, false, codes, scales,
+                                static_cast<hipStream_t>(stream)),
+                    "pack_v launch");
+}
+
+kvq_status kvq_dequant_k(const uint8_t* codes, const float* scales, int B, int H, int N, int D,
+                         int bits, int group, float* out, void* stream) {
+  const kvq_status st = codec_check(codes, scales, out, B, H, N, D, bits, group);
+  if (st != KVQ_OK) return st;
+  return hip_status(launch_dequant(codes, scales, B, H, N, D, bits, group, true, out,
+                                   static_cast<hipStream_t>(stream)),
+                    "dequant_k launch");
+}
+
+kvq_status kvq_dequant_v(const uint8_t* codes, const float* scales, int B, int H, int N, int D,
+                         int bits, int group, float* out, void* stream) {
+  const kvq_status st = codec_check(codes, scales, out, B, H, N, D, bits, group);
+  if (st != KVQ_OK) return st;
+  return hip_status(launch_dequant(codes, scales, B, H, N, D, bits, group, false, out,
+                                   static_cast<hipStream_t>(stream)),
+                    "dequant_v launch");
+}
+
+kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,
+                              const uint8_t* v_codes, const float* v_scales, int B, int Hq,
+                              int Hkv, int R, int N, int D, int bits, int group, float sm_scale,
+                              int num_splits, void* workspace, size_t workspace_bytes,
+                              float* out, int variant, void* stream) {
+  AttendProblem p;
+  kvq_status st = check_attend(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N, D, bits,
+                               group, sm_scale, num_splits, workspace, workspace_bytes, out, &p);
+  if (st != KVQ_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (variant) {
+    case KVQ_VARIANT_AUTO:
+      if (mfma_eligible(p)) return hip_status(launch_attend_mfma(p, s), "attend (mfma) launch");
+      return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
+    case KVQ_VARIANT_VALU:
+      return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
+    case KVQ_VARIANT_MFMA:
+      if (!mfma_eligible(p))
+        return fail(KVQ_ERR_UNSUPPORTED,
+                    "matrix-core kernel needs bits=4, group=32, D=128, <= 32 rows per KV head "
+                    "and 16-byte aligned codes/scales");
+      return hip_status(launch_attend_mfma(p, s), "attend (mfma) launch");
+    default:
+      return fail(KVQ_ERR_INVALID, "unknown variant %d", variant);
+  }
+}
+
+kvq_status kvq_attend(const float* q, const uint8_t* k_codes, const float* k_scales,
+                      const uint8_t* v_codes, const float* v_scales, int B, int Hq, int Hkv,
+                      int R, int N, int D, int bits, int group, float sm_scale, int num_splits,
+                      void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  return kvq_attend_variant(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N, D, bits,
+                            group, sm_scale, num_splits, workspace, workspace_bytes, out,
+                            KVQ_VARIANT_AUTO, stream);
+}
+
+kvq_status kvq_attend_f32(const float* q, const float* k, const float* v, int B, int Hq, int Hkv,
+                          int R, int N, int D, float sm_scale, int num_splits, void* workspace,
+                          size_t workspace_bytes, float* out, void* stream) {
+  AttendProblem p;
+  kvq_status st = check_attend(q, k, nullptr, v, nullptr, B, Hq, Hkv, R, N, D, 32, 1, sm_scale,
+                               num_splits, workspace, workspace_bytes, out, &p);
+  if (st != KVQ_OK) return st;
+  return hip_status(launch_attend_valu(p, static_cast<hipStream_t>(stream)),
+                    "attend_f32 launch");
+}
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_HIP: return "HIP runtime error";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* kvq_last_error(void) { return g_last_error; }
+
+int kvq_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,245 @@
+// General fused attention over the packed cache, plain float32 VALU
+// arithmetic.  Serves every supported format (4/8-bit, any even group,
+// D in {32, 64, 128}, up to 64 query rows per KV head) and the float32-cache
+// path; the 4-bit group-32 D=128 hot case has a matrix-core kernel of its own.
+//
+// Method, from "Block KV decoding: less workspace, more time"
+// (huhohoo.com/en/docs/llm/kv-block-decode-cost), section "Do not average
+// independently normalized blocks", and "给长前缀列一张有单位的资源账本"
+// (codingai-lec05.pages.dev resource-ledger), section "why FlashAttention
+// need not keep the whole heat map": per query row keep the running max m,
+// the exponential sum z and the unnormalized value sum u; for each block
+//   m' = max(m, max s),  a = 2^(m - m'),  z' = a z + sum 2^(s - m'),
+//   u' = a u + sum 2^(s - m') v,
+// and finally out = u / z.  Scores are in base-2 units (q is pre-multiplied
+// by sm_scale * log2 e), which leaves the softmax unchanged.
+//
+// Work split: one workgroup per (KV split, KV head, batch).  A tile of
+// kTile tokens is decoded to float32 in LDS (the exact value
+// fl32((stored - qmax) * scale) the decode-all path produces), shared by
+// all query rows of the KV head (every GQA head and query), then scored,
+// folded into (m, z) and into u.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 32;
+
+template <int SRC>
+__device__ __forceinline__ float decode_k(const AttendProblem& p, long long bh, int d, int n) {
+  if (SRC == 32) return p.k_f32[(bh * p.N + n) * p.D + d];
+  const int npad = (p.N + p.group - 1) / p.group * p.group;
+  const long long row = bh * p.D + d;
+  const uint8_t* codes = p.k_codes + row * (static_cast<long long>(npad) * SRC / 8);
+  int c;
+  if (SRC == 4) {
+    const unsigned b = codes[n >> 1];
+    c = static_cast<int>((n & 1) ? (b >> 4) : (b & 15u)) - 7;
+  } else {
+    c = static_cast<int>(codes[n]) - 127;
+  }
+  const float s = p.k_scales[row * (npad / p.group) + n / p.group];
+  return static_cast<float>(c) * s;
+}
+
+template <int SRC>
+__device__ __forceinline__ float decode_v(const AttendProblem& p, long long bh, int n, int f) {
+  if (SRC == 32) return p.v_f32[(bh * p.N + n) * p.D + f];
+  const int dpad = (p.D + p.group - 1) / p.group * p.group;
+  const long long row = bh * p.N + n;
+  const uint8_t* codes = p.v_codes + row * (static_cast<long long>(dpad) * SRC / 8);
+  int c;
+  if (SRC == 4) {
+    const unsigned b = codes[f >> 1];
+    c = static_cast<int>((f & 1) ? (b >> 4) : (b & 15u)) - 7;
+  } else {
+    c = static_cast<int>(codes[f]) - 127;
+  }
+  const float s = p.v_scales[row * (dpad / p.group) + f / p.group];
+  return static_cast<float>(c) * s;
+}
+
+template <int D, int SRC>
+__global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) {
+  constexpr int kAcc = kMaxRows * D / kThreads;  // u accumulators per thread
+  __shared__ float sQ[kMaxRows][D];
+  __shared__ float sK[kTile][D + 1];
+  __shared__ float sV[kTile][D];
+  __shared__ float sP[kMaxRows][kTile + 1];
+  __shared__ float sM[kMaxRows], sZ[kMaxRows], sA[kMaxRows];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int split = blockIdx.x;
+  const int rows = p.rows;
+  const long long bh = static_cast<long long>(blockIdx.z) * p.Hkv + blockIdx.y;
+  const int t_begin = split * p.tokens_per_split;
+  const int t_end = min(p.N, t_begin + p.tokens_per_split);
+
+  // Query rows of this KV head are contiguous in q: [bh*rows, bh*rows + rows).
+  for (int i = tid; i < rows * D; i += kThreads)
+    sQ[i / D][i % D] = p.q[bh * rows * D + i] * p.qscale;
+  for (int r = tid; r < rows; r += kThreads) {
+    sM[r] = -INFINITY;
+    sZ[r] = 0.0f;
+  }
+  float acc[kAcc];
+#pragma unroll
+  for (int i = 0; i < kAcc; ++i) acc[i] = 0.0f;
+  __syncthreads();
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+    const int tn = min(kTile, t_end - t0);
+    // Decode the tile.  K: token index fastest (K codes are channel-major);
+    // V: feature index fastest (V codes are token-major).
+    for (int i = tid; i < kTile * D; i += kThreads) {
+      const int j = i % kTile, d = i / kTile;
+      sK[j][d] = j < tn ? decode_k<SRC>(p, bh, d, t0 + j) : 0.0f;
+    }
+    for (int i = tid; i < kTile * D; i += kThreads) {
+      const int f = i % D, j = i / D;
+      sV[j][f] = j < tn ? decode_v<SRC>(p, bh, t0 + j, f) : 0.0f;
+    }
+    __syncthreads();
+
+    // Scores of every (row, token); tokens past N are masked out (-inf).
+    for (int i = tid; i < rows * kTile; i += kThreads) {
+      const int r = i / kTile, j = i % kTile;
+      float s = -INFINITY;
+      if (j < tn) {
+        s = 0.0f;
+#pragma unroll 8
+        for (int d = 0; d < D; ++d) s = fmaf(sQ[r][d], sK[j][d], s);
+      }
+      sP[r][j] = s;
+    }
+    __syncthreads();
+
+    // (m, z) update: each wave takes two rows at a time, one per 32-lane half.
+    for (int rb = wave * 2; rb < rows; rb += 2 * (kThreads / 64)) {
+      const int r = rb + (lane >> 5);
+      const int j = lane & 31;
+      const bool live = r < rows;
+      const float s = live ? sP[r][j] : -INFINITY;
+      float mx = s;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float m_old = live ? sM[r] : 0.0f;
+      // The tile holds at least one real token, so m_new is finite and
+      // neither exponent below can be (-inf) - (-inf).
+      const float m_new = fmaxf(m_old, mx);
+      const float pj = exp2f(s - m_new);
+      const float alpha = exp2f(m_old - m_new);
+      float sum = pj;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      if (live) {
+        sP[r][j] = pj;
+        if (j == 0) {
+          sM[r] = m_new;
+          sZ[r] = alpha * sZ[r] + sum;
+          sA[r] = alpha;
+        }
+      }
+    }
+    __syncthreads();
+
+    // u update: thread owns (row, feature) pairs; both z (above) and u
+    // (here) are rescaled by the same alpha.
+#pragma unroll
+    for (int i = 0; i < kAcc; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx < rows * D) {
+        const int r = idx / D, f = idx % D;
+        float add = 0.0f;
+#pragma unroll 8
+        for (int j = 0; j < kTile; ++j) add = fmaf(sP[r][j], sV[j][f], add);
+        acc[i] = fmaf(sA[r], acc[i], add);
+      }
+    }
+    __syncthreads();
+  }
+
+  const long long row0 = bh * rows;
+  if (p.splits == 1) {
+#pragma unroll
+    for (int i = 0; i < kAcc; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx < rows * D) {
+        const int r = idx / D;
+        p.out[(row0 + r) * D + idx % D] = acc[i] / sZ[r];
+      }
+    }
+  } else {
+    const long long total_rows = static_cast<long long>(p.B) * p.Hkv * rows;
+    const long long base = static_cast<long long>(split) * total_rows + row0;
+#pragma unroll
+    for (int i = 0; i < kAcc; ++i) {
+      const int idx = tid + i * kThreads;
+      if (idx < rows * D) p.part_u[base * D + idx] = acc[i];
+    }
+    for (int r = tid; r < rows; r += kThreads) {
+      p.part_m[base + r] = sM[r];
+      p.part_z[base + r] = sZ[r];
+    }
+  }
+}
+
+// Merge the per-split (m, z, u) of one row ([RL] "two stops of the online
+// accumulation": partial statistics compose once brought to one base):
+//   M = max_s m_s,  Z = sum_s 2^(m_s - M) z_s,  U = sum_s 2^(m_s - M) u_s.
+// Splits that saw no token carry m = -inf and are skipped.  One thread per
+// (row, feature).
+__global__ __launch_bounds__(kThreads) void combine_kernel(AttendProblem p) {
+  const long long total_rows = static_cast<long long>(p.B) * p.Hkv * p.rows;
+  const long long tid = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+  if (tid >= total_rows * p.D) return;
+  const long long row = tid / p.D;
+  float big_m = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) big_m = fmaxf(big_m, p.part_m[s * total_rows + row]);
+  float z = 0.0f, u = 0.0f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float m = p.part_m[s * total_rows + row];
+    if (m == -INFINITY) continue;
+    const float w = exp2f(m - big_m);
+    z = fmaf(w, p.part_z[s * total_rows + row], z);
+    u = fmaf(w, p.part_u[s * total_rows * p.D + tid], u);
+  }
+  p.out[tid] = u / z;
+}
+
+template <int D>
+hipError_t launch_valu_d(const AttendProblem& p, hipStream_t stream) {
+  const dim3 grid(p.splits, p.Hkv, p.B);
+  switch (p.bits) {
+    case 4: hipLaunchKernelGGL((attend_valu_kernel<D, 4>), grid, dim3(kThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((attend_valu_kernel<D, 8>), grid, dim3(kThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL((attend_valu_kernel<D, 32>), grid, dim3(kThreads), 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attend_valu(const AttendProblem& p, hipStream_t stream) {
+  hipError_t e;
+  switch (p.D) {
+    case 32: e = launch_valu_d<32>(p, stream); break;
+    case 64: e = launch_valu_d<64>(p, stream); break;
+    default: e = launch_valu_d<128>(p, stream); break;
+  }
+  if (e != hipSuccess || p.splits == 1) return e;
+  return launch_combine(p, stream);
+}
+
+hipError_t launch_combine(const AttendProblem& p, hipStream_t stream) {
+  const long long n = static_cast<long long>(p.B) * p.Hkv * p.rows * p.D;
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

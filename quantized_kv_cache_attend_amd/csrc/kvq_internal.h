@@ -1,0 +1,56 @@
+// Internal declarations shared by the library's translation units.
+// Not part of the public C ABI (that is include/kvq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kvq {
+
+// log2(e): scores are kept in base-2 units so the kernels can use exp2.
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Largest KV-head row count (GQA heads x queries) the kernels support.
+constexpr int kMaxRows = 64;
+
+// One attention problem after validation.
+struct AttendProblem {
+  const float* q;          // [B][Hq][R][D]
+  const uint8_t* k_codes;  // packed (or float32 for the float32-cache path)
+  const float* k_scales;
+  const uint8_t* v_codes;
+  const float* v_scales;
+  const float* k_f32;      // float32-cache path only
+  const float* v_f32;
+  float* out;              // [B][Hq][R][D]
+  int B, Hq, Hkv, R, N, D;
+  int rows;                // (Hq / Hkv) * R: query rows sharing one KV head
+  int bits, group;         // 4/8 and group; bits == 32 marks the float32 cache
+  float qscale;            // sm_scale * log2(e)
+  int splits;              // >= 1
+  int tokens_per_split;    // ceil(N / splits), rounded as the kernel requires
+  // Workspace views (valid when splits > 1).
+  float* part_m;           // [splits][B*Hkv*rows]
+  float* part_z;           // [splits][B*Hkv*rows]
+  float* part_u;           // [splits][B*Hkv*rows][D]
+  unsigned* counters;      // [B*Hkv]
+};
+
+// Workspace carving, shared by the sizing call and the launchers.
+struct WorkspaceLayout {
+  size_t m_off, z_off, u_off, cnt_off, total;
+};
+WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int R, int D, int splits);
+
+// Launchers (host functions; return the launch's hipError_t).
+hipError_t launch_pack(const float* x, int B, int H, int N, int D, int bits, int group,
+                       bool k_style, uint8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_dequant(const uint8_t* codes, const float* scales, int B, int H, int N, int D,
+                          int bits, int group, bool k_style, float* out, hipStream_t stream);
+hipError_t launch_attend_valu(const AttendProblem& p, hipStream_t stream);
+hipError_t launch_attend_mfma(const AttendProblem& p, hipStream_t stream);
+hipError_t launch_combine(const AttendProblem& p, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,123 @@
+"""Host-side tests of the C ABI that need no GPU: the library loads, exports
+every function include/kvq.h declares, sizes the packed arrays like the
+oracle does, and rejects bad arguments before any work reaches a device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import kvq_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+kvq = pytest.importorskip("quantized_kv_cache_attend_amd",
+                          reason="libkvq.so not built (python -m quantized_kv_cache_attend_amd.build)")
+lib = kvq.lib
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails validation first
+FAKE2 = ctypes.c_void_p(0x20000000)
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in kvq._SIGNATURES, f"binding lacks {name}"
+
+
+def test_abi_version_and_strings():
+    assert lib.kvq_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, 7):
+        assert lib.kvq_status_string(st)
+
+
+@pytest.mark.parametrize("N,D", [(128, 32), (512, 32), (35, 13), (1, 1), (4096, 128)])
+@pytest.mark.parametrize("bits,group", [(4, 8), (4, 32), (8, 8), (8, 32), (4, 2)])
+def test_sizes_match_oracle_arrays(N, D, bits, group):
+    x = np.zeros((2, 3, N, D), np.float32)
+    kc, ks = O.pack_k(x, bits, group)
+    vc, vs = O.pack_v(x, bits, group)
+    assert lib.kvq_k_code_bytes(2, 3, N, D, bits, group) == kc.nbytes
+    assert lib.kvq_k_scale_count(2, 3, N, D, bits, group) == ks.size
+    assert lib.kvq_v_code_bytes(2, 3, N, D, bits, group) == vc.nbytes
+    assert lib.kvq_v_scale_count(2, 3, N, D, bits, group) == vs.size
+    shapes = kvq.packed_shapes(2, 3, N, D, bits, group)
+    assert shapes == (kc.shape, ks.shape, vc.shape, vs.shape)
+
+
+def test_sizes_reject_bad_format():
+    assert lib.kvq_k_code_bytes(1, 1, 128, 32, 3, 32) == 0
+    assert lib.kvq_k_code_bytes(1, 1, 128, 32, 4, 7) == 0
+    assert lib.kvq_v_scale_count(1, 1, 0, 32, 4, 32) == 0
+
+
+def test_auto_splits_and_workspace():
+    # many workgroups for few heads, never splits shorter than 256 tokens
+    assert lib.kvq_attend_auto_splits(8, 8, 4096) == 16
+    assert lib.kvq_attend_auto_splits(1, 1, 128) == 1
+    assert lib.kvq_attend_auto_splits(1, 1, 1024) == 4
+    assert lib.kvq_attend_auto_splits(16, 8, 32768) == 8
+    w1 = lib.kvq_attend_workspace_bytes(8, 32, 8, 1, 4096, 128, 16)
+    rows = 8 * 32 * 1
+    assert w1 >= 16 * rows * (128 + 2) * 4 + 8 * 8 * 4
+    assert w1 % 256 == 0
+    assert lib.kvq_attend_workspace_bytes(8, 32, 8, 1, 4096, 128, 0) == w1
+
+
+def _attend(**kw):
+    a = dict(q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, B=1, Hq=4, Hkv=2, R=1, N=64, D=32,
+             bits=4, group=32, sm=0.0, splits=1, ws=None, wsb=0, out=FAKE2, variant=0)
+    a.update(kw)
+    return lib.kvq_attend_variant(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["B"], a["Hq"],
+                                  a["Hkv"], a["R"], a["N"], a["D"], a["bits"], a["group"],
+                                  a["sm"], a["splits"], a["ws"], a["wsb"], a["out"], a["variant"],
+                                  None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), kvq.KVQ_ERR_INVALID),
+    (dict(N=0), kvq.KVQ_ERR_INVALID),
+    (dict(Hq=3), kvq.KVQ_ERR_INVALID),
+    (dict(bits=5), kvq.KVQ_ERR_INVALID),
+    (dict(group=7), kvq.KVQ_ERR_INVALID),
+    (dict(splits=-1), kvq.KVQ_ERR_INVALID),
+    (dict(sm=float("nan")), kvq.KVQ_ERR_INVALID),
+    (dict(out=FAKE), kvq.KVQ_ERR_INVALID),                    # aliases q
+    (dict(q=ctypes.c_void_p(0x10002)), kvq.KVQ_ERR_INVALID),  # misaligned float pointer
+    (dict(D=48), kvq.KVQ_ERR_UNSUPPORTED),
+    (dict(Hq=128, Hkv=1), kvq.KVQ_ERR_UNSUPPORTED),          # 128 rows per KV head
+    (dict(splits=4), kvq.KVQ_ERR_WORKSPACE),                 # no workspace
+    (dict(splits=4, ws=ctypes.c_void_p(0x40000000), wsb=64), kvq.KVQ_ERR_WORKSPACE),
+    (dict(variant=9), kvq.KVQ_ERR_INVALID),
+    (dict(variant=2, bits=8), kvq.KVQ_ERR_UNSUPPORTED),      # matrix-core kernel is 4-bit g32 D128
+])
+def test_attend_rejects_before_launch(kw, status):
+    assert _attend(**kw) == status
+    assert lib.kvq_last_error()
+
+
+def test_codec_rejects_before_launch():
+    for fn in (lib.kvq_pack_k, lib.kvq_pack_v):
+        assert fn(None, 1, 1, 8, 8, 4, 8, FAKE, FAKE2, None) == kvq.KVQ_ERR_INVALID
+        assert fn(FAKE, 1, 1, 8, 8, 4, 3, FAKE, FAKE2, None) == kvq.KVQ_ERR_INVALID
+        assert fn(FAKE, 1, 0, 8, 8, 4, 8, FAKE, FAKE2, None) == kvq.KVQ_ERR_INVALID
+    for fn in (lib.kvq_dequant_k, lib.kvq_dequant_v):
+        assert fn(FAKE, None, 1, 1, 8, 8, 4, 8, FAKE2, None) == kvq.KVQ_ERR_INVALID
+        assert fn(FAKE, FAKE2, 1, 1, 8, 8, 6, 8, FAKE2, None) == kvq.KVQ_ERR_INVALID
+
+
+def test_attend_f32_rejects_before_launch():
+    assert lib.kvq_attend_f32(FAKE, FAKE, None, 1, 1, 1, 1, 8, 32, 0.0, 1, None, 0, FAKE2,
+                              None) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_attend_f32(FAKE, FAKE, FAKE, 1, 1, 1, 1, 8, 96, 0.0, 1, None, 0, FAKE2,
+                              None) == kvq.KVQ_ERR_UNSUPPORTED

@@ -1,0 +1,144 @@
+"""GPU parity of kvq_attend (and the decode-all baseline) against the float64
+oracle on the same quantized cache: max abs error <= 1e-4."""
+import numpy as np
+import pytest
+
+from oracle import kvq_oracle as O
+from workloads import WORKLOADS, Workload, make_qkv
+
+from gpu_helpers import announce, dev, host, max_abs, oracle_pack
+
+pytestmark = pytest.mark.gpu
+
+kvq = pytest.importorskip("quantized_kv_cache_attend_amd")
+
+TOL = 1e-4          # max abs error vs the float64 oracle (unit-variance inputs)
+SPLIT_TOL = 2e-5    # between split counts / kernels on the GPU
+
+
+def _gpu_cache(k, v, bits, group):
+    gkc, gks = kvq.pack_k(dev(k), bits, group)
+    gvc, gvs = kvq.pack_v(dev(v), bits, group)
+    return gkc, gks, gvc, gvs
+
+
+def _run(q, cache, n, bits, group, **kw):
+    return host(kvq.attend(dev(q), *cache, n, bits, group, **kw))
+
+
+def _oracle(q, k, v, bits, group):
+    kc, ks, vc, vs = oracle_pack(k, v, bits, group)
+    return O.attend_packed(q, kc, ks, vc, vs, k.shape[2], bits, group)
+
+
+VARIANTS = ["valu"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("name,bits,group,dist", [
+    ("single_n128", 4, 32, "clean"),
+    ("single_n512", 4, 8, "clean"), ("single_n512", 4, 32, "clean"),
+    ("single_n512", 8, 8, "clean"), ("single_n512", 8, 32, "clean"),
+    ("single_n1024", 4, 8, "clean"), ("single_n1024", 4, 8, "early"),
+    ("single_n1024", 4, 8, "late"),
+])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_attend_small_workloads(name, bits, group, dist, seed, variant):
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w, seed, dist)
+    announce(f"attend {name}/{dist} seed={seed} {bits}b g{group} {variant}")
+    want = _oracle(q, k, v, bits, group)
+    cache = _gpu_cache(k, v, bits, group)
+    for splits in (1, 2, 0):
+        got = _run(q, cache, w.N, bits, group, num_splits=splits, variant=variant)
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_float32_cache_and_decode_all(seed):
+    """The float32-cache reference and decode-all (dequant + attend_f32)."""
+    w = WORKLOADS["single_n512"]
+    q, k, v = make_qkv(w, seed)
+    announce(f"attend_f32 single_n512 seed={seed}")
+    got = host(kvq.attend_f32(dev(q), dev(k), dev(v)))
+    assert max_abs(got, O.attend_dense(q, k, v)) <= TOL
+    for bits, group in w.formats:
+        gkc, gks, gvc, gvs = _gpu_cache(k, v, bits, group)
+        kd = kvq.dequant_k(gkc, gks, w.N, w.D, bits, group)
+        vd = kvq.dequant_v(gvc, gvs, w.N, w.D, bits, group)
+        got = host(kvq.attend_f32(dev(q), kd, vd, num_splits=3))
+        assert max_abs(got, _oracle(q, k, v, bits, group)) <= TOL
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_attend_gqa_n4096_full(variant):
+    w = WORKLOADS["gqa_n4096"]
+    q, k, v = make_qkv(w, 0)
+    announce(f"attend gqa_n4096 full {variant}")
+    want = _oracle(q, k, v, 4, 32)
+    cache = _gpu_cache(k, v, 4, 32)
+    outs = {}
+    for splits in (1, 2, 16, 0):
+        outs[splits] = _run(q, cache, w.N, 4, 32, num_splits=splits, variant=variant)
+        assert max_abs(outs[splits], want) <= TOL, (splits, max_abs(outs[splits], want))
+    for s in (1, 2, 16):
+        assert max_abs(outs[s], outs[0]) <= SPLIT_TOL
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("seed", [0, 1])
+def test_attend_gqa_n32768_sampled(variant, seed):
+    """Full-size long-context workload (16 splits).  The GPU attends over the
+    whole cache; the oracle recomputes every query row of sampled KV heads."""
+    w = WORKLOADS["gqa_n32768"]
+    q, k, v = make_qkv(w, seed)
+    announce(f"attend gqa_n32768 full seed={seed} {variant}")
+    cache = _gpu_cache(k, v, 4, 32)
+    got = _run(q, cache, w.N, 4, 32, num_splits=w.num_splits, variant=variant)
+    rep = w.Hq // w.Hkv
+    for b, h in ((0, 0), (5, 6), (15, 7)):
+        qs = q[b:b + 1, h * rep:(h + 1) * rep]
+        want = _oracle(qs, k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], 4, 32)
+        assert max_abs(got[b:b + 1, h * rep:(h + 1) * rep], want) <= TOL
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("n", [1, 7, 35, 1021, 4097])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_attend_ragged_tokens(n, d, variant):
+    w = Workload("ragged", 2, 8, 2, 2, n, d, ((4, 32),))
+    q, k, v = make_qkv(w, 3)
+    announce(f"attend ragged n={n} d={d} {variant}")
+    want = _oracle(q, k, v, 4, 32)
+    cache = _gpu_cache(k, v, 4, 32)
+    for splits in (1, 3, 0, 64):
+        got = _run(q, cache, n, 4, 32, num_splits=splits, variant=variant)
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
+
+
+def test_attend_sm_scale_and_peaky_scores():
+    """Explicit temperature, and large scores that need the max shift."""
+    w = WORKLOADS["single_n512"]
+    q, k, v = make_qkv(w, 2)
+    announce("attend sm_scale")
+    cache = _gpu_cache(k, v, 4, 32)
+    kc, ks, vc, vs = oracle_pack(k, v, 4, 32)
+    for sm in (0.05, 1.0, 3.0):
+        got = _run(q, cache, w.N, 4, 32, sm_scale=sm, num_splits=4)
+        want = O.attend_packed(q, kc, ks, vc, vs, w.N, 4, 32, sm_scale=sm)
+        assert np.all(np.isfinite(got))
+        assert max_abs(got, want) <= TOL
+
+
+def test_attend_deterministic_and_counters_reset():
+    w = WORKLOADS["gqa_n4096"]
+    q, k, v = make_qkv(w, 1)
+    announce("attend determinism")
+    cache = _gpu_cache(k, v, 4, 32)
+    ws = kvq.new_workspace(w.B, w.Hq, w.Hkv, w.R, w.N, w.D, 0)
+    a = _run(q, cache, w.N, 4, 32, workspace=ws)
+    b = _run(q, cache, w.N, 4, 32, workspace=ws)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    # the arrival counters sit in the last 256-byte-aligned block of the workspace
+    tail = host(ws)[-256:]
+    assert not tail.any()

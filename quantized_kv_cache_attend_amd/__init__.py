@@ -7,11 +7,19 @@ current stream.  The names follow the C ABI in ``include/kvq.h``.
 Importing this package loads ``libkvq.so`` and raises ``ImportError`` if it
 has not been built (``python -m quantized_kv_cache_attend_amd.build``); there
 is no fallback path.
+
+torch is imported first: PyTorch-ROCm ships its own HIP runtime, and loading
+it before ``libkvq.so`` makes the library bind to that same runtime (both
+carry the soname libamdhip64.so.7), so streams and device pointers from torch
+are valid in the library's launches.  Loading the system runtime first would
+put a second HIP runtime under torch.
 """
 from __future__ import annotations
 
 import ctypes
 import os
+
+import torch  # noqa: F401  (must precede the CDLL below)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")

@@ -67,11 +67,13 @@ using namespace kvq;
 namespace {
 
 int auto_splits(int B, int Hkv, int N) {
-  // Enough workgroups to cover the 256 compute units several times over,
-  // but never splits shorter than 256 tokens.
+  // About 512 workgroups: two per compute unit, all resident at once, so
+  // every KV byte's load can be in flight early; and no split shorter than
+  // 512 tokens, so each workgroup streams at least two 256-token tiles and
+  // overlaps the second tile's loads with the first tile's math.
   const long long heads = static_cast<long long>(B) * Hkv;
-  const long long want = (1024 + heads - 1) / heads;
-  const long long cap = (N + 255) / 256;
+  const long long want = (512 + heads - 1) / heads;
+  const long long cap = (N + 511) / 512;
   long long s = want < cap ? want : cap;
   if (s < 1) s = 1;
   if (s > 1024) s = 1024;
@@ -166,8 +168,14 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
 }
 
 bool mfma_eligible(const AttendProblem& p) {
-  (void)p;
-  return false;
+  return p.bits == 4 && p.group == 32 && p.D == 128 && p.rows <= kMfmaMaxRows &&
+         aligned(p.q, 16) && aligned(p.k_codes, 16) && aligned(p.v_codes, 16) &&
+         aligned(p.v_scales, 16);
+}
+
+hipError_t run_mfma(AttendProblem p, hipStream_t s) {
+  p.tokens_per_split = mfma_tokens_per_split(p.N, p.splits);
+  return launch_attend_mfma(p, s);
 }
 
 kvq_status codec_check(const void* a, const void* b, const void* c, int B, int H, int N, int D,
@@ -261,16 +269,16 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
   const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
     case KVQ_VARIANT_AUTO:
-      if (mfma_eligible(p)) return hip_status(launch_attend_mfma(p, s), "attend (mfma) launch");
+      if (mfma_eligible(p)) return hip_status(run_mfma(p, s), "attend (mfma) launch");
       return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
     case KVQ_VARIANT_VALU:
       return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
     case KVQ_VARIANT_MFMA:
       if (!mfma_eligible(p))
         return fail(KVQ_ERR_UNSUPPORTED,
-                    "matrix-core kernel needs bits=4, group=32, D=128, <= 32 rows per KV head "
-                    "and 16-byte aligned codes/scales");
-      return hip_status(launch_attend_mfma(p, s), "attend (mfma) launch");
+                    "matrix-core kernel needs bits=4, group=32, D=128, <= %d query rows per "
+                    "KV head and 16-byte aligned q, codes and V scales", kMfmaMaxRows);
+      return hip_status(run_mfma(p, s), "attend (mfma) launch");
     default:
       return fail(KVQ_ERR_INVALID, "unknown variant %d", variant);
   }

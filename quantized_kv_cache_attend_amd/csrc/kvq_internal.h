@@ -51,6 +51,10 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scales, int B, int 
                           int bits, int group, bool k_style, float* out, hipStream_t stream);
 hipError_t launch_attend_valu(const AttendProblem& p, hipStream_t stream);
 hipError_t launch_attend_mfma(const AttendProblem& p, hipStream_t stream);
+// Query rows per KV head the matrix-core kernel handles, and its split
+// granularity (tokens per split rounded up to whole 256-token tiles).
+constexpr int kMfmaMaxRows = 4;
+int mfma_tokens_per_split(int N, int splits);
 hipError_t launch_combine(const AttendProblem& p, hipStream_t stream);
 
 }  // namespace kvq

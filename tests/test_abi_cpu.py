@@ -62,14 +62,15 @@ def test_sizes_reject_bad_format():
 
 
 def test_auto_splits_and_workspace():
-    # many workgroups for few heads, never splits shorter than 256 tokens
-    assert lib.kvq_attend_auto_splits(8, 8, 4096) == 16
+    # about 512 workgroups, never splits shorter than 512 tokens
+    assert lib.kvq_attend_auto_splits(8, 8, 4096) == 8
     assert lib.kvq_attend_auto_splits(1, 1, 128) == 1
-    assert lib.kvq_attend_auto_splits(1, 1, 1024) == 4
-    assert lib.kvq_attend_auto_splits(16, 8, 32768) == 8
-    w1 = lib.kvq_attend_workspace_bytes(8, 32, 8, 1, 4096, 128, 16)
+    assert lib.kvq_attend_auto_splits(1, 1, 1024) == 2
+    assert lib.kvq_attend_auto_splits(1, 1, 1 << 20) == 512
+    assert lib.kvq_attend_auto_splits(16, 8, 32768) == 4
+    w1 = lib.kvq_attend_workspace_bytes(8, 32, 8, 1, 4096, 128, 8)
     rows = 8 * 32 * 1
-    assert w1 >= 16 * rows * (128 + 2) * 4 + 8 * 8 * 4
+    assert w1 >= 8 * rows * (128 + 2) * 4 + 8 * 8 * 4
     assert w1 % 256 == 0
     assert lib.kvq_attend_workspace_bytes(8, 32, 8, 1, 4096, 128, 0) == w1
 

@@ -31,7 +31,8 @@ def _oracle(q, k, v, bits, group):
     return O.attend_packed(q, kc, ks, vc, vs, k.shape[2], bits, group)
 
 
-VARIANTS = ["valu"]
+VARIANTS = ["valu"]                 # head dim 32 or > 4 rows per KV head: VALU kernel only
+MFMA_VARIANTS = ["valu", "mfma", "auto"]  # 4-bit g32 D=128 with <= 4 rows per KV head
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -70,7 +71,7 @@ def test_float32_cache_and_decode_all(seed):
         assert max_abs(got, _oracle(q, k, v, bits, group)) <= TOL
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", MFMA_VARIANTS)
 def test_attend_gqa_n4096_full(variant):
     w = WORKLOADS["gqa_n4096"]
     q, k, v = make_qkv(w, 0)
@@ -130,15 +131,55 @@ def test_attend_sm_scale_and_peaky_scores():
         assert max_abs(got, want) <= TOL
 
 
-def test_attend_deterministic_and_counters_reset():
+@pytest.mark.parametrize("variant", MFMA_VARIANTS)
+def test_attend_deterministic_and_counters_reset(variant):
     w = WORKLOADS["gqa_n4096"]
     q, k, v = make_qkv(w, 1)
-    announce("attend determinism")
+    announce(f"attend determinism {variant}")
     cache = _gpu_cache(k, v, 4, 32)
     ws = kvq.new_workspace(w.B, w.Hq, w.Hkv, w.R, w.N, w.D, 0)
-    a = _run(q, cache, w.N, 4, 32, workspace=ws)
-    b = _run(q, cache, w.N, 4, 32, workspace=ws)
+    a = _run(q, cache, w.N, 4, 32, workspace=ws, variant=variant)
+    b = _run(q, cache, w.N, 4, 32, workspace=ws, variant=variant)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     # the arrival counters sit in the last 256-byte-aligned block of the workspace
     tail = host(ws)[-256:]
     assert not tail.any()
+
+
+@pytest.mark.parametrize("hq,hkv,r", [(8, 2, 1), (2, 2, 3), (1, 1, 1), (4, 1, 1), (6, 3, 2)])
+@pytest.mark.parametrize("n", [1, 7, 35, 1021, 4097])
+def test_attend_mfma_ragged_and_gqa_shapes(hq, hkv, r, n):
+    """Matrix-core kernel: 1..4 query rows per KV head, ragged token counts,
+    empty trailing splits."""
+    w = Workload("mfma", 2, hq, hkv, r, n, 128, ((4, 32),))
+    q, k, v = make_qkv(w, 4)
+    announce(f"attend mfma hq={hq} hkv={hkv} r={r} n={n}")
+    want = _oracle(q, k, v, 4, 32)
+    cache = _gpu_cache(k, v, 4, 32)
+    for splits in (1, 3, 0, 64):
+        got = _run(q, cache, n, 4, 32, num_splits=splits, variant="mfma")
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
+
+
+@pytest.mark.parametrize("dist", ["clean", "early", "late"])
+@pytest.mark.parametrize("scale_k", [False, True])
+def test_attend_mfma_peaky_and_channel_scaled(dist, scale_k):
+    """Biased keys (+4 sigma on 16 tokens) and log-uniform K channel scales
+    concentrate the softmax: the hi/lo fp16 split must hold 1e-4 there."""
+    w = Workload("peaky", 4, 16, 4, 1, 4096, 128, ((4, 32),), k_channel_scale=scale_k)
+    q, k, v = make_qkv(w, 5, dist)
+    announce(f"attend mfma peaky dist={dist} scale_k={scale_k}")
+    want = _oracle(q, k, v, 4, 32)
+    cache = _gpu_cache(k, v, 4, 32)
+    for splits in (1, 0):
+        got = _run(q, cache, w.N, 4, 32, num_splits=splits, variant="mfma")
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
+
+
+def test_attend_mfma_rejects_unsupported():
+    w = WORKLOADS["single_n128"]
+    q, k, v = make_qkv(w, 0)
+    cache = _gpu_cache(k, v, 4, 32)
+    with pytest.raises(kvq.KvqError) as e:
+        _run(q, cache, w.N, 4, 32, variant="mfma")
+    assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED

@@ -17,14 +17,30 @@
  *     (qmax = 7 for 4-bit, 127 for 8-bit); a scale that comes out 0 is 1;
  *   - codes are rint(x/scale) (round half to even, IEEE float32 division)
  *     clipped to [-qmax, qmax] and stored unsigned as code + qmax;
- *   - 4-bit: element 2i of a row goes to the low nibble, 2i+1 to the high
- *     nibble of byte i; 8-bit: one byte per code;
- *   - K ([B,H,N,D] float32) is grouped along tokens inside each channel:
- *       K codes  [B][H][D][Npad*bits/8]  uint8,  K scales [B][H][D][Npad/group] float32
- *   - V ([B,H,N,D] float32) is grouped along features inside each token:
- *       V codes  [B][H][N][Dpad*bits/8]  uint8,  V scales [B][H][N][Dpad/group] float32
- *   where Npad, Dpad round N, D up to a multiple of `group`; padding
- *   elements are zeros before quantization (stored code = qmax).
+ *   - 4-bit: a byte holds two neighbouring elements of one group, the
+ *     lower-indexed in the low nibble; 8-bit: one byte per code;
+ *   - K ([B,H,N,D] float32) is grouped along tokens inside each channel,
+ *     V ([B,H,N,D] float32) along features inside each token; padding
+ *     elements are zeros before quantization (stored code = qmax).
+ *
+ * Byte layout (the pages fix the groups and the byte contents, not the byte
+ * order; this one lets the kernels read whole 32-token blocks with
+ * contiguous loads that land in registers in matrix-core operand order).
+ * Per (b, h): nblocks = ceil(N/32) blocks of 32 tokens; every position that
+ * holds no element (token >= N, channel >= D, feature past the last group)
+ * stores the zero code qmax.  With kcols = 32*bits/8, D8 = ceil(D/8),
+ * Dpad = D rounded up to `group` and vcols = Dpad*bits/8:
+ *   K codes  [B][H][nblocks][D8*kcols*8] uint8: in a block, byte
+ *            (o*kcols + j)*8 + e holds channel 8o+e of byte column j; a
+ *            4-bit column j holds tokens 2j (low nibble) and 2j+1 (high),
+ *            an 8-bit column j token j.
+ *   K scales [B][H][ceil(N/group)][D] float32 (group-major).
+ *   V codes  [B][H][nblocks][4*vcols*8] uint8: in a block, byte
+ *            (o*vcols + f)*8 + e holds token 8o+e (o < 4) of byte column f;
+ *            a 4-bit column f holds features 2f (low) and 2f+1 (high), an
+ *            8-bit column f feature f.
+ *   V scales [B][H][nblocks][Dpad/group][32] float32 (token-minor; tokens
+ *            >= N carry scale 1, the scale of an all-zero group).
  *
  * Conventions for every call:
  *   - All array pointers are DEVICE pointers to dense row-major arrays in
@@ -68,10 +84,10 @@ typedef enum kvq_variant {
 /* ---- host-only sizing (no device work, never fails) ------------------------
  * Byte / element counts of the packed arrays; 0 if an argument is invalid
  * (size < 1, bits not 4 or 8, group odd or < 2). */
-size_t kvq_k_code_bytes(int B, int H, int N, int D, int bits, int group);  /* B*H*D*Npad*bits/8 */
-size_t kvq_k_scale_count(int B, int H, int N, int D, int bits, int group); /* B*H*D*Npad/group  */
-size_t kvq_v_code_bytes(int B, int H, int N, int D, int bits, int group);  /* B*H*N*Dpad*bits/8 */
-size_t kvq_v_scale_count(int B, int H, int N, int D, int bits, int group); /* B*H*N*Dpad/group  */
+size_t kvq_k_code_bytes(int B, int H, int N, int D, int bits, int group);  /* B*H*nblocks*D8*32*bits */
+size_t kvq_k_scale_count(int B, int H, int N, int D, int bits, int group); /* B*H*ceil(N/group)*D */
+size_t kvq_v_code_bytes(int B, int H, int N, int D, int bits, int group);  /* B*H*nblocks*32*Dpad*bits/8 */
+size_t kvq_v_scale_count(int B, int H, int N, int D, int bits, int group); /* B*H*nblocks*(Dpad/group)*32 */
 
 /* Number of KV splits kvq_attend uses when num_splits == 0 ([RL] "two stops
  * of the online accumulation": per-split (m, z, u) are composable). */
@@ -134,9 +150,8 @@ kvq_status kvq_attend(const float* q, const uint8_t* k_codes, const float* k_sca
 
 /* Same contract as kvq_attend with an explicit kernel family.
  * KVQ_VARIANT_MFMA returns KVQ_ERR_UNSUPPORTED unless bits == 4,
- * group == 32, D == 128, (Hq/Hkv)*R <= 4 and q, k_codes, v_codes and
- * v_scales are 16-byte aligned; KVQ_VARIANT_AUTO picks it whenever those
- * hold. */
+ * group == 32, D == 128, (Hq/Hkv)*R <= 4 and q and all four cache arrays
+ * are 16-byte aligned; KVQ_VARIANT_AUTO picks it whenever those hold. */
 kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,
                               const uint8_t* v_codes, const float* v_scales,
                               int B, int Hq, int Hkv, int R, int N, int D, int bits, int group,

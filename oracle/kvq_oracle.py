@@ -211,6 +211,81 @@ def dequant_v(codes, scales, shape, bits, group):
 
 
 # ---------------------------------------------------------------------------
+# Byte order in device memory
+# ---------------------------------------------------------------------------
+#
+# The pages fix the groups, the scales and what one byte holds ([KPG] "what a
+# byte holds": two neighbouring codes of one group, the lower-indexed one in
+# the low nibble) but not the order of the bytes.  The library stores the
+# cache in 32-token blocks (the byte order documented in include/kvq.h); the
+# two functions below state that order with NumPy reshapes, starting from the
+# canonical arrays above, so device packing can be compared byte for byte.
+# Positions that hold no element store the zero code QMAX; V scales of
+# tokens past N are 1, the scale of an all-zero group ([KPG] "exercises and
+# common mistakes").
+
+BLOCK_TOKENS = 32
+
+
+def store_k(codes: np.ndarray, scales: np.ndarray, n: int, d: int, bits: int, group: int):
+    """Canonical packed K (``pack_k``) -> block layout.
+
+    Codes become ``[..., nblocks, D8*kcols*8]``: inside a block the byte
+    ``(o*kcols + j)*8 + e`` holds channel ``8o+e`` of byte column ``j``, a
+    4-bit column ``j`` pairing tokens ``2j`` (low nibble) and ``2j+1``
+    (high), an 8-bit column ``j`` being token ``j``.  Scales become
+    group-major ``[..., ceil(N/group), D]``.
+    """
+    _check_format(bits, group)
+    lead = codes.shape[:-2]
+    stored = unpack_stored(codes, lead + (n, d), -2, bits, group)      # [..., N, D]
+    nb, d8 = -(-n // BLOCK_TOKENS), -(-d // 8)
+    full = np.full(lead + (nb * BLOCK_TOKENS, d8 * 8), QMAX[bits], np.uint8)
+    full[..., :n, :d] = stored
+    tok = full.reshape(lead + (nb, BLOCK_TOKENS, d8, 8))                # [..., blk, t, o, e]
+    if bits == 4:
+        pairs = tok.reshape(lead + (nb, BLOCK_TOKENS // 2, 2, d8, 8))
+        cols = pairs[..., 0, :, :] | (pairs[..., 1, :, :] << 4)         # [..., blk, j, o, e]
+    else:
+        cols = tok
+    blocks = np.moveaxis(cols, -2, -3)                                  # [..., blk, o, j, e]
+    k_store = np.ascontiguousarray(blocks).reshape(lead + (nb, -1))
+    s_store = np.ascontiguousarray(np.swapaxes(np.asarray(scales, np.float32), -1, -2))
+    return k_store, s_store
+
+
+def store_v(codes: np.ndarray, scales: np.ndarray, n: int, d: int, bits: int, group: int):
+    """Canonical packed V (``pack_v``) -> block layout.
+
+    Codes become ``[..., nblocks, 4*vcols*8]``: inside a block the byte
+    ``(o*vcols + f)*8 + e`` holds token ``8o+e`` of byte column ``f``, a
+    4-bit column ``f`` pairing features ``2f`` (low) and ``2f+1`` (high).
+    Scales become ``[..., nblocks, Dpad/group * 32]``, token-minor.
+    """
+    _check_format(bits, group)
+    lead = codes.shape[:-2]
+    stored = unpack_stored(codes, lead + (n, d), -1, bits, group)      # [..., N, D]
+    nb = -(-n // BLOCK_TOKENS)
+    dpad = -(-d // group) * group
+    full = np.full(lead + (nb * BLOCK_TOKENS, dpad), QMAX[bits], np.uint8)
+    full[..., :n, :d] = stored
+    tok = full.reshape(lead + (nb, 4, 8, dpad))                         # [..., blk, o, e, f]
+    if bits == 4:
+        pairs = tok.reshape(lead + (nb, 4, 8, dpad // 2, 2))
+        cols = pairs[..., 0] | (pairs[..., 1] << 4)                     # [..., blk, o, e, col]
+    else:
+        cols = tok
+    blocks = np.swapaxes(cols, -1, -2)                                  # [..., blk, o, col, e]
+    v_store = np.ascontiguousarray(blocks).reshape(lead + (nb, -1))
+    sc = np.asarray(scales, np.float32)
+    padded = np.ones(lead + (nb * BLOCK_TOKENS, sc.shape[-1]), np.float32)
+    padded[..., :n, :] = sc
+    per_block = padded.reshape(lead + (nb, BLOCK_TOKENS, sc.shape[-1]))
+    s_store = np.ascontiguousarray(np.swapaxes(per_block, -1, -2)).reshape(lead + (nb, -1))
+    return v_store, s_store
+
+
+# ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
 

@@ -105,11 +105,13 @@ def _need(t, dtype, name):
 # --- sizing -------------------------------------------------------------------------
 
 def packed_shapes(B, H, N, D, bits, group):
-    """Shapes of (k_codes, k_scales, v_codes, v_scales) for K/V of [B,H,N,D]."""
-    npad = -(-N // group) * group
+    """Shapes of (k_codes, k_scales, v_codes, v_scales) for K/V of [B,H,N,D]
+    in the 32-token block layout of include/kvq.h."""
+    nblocks = -(-N // 32)
+    d8 = -(-D // 8)
     dpad = -(-D // group) * group
-    return ((B, H, D, npad * bits // 8), (B, H, D, npad // group),
-            (B, H, N, dpad * bits // 8), (B, H, N, dpad // group))
+    return ((B, H, nblocks, d8 * 8 * 32 * bits // 8), (B, H, -(-N // group), D),
+            (B, H, nblocks, 32 * dpad * bits // 8), (B, H, nblocks, dpad // group * 32))
 
 
 def workspace_bytes(B, Hq, Hkv, R, N, D, num_splits=0) -> int:
@@ -143,12 +145,12 @@ def _pack(fn, x, bits, group, k_style):
 
 
 def pack_k(k, bits=4, group=32):
-    """Pack float32 K [B,H,N,D] -> (codes [B,H,D,Npad*bits/8] u8, scales [B,H,D,Npad/g] f32)."""
+    """Pack float32 K [B,H,N,D] -> (codes u8, scales f32) in the block layout."""
     return _pack(lib.kvq_pack_k, k, bits, group, True)
 
 
 def pack_v(v, bits=4, group=32):
-    """Pack float32 V [B,H,N,D] -> (codes [B,H,N,Dpad*bits/8] u8, scales [B,H,N,Dpad/g] f32)."""
+    """Pack float32 V [B,H,N,D] -> (codes u8, scales f32) in the block layout."""
     return _pack(lib.kvq_pack_v, v, bits, group, False)
 
 

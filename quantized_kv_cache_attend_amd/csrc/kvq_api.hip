@@ -4,6 +4,7 @@
 // message.
 #include "kvq.h"
 #include "kvq_internal.h"
+#include "kvq_layout.h"
 
 #include <cmath>
 #include <cstdarg>
@@ -114,11 +115,11 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   if (bits == 32) {
     kb = vb = sizeof(float) * static_cast<size_t>(BH) * N * D;
   } else {
-    const long long npad = round_up(N, group), dpad = round_up(D, group);
-    kb = static_cast<size_t>(BH * D * npad * bits / 8);
-    vb = static_cast<size_t>(BH * N * dpad * bits / 8);
-    ksb = sizeof(float) * static_cast<size_t>(BH * D * (npad / group));
-    vsb = sizeof(float) * static_cast<size_t>(BH * N * (dpad / group));
+    const Layout L = make_layout(N, D, bits, group);
+    kb = static_cast<size_t>(BH * k_code_bytes_per_head(L));
+    vb = static_cast<size_t>(BH * v_code_bytes_per_head(L));
+    ksb = sizeof(float) * static_cast<size_t>(BH * k_scales_per_head(L));
+    vsb = sizeof(float) * static_cast<size_t>(BH * v_scales_per_head(L));
   }
   if (overlaps(out, out_bytes, q, out_bytes) || overlaps(out, out_bytes, k, kb) ||
       overlaps(out, out_bytes, v, vb) || (ksb && overlaps(out, out_bytes, ks, ksb)) ||
@@ -170,7 +171,7 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
 bool mfma_eligible(const AttendProblem& p) {
   return p.bits == 4 && p.group == 32 && p.D == 128 && p.rows <= kMfmaMaxRows &&
          aligned(p.q, 16) && aligned(p.k_codes, 16) && aligned(p.v_codes, 16) &&
-         aligned(p.v_scales, 16);
+         aligned(p.k_scales, 16) && aligned(p.v_scales, 16);
 }
 
 hipError_t run_mfma(AttendProblem p, hipStream_t s) {
@@ -195,19 +196,19 @@ extern "C" {
 
 size_t kvq_k_code_bytes(int B, int H, int N, int D, int bits, int group) {
   if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
-  return static_cast<size_t>(B) * H * D * round_up(N, group) * bits / 8;
+  return static_cast<size_t>(B) * H * k_code_bytes_per_head(make_layout(N, D, bits, group));
 }
 size_t kvq_k_scale_count(int B, int H, int N, int D, int bits, int group) {
   if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
-  return static_cast<size_t>(B) * H * D * (round_up(N, group) / group);
+  return static_cast<size_t>(B) * H * k_scales_per_head(make_layout(N, D, bits, group));
 }
 size_t kvq_v_code_bytes(int B, int H, int N, int D, int bits, int group) {
   if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
-  return static_cast<size_t>(B) * H * N * round_up(D, group) * bits / 8;
+  return static_cast<size_t>(B) * H * v_code_bytes_per_head(make_layout(N, D, bits, group));
 }
 size_t kvq_v_scale_count(int B, int H, int N, int D, int bits, int group) {
   if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
-  return static_cast<size_t>(B) * H * N * (round_up(D, group) / group);
+  return static_cast<size_t>(B) * H * v_scales_per_head(make_layout(N, D, bits, group));
 }
 
 int kvq_attend_auto_splits(int B, int Hkv, int N) {
@@ -317,6 +318,6 @@ const char* kvq_status_string(int status) {
 
 const char* kvq_last_error(void) { return g_last_error; }
 
-int kvq_abi_version(void) { return 1; }
+int kvq_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -20,6 +20,7 @@
 // all query rows of the KV head (every GQA head and query), then scored,
 // folded into (m, z) and into u.
 #include "kvq_internal.h"
+#include "kvq_layout.h"
 
 namespace kvq {
 namespace {
@@ -27,38 +28,26 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 32;
 
+// Decoded K (token n, channel d) and V (token n, feature f) of head bh:
+// fl32((stored - qmax) * scale), addressed through the block layout.
 template <int SRC>
-__device__ __forceinline__ float decode_k(const AttendProblem& p, long long bh, int d, int n) {
+__device__ __forceinline__ float decode_k(const AttendProblem& p, const Layout& L, long long bh,
+                                          int d, int n) {
   if (SRC == 32) return p.k_f32[(bh * p.N + n) * p.D + d];
-  const int npad = (p.N + p.group - 1) / p.group * p.group;
-  const long long row = bh * p.D + d;
-  const uint8_t* codes = p.k_codes + row * (static_cast<long long>(npad) * SRC / 8);
-  int c;
-  if (SRC == 4) {
-    const unsigned b = codes[n >> 1];
-    c = static_cast<int>((n & 1) ? (b >> 4) : (b & 15u)) - 7;
-  } else {
-    c = static_cast<int>(codes[n]) - 127;
-  }
-  const float s = p.k_scales[row * (npad / p.group) + n / p.group];
-  return static_cast<float>(c) * s;
+  const unsigned b = p.k_codes[bh * k_code_bytes_per_head(L) + k_code_byte(L, n, d)];
+  const int c = SRC == 4 ? static_cast<int>((n & 1) ? (b >> 4) : (b & 15u)) - 7
+                         : static_cast<int>(b) - 127;
+  return static_cast<float>(c) * p.k_scales[bh * k_scales_per_head(L) + k_scale_index(L, n, d)];
 }
 
 template <int SRC>
-__device__ __forceinline__ float decode_v(const AttendProblem& p, long long bh, int n, int f) {
+__device__ __forceinline__ float decode_v(const AttendProblem& p, const Layout& L, long long bh,
+                                          int n, int f) {
   if (SRC == 32) return p.v_f32[(bh * p.N + n) * p.D + f];
-  const int dpad = (p.D + p.group - 1) / p.group * p.group;
-  const long long row = bh * p.N + n;
-  const uint8_t* codes = p.v_codes + row * (static_cast<long long>(dpad) * SRC / 8);
-  int c;
-  if (SRC == 4) {
-    const unsigned b = codes[f >> 1];
-    c = static_cast<int>((f & 1) ? (b >> 4) : (b & 15u)) - 7;
-  } else {
-    c = static_cast<int>(codes[f]) - 127;
-  }
-  const float s = p.v_scales[row * (dpad / p.group) + f / p.group];
-  return static_cast<float>(c) * s;
+  const unsigned b = p.v_codes[bh * v_code_bytes_per_head(L) + v_code_byte(L, n, f)];
+  const int c = SRC == 4 ? static_cast<int>((f & 1) ? (b >> 4) : (b & 15u)) - 7
+                         : static_cast<int>(b) - 127;
+  return static_cast<float>(c) * p.v_scales[bh * v_scales_per_head(L) + v_scale_index(L, n, f)];
 }
 
 template <int D, int SRC>
@@ -78,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   const long long bh = static_cast<long long>(blockIdx.z) * p.Hkv + blockIdx.y;
   const int t_begin = split * p.tokens_per_split;
   const int t_end = min(p.N, t_begin + p.tokens_per_split);
+  const Layout L = make_layout(p.N, p.D, SRC == 32 ? 8 : SRC, SRC == 32 ? 2 : p.group);
 
   // Query rows of this KV head are contiguous in q: [bh*rows, bh*rows + rows).
   for (int i = tid; i < rows * D; i += kThreads)
@@ -93,15 +83,16 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
 
   for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
     const int tn = min(kTile, t_end - t0);
-    // Decode the tile.  K: token index fastest (K codes are channel-major);
-    // V: feature index fastest (V codes are token-major).
+    // Decode the tile.  K: the 8 channels of an octet fastest, then the
+    // token (one 8-byte run of the block layout per token column); V: the
+    // feature fastest.
     for (int i = tid; i < kTile * D; i += kThreads) {
-      const int j = i % kTile, d = i / kTile;
-      sK[j][d] = j < tn ? decode_k<SRC>(p, bh, d, t0 + j) : 0.0f;
+      const int j = (i >> 3) % kTile, d = (i / (8 * kTile)) * 8 + (i & 7);
+      sK[j][d] = j < tn ? decode_k<SRC>(p, L, bh, d, t0 + j) : 0.0f;
     }
     for (int i = tid; i < kTile * D; i += kThreads) {
       const int f = i % D, j = i / D;
-      sV[j][f] = j < tn ? decode_v<SRC>(p, bh, t0 + j, f) : 0.0f;
+      sV[j][f] = j < tn ? decode_v<SRC>(p, L, bh, t0 + j, f) : 0.0f;
     }
     __syncthreads();
 

@@ -5,13 +5,20 @@
 // length": per group of `group` elements one float32 scale max|x|/qmax
 // (1 if that is 0), codes rint(x/scale) clipped to [-qmax, qmax] and stored
 // as code + qmax; 4-bit codes pair up as low | high << 4.  K groups run along
-// tokens inside a channel, V groups along features inside a token.
+// tokens inside a channel, V groups along features inside a token.  The byte
+// order in memory is the block layout of kvq_layout.h.
+//
+// Packing runs in two passes: one thread per group computes the scale, then
+// one thread per stored byte quantizes its one or two elements against the
+// scales just written (every byte of the layout is written, padding
+// included).
 //
 // Bit-exactness rests on three properties of this translation unit's build:
 // float32 division is IEEE correctly rounded (hipcc's default for HIP,
 // requested explicitly with -fhip-fp32-correctly-rounded-divide-sqrt),
 // denormals are kept (no flush-to-zero flag), and rintf rounds half to even.
 #include "kvq_internal.h"
+#include "kvq_layout.h"
 
 namespace kvq {
 namespace {
@@ -37,93 +44,113 @@ __device__ __forceinline__ unsigned stored_code(float x, float s) {
   return static_cast<unsigned>(static_cast<int>(c) + Codec<BITS>::kQmaxInt);
 }
 
-// K-style: one thread per (b*h, group index G, channel d).  Consecutive
-// threads take consecutive channels, so each of the `group` token reads is
-// one coalesced row segment.  The thread writes its group's codes
-// (group*BITS/8 bytes) into channel d's row and one scale.
+// K scales: one thread per (head, token group G, channel d), d fastest so
+// both the token-row reads and the group-major scale writes coalesce.
 template <int BITS>
-__global__ __launch_bounds__(256) void pack_k_kernel(const float* __restrict__ x, long long BH,
-                                                     int N, int D, int group, int ngroups,
-                                                     uint8_t* __restrict__ codes,
-                                                     float* __restrict__ scales) {
+__global__ __launch_bounds__(256) void pack_k_scales_kernel(const float* __restrict__ x,
+                                                            long long BH, Layout L,
+                                                            float* __restrict__ scales) {
   const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (tid >= BH * ngroups * D) return;
-  const int d = static_cast<int>(tid % D);
-  const long long rest = tid / D;
-  const int g = static_cast<int>(rest % ngroups);
-  const long long bh = rest / ngroups;
-  const float* src = x + bh * N * static_cast<long long>(D) + d;
-  const int n0 = g * group;
-  const int n1 = min(N, n0 + group);
-
+  if (tid >= BH * L.kgroups * L.D) return;
+  const int d = static_cast<int>(tid % L.D);
+  const long long rest = tid / L.D;
+  const int g = static_cast<int>(rest % L.kgroups);
+  const long long bh = rest / L.kgroups;
+  const float* src = x + bh * L.N * static_cast<long long>(L.D) + d;
+  const int n1 = min(L.N, (g + 1) * L.group);
   float amax = 0.0f;
-  for (int n = n0; n < n1; ++n) amax = fmaxf(amax, fabsf(src[static_cast<long long>(n) * D]));
-  const float s = group_scale<BITS>(amax);
-
-  const long long row = bh * D + d;
-  scales[row * ngroups + g] = s;
-  const long long row_bytes = static_cast<long long>(ngroups) * group * BITS / 8;
-  uint8_t* dst = codes + row * row_bytes + static_cast<long long>(n0) * BITS / 8;
-  for (int t = 0; t < group; t += 2) {
-    const int n = n0 + t;
-    const float x0 = n < N ? src[static_cast<long long>(n) * D] : 0.0f;
-    const float x1 = n + 1 < N ? src[static_cast<long long>(n + 1) * D] : 0.0f;
-    const unsigned c0 = stored_code<BITS>(x0, s);
-    const unsigned c1 = stored_code<BITS>(x1, s);
-    if (BITS == 4) {
-      dst[t / 2] = static_cast<uint8_t>(c0 | (c1 << 4));
-    } else {
-      dst[t] = static_cast<uint8_t>(c0);
-      dst[t + 1] = static_cast<uint8_t>(c1);
-    }
-  }
+  for (int n = g * L.group; n < n1; ++n)
+    amax = fmaxf(amax, fabsf(src[static_cast<long long>(n) * L.D]));
+  scales[bh * k_scales_per_head(L) + k_scale_index(L, g * L.group, d)] = group_scale<BITS>(amax);
 }
 
-// V-style: one thread per (token row, group index G); the group is a
-// contiguous run of features.
+// K codes: one thread per stored byte.
 template <int BITS>
-__global__ __launch_bounds__(256) void pack_v_kernel(const float* __restrict__ x, long long rows,
-                                                     int D, int group, int ngroups,
-                                                     uint8_t* __restrict__ codes,
-                                                     float* __restrict__ scales) {
+__global__ __launch_bounds__(256) void pack_k_codes_kernel(const float* __restrict__ x,
+                                                           long long BH, Layout L,
+                                                           const float* __restrict__ scales,
+                                                           uint8_t* __restrict__ codes) {
+  const long long per_head = k_code_bytes_per_head(L);
   const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (tid >= rows * ngroups) return;
-  const int g = static_cast<int>(tid % ngroups);
-  const long long row = tid / ngroups;
-  const float* src = x + row * D;
-  const int f0 = g * group;
-  const int f1 = min(D, f0 + group);
-
-  float amax = 0.0f;
-  for (int f = f0; f < f1; ++f) amax = fmaxf(amax, fabsf(src[f]));
-  const float s = group_scale<BITS>(amax);
-
-  scales[row * ngroups + g] = s;
-  const long long row_bytes = static_cast<long long>(ngroups) * group * BITS / 8;
-  uint8_t* dst = codes + row * row_bytes + static_cast<long long>(f0) * BITS / 8;
-  for (int t = 0; t < group; t += 2) {
-    const int f = f0 + t;
-    const float x0 = f < D ? src[f] : 0.0f;
-    const float x1 = f + 1 < D ? src[f + 1] : 0.0f;
-    const unsigned c0 = stored_code<BITS>(x0, s);
-    const unsigned c1 = stored_code<BITS>(x1, s);
-    if (BITS == 4) {
-      dst[t / 2] = static_cast<uint8_t>(c0 | (c1 << 4));
-    } else {
-      dst[t] = static_cast<uint8_t>(c0);
-      dst[t + 1] = static_cast<uint8_t>(c1);
-    }
-  }
+  if (tid >= BH * per_head) return;
+  const long long bh = tid / per_head;
+  const long long i = tid % per_head;
+  const int blk = static_cast<int>(i / L.kblock_bytes);
+  const int r = static_cast<int>(i % L.kblock_bytes);
+  const int d = (r / (L.kcols * 8)) * 8 + (r & 7);
+  const int j = (r / 8) % L.kcols;
+  const float* src = x + bh * L.N * static_cast<long long>(L.D);
+  const float* ks = scales + bh * k_scales_per_head(L);
+  auto code = [&](int t) -> unsigned {
+    if (t >= L.N || d >= L.D) return Codec<BITS>::kQmaxInt;
+    return stored_code<BITS>(src[static_cast<long long>(t) * L.D + d], ks[k_scale_index(L, t, d)]);
+  };
+  const int t0 = blk * kBlockTokens + (BITS == 4 ? 2 * j : j);
+  const unsigned byte = BITS == 4 ? (code(t0) | (code(t0 + 1) << 4)) : code(t0);
+  codes[tid] = static_cast<uint8_t>(byte);
 }
 
-// Stored code of element `i` of a packed row.
+// V scales: one thread per (head, token t < 32 * nblocks, feature group G),
+// token fastest so the token-minor scale writes coalesce.
 template <int BITS>
-__device__ __forceinline__ int load_code(const uint8_t* row, long long i) {
-  if (BITS == 4) {
-    const unsigned b = row[i >> 1];
-    return static_cast<int>((i & 1) ? (b >> 4) : (b & 15u));
+__global__ __launch_bounds__(256) void pack_v_scales_kernel(const float* __restrict__ x,
+                                                            long long BH, Layout L,
+                                                            float* __restrict__ scales) {
+  const int tpad = L.nblocks * kBlockTokens;
+  const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (tid >= BH * L.vgroups * tpad) return;
+  const int tl = static_cast<int>(tid % kBlockTokens);
+  long long rest = tid / kBlockTokens;
+  const int g = static_cast<int>(rest % L.vgroups);
+  rest /= L.vgroups;
+  const int blk = static_cast<int>(rest % L.nblocks);
+  const long long bh = rest / L.nblocks;
+  const int t = blk * kBlockTokens + tl;
+  float amax = 0.0f;
+  if (t < L.N) {
+    const float* src = x + (bh * L.N + t) * static_cast<long long>(L.D);
+    const int f1 = min(L.D, (g + 1) * L.group);
+    for (int f = g * L.group; f < f1; ++f) amax = fmaxf(amax, fabsf(src[f]));
   }
-  return static_cast<int>(row[i]);
+  scales[bh * v_scales_per_head(L) + v_scale_index(L, t, g * L.group)] = group_scale<BITS>(amax);
+}
+
+// V codes: one thread per stored byte.
+template <int BITS>
+__global__ __launch_bounds__(256) void pack_v_codes_kernel(const float* __restrict__ x,
+                                                           long long BH, Layout L,
+                                                           const float* __restrict__ scales,
+                                                           uint8_t* __restrict__ codes) {
+  const long long per_head = v_code_bytes_per_head(L);
+  const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (tid >= BH * per_head) return;
+  const long long bh = tid / per_head;
+  const long long i = tid % per_head;
+  const int blk = static_cast<int>(i / L.vblock_bytes);
+  const int r = static_cast<int>(i % L.vblock_bytes);
+  const int t = blk * kBlockTokens + (r / (L.vcols * 8)) * 8 + (r & 7);
+  const int col = (r / 8) % L.vcols;
+  unsigned byte;
+  if (t >= L.N) {
+    byte = BITS == 4 ? Codec<4>::kQmaxInt * 0x11u : Codec<8>::kQmaxInt;
+  } else {
+    const float* src = x + (bh * L.N + t) * static_cast<long long>(L.D);
+    const float* vs = scales + bh * v_scales_per_head(L);
+    auto code = [&](int f) -> unsigned {
+      const float v = f < L.D ? src[f] : 0.0f;
+      return stored_code<BITS>(v, vs[v_scale_index(L, t, f)]);
+    };
+    byte = BITS == 4 ? (code(2 * col) | (code(2 * col + 1) << 4)) : code(col);
+  }
+  codes[tid] = static_cast<uint8_t>(byte);
+}
+
+// Stored code of element (t, i) given its byte offset within the head.
+template <int BITS>
+__device__ __forceinline__ int load_code(const uint8_t* head, long long byte, int odd) {
+  const unsigned b = head[byte];
+  if (BITS == 4) return static_cast<int>(odd ? (b >> 4) : (b & 15u));
+  return static_cast<int>(b);
 }
 
 // Decode to the original [B][H][N][D] layout, one thread per output element
@@ -132,26 +159,23 @@ __device__ __forceinline__ int load_code(const uint8_t* row, long long i) {
 template <int BITS, bool K_STYLE>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ scales,
-                                                      long long BH, int N, int D, int group,
-                                                      int ngroups, float* __restrict__ out) {
+                                                      long long BH, Layout L,
+                                                      float* __restrict__ out) {
   const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (tid >= BH * N * static_cast<long long>(D)) return;
-  const int d = static_cast<int>(tid % D);
-  const long long rest = tid / D;
-  const int n = static_cast<int>(rest % N);
-  const long long bh = rest / N;
-  const long long row_bytes = static_cast<long long>(ngroups) * group * BITS / 8;
-  long long row;
-  int i;
+  if (tid >= BH * L.N * static_cast<long long>(L.D)) return;
+  const int d = static_cast<int>(tid % L.D);
+  const long long rest = tid / L.D;
+  const int n = static_cast<int>(rest % L.N);
+  const long long bh = rest / L.N;
+  int c;
+  float s;
   if (K_STYLE) {
-    row = bh * D + d;
-    i = n;
+    c = load_code<BITS>(codes + bh * k_code_bytes_per_head(L), k_code_byte(L, n, d), n & 1);
+    s = scales[bh * k_scales_per_head(L) + k_scale_index(L, n, d)];
   } else {
-    row = bh * N + n;
-    i = d;
+    c = load_code<BITS>(codes + bh * v_code_bytes_per_head(L), v_code_byte(L, n, d), d & 1);
+    s = scales[bh * v_scales_per_head(L) + v_scale_index(L, n, d)];
   }
-  const int c = load_code<BITS>(codes + row * row_bytes, i);
-  const float s = scales[row * ngroups + i / group];
   out[tid] = static_cast<float>(c - Codec<BITS>::kQmaxInt) * s;
 }
 
@@ -159,53 +183,53 @@ inline unsigned grid_for(long long threads) {
   return static_cast<unsigned>((threads + 255) / 256);
 }
 
+template <int BITS>
+hipError_t pack_bits(const float* x, long long BH, const Layout& L, bool k_style, uint8_t* codes,
+                     float* scales, hipStream_t stream) {
+  if (k_style) {
+    hipLaunchKernelGGL(pack_k_scales_kernel<BITS>, dim3(grid_for(BH * L.kgroups * L.D)),
+                       dim3(256), 0, stream, x, BH, L, scales);
+    hipLaunchKernelGGL(pack_k_codes_kernel<BITS>, dim3(grid_for(BH * k_code_bytes_per_head(L))),
+                       dim3(256), 0, stream, x, BH, L, scales, codes);
+  } else {
+    hipLaunchKernelGGL(pack_v_scales_kernel<BITS>,
+                       dim3(grid_for(BH * L.vgroups * L.nblocks * kBlockTokens)), dim3(256), 0,
+                       stream, x, BH, L, scales);
+    hipLaunchKernelGGL(pack_v_codes_kernel<BITS>, dim3(grid_for(BH * v_code_bytes_per_head(L))),
+                       dim3(256), 0, stream, x, BH, L, scales, codes);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_pack(const float* x, int B, int H, int N, int D, int bits, int group,
                        bool k_style, uint8_t* codes, float* scales, hipStream_t stream) {
   const long long BH = static_cast<long long>(B) * H;
-  if (k_style) {
-    const int ngroups = (N + group - 1) / group;
-    const unsigned grid = grid_for(BH * ngroups * D);
-    if (bits == 4)
-      hipLaunchKernelGGL(pack_k_kernel<4>, dim3(grid), dim3(256), 0, stream, x, BH, N, D, group,
-                         ngroups, codes, scales);
-    else
-      hipLaunchKernelGGL(pack_k_kernel<8>, dim3(grid), dim3(256), 0, stream, x, BH, N, D, group,
-                         ngroups, codes, scales);
-  } else {
-    const int ngroups = (D + group - 1) / group;
-    const long long rows = BH * N;
-    const unsigned grid = grid_for(rows * ngroups);
-    if (bits == 4)
-      hipLaunchKernelGGL(pack_v_kernel<4>, dim3(grid), dim3(256), 0, stream, x, rows, D, group,
-                         ngroups, codes, scales);
-    else
-      hipLaunchKernelGGL(pack_v_kernel<8>, dim3(grid), dim3(256), 0, stream, x, rows, D, group,
-                         ngroups, codes, scales);
-  }
-  return hipGetLastError();
+  const Layout L = make_layout(N, D, bits, group);
+  return bits == 4 ? pack_bits<4>(x, BH, L, k_style, codes, scales, stream)
+                   : pack_bits<8>(x, BH, L, k_style, codes, scales, stream);
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const float* scales, int B, int H, int N, int D,
                           int bits, int group, bool k_style, float* out, hipStream_t stream) {
   const long long BH = static_cast<long long>(B) * H;
-  const int ngroups = k_style ? (N + group - 1) / group : (D + group - 1) / group;
+  const Layout L = make_layout(N, D, bits, group);
   const unsigned grid = grid_for(BH * N * static_cast<long long>(D));
   if (k_style) {
     if (bits == 4)
       hipLaunchKernelGGL((dequant_kernel<4, true>), dim3(grid), dim3(256), 0, stream, codes,
-                         scales, BH, N, D, group, ngroups, out);
+                         scales, BH, L, out);
     else
       hipLaunchKernelGGL((dequant_kernel<8, true>), dim3(grid), dim3(256), 0, stream, codes,
-                         scales, BH, N, D, group, ngroups, out);
+                         scales, BH, L, out);
   } else {
     if (bits == 4)
       hipLaunchKernelGGL((dequant_kernel<4, false>), dim3(grid), dim3(256), 0, stream, codes,
-                         scales, BH, N, D, group, ngroups, out);
+                         scales, BH, L, out);
     else
       hipLaunchKernelGGL((dequant_kernel<8, false>), dim3(grid), dim3(256), 0, stream, codes,
-                         scales, BH, N, D, group, ngroups, out);
+                         scales, BH, L, out);
   }
   return hipGetLastError();
 }

@@ -28,5 +28,12 @@ def oracle_pack(k, v, bits, group):
     return kc, ks, vc, vs
 
 
+def oracle_store(k, v, bits, group):
+    """The oracle's packing of k, v in the library's block byte order."""
+    n, d = k.shape[-2], k.shape[-1]
+    kc, ks, vc, vs = oracle_pack(k, v, bits, group)
+    return O.store_k(kc, ks, n, d, bits, group) + O.store_v(vc, vs, n, d, bits, group)
+
+
 def max_abs(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))))

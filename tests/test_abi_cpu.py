@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert lib.kvq_abi_version() == 1
+    assert lib.kvq_abi_version() == 2
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.kvq_status_string(st)
 
@@ -45,8 +45,8 @@ def test_abi_version_and_strings():
 @pytest.mark.parametrize("bits,group", [(4, 8), (4, 32), (8, 8), (8, 32), (4, 2)])
 def test_sizes_match_oracle_arrays(N, D, bits, group):
     x = np.zeros((2, 3, N, D), np.float32)
-    kc, ks = O.pack_k(x, bits, group)
-    vc, vs = O.pack_v(x, bits, group)
+    kc, ks = O.store_k(*O.pack_k(x, bits, group), N, D, bits, group)
+    vc, vs = O.store_v(*O.pack_v(x, bits, group), N, D, bits, group)
     assert lib.kvq_k_code_bytes(2, 3, N, D, bits, group) == kc.nbytes
     assert lib.kvq_k_scale_count(2, 3, N, D, bits, group) == ks.size
     assert lib.kvq_v_code_bytes(2, 3, N, D, bits, group) == vc.nbytes

@@ -5,7 +5,7 @@ import pytest
 from oracle import kvq_oracle as O
 from workloads import WORKLOADS, make_crafted, make_qkv
 
-from gpu_helpers import announce, dev, host, oracle_pack
+from gpu_helpers import announce, dev, host, oracle_pack, oracle_store
 
 pytestmark = pytest.mark.gpu
 
@@ -15,12 +15,13 @@ kvq = pytest.importorskip("quantized_kv_cache_attend_amd")
 def _check_pack_dequant(k, v, bits, group, label):
     announce(f"pack/dequant {label} shape={k.shape} bits={bits} group={group}")
     kc, ks, vc, vs = oracle_pack(k, v, bits, group)
+    skc, sks, svc, svs = oracle_store(k, v, bits, group)
     gkc, gks = kvq.pack_k(dev(k), bits, group)
     gvc, gvs = kvq.pack_v(dev(v), bits, group)
-    assert np.array_equal(host(gkc), kc)
-    assert np.array_equal(host(gks).view(np.uint32), ks.view(np.uint32))
-    assert np.array_equal(host(gvc), vc)
-    assert np.array_equal(host(gvs).view(np.uint32), vs.view(np.uint32))
+    assert np.array_equal(host(gkc), skc)
+    assert np.array_equal(host(gks).view(np.uint32), sks.view(np.uint32))
+    assert np.array_equal(host(gvc), svc)
+    assert np.array_equal(host(gvs).view(np.uint32), svs.view(np.uint32))
     B, H, N, D = k.shape
     kd = host(kvq.dequant_k(gkc, gks, N, D, bits, group))
     vd = host(kvq.dequant_v(gvc, gvs, N, D, bits, group))
@@ -74,7 +75,7 @@ def test_pack_full_gqa_n32768_sampled_heads():
     gkc, gks = kvq.pack_k(dev(k), 4, 32)
     gvc, gvs = kvq.pack_v(dev(v), 4, 32)
     for b, h in ((0, 0), (7, 3), (15, 7)):
-        kc, ks, vc, vs = oracle_pack(k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], 4, 32)
+        kc, ks, vc, vs = oracle_store(k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], 4, 32)
         assert np.array_equal(host(gkc[b:b + 1, h:h + 1]), kc)
         assert np.array_equal(host(gks[b:b + 1, h:h + 1]), ks)
         assert np.array_equal(host(gvc[b:b + 1, h:h + 1]), vc)

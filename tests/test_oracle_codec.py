@@ -255,3 +255,99 @@ def test_kv_bytes_formula(golden):
     per_layer = O.kv_bytes(1, w.B, w.N, w.Hkv, w.D, O.bytes_per_element(4, 32))
     assert per_layer == w.B * w.Hkv * (O.packed_payload_bytes(w.N, w.D, 4, 32, shape_record=False))
     assert per_layer == 41943040
+
+
+# --- block byte order of the device layout ------------------------------------
+# The pages leave the byte order open; the library's block order is checked
+# here against the canonical arrays directly (no reshape shared with
+# store_k / store_v): first in the form the matrix-core kernel consumes it,
+# then element by element through the byte formula written in include/kvq.h.
+
+def _random_cache(n, d, seed=11):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((1, 1, n, d), dtype=np.float32),
+            rng.standard_normal((1, 1, n, d), dtype=np.float32))
+
+
+def test_store_k_gives_matrix_core_rows():
+    """4-bit, D=128: the 8 bytes at k-step ks*512 + lane*8 of a block are the
+    bytes of token pair 16*blk + n (n = lane % 16) for channels
+    ks*32 + 8*(lane // 16) + e, e = 0..7."""
+    n_tok, d = 96, 128
+    k, _ = _random_cache(n_tok, d)
+    kc, ks = O.pack_k(k, 4, 32)
+    st, sst = O.store_k(kc, ks, n_tok, d, 4, 32)
+    assert st.shape == (1, 1, 3, 2048)
+    for blk in range(3):
+        for ks_ in range(4):
+            for lane in range(64):
+                n, q = lane % 16, lane // 16
+                got = st[0, 0, blk, ks_ * 512 + lane * 8: ks_ * 512 + lane * 8 + 8]
+                want = [kc[0, 0, ks_ * 32 + 8 * q + e, 16 * blk + n] for e in range(8)]
+                assert list(got) == want
+    assert np.array_equal(sst[0, 0].T, ks[0, 0])      # group-major scales
+
+
+def test_store_v_gives_matrix_core_columns():
+    """4-bit, D=128: the 8 bytes at q*512 + g*128 + n*8 of a block are byte
+    column 16g + n of tokens 32*blk + 8q + e, e = 0..7; the V scales of
+    value group G for tokens 8q..8q+7 sit at G*32 + 8q .. + 7."""
+    n_tok, d = 64, 128
+    _, v = _random_cache(n_tok, d)
+    vc, vs = O.pack_v(v, 4, 32)
+    st, sst = O.store_v(vc, vs, n_tok, d, 4, 32)
+    assert st.shape == (1, 1, 2, 2048) and sst.shape == (1, 1, 2, 128)
+    for blk in range(2):
+        for q in range(4):
+            for g in range(4):
+                for n in range(16):
+                    off = q * 512 + g * 128 + n * 8
+                    want = [vc[0, 0, 32 * blk + 8 * q + e, 16 * g + n] for e in range(8)]
+                    assert list(st[0, 0, blk, off:off + 8]) == want
+            for G in range(4):
+                assert np.array_equal(sst[0, 0, blk, G * 32 + 8 * q: G * 32 + 8 * q + 8],
+                                      vs[0, 0, 32 * blk + 8 * q: 32 * blk + 8 * q + 8, G])
+
+
+def _nibble(byte, hi, bits):
+    return (byte >> 4 if hi else byte & 15) if bits == 4 else byte
+
+
+@pytest.mark.parametrize("bits,group", [(4, 8), (4, 32), (8, 8), (8, 6), (4, 2), (4, 64)])
+@pytest.mark.parametrize("n,d", [(35, 13), (1, 1), (64, 32), (33, 40)])
+def test_store_matches_header_formula(bits, group, n, d):
+    """Every element through the byte formula of include/kvq.h, every other
+    position holds the zero code, padded V scales are 1."""
+    k, v = _random_cache(n, d, seed=n * 100 + d)
+    kc, ks = O.pack_k(k, bits, group)
+    vc, vs = O.pack_v(v, bits, group)
+    sk, sks = O.store_k(kc, ks, n, d, bits, group)
+    sv, svs = O.store_v(vc, vs, n, d, bits, group)
+    kst = O.unpack_stored(kc, k.shape, -2, bits, group)[0, 0]
+    vst = O.unpack_stored(vc, v.shape, -1, bits, group)[0, 0]
+    nb, d8, dpad = -(-n // 32), -(-d // 8), -(-d // group) * group
+    kcols, vcols = 32 * bits // 8, dpad * bits // 8
+    kflat, vflat = sk[0, 0].reshape(-1), sv[0, 0].reshape(-1)
+    kseen, vseen = set(), set()
+    for t in range(n):
+        for c in range(d):
+            j = (t % 32) // 2 if bits == 4 else t % 32
+            kb = (t // 32) * d8 * kcols * 8 + ((c // 8) * kcols + j) * 8 + c % 8
+            assert _nibble(int(kflat[kb]), t % 2, bits) == kst[t, c]
+            kseen.add((kb, t % 2 if bits == 4 else 0))
+            col = c // 2 if bits == 4 else c
+            vb = (t // 32) * 4 * vcols * 8 + (((t % 32) // 8) * vcols + col) * 8 + t % 8
+            assert _nibble(int(vflat[vb]), c % 2, bits) == vst[t, c]
+            vseen.add((vb, c % 2 if bits == 4 else 0))
+            assert sks[0, 0, t // group, c] == ks[0, 0, c, t // group]
+            vsi = ((t // 32) * (dpad // group) + c // group) * 32 + t % 32
+            assert svs[0, 0].reshape(-1)[vsi] == vs[0, 0, t, c // group]
+    zero = O.QMAX[bits]
+    halves = (0, 1) if bits == 4 else (0,)
+    for flat, seen in ((kflat, kseen), (vflat, vseen)):
+        for b in range(flat.size):
+            for h in halves:
+                if (b, h) not in seen:
+                    assert _nibble(int(flat[b]), h, bits) == zero
+    vsflat = svs[0, 0].reshape(nb, dpad // group, 32)
+    assert np.all(vsflat[:, :, :][np.arange(nb * 32).reshape(nb, 1, 32).repeat(dpad // group, 1) >= n] == 1.0)

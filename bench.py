@@ -51,6 +51,43 @@ def kv_bytes(w, bits, group):
     return w.B * w.Hkv * per_head
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_mfma_gqa_n4096_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "quantized_kv_cache_attend_amd", "csrc", "kvq_attend_mfma.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the matrix-core attend kernel from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same
+    counter's reading for a copy of known size), or None when the summary is
+    missing or was taken on a different kernel source."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE, encoding="utf-8").read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch:", "kernel_source_sha256:")))
+    if fields.get("kernel_source_sha256", "").strip() != src:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib, reps):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {mib} MiB (read {mib} MiB, write {mib} MiB each)")
+
+
 def cpu_baseline(w, q, k, v, bits, group, seconds):
     """Time the float64 oracle (decode the whole packed cache, dense attention)
     on this host, as it stands, over whole passes of the workload until
@@ -95,6 +132,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip pack / decode-all timings")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run device copies of MIB MiB (for counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -102,6 +141,10 @@ def main():
               "(the path shards by (batch, KV head) with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
 
     import torch
     import quantized_kv_cache_attend_amd as kvq
@@ -113,7 +156,7 @@ def main():
     torch.cuda.set_device(dev)
 
     log(f"[bench] workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} R={w.R} N={w.N} D={w.D} "
-        f"{bits}-bit g{group} splits={splits or kvq.auto_splits(w.B, w.Hkv, w.N)}")
+        f"{bits}-bit g{group} splits={splits or 'auto'}")
     q, k, v = make_qkv(w, 0)
     qd, kd, vd = (torch.from_numpy(a).to(dev) for a in (q, k, v))
     kc, ks = kvq.pack_k(kd, bits, group)
@@ -175,7 +218,7 @@ def main():
     extra = {"wall_us_per_step": round(ms_per_step * 1e3, 3),
              "stream_event_us_per_step": round(region_ms * 1e3, 3),
              "per_launch_event_us_median": round(launch_us, 3),
-             "cache_copies": copies, "splits": splits or kvq.auto_splits(w.B, w.Hkv, w.N),
+             "cache_copies": copies, "splits": splits or "auto",
              "variant": args.variant, "output_finite": finite}
 
     if not args.no_extra:
@@ -213,6 +256,7 @@ def main():
         cpu = cpu_baseline(w, q, k, v, bits, group, args.cpu_seconds)
         log(f"[bench] oracle {cpu['value']:.3f} GB/s ({cpu['sample']})")
 
+    traffic = measured_traffic() if args.variant in ("auto", "mfma") and w.name == "gqa_n4096" else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -230,7 +274,8 @@ def main():
                    "queries_per_head": w.R, "head_dim": w.D, "bits": bits, "group": group,
                    "kv_bytes": nbytes, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -89,8 +89,10 @@ size_t kvq_k_scale_count(int B, int H, int N, int D, int bits, int group); /* B*
 size_t kvq_v_code_bytes(int B, int H, int N, int D, int bits, int group);  /* B*H*nblocks*32*Dpad*bits/8 */
 size_t kvq_v_scale_count(int B, int H, int N, int D, int bits, int group); /* B*H*nblocks*(Dpad/group)*32 */
 
-/* Number of KV splits kvq_attend uses when num_splits == 0 ([RL] "two stops
- * of the online accumulation": per-split (m, z, u) are composable). */
+/* Upper bound on the KV splits kvq_attend uses when num_splits == 0, and the
+ * split count that sizes the workspace ([RL] "two stops of the online
+ * accumulation": per-split (m, z, u) are composable).  The general kernel
+ * uses exactly this many; the matrix-core kernel may use fewer. */
 int kvq_attend_auto_splits(int B, int Hkv, int N);
 
 /* Workspace bytes kvq_attend / kvq_attend_f32 need for `num_splits` splits
@@ -135,7 +137,7 @@ kvq_status kvq_dequant_v(const uint8_t* codes, const float* scales, int B, int H
  *   q      [B][Hq][R][D] float32          out [B][Hq][R][D] float32
  *   k_codes/k_scales, v_codes/v_scales: the packed layouts above, H = Hkv.
  *   sm_scale: softmax temperature; 0 means 1/sqrt(D) ([RL] "prefill and decode").
- *   num_splits: KV splits; 0 = kvq_attend_auto_splits.
+ *   num_splits: KV splits; 0 = automatic (at most kvq_attend_auto_splits).
  *   workspace: device buffer of >= kvq_attend_workspace_bytes(...) bytes,
  *     zero-filled before first use (may be NULL only when one split is used).
  * Supported: D in {32, 64, 128}; (Hq/Hkv)*R <= 64; any N >= 1.

@@ -174,7 +174,24 @@ bool mfma_eligible(const AttendProblem& p) {
          aligned(p.k_scales, 16) && aligned(p.v_scales, 16);
 }
 
-hipError_t run_mfma(AttendProblem p, hipStream_t s) {
+// Split count of the matrix-core kernel when the caller asks for auto: one
+// 8-wave workgroup per compute unit (about 256 workgroups; every split is
+// merged by the fused tail, so fewer, larger splits are cheaper once the
+// compute units are covered), and no split shorter than 1024 tokens.  Never
+// more than auto_splits(), so a workspace sized by
+// kvq_attend_workspace_bytes(..., 0) always suffices.
+int mfma_auto_splits(int B, int Hkv, int N) {
+  const long long heads = static_cast<long long>(B) * Hkv;
+  const long long want = (256 + heads - 1) / heads;
+  const long long cap = (N + 1023) / 1024;
+  long long s = want < cap ? want : cap;
+  if (s < 1) s = 1;
+  const long long general = auto_splits(B, Hkv, N);
+  return static_cast<int>(s < general ? s : general);
+}
+
+hipError_t run_mfma(AttendProblem p, bool auto_split, hipStream_t s) {
+  if (auto_split) p.splits = mfma_auto_splits(p.B, p.Hkv, p.N);
   p.tokens_per_split = mfma_tokens_per_split(p.N, p.splits);
   return launch_attend_mfma(p, s);
 }
@@ -270,7 +287,7 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
   const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
     case KVQ_VARIANT_AUTO:
-      if (mfma_eligible(p)) return hip_status(run_mfma(p, s), "attend (mfma) launch");
+      if (mfma_eligible(p)) return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
       return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
     case KVQ_VARIANT_VALU:
       return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
@@ -279,7 +296,7 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
         return fail(KVQ_ERR_UNSUPPORTED,
                     "matrix-core kernel needs bits=4, group=32, D=128, <= %d query rows per "
                     "KV head and 16-byte aligned q, codes and V scales", kMfmaMaxRows);
-      return hip_status(run_mfma(p, s), "attend (mfma) launch");
+      return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
     default:
       return fail(KVQ_ERR_INVALID, "unknown variant %d", variant);
   }

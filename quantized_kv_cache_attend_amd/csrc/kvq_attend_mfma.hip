@@ -66,8 +66,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+#ifndef KVQ_MFMA_WAVES
+#define KVQ_MFMA_WAVES 8
+#endif
+constexpr int kWaves = KVQ_MFMA_WAVES;   // waves per workgroup, one KV head split each
+constexpr int kThreads = kWaves * 64;
+constexpr int kOut = 4 * 128;            // outputs of one KV head: 4 rows x D
+constexpr int kSlots = kOut / kThreads > 0 ? kOut / kThreads : 1;  // outputs per thread
 constexpr int kD = 128;
 constexpr int kBlockBytes = 2048;   // K or V codes of one 32-token block
 constexpr int kBlockScales = 128;   // K or V scales of one block
@@ -105,7 +110,7 @@ __device__ __forceinline__ int prescale_exp(float max_abs, int top) {
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
   return as_f32(static_cast<unsigned>(
-      __builtin_amdgcn_mov_dpp(static_cast<int>(as_u32(x)), kCtrl, 0xf, 0xf, false)));
+      __builtin_amdgcn_mov_dpp(static_cast<int>(as_u32(x)), kCtrl, 0xf, 0xf, true)));
 }
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
@@ -181,17 +186,30 @@ __device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// fp16 hi/lo split of 8 float32 values, packed in k-slot order.
+// x - (float)h for the fp16 h in half `sel` of a packed pair: one
+// v_fma_mix_f32 (the fp16 operand is widened inside the instruction).
+template <int kSel>
+__device__ __forceinline__ float sub_half(float x, unsigned h2) {
+  float r;
+  if (kSel == 0)
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(x));
+  else
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(r) : "v"(h2), "v"(x));
+  return r;
+}
+
+// fp16 hi/lo split of 8 float32 values, packed in k-slot order: hi rounds
+// toward zero, lo is the exact float32 remainder rounded toward zero.
 __device__ __forceinline__ void split_hilo(const float x[8], half8_t& hi, half8_t& lo) {
   u32x4 h, l;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    auto hp = __builtin_amdgcn_cvt_pkrtz(x[2 * i], x[2 * i + 1]);
-    const float r0 = x[2 * i] - static_cast<float>(hp[0]);
-    const float r1 = x[2 * i + 1] - static_cast<float>(hp[1]);
-    auto lp = __builtin_amdgcn_cvt_pkrtz(r0, r1);
-    h[i] = __builtin_bit_cast(unsigned, hp);
-    l[i] = __builtin_bit_cast(unsigned, lp);
+    const unsigned hp = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(x[2 * i], x[2 * i + 1]));
+    const float r0 = sub_half<0>(x[2 * i], hp);
+    const float r1 = sub_half<1>(x[2 * i + 1], hp);
+    h[i] = hp;
+    l[i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(r0, r1));
   }
   hi = __builtin_bit_cast(half8_t, h);
   lo = __builtin_bit_cast(half8_t, l);
@@ -212,40 +230,67 @@ struct Head {
   const float* vsc;
 };
 
-__device__ __forceinline__ void load_block(BlockRegs& r, const Head& h, int blk, int lane,
-                                           int d0) {
+// Loaders of the four parts of one block's operands.  Each part is
+// reloaded for the next block as soon as the current block has consumed it,
+// so about one block of loads stays in flight with a single register set.
+struct Lanes {
+  unsigned k_off, v_off, ks_off, vs_off;  // byte / element offsets of this lane
+};
+__device__ __forceinline__ Lanes lane_offsets(int lane, int d0) {
   const int n = lane & 15, q = lane >> 4;
-  const uint8_t* kb = h.kc + static_cast<long long>(blk) * kBlockBytes + lane * 8;
-  const uint8_t* vb = h.vc + static_cast<long long>(blk) * kBlockBytes + q * 512 + n * 8;
+  return {static_cast<unsigned>(lane * 8), static_cast<unsigned>(q * 512 + n * 8),
+          static_cast<unsigned>(d0), static_cast<unsigned>((n >> 2) * 32 + q * 8)};
+}
+__device__ __forceinline__ void load_ks(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
+  const float* p = h.ksc + static_cast<long long>(blk) * kBlockScales + o.ks_off;
+  r.ks[0] = *reinterpret_cast<const f32x4*>(p);
+  r.ks[1] = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void load_k(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
+  const uint8_t* p = h.kc + static_cast<long long>(blk) * kBlockBytes + o.k_off;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r.k[i] = *reinterpret_cast<const i32x2*>(kb + i * 512);
-    r.v[i] = *reinterpret_cast<const i32x2*>(vb + i * 128);
-  }
-  const float* ksb = h.ksc + static_cast<long long>(blk) * kBlockScales + d0;
-  const float* vsb = h.vsc + static_cast<long long>(blk) * kBlockScales + (n >> 2) * 32 + q * 8;
-  r.ks[0] = *reinterpret_cast<const f32x4*>(ksb);
-  r.ks[1] = *reinterpret_cast<const f32x4*>(ksb + 4);
-  r.vs[0] = *reinterpret_cast<const f32x4*>(vsb);
-  r.vs[1] = *reinterpret_cast<const f32x4*>(vsb + 4);
+  for (int i = 0; i < 4; ++i) r.k[i] = *reinterpret_cast<const i32x2*>(p + i * 512);
+}
+__device__ __forceinline__ void load_vs(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
+  const float* p = h.vsc + static_cast<long long>(blk) * kBlockScales + o.vs_off;
+  r.vs[0] = *reinterpret_cast<const f32x4*>(p);
+  r.vs[1] = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void load_v(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
+  const uint8_t* p = h.vc + static_cast<long long>(blk) * kBlockBytes + o.v_off;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.v[i] = *reinterpret_cast<const i32x2*>(p + i * 128);
+}
+__device__ __forceinline__ void load_block(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
+  load_ks(r, h, blk, o);
+  load_k(r, h, blk, o);
+  load_vs(r, h, blk, o);
+  load_v(r, h, blk, o);
 }
 
-// Running state of one wave.  Lane (n, q) tracks query row n & 3 in m, z;
-// acc[g][e] holds the value sums of feature group g, even (e = 0) or odd
-// (e = 1) features, rows 4q + i = (value group q, query row i), in units of
-// 2^(m + sv).
+// Running state of one wave.  Lane (n, q) tracks query row n & 3: m is the
+// row's reference max (the same in all its lanes), z the sum of p over this
+// lane's tokens (8q .. 8q+7 of each block; summed over the q-blocks at the
+// end).  acc[g][e] holds the value sums of feature group g, even (e = 0) or
+// odd (e = 1) features, rows 4q + i = (value group q, query row i), in
+// units of 2^(m + sv).  vhi / vlo are the V-scale bounds 2^(kSvTop - sv)
+// and 2^(kSvLow - sv) that keep the current sv valid.
 struct WaveState {
   float m, z;
   f32x4 acc[4][2];
   int sv;
+  float vhi, vlo;
   bool live;  // a block has been folded in
 };
 
-// Attend one 32-token block (tokens tok0 .. tok0+31, those >= t_end masked).
-__device__ __forceinline__ void attend_block(Smem& sm, const BlockRegs& br, int tok0, int t_end,
-                                             const CodeConsts& cc, WaveState& ws) {
+// Attend one 32-token block (tokens tok0 .. tok0+31; with kMasked, those
+// >= t_end are masked out).
+template <bool kMasked>
+__device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, int t_end,
+                                             const CodeConsts& cc, WaveState& ws, const Head& h,
+                                             int next, const Lanes& lo_) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int q = lane >> 4;
 
@@ -263,9 +308,8 @@ __device__ __forceinline__ void attend_block(Smem& sm, const BlockRegs& br, int 
       x[i] = qa[i] * br.ks[0][i];
       x[i + 4] = qb[i] * br.ks[1][i];
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    float amax = fmaxf(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))),
+                       fmaxf(fmaxf(fabsf(x[4]), fabsf(x[5])), fmaxf(fabsf(x[6]), fabsf(x[7]))));
     amax = fmaxf(amax, dpp<kRowRor1>(amax));
     amax = fmaxf(amax, dpp<kRowRor2>(amax));
     amax = fmaxf(amax, dpp<kRowRor4>(amax));
@@ -280,65 +324,59 @@ __device__ __forceinline__ void attend_block(Smem& sm, const BlockRegs& br, int 
     *reinterpret_cast<half8_t*>(&sm.u.qt[wave][ksq][1][rq][kbq][0]) = lo;
     if ((lane & 15) == 0) sm.qus[wave][rq] = __builtin_ldexpf(1.0f, -sq);
   }
+  load_ks(br, h, next, lo_);
 
   // S^T = codes^T * q~^T over 4 k-steps of 32 channels.
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 se = zero4, so = zero4;
   const int part = n >> 3, row = n & 3;
+  const uint8_t* knext = h.kc + static_cast<long long>(next) * kBlockBytes + lo_.k_off;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     half8_t alo, ahi;
     codes_to_half(br.k[ks], cc, alo, ahi);
+    br.k[ks] = *reinterpret_cast<const i32x2*>(knext + ks * 512);  // next block's k-step
     const half8_t b = *reinterpret_cast<const half8_t*>(&sm.u.qt[wave][ks][part][row][q][0]);
     se = mfma(alo, b, se);
     so = mfma(ahi, b, so);
   }
   const float us = sm.qus[wave][row];
-  // hi + lo columns; token 8q + t in sc[t], base-2 units
-  float sc[8];
+  // hi + lo columns: token 8q + t in raw[t], in units of 2^S of q~
+  float raw[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sc[2 * i] = (se[i] + dpp<kRowRor8>(se[i])) * us;
-    sc[2 * i + 1] = (so[i] + dpp<kRowRor8>(so[i])) * us;
+    raw[2 * i] = se[i] + dpp<kRowRor8>(se[i]);
+    raw[2 * i + 1] = so[i] + dpp<kRowRor8>(so[i]);
   }
-  if (tok0 + 32 > t_end) {
+  if (kMasked) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      if (tok0 + 8 * q + t >= t_end) sc[t] = -INFINITY;
+      if (tok0 + 8 * q + t >= t_end) raw[t] = -INFINITY;
   }
+  // this lane's max over its 8 tokens, base-2 units (2^-S > 0 commutes with max)
+  const float lmx =
+      fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
+            fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7]))) * us;
+  // this lane's largest V scale (value group n >> 2, tokens 8q .. 8q+7)
+  const float lvs = fmaxf(fmaxf(fmaxf(br.vs[0][0], br.vs[0][1]), fmaxf(br.vs[0][2], br.vs[0][3])),
+                          fmaxf(fmaxf(br.vs[1][0], br.vs[1][1]), fmaxf(br.vs[1][2], br.vs[1][3])));
 
-  // block max per row; finite: the block has a real token
-  float mx = sc[0];
-#pragma unroll
-  for (int t = 1; t < 8; ++t) mx = fmaxf(mx, sc[t]);
-  mx = qblock_max(mx);
-
-  // V prescale: the block's largest V scale (whole wave)
-  float vmx = fmaxf(fmaxf(fmaxf(br.vs[0][0], br.vs[0][1]), fmaxf(br.vs[0][2], br.vs[0][3])),
-                    fmaxf(fmaxf(br.vs[1][0], br.vs[1][1]), fmaxf(br.vs[1][2], br.vs[1][3])));
-  vmx = fmaxf(vmx, dpp<kRowRor4>(vmx));
-  vmx = fmaxf(vmx, dpp<kRowRor8>(vmx));
-  vmx = qblock_max(vmx);
-
-  if (!ws.live) {
-    ws.m = mx;
-    ws.sv = prescale_exp(vmx, kSvTop);
-    ws.live = true;
-  } else {
-    // move the reference of any row that overshoots it by more than kLazy,
-    // and the V prescale if the block's scales leave [2^kSvLow, 2^kSvTop)
-    const float vtest = __builtin_ldexpf(vmx, ws.sv);
-    const bool move_sv = !(vtest < static_cast<float>(1 << kSvTop)) ||
-                         vtest < static_cast<float>(1 << kSvLow);
-    const bool move_m = mx > ws.m + kLazy;
-    if (__builtin_amdgcn_ballot_w64(move_m) != 0 || move_sv) {  // wave-uniform branch
-      const float m_new = move_m ? mx : ws.m;
+  // Move the reference when any row's block max overshoots it by more than
+  // kLazy, the V prescale when the block's largest V scale leaves
+  // [2^kSvLow, 2^kSvTop) after scaling; both decisions are wave-uniform.
+  const bool move_m = !ws.live || __builtin_amdgcn_ballot_w64(lmx > ws.m + kLazy) != 0;
+  const bool move_sv = !ws.live || __builtin_amdgcn_ballot_w64(!(lvs < ws.vhi)) != 0 ||
+                       __builtin_amdgcn_ballot_w64(lvs >= ws.vlo) == 0;
+  if (move_m || move_sv) {
+    const float mx = qblock_max(lmx);  // row max over the block; finite
+    float vmx = fmaxf(lvs, dpp<kRowRor4>(lvs));
+    vmx = qblock_max(fmaxf(vmx, dpp<kRowRor8>(vmx)));  // block max over the wave
+    const float m_new = ws.live ? (mx > ws.m + kLazy ? mx : ws.m) : mx;
+    const int sv_new = move_sv ? prescale_exp(vmx, kSvTop) : ws.sv;
+    if (ws.live) {
       const float alpha = fast_exp2(ws.m - m_new);
-      const int sv_new = move_sv ? prescale_exp(vmx, kSvTop) : ws.sv;
       ws.z *= alpha;
-      ws.m = m_new;
       const float t = __builtin_ldexpf(1.0f, sv_new - ws.sv);
-      ws.sv = sv_new;
       const float a0 = as_f32(__builtin_amdgcn_readlane(static_cast<int>(as_u32(alpha)), 0));
       const float a1 = as_f32(__builtin_amdgcn_readlane(static_cast<int>(as_u32(alpha)), 1));
       const float a2 = as_f32(__builtin_amdgcn_readlane(static_cast<int>(as_u32(alpha)), 2));
@@ -350,17 +388,20 @@ __device__ __forceinline__ void attend_block(Smem& sm, const BlockRegs& br, int 
         ws.acc[g][1] *= f;
       }
     }
+    ws.m = m_new;
+    ws.sv = sv_new;
+    ws.vhi = __builtin_ldexpf(1.0f, kSvTop - sv_new);
+    ws.vlo = __builtin_ldexpf(1.0f, kSvLow - sv_new);
+    ws.live = true;
   }
 
   // pt = 2^(s - m + Sv) (the V prescale rides in the exponent), z += sum p
   const float shift = static_cast<float>(ws.sv) - ws.m;
-  float pt[8], psum = 0.0f;
+  float pt[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    pt[t] = fast_exp2(sc[t] + shift);
-    psum += pt[t];
-  }
-  ws.z = fmaf(qblock_sum(psum), __builtin_ldexpf(1.0f, -ws.sv), ws.z);
+  for (int t = 0; t < 8; ++t) pt[t] = fast_exp2(fmaf(raw[t], us, shift));
+  const float psum = ((pt[0] + pt[1]) + (pt[2] + pt[3])) + ((pt[4] + pt[5]) + (pt[6] + pt[7]));
+  ws.z = fmaf(psum, __builtin_ldexpf(1.0f, -ws.sv), ws.z);
 
   // p~ = pt * sV[token][G'] for this lane's value group, in k-slot order
   half8_t ah, al;
@@ -375,12 +416,15 @@ __device__ __forceinline__ void attend_block(Smem& sm, const BlockRegs& br, int 
     for (int j = 0; j < 8; ++j) xv[j] = xt[kSlotByte[j]];
     split_hilo(xv, ah, al);
   }
+  load_vs(br, h, next, lo_);
 
   // u[4G'+r][f] += p~ x V codes, one feature group of 32 at a time
+  const uint8_t* vnext = h.vc + static_cast<long long>(next) * kBlockBytes + lo_.v_off;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     half8_t be, bo;
     codes_to_half(br.v[g], cc, be, bo);
+    br.v[g] = *reinterpret_cast<const i32x2*>(vnext + g * 128);  // next block's group
     ws.acc[g][0] = mfma(ah, be, ws.acc[g][0]);
     ws.acc[g][0] = mfma(al, be, ws.acc[g][0]);
     ws.acc[g][1] = mfma(ah, bo, ws.acc[g][1]);
@@ -388,13 +432,13 @@ __device__ __forceinline__ void attend_block(Smem& sm, const BlockRegs& br, int 
   }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 attend_mfma_r4_kernel(AttendProblem p) {
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;  // MFMA column / A row
   const int q = lane >> 4;  // MFMA k-block / output row quad
 
@@ -429,28 +473,39 @@ attend_mfma_r4_kernel(AttendProblem p) {
   const int b_first = b_begin + wave;
   const int b_last = b_first + (b_end - 1 - b_first) / kWaves * kWaves;  // valid if b_first < b_end
 
-  // q * qscale of the head's query rows into LDS: thread -> (row tid >> 6,
-  // channels 2 (tid & 63), +1).  Rows past `rows` are zero.
-  {
-    const int rq = tid >> 6, c = (tid & 63) * 2;
-    float a = 0.0f, b = 0.0f;
-    if (rq < rows) {
-      const float* qrow = p.q + (bh * rows + rq) * kD + c;
-      a = qrow[0] * p.qscale;
-      b = qrow[1] * p.qscale;
-    }
-    sm.qs[rq][c] = a;
-    sm.qs[rq][c + 1] = b;
-  }
-  __syncthreads();
   // this lane's K-scale slot in the q~ precompute: channels d0 .. d0+7
   const int d0 = ((lane >> 2) & 3) * 32 + (lane & 3) * 8;
+  const Lanes lo = lane_offsets(lane, d0);
+
+  // The block holding token N-1 is masked when N is not a multiple of 32;
+  // the wave that owns it attends it first, so only the peeled first block
+  // carries masking code.  Its loads go out before the query is staged.
+  const bool active = b_first < b_end;  // wave-uniform
+  const bool partial = (p.N % kBlockTokens) != 0 && b_last == nblocks - 1;
+  const int first = partial ? b_last : b_first;
+  const int loop_begin = partial ? b_first : b_first + kWaves;
+  const int loop_end = partial ? b_last - kWaves : b_last;  // inclusive
+  BlockRegs br;
+  if (active) load_block(br, h, first, lo);
+
+  // q * qscale of the head's query rows into LDS, output slot e = tid +
+  // j * kThreads -> (row e >> 7, channel e & 127).  Rows past `rows` are zero.
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < kOut) {
+      const int rq = e >> 7, c = e & 127;
+      sm.qs[rq][c] = rq < rows ? p.q[(bh * rows + rq) * kD + c] * p.qscale : 0.0f;
+    }
+  }
+  __syncthreads();
 
   const CodeConsts cc = code_consts();
   WaveState ws;
   ws.m = -INFINITY;
   ws.z = 0.0f;
   ws.sv = 0;
+  ws.vhi = ws.vlo = 0.0f;
   ws.live = false;
   {
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -458,23 +513,17 @@ attend_mfma_r4_kernel(AttendProblem p) {
     for (int g = 0; g < 4; ++g) ws.acc[g][0] = ws.acc[g][1] = zero4;
   }
 
-  if (b_first < b_end) {  // wave-uniform
-    // Two register sets: the next block's loads are always in flight while a
-    // block is attended (the last prefetch re-reads block b_last; it is
-    // never used).
-    BlockRegs ra, rb;
-    load_block(ra, h, b_first, lane, d0);
-    for (int b = b_first;;) {
-      load_block(rb, h, min(b + kWaves, b_last), lane, d0);
-      attend_block(sm, ra, b * kBlockTokens, t_end, cc, ws);
-      b += kWaves;
-      if (b > b_last) break;
-      load_block(ra, h, min(b + kWaves, b_last), lane, d0);
-      attend_block(sm, rb, b * kBlockTokens, t_end, cc, ws);
-      b += kWaves;
-      if (b > b_last) break;
-    }
+  if (active) {
+    // One register set: each part of the next block is loaded as soon as
+    // the current block has consumed that part.
+    attend_block<true>(sm, br, first * kBlockTokens, t_end, cc, ws, h,
+                       loop_begin <= loop_end ? loop_begin : first, lo);
+    for (int b = loop_begin; b <= loop_end; b += kWaves)
+      attend_block<false>(sm, br, b * kBlockTokens, t_end, cc, ws, h, min(b + kWaves, loop_end),
+                          lo);
   }
+  // z of each row: sum this lane's share over the four q-blocks
+  ws.z = qblock_sum(ws.z);
 
   // ---- this wave's u: lanes with q == G hold feature group G ----------------
   f32x4 ue = ws.acc[0][0], uo = ws.acc[0][1];
@@ -498,29 +547,37 @@ attend_mfma_r4_kernel(AttendProblem p) {
   }
   __syncthreads();
 
-  // ---- merge the waves: thread -> (row r, features f, f + 1) ---------------
-  const int r = tid >> 6;  // 0..3
-  const int f = (tid & 63) * 2;
-  float M = -INFINITY;
+  // ---- merge the waves: output slot e = tid + j * kThreads -> (row e >> 7,
+  // feature e & 127) -------------------------------------------------------
+  float M[kSlots], Z[kSlots], U[kSlots];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][r]);
-  float Z = 0.0f, U0 = 0.0f, U1 = 0.0f;
-  if (M != -INFINITY) {
+  for (int j = 0; j < kSlots; ++j) {
+    const int e = min(tid + j * kThreads, kOut - 1);
+    const int r = e >> 7, f = e & 127;
+    float m = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm.wm[w][r];
-      if (mw == -INFINITY) continue;
-      const float e = fast_exp2(mw - M);
-      Z = fmaf(e, sm.wz[w][r], Z);
-      U0 = fmaf(e, sm.u.wu[w][r][f], U0);
-      U1 = fmaf(e, sm.u.wu[w][r][f + 1], U1);
+    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm.wm[w][r]);
+    float z = 0.0f, u = 0.0f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm.wm[w][r];
+        if (mw == -INFINITY) continue;
+        const float x = fast_exp2(mw - m);
+        z = fmaf(x, sm.wz[w][r], z);
+        u = fmaf(x, sm.u.wu[w][r][f], u);
+      }
     }
+    M[j] = m;
+    Z[j] = z;
+    U[j] = u;
   }
   const long long row0 = bh * rows;
   if (p.splits == 1) {
-    if (r < rows) {
-      p.out[(row0 + r) * kD + f] = U0 / Z;
-      p.out[(row0 + r) * kD + f + 1] = U1 / Z;
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      const int e = tid + j * kThreads;
+      if (e < kOut && (e >> 7) < rows) p.out[(row0 + (e >> 7)) * kD + (e & 127)] = U[j] / Z[j];
     }
     return;
   }
@@ -533,14 +590,17 @@ attend_mfma_r4_kernel(AttendProblem p) {
   // loads.  (A device-scope release/acquire fence would instead write back
   // and invalidate the whole L2 of the XCD, once per workgroup.)
   const long long total_rows = static_cast<long long>(p.B) * p.Hkv * rows;
-  if (r < rows) {
-    const long long prow = split * total_rows + row0 + r;
-    __hip_atomic_store(&p.part_u[prow * kD + f], U0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&p.part_u[prow * kD + f + 1], U1, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    if (f == 0) {
-      __hip_atomic_store(&p.part_m[prow], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.part_z[prow], Z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    const int e = tid + j * kThreads;
+    const int r = e >> 7, f = e & 127;
+    if (e < kOut && r < rows) {
+      const long long prow = split * total_rows + row0 + r;
+      __hip_atomic_store(&p.part_u[prow * kD + f], U[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (f == 0) {
+        __hip_atomic_store(&p.part_m[prow], M[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.part_z[prow], Z[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above are acknowledged
@@ -552,45 +612,45 @@ attend_mfma_r4_kernel(AttendProblem p) {
   }
   __syncthreads();
   if (!sm.last) return;
-  if (r < rows) {
-    // Online merge over the splits, eight at a time so the loads of a batch
-    // are all in flight together.
-    const long long prow = row0 + r;
-    float Mg = -INFINITY, Zg = 0.0f, V0 = 0.0f, V1 = 0.0f;
-    for (int s0 = 0; s0 < p.splits; s0 += 8) {
-      float ms[8], zs[8], u0[8], u1[8];
+  // Online merge over the splits, eight at a time so the loads of a batch
+  // are all in flight together.
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sidx = s0 + j < p.splits ? s0 + j : s0;
-        const long long pr = sidx * total_rows + prow;
-        ms[j] = __hip_atomic_load(&p.part_m[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        zs[j] = __hip_atomic_load(&p.part_z[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        u0[j] = __hip_atomic_load(&p.part_u[pr * kD + f], __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-        u1[j] = __hip_atomic_load(&p.part_u[pr * kD + f + 1], __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-        if (s0 + j >= p.splits) ms[j] = -INFINITY;
+  for (int j = 0; j < kSlots; ++j) {
+    const int e = tid + j * kThreads;
+    const int r = e >> 7, f = e & 127;
+    if (e < kOut && r < rows) {
+      const long long prow = row0 + r;
+      float Mg = -INFINITY, Zg = 0.0f, Vg = 0.0f;
+      for (int s0 = 0; s0 < p.splits; s0 += 8) {
+        float ms[8], zs[8], us[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int sidx = s0 + i < p.splits ? s0 + i : s0;
+          const long long pr = sidx * total_rows + prow;
+          ms[i] = __hip_atomic_load(&p.part_m[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          zs[i] = __hip_atomic_load(&p.part_z[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          us[i] = __hip_atomic_load(&p.part_u[pr * kD + f], __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+          if (s0 + i >= p.splits) ms[i] = -INFINITY;
+        }
+        float mb = Mg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mb = fmaxf(mb, ms[i]);
+        if (mb == -INFINITY) continue;
+        const float a = fast_exp2(Mg - mb);  // 0 while nothing merged yet
+        Zg *= a;
+        Vg *= a;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (ms[i] == -INFINITY) continue;
+          const float x = fast_exp2(ms[i] - mb);
+          Zg = fmaf(x, zs[i], Zg);
+          Vg = fmaf(x, us[i], Vg);
+        }
+        Mg = mb;
       }
-      float mb = Mg;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mb = fmaxf(mb, ms[j]);
-      if (mb == -INFINITY) continue;
-      const float a = fast_exp2(Mg - mb);  // 0 while nothing merged yet
-      Zg *= a;
-      V0 *= a;
-      V1 *= a;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (ms[j] == -INFINITY) continue;
-        const float e = fast_exp2(ms[j] - mb);
-        Zg = fmaf(e, zs[j], Zg);
-        V0 = fmaf(e, u0[j], V0);
-        V1 = fmaf(e, u1[j], V1);
-      }
-      Mg = mb;
+      p.out[prow * kD + f] = Vg / Zg;
     }
-    p.out[prow * kD + f] = V0 / Zg;
-    p.out[prow * kD + f + 1] = V1 / Zg;
   }
   if (tid == 0) __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

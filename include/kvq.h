@@ -77,7 +77,7 @@ typedef enum kvq_status {
 typedef enum kvq_variant {
   KVQ_VARIANT_AUTO = 0,  /* what kvq_attend uses */
   KVQ_VARIANT_VALU = 1,  /* any supported format: decode a tile to float32 in LDS */
-  KVQ_VARIANT_MFMA = 2   /* 4-bit, group 32, D = 128, <= 4 query rows per KV head:
+  KVQ_VARIANT_MFMA = 2   /* 4-bit, group 32, D = 128, <= 32 query rows per KV head:
                             fp16 matrix cores on exact codes */
 } kvq_variant;
 
@@ -152,7 +152,7 @@ kvq_status kvq_attend(const float* q, const uint8_t* k_codes, const float* k_sca
 
 /* Same contract as kvq_attend with an explicit kernel family.
  * KVQ_VARIANT_MFMA returns KVQ_ERR_UNSUPPORTED unless bits == 4,
- * group == 32, D == 128, (Hq/Hkv)*R <= 4 and q and all four cache arrays
+ * group == 32, D == 128, (Hq/Hkv)*R <= 32 and q and all four cache arrays
  * are 16-byte aligned; KVQ_VARIANT_AUTO picks it whenever those hold. */
 kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,
                               const uint8_t* v_codes, const float* v_scales,

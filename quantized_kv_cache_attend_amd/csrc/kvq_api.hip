@@ -169,7 +169,7 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
 }
 
 bool mfma_eligible(const AttendProblem& p) {
-  return p.bits == 4 && p.group == 32 && p.D == 128 && p.rows <= kMfmaMaxRows &&
+  return p.bits == 4 && p.group == 32 && p.D == 128 && p.rows <= kMfma32MaxRows &&
          aligned(p.q, 16) && aligned(p.k_codes, 16) && aligned(p.v_codes, 16) &&
          aligned(p.k_scales, 16) && aligned(p.v_scales, 16);
 }
@@ -190,10 +190,24 @@ int mfma_auto_splits(int B, int Hkv, int N) {
   return static_cast<int>(s < general ? s : general);
 }
 
+// The 32-row kernel runs 4-wave workgroups, two per compute unit: about 512
+// workgroups, no split shorter than 2048 tokens.
+int mfma32_auto_splits(int B, int Hkv, int N) {
+  const long long heads = static_cast<long long>(B) * Hkv;
+  const long long want = (512 + heads - 1) / heads;
+  const long long cap = (N + 2047) / 2048;
+  long long s = want < cap ? want : cap;
+  if (s < 1) s = 1;
+  const long long general = auto_splits(B, Hkv, N);
+  return static_cast<int>(s < general ? s : general);
+}
+
 hipError_t run_mfma(AttendProblem p, bool auto_split, hipStream_t s) {
-  if (auto_split) p.splits = mfma_auto_splits(p.B, p.Hkv, p.N);
+  const bool wide = p.rows > kMfmaMaxRows;
+  if (auto_split)
+    p.splits = wide ? mfma32_auto_splits(p.B, p.Hkv, p.N) : mfma_auto_splits(p.B, p.Hkv, p.N);
   p.tokens_per_split = mfma_tokens_per_split(p.N, p.splits);
-  return launch_attend_mfma(p, s);
+  return wide ? launch_attend_mfma32(p, s) : launch_attend_mfma(p, s);
 }
 
 kvq_status codec_check(const void* a, const void* b, const void* c, int B, int H, int N, int D,
@@ -294,8 +308,8 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
     case KVQ_VARIANT_MFMA:
       if (!mfma_eligible(p))
         return fail(KVQ_ERR_UNSUPPORTED,
-                    "matrix-core kernel needs bits=4, group=32, D=128, <= %d query rows per "
-                    "KV head and 16-byte aligned q, codes and V scales", kMfmaMaxRows);
+                    "matrix-core kernels need bits=4, group=32, D=128, <= %d query rows per "
+                    "KV head and 16-byte aligned q and cache arrays", kMfma32MaxRows);
       return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
     default:
       return fail(KVQ_ERR_INVALID, "unknown variant %d", variant);

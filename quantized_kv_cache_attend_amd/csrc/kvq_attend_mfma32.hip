@@ -1,0 +1,563 @@
+// Matrix-core fused attention for the 4-bit, group-32, D=128 packed cache
+// with 5 to 32 query rows per KV head (GQA group x queries), rows padded to
+// 32 so both products fill whole 16x16 matrix-core tiles.
+//
+// Method: the blocked online softmax of "Block KV decoding: less workspace,
+// more time" (huhohoo.com/en/docs/llm/kv-block-decode-cost), section "Do not
+// average independently normalized blocks", and of "给长前缀列一张有单位的资源账本"
+// (codingai-lec05.pages.dev resource-ledger), section "why FlashAttention need
+// not keep the whole heat map": per query row a reference max m, an
+// exponential sum z and an unnormalized value sum u relative to 2^m, both
+// rescaled by 2^(m_old - m_new) when the reference moves (lazily: only when a
+// block's max exceeds it by more than 2^kLazy, which bounds p = 2^(s - m)).
+// Waves and KV splits are merged with the same rescale ("two stops of the
+// online accumulation" on the same page).
+//
+// Packed format: the 32-token block byte order of kvq_layout.h, whose K and V
+// blocks hand each lane its matrix-core operand bytes at consecutive
+// addresses (see the 4-row kernel in kvq_attend_mfma.hip for the byte map).
+// Codes become exact fp16 (c - 7) operands; float32 factors are split into
+// fp16 hi + lo (kvq_mfma_common.h).
+//
+// Math per 32-token block, one wave, row tile t = 0, 1 (rows 16t .. 16t+15):
+//   S^T[pair][16t + n] = codes^T (A: 16 token pairs x 32 channels, low and
+//     high nibbles as two products) x q~^T (B: 32 channels x 16 rows), with
+//     the hi and lo halves of q~ accumulated into the same tile;
+//   u[16t + m][f] += p~_g (A: 16 rows x 32 tokens, p~ = p * sV[token][g])
+//     x V codes (B: 32 tokens x 16 feature pairs of value group g).
+// The score tile gives lane (n, q) rows 16t + n and tokens 8q .. 8q+7, which
+// is exactly the A operand of the value product: no data moves between the
+// two products.
+//
+// q~ = q * qscale * sK[d][G] is formed per block: q * qscale sits in LDS,
+// prescaled per row by a power of two that puts its largest element in
+// [2^9, 2^10); K scales below 32 then keep every q~ inside the fp16 range
+// (a block whose K scales reach 32 is rescaled by a power of two first).
+#include "kvq_internal.h"
+#include "kvq_layout.h"
+#include "kvq_mfma_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kW = 4;            // waves per workgroup
+constexpr int kT = kW * 64;      // threads per workgroup
+constexpr int kR = 32;           // query rows per KV head (padded)
+constexpr int kD = 128;
+constexpr int kBB = 2048;        // K or V code bytes of one 32-token block
+constexpr int kBS = 128;         // K or V scales of one block
+constexpr int kQStride = 132;    // LDS row of q: 4 words of padding keep the
+                                 // 16 rows read by a quarter-wave on distinct banks
+constexpr float kLazy = 6.0f;    // reference moves only past m + kLazy
+constexpr int kSvTop = 9;        // V prescale: max V scale * 2^Sv in [2^8, 2^9),
+constexpr int kSvLow = 2;        //   kept while it stays in [2^2, 2^9)
+constexpr int kQTop = 10;        // q rows prescaled to max |.| in [2^9, 2^10)
+constexpr float kSkMax = 32.0f;  // K scales below this need no block rescale
+
+struct alignas(16) Smem32 {
+  union {
+    float qs[kR][kQStride];      // q * qscale * 2^Sq(row)
+    float wu[kW][kR][kD];        // per-wave u for the merge
+  } u;
+  float sks[kW][kBS];            // this block's K scales (per wave), channel order
+  float svs[kW][kBS];            // this block's V scales (per wave), [group][token]
+  float alp[kW][kR];             // rescale factors of a reference move (per wave)
+  float qus[kR];                 // 2^-Sq(row)
+  float wm[kW][kR];
+  float wz[kW][kR];
+  int last;
+};
+
+struct Regs32 {
+  i32x2 k[4];   // K codes, k-step 0..3
+  i32x2 v[4];   // V codes, value group 0..3
+  float2 ks;    // K scales 2 lane, 2 lane + 1 of the block
+  float2 vs;    // V scales 2 lane, 2 lane + 1 of the block ([group][token])
+};
+
+struct Head32 {
+  const uint8_t* kc;
+  const float* ksc;
+  const uint8_t* vc;
+  const float* vsc;
+};
+
+struct Lanes32 {
+  unsigned k_off, v_off, s_off;
+};
+
+__device__ __forceinline__ void load_scales32(Regs32& r, const Head32& h, int blk,
+                                              const Lanes32& o) {
+  r.ks = *reinterpret_cast<const float2*>(h.ksc + static_cast<long long>(blk) * kBS + o.s_off);
+  r.vs = *reinterpret_cast<const float2*>(h.vsc + static_cast<long long>(blk) * kBS + o.s_off);
+}
+__device__ __forceinline__ void load_block32(Regs32& r, const Head32& h, int blk,
+                                             const Lanes32& o) {
+  load_scales32(r, h, blk, o);
+  const uint8_t* kb = h.kc + static_cast<long long>(blk) * kBB + o.k_off;
+  const uint8_t* vb = h.vc + static_cast<long long>(blk) * kBB + o.v_off;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.k[i] = *reinterpret_cast<const i32x2*>(kb + i * 512);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.v[i] = *reinterpret_cast<const i32x2*>(vb + i * 128);
+}
+
+// Running state of one wave.  Lane (n, q) owns score rows 16t + n (t = 0, 1):
+// m[t] is that row's reference max (equal in all its lanes), z[t] the sum of
+// p over this lane's tokens 8q .. 8q+7 of every block (summed over the four
+// q-blocks at the end).  acc[g][t][e] holds u of rows 16t + 4q + i, features
+// 32g + 2n + e, in units of 2^(m + sv).
+struct State32 {
+  float m[2], z[2];
+  f32x4 acc[4][2][2];
+  int sv;
+  float vhi, vlo;
+  bool live;
+};
+
+template <bool kMasked>
+__device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0, int t_end,
+                                               const CodeConsts& cc, State32& st,
+                                               const Head32& h, int next, const Lanes32& lo,
+                                               const float us_row[2]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int q = lane >> 4;
+
+  // This block's scales into the wave's LDS slots; then reload them for the
+  // next block into the same registers.
+  *reinterpret_cast<float2*>(&sm.sks[wave][2 * lane]) = br.ks;
+  *reinterpret_cast<float2*>(&sm.svs[wave][2 * lane]) = br.vs;
+  const float lks = fmaxf(br.ks.x, br.ks.y);
+  const float lvs = fmaxf(br.vs.x, br.vs.y);
+  load_scales32(br, h, next, lo);
+
+  // A block whose K scales reach kSkMax is scaled down by 2^-e first
+  // (kf), and its scores back up (kun); otherwise both are 1.
+  float kf = 1.0f, kun = 1.0f;
+  if (__builtin_amdgcn_ballot_w64(lks >= kSkMax) != 0) {
+    float mx = fmaxf(lks, dpp<kRowRor1>(lks));
+    mx = fmaxf(mx, dpp<kRowRor2>(mx));
+    mx = fmaxf(mx, dpp<kRowRor4>(mx));
+    mx = fmaxf(mx, dpp<kRowRor8>(mx));
+    mx = qblock_max(mx);
+    const int e = __builtin_amdgcn_frexp_expf(mx);
+    kf = __builtin_ldexpf(1.0f, -e);
+    kun = __builtin_ldexpf(1.0f, e);
+  }
+  const float us0 = us_row[0] * kun, us1 = us_row[1] * kun;
+
+  // ---- S^T = codes^T * q~^T, 4 k-steps of 32 channels, two row tiles ------
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 se[2] = {zero4, zero4}, so[2] = {zero4, zero4};
+  const uint8_t* knext = h.kc + static_cast<long long>(next) * kBB + lo.k_off;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c0 = ks * 32 + q * 8;
+    f32x4 sa = *reinterpret_cast<const f32x4*>(&sm.sks[wave][c0]);
+    f32x4 sb = *reinterpret_cast<const f32x4*>(&sm.sks[wave][c0 + 4]);
+    sa *= kf;
+    sb *= kf;
+    half8_t bh[2], bl[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float* qrow = &sm.u.qs[16 * t + n][c0];
+      const f32x4 qa = *reinterpret_cast<const f32x4*>(qrow);
+      const f32x4 qb = *reinterpret_cast<const f32x4*>(qrow + 4);
+      float x[8], xs[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = qa[i] * sa[i];
+        x[i + 4] = qb[i] * sb[i];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[j] = x[kSlotByte[j]];
+      split_hilo(xs, bh[t], bl[t]);
+    }
+    half8_t alo, ahi;
+    codes_to_half(br.k[ks], cc, alo, ahi);
+    br.k[ks] = *reinterpret_cast<const i32x2*>(knext + ks * 512);  // next block's k-step
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      se[t] = mfma(alo, bh[t], se[t]);
+      se[t] = mfma(alo, bl[t], se[t]);
+      so[t] = mfma(ahi, bh[t], so[t]);
+      so[t] = mfma(ahi, bl[t], so[t]);
+    }
+  }
+
+  // raw[t][j]: row 16t + n, token 8q + j, in units of 2^Sq(row) (x kf)
+  float raw[2][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      raw[t][2 * i] = se[t][i];
+      raw[t][2 * i + 1] = so[t][i];
+    }
+    if (kMasked) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (tok0 + 8 * q + j >= t_end) raw[t][j] = -INFINITY;
+    }
+  }
+  const float us[2] = {us0, us1};
+  float lmx[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    lmx[t] = fmaxf(fmaxf(fmaxf(raw[t][0], raw[t][1]), fmaxf(raw[t][2], raw[t][3])),
+                   fmaxf(fmaxf(raw[t][4], raw[t][5]), fmaxf(raw[t][6], raw[t][7]))) * us[t];
+
+  // Move the reference of rows that overshoot it by more than kLazy, and the
+  // V prescale when the block's largest V scale leaves [2^kSvLow, 2^kSvTop)
+  // after scaling; both decisions are wave-uniform.
+  const bool move_m =
+      !st.live || __builtin_amdgcn_ballot_w64(lmx[0] > st.m[0] + kLazy ||
+                                              lmx[1] > st.m[1] + kLazy) != 0;
+  const bool move_sv = !st.live || __builtin_amdgcn_ballot_w64(!(lvs < st.vhi)) != 0 ||
+                       __builtin_amdgcn_ballot_w64(lvs >= st.vlo) == 0;
+  if (move_m || move_sv) {
+    float vmx = fmaxf(lvs, dpp<kRowRor1>(lvs));
+    vmx = fmaxf(vmx, dpp<kRowRor2>(vmx));
+    vmx = fmaxf(vmx, dpp<kRowRor4>(vmx));
+    vmx = qblock_max(fmaxf(vmx, dpp<kRowRor8>(vmx)));  // block max over the wave
+    const int sv_new = move_sv ? prescale_exp(vmx, kSvTop) : st.sv;
+    float m_new[2], alpha[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float mx = qblock_max(lmx[t]);  // row max over the block; finite
+      m_new[t] = st.live ? (mx > st.m[t] + kLazy ? mx : st.m[t]) : mx;
+      alpha[t] = st.live ? fast_exp2(st.m[t] - m_new[t]) : 0.0f;
+      st.z[t] *= alpha[t];
+      st.m[t] = m_new[t];
+    }
+    if (st.live) {
+      // acc rows 16t + 4q + i take the factor of score row 16t + 4q + i,
+      // owned by lanes n = 4q + i: exchange through this wave's LDS slot.
+      if (q == 0) {
+        sm.alp[wave][n] = alpha[0];
+        sm.alp[wave][16 + n] = alpha[1];
+      }
+      const float f = __builtin_ldexpf(1.0f, sv_new - st.sv);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x4 a = *reinterpret_cast<const f32x4*>(&sm.alp[wave][16 * t + 4 * q]);
+        a *= f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          st.acc[g][t][0] *= a;
+          st.acc[g][t][1] *= a;
+        }
+      }
+    }
+    st.sv = sv_new;
+    st.vhi = __builtin_ldexpf(1.0f, kSvTop - sv_new);
+    st.vlo = __builtin_ldexpf(1.0f, kSvLow - sv_new);
+    st.live = true;
+  }
+
+  // pt = 2^(s - m + Sv) (the V prescale rides in the exponent); z += sum p
+  float pt[2][8];
+  const float zf = __builtin_ldexpf(1.0f, -st.sv);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float shift = static_cast<float>(st.sv) - st.m[t];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pt[t][j] = fast_exp2(fmaf(raw[t][j], us[t], shift));
+    const float ps = ((pt[t][0] + pt[t][1]) + (pt[t][2] + pt[t][3])) +
+                     ((pt[t][4] + pt[t][5]) + (pt[t][6] + pt[t][7]));
+    st.z[t] = fmaf(ps, zf, st.z[t]);
+  }
+
+  // ---- u += p~ x V codes, one value group of 32 features at a time --------
+  const uint8_t* vnext = h.vc + static_cast<long long>(next) * kBB + lo.v_off;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 va = *reinterpret_cast<const f32x4*>(&sm.svs[wave][g * 32 + q * 8]);
+    const f32x4 vb = *reinterpret_cast<const f32x4*>(&sm.svs[wave][g * 32 + q * 8 + 4]);
+    half8_t ah[2], al[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float xt[8], xv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xt[i] = pt[t][i] * va[i];
+        xt[i + 4] = pt[t][i + 4] * vb[i];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] = xt[kSlotByte[j]];
+      split_hilo(xv, ah[t], al[t]);
+    }
+    half8_t be, bo;
+    codes_to_half(br.v[g], cc, be, bo);
+    br.v[g] = *reinterpret_cast<const i32x2*>(vnext + g * 128);  // next block's group
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st.acc[g][t][0] = mfma(ah[t], be, st.acc[g][t][0]);
+      st.acc[g][t][0] = mfma(al[t], be, st.acc[g][t][0]);
+      st.acc[g][t][1] = mfma(ah[t], bo, st.acc[g][t][1]);
+      st.acc[g][t][1] = mfma(al[t], bo, st.acc[g][t][1]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+attend_mfma_r32_kernel(AttendProblem p) {
+  __shared__ Smem32 sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int q = lane >> 4;
+
+  // Workgroup -> (KV head, split); all splits of a head on one XCD when the
+  // head count allows (workgroups are dealt to the 8 XCDs round-robin).
+  const int heads = p.B * p.Hkv;
+  const int L = blockIdx.x;
+  int head, split;
+  if (heads % 8 == 0) {
+    const int slot = L >> 3;
+    head = (L & 7) + 8 * (slot / p.splits);
+    split = slot % p.splits;
+  } else {
+    head = L / p.splits;
+    split = L % p.splits;
+  }
+  const long long bh = head;
+  const int rows = p.rows;
+  const int nblocks = (p.N + kBlockTokens - 1) / kBlockTokens;
+  Head32 h;
+  h.kc = p.k_codes + bh * nblocks * kBB;
+  h.ksc = p.k_scales + bh * nblocks * kBS;
+  h.vc = p.v_codes + bh * nblocks * kBB;
+  h.vsc = p.v_scales + bh * nblocks * kBS;
+
+  const int t_begin = split * p.tokens_per_split;
+  const int t_end = min(p.N, t_begin + p.tokens_per_split);
+  const int b_begin = t_begin / kBlockTokens;
+  const int b_end = t_end > t_begin ? (t_end + kBlockTokens - 1) / kBlockTokens : b_begin;
+  const int b_first = b_begin + wave;
+  const int b_last = b_first + (b_end - 1 - b_first) / kW * kW;  // valid if b_first < b_end
+  const Lanes32 lo = {static_cast<unsigned>(lane * 8), static_cast<unsigned>(q * 512 + n * 8),
+                      static_cast<unsigned>(lane * 2)};
+
+  // The block holding token N-1 is masked when N is not a multiple of 32;
+  // the wave that owns it attends it first.  Its loads go out before the
+  // query rows are staged.
+  const bool active = b_first < b_end;
+  const bool partial = (p.N % kBlockTokens) != 0 && b_last == nblocks - 1;
+  const int first = partial ? b_last : b_first;
+  const int loop_begin = partial ? b_first : b_first + kW;
+  const int loop_end = partial ? b_last - kW : b_last;  // inclusive
+  Regs32 br;
+  if (active) load_block32(br, h, first, lo);
+
+  // q * qscale into LDS, each row prescaled by 2^Sq so its largest element
+  // lies in [2^9, 2^10): thread -> (row tid >> 3, channels 16 (tid & 7) ..
+  // +15).  Rows past `rows` are zero.
+  {
+    const int r = tid >> 3, c0 = (tid & 7) * 16;
+    float v[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    if (r < rows) {
+      const float* qrow = p.q + (bh * rows + r) * kD + c0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(qrow + 4 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * i + j] = a[j] * p.qscale;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    const int sq = prescale_exp(amax, kQTop);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = __builtin_ldexpf(v[4 * i + j], sq);
+      *reinterpret_cast<f32x4*>(&sm.u.qs[r][c0 + 4 * i]) = a;
+    }
+    if ((tid & 7) == 0) sm.qus[r] = __builtin_ldexpf(1.0f, -sq);
+  }
+  __syncthreads();
+  const float us_row[2] = {sm.qus[n], sm.qus[16 + n]};
+
+  const CodeConsts cc = code_consts();
+  State32 st;
+  st.m[0] = st.m[1] = -INFINITY;
+  st.z[0] = st.z[1] = 0.0f;
+  st.sv = 0;
+  st.vhi = st.vlo = 0.0f;
+  st.live = false;
+  {
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) st.acc[g][t][0] = st.acc[g][t][1] = zero4;
+  }
+
+  if (active) {
+    attend_block32<true>(sm, br, first * kBlockTokens, t_end, cc, st, h,
+                         loop_begin <= loop_end ? loop_begin : first, lo, us_row);
+    for (int b = loop_begin; b <= loop_end; b += kW)
+      attend_block32<false>(sm, br, b * kBlockTokens, t_end, cc, st, h, min(b + kW, loop_end),
+                            lo, us_row);
+  }
+  st.z[0] = qblock_sum(st.z[0]);
+  st.z[1] = qblock_sum(st.z[1]);
+
+  // ---- merge the waves --------------------------------------------------
+  __syncthreads();  // every wave is done with q (aliased by wu)
+  {
+    const float fu = __builtin_ldexpf(1.0f, -st.sv);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float2 u2;
+          u2.x = st.acc[g][t][0][i] * fu;
+          u2.y = st.acc[g][t][1][i] * fu;
+          *reinterpret_cast<float2*>(&sm.u.wu[wave][16 * t + 4 * q + i][32 * g + 2 * n]) = u2;
+        }
+    if (q == 0) {
+      sm.wm[wave][n] = st.m[0];
+      sm.wm[wave][16 + n] = st.m[1];
+      sm.wz[wave][n] = st.z[0];
+      sm.wz[wave][16 + n] = st.z[1];
+    }
+  }
+  __syncthreads();
+
+  // thread -> (row r = tid >> 3, features f0 = 16 (tid & 7) .. +15)
+  const int r = tid >> 3;
+  const int f0 = (tid & 7) * 16;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) M = fmaxf(M, sm.wm[w][r]);
+  float Z = 0.0f;
+  float U[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) U[i] = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const float mw = sm.wm[w][r];
+      if (mw == -INFINITY) continue;
+      const float e = fast_exp2(mw - M);
+      Z = fmaf(e, sm.wz[w][r], Z);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.u.wu[w][r][f0 + 4 * i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) U[4 * i + j] = fmaf(e, a[j], U[4 * i + j]);
+      }
+    }
+  }
+  const long long row0 = bh * rows;
+  if (p.splits == 1) {
+    if (r < rows) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = U[4 * i + j] / Z;
+        *reinterpret_cast<f32x4*>(&p.out[(row0 + r) * kD + f0 + 4 * i]) = o;
+      }
+    }
+    return;
+  }
+
+  // Fused combine (as in the 4-row kernel): device-scope partial stores, a
+  // wait for their acknowledgement, a device-scope ticket, and the last
+  // workgroup of the head merges every split with device-scope loads.
+  const long long total_rows = static_cast<long long>(p.B) * p.Hkv * rows;
+  if (r < rows) {
+    const long long prow = split * total_rows + row0 + r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      __hip_atomic_store(&p.part_u[prow * kD + f0 + i], U[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    if ((tid & 7) == 0) {
+      __hip_atomic_store(&p.part_m[prow], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.part_z[prow], Z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above are acknowledged
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(&p.counters[bh], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = prev == static_cast<unsigned>(p.splits - 1);
+  }
+  __syncthreads();
+  if (!sm.last) return;
+  if (r < rows) {
+    // Online merge over the splits, four at a time so a batch's loads are in
+    // flight together.
+    const long long prow = row0 + r;
+    float Mg = -INFINITY, Zg = 0.0f, V[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) V[i] = 0.0f;
+    for (int s0 = 0; s0 < p.splits; s0 += 4) {
+      float ms[4], zs[4], us[4][16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sidx = s0 + j < p.splits ? s0 + j : s0;
+        const long long pr = sidx * total_rows + prow;
+        ms[j] = __hip_atomic_load(&p.part_m[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        zs[j] = __hip_atomic_load(&p.part_z[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          us[j][i] = __hip_atomic_load(&p.part_u[pr * kD + f0 + i], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        if (s0 + j >= p.splits) ms[j] = -INFINITY;
+      }
+      float mb = Mg;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mb = fmaxf(mb, ms[j]);
+      if (mb == -INFINITY) continue;
+      const float a = fast_exp2(Mg - mb);  // 0 while nothing merged yet
+      Zg *= a;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) V[i] *= a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (ms[j] == -INFINITY) continue;
+        const float e = fast_exp2(ms[j] - mb);
+        Zg = fmaf(e, zs[j], Zg);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) V[i] = fmaf(e, us[j][i], V[i]);
+      }
+      Mg = mb;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = V[4 * i + j] / Zg;
+      *reinterpret_cast<f32x4*>(&p.out[prow * kD + f0 + 4 * i]) = o;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
+  hipLaunchKernelGGL(attend_mfma_r32_kernel, dim3(grid), dim3(kT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

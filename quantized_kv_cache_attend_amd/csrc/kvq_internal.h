@@ -51,10 +51,13 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scales, int B, int 
                           int bits, int group, bool k_style, float* out, hipStream_t stream);
 hipError_t launch_attend_valu(const AttendProblem& p, hipStream_t stream);
 hipError_t launch_attend_mfma(const AttendProblem& p, hipStream_t stream);
-// Query rows per KV head the matrix-core kernel handles, and its split
-// granularity (tokens per split rounded up to whole 256-token tiles).
+// Matrix-core kernels: up to kMfmaMaxRows query rows per KV head (4-row
+// kernel) and up to kMfma32MaxRows (32-row kernel); both take splits in
+// whole 32-token blocks.
 constexpr int kMfmaMaxRows = 4;
+constexpr int kMfma32MaxRows = 32;
 int mfma_tokens_per_split(int N, int splits);
+hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream);
 hipError_t launch_combine(const AttendProblem& p, hipStream_t stream);
 
 }  // namespace kvq

@@ -1,0 +1,142 @@
+// Device helpers shared by the matrix-core attention kernels: exact fp16
+// code operands, fp16 hi/lo splits of float32 factors, power-of-two
+// prescales and cross-lane reductions on 64-wide waves.  Internal header
+// (each kernel translation unit gets its own copy of these inline helpers).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ unsigned as_u32(float x) { return __builtin_bit_cast(unsigned, x); }
+__device__ __forceinline__ float as_f32(unsigned x) { return __builtin_bit_cast(float, x); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// S with max_abs * 2^S in [2^(top-1), 2^top) (0 for a zero maximum), clamped
+// so scaled values and inverse factors stay finite and normal in float32.
+__device__ __forceinline__ int prescale_exp(float max_abs, int top) {
+  if (!(max_abs > 0.0f)) return 0;
+  const int e = __builtin_amdgcn_frexp_expf(max_abs);
+  return min(100, max(-100, top - e));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return as_f32(static_cast<unsigned>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(as_u32(x)), kCtrl, 0xf, 0xf, true)));
+}
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// Lane ^ 16 and lane ^ 32 exchanges (gfx950 row swaps): returns both halves.
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  a = as_f32(r[0]);
+  b = as_f32(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  a = as_f32(r[0]);
+  b = as_f32(r[1]);
+}
+// Max / sum over the four 16-lane q-blocks of a wave (lanes n, n^16, n^32, n^48).
+__device__ __forceinline__ float qblock_max(float x) {
+  float a, b;
+  swap16(x, a, b);
+  x = fmaxf(a, b);
+  swap32(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float qblock_sum(float x) {
+  float a, b;
+  swap16(x, a, b);
+  x = a + b;
+  swap32(x, a, b);
+  return a + b;
+}
+
+// Constants kept in VGPRs: gfx9 VOP3 encodings take no literal operand and
+// at most one scalar one, so this lets each nibble extraction be a single
+// v_and_or_b32.
+struct CodeConsts {
+  unsigned lo_mask, hi_mask, magic;
+};
+__device__ __forceinline__ unsigned in_vgpr(unsigned x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ CodeConsts code_consts() {
+  return {in_vgpr(0x000F000Fu), in_vgpr(0x00F000F0u), in_vgpr(0x64006400u)};
+}
+
+// Eight code bytes b0..b7 -> fp16 (c - 7) of their low nibbles (lo) and high
+// nibbles (hi), in k-slot order (b0, b2, b1, b3, b4, b6, b5, b7).  OR-ing a
+// nibble into 0x6400 gives 1024 + c (low) or 1024 + 16c (high, masked in
+// place); one packed add, or multiply-add by 1/16, removes the bias exactly.
+__device__ __forceinline__ void codes_to_half(i32x2 w, const CodeConsts& k, half8_t& lo,
+                                              half8_t& hi) {
+  const half2_t bias_lo = {(_Float16)-1031.0f, (_Float16)-1031.0f};
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t bias_hi = {(_Float16)-71.0f, (_Float16)-71.0f};
+  const unsigned src[4] = {static_cast<unsigned>(w.x), static_cast<unsigned>(w.x) >> 8,
+                           static_cast<unsigned>(w.y), static_cast<unsigned>(w.y) >> 8};
+  u32x4 l, h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned xl = (src[i] & k.lo_mask) | k.magic;
+    const unsigned xh = (src[i] & k.hi_mask) | k.magic;
+    l[i] = __builtin_bit_cast(unsigned, __builtin_bit_cast(half2_t, xl) + bias_lo);
+    h[i] = __builtin_bit_cast(
+        unsigned, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, xh), sixteenth, bias_hi));
+  }
+  lo = __builtin_bit_cast(half8_t, l);
+  hi = __builtin_bit_cast(half8_t, h);
+}
+
+// k-slot j of a converted operand holds byte kSlotByte[j] of the 8 read.
+__device__ constexpr int kSlotByte[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+
+__device__ __forceinline__ f32x4 mfma(half8_t a, half8_t b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// x - (float)h for the fp16 h in half `sel` of a packed pair: one
+// v_fma_mix_f32 (the fp16 operand is widened inside the instruction).
+template <int kSel>
+__device__ __forceinline__ float sub_half(float x, unsigned h2) {
+  float r;
+  if (kSel == 0)
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h2), "v"(x));
+  else
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(r) : "v"(h2), "v"(x));
+  return r;
+}
+
+// fp16 hi/lo split of 8 float32 values, packed in k-slot order: hi rounds
+// toward zero, lo is the exact float32 remainder rounded toward zero.
+__device__ __forceinline__ void split_hilo(const float x[8], half8_t& hi, half8_t& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned hp = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(x[2 * i], x[2 * i + 1]));
+    const float r0 = sub_half<0>(x[2 * i], hp);
+    const float r1 = sub_half<1>(x[2 * i + 1], hp);
+    h[i] = hp;
+    l[i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+  }
+  hi = __builtin_bit_cast(half8_t, h);
+  lo = __builtin_bit_cast(half8_t, l);
+}
+
+}  // namespace
+}  // namespace kvq

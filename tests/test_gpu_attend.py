@@ -31,8 +31,8 @@ def _oracle(q, k, v, bits, group):
     return O.attend_packed(q, kc, ks, vc, vs, k.shape[2], bits, group)
 
 
-VARIANTS = ["valu"]                 # head dim 32 or > 4 rows per KV head: VALU kernel only
-MFMA_VARIANTS = ["valu", "mfma", "auto"]  # 4-bit g32 D=128 with <= 4 rows per KV head
+VARIANTS = ["valu"]                 # head dim 32: VALU kernel only
+MFMA_VARIANTS = ["valu", "mfma", "auto"]  # 4-bit g32 D=128 with <= 32 rows per KV head
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -86,7 +86,7 @@ def test_attend_gqa_n4096_full(variant):
         assert max_abs(outs[s], outs[0]) <= SPLIT_TOL
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", MFMA_VARIANTS)
 @pytest.mark.parametrize("seed", [0, 1])
 def test_attend_gqa_n32768_sampled(variant, seed):
     """Full-size long-context workload (16 splits).  The GPU attends over the
@@ -183,3 +183,50 @@ def test_attend_mfma_rejects_unsupported():
     with pytest.raises(kvq.KvqError) as e:
         _run(q, cache, w.N, 4, 32, variant="mfma")
     assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("hq,hkv,r", [(8, 1, 4), (16, 2, 2), (5, 1, 1), (12, 3, 8), (6, 1, 3)])
+@pytest.mark.parametrize("n", [1, 7, 35, 1021, 4097])
+def test_attend_mfma32_ragged_and_gqa_shapes(hq, hkv, r, n):
+    """32-row matrix-core kernel: 5..32 query rows per KV head (padded to 32),
+    ragged token counts, empty trailing splits."""
+    w = Workload("mfma32", 2, hq, hkv, r, n, 128, ((4, 32),))
+    q, k, v = make_qkv(w, 6)
+    announce(f"attend mfma32 hq={hq} hkv={hkv} r={r} n={n}")
+    want = _oracle(q, k, v, 4, 32)
+    cache = _gpu_cache(k, v, 4, 32)
+    for splits in (1, 3, 0, 64):
+        got = _run(q, cache, n, 4, 32, num_splits=splits, variant="mfma")
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
+
+
+@pytest.mark.parametrize("dist", ["clean", "early", "late"])
+@pytest.mark.parametrize("scale_k", [False, True])
+def test_attend_mfma32_peaky_and_channel_scaled(dist, scale_k):
+    """C5-like heads (8 GQA heads x 4 queries per KV head) with biased keys and
+    log-uniform K channel scales."""
+    w = Workload("peaky32", 2, 16, 2, 4, 4096, 128, ((4, 32),), k_channel_scale=scale_k)
+    q, k, v = make_qkv(w, 7, dist)
+    announce(f"attend mfma32 peaky dist={dist} scale_k={scale_k}")
+    want = _oracle(q, k, v, 4, 32)
+    cache = _gpu_cache(k, v, 4, 32)
+    for splits in (1, 0):
+        got = _run(q, cache, w.N, 4, 32, num_splits=splits, variant="mfma")
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
+
+
+@pytest.mark.parametrize("hq,r", [(4, 1), (16, 2)])
+def test_attend_mfma_large_k_scales(hq, r):
+    """K magnitudes large enough that K scales reach 32 (the 32-row kernel
+    rescales such blocks by a power of two) and very peaky softmax."""
+    w = Workload("bigk", 1, hq, 1, r, 1000, 128, ((4, 32),))
+    q, k, v = make_qkv(w, 8)
+    k = (k * np.float32(300.0)).astype(np.float32)
+    k[0, 0, 500:532] *= np.float32(0.01)   # one group with small scales among large ones
+    announce(f"attend mfma large K scales hq={hq} r={r}")
+    want = _oracle(q, k, v, 4, 32)
+    cache = _gpu_cache(k, v, 4, 32)
+    for splits in (1, 0):
+        got = _run(q, cache, w.N, 4, 32, num_splits=splits, variant="mfma")
+        assert np.all(np.isfinite(got))
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))

@@ -57,7 +57,7 @@ constexpr float kSkMax = 32.0f;  // K scales below this need no block rescale
 struct alignas(16) Smem32 {
   union {
     float qs[kR][kQStride];      // q * qscale * 2^Sq(row)
-    float wu[kW][kR][kD];        // per-wave u for the merge
+    float wu[2][kR][kD];         // u of two waves at a time, for the merge
   } u;
   float sks[kW][kBS];            // this block's K scales (per wave), channel order
   float svs[kW][kBS];            // this block's V scales (per wave), [group][token]
@@ -75,66 +75,112 @@ struct Regs32 {
   float2 vs;    // V scales 2 lane, 2 lane + 1 of the block ([group][token])
 };
 
+// Buffer descriptors of one KV head's four arrays (SGPRs): loads take a
+// 32-bit lane offset in a VGPR and the block offset in an SGPR, so no 64-bit
+// per-lane address is kept in registers, and an offset past the head's
+// arrays reads zero instead of faulting.
 struct Head32 {
-  const uint8_t* kc;
-  const float* ksc;
-  const uint8_t* vc;
-  const float* vsc;
+  __amdgpu_buffer_rsrc_t kc, ksc, vc, vsc;
 };
 
+// Raw buffer descriptor word 3 for gfx9-family MUBUF loads (32-bit data
+// format, no swizzle, no index stride).
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRawBufferWord3);
+}
+
 struct Lanes32 {
-  unsigned k_off, v_off, s_off;
+  unsigned k_off, v_off, s_off;  // byte offsets of this lane in a block
 };
+
+__device__ __forceinline__ i32x2 buf_b64(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+  return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ float2 buf_f2(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
 
 __device__ __forceinline__ void load_scales32(Regs32& r, const Head32& h, int blk,
                                               const Lanes32& o) {
-  r.ks = *reinterpret_cast<const float2*>(h.ksc + static_cast<long long>(blk) * kBS + o.s_off);
-  r.vs = *reinterpret_cast<const float2*>(h.vsc + static_cast<long long>(blk) * kBS + o.s_off);
+  r.ks = buf_f2(h.ksc, o.s_off, blk * kBS * 4);
+  r.vs = buf_f2(h.vsc, o.s_off, blk * kBS * 4);
 }
 __device__ __forceinline__ void load_block32(Regs32& r, const Head32& h, int blk,
                                              const Lanes32& o) {
   load_scales32(r, h, blk, o);
-  const uint8_t* kb = h.kc + static_cast<long long>(blk) * kBB + o.k_off;
-  const uint8_t* vb = h.vc + static_cast<long long>(blk) * kBB + o.v_off;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.k[i] = *reinterpret_cast<const i32x2*>(kb + i * 512);
+  for (int i = 0; i < 4; ++i) r.k[i] = buf_b64(h.kc, o.k_off + i * 512, blk * kBB);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = *reinterpret_cast<const i32x2*>(vb + i * 128);
+  for (int i = 0; i < 4; ++i) r.v[i] = buf_b64(h.vc, o.v_off + i * 128, blk * kBB);
 }
 
 // Running state of one wave.  Lane (n, q) owns score rows 16t + n (t = 0, 1):
 // m[t] is that row's reference max (equal in all its lanes), z[t] the sum of
 // p over this lane's tokens 8q .. 8q+7 of every block (summed over the four
 // q-blocks at the end).  acc[g][t][e] holds u of rows 16t + 4q + i, features
-// 32g + 2n + e, in units of 2^(m + sv).
+// 32g + 2n + e, in units of 2^(m + sv).  vscale = 2^sv multiplies the V
+// scales parked in LDS; vhi / vlo bound the V scales that keep sv valid.
 struct State32 {
   float m[2], z[2];
   f32x4 acc[4][2][2];
   int sv;
-  float vhi, vlo;
+  float vscale, vhi, vlo;
   bool live;
 };
+
+// Packed fp16 pair of exact residuals a.x*b.x - h.lo, a.y*b.y - h.hi, each
+// computed by one fused multiply-add and rounded once to fp16
+// (v_fma_mixlo_f16 / v_fma_mixhi_f16 widen the fp16 operand internally).
+__device__ __forceinline__ unsigned residual_pair(float a0, float b0, float a1, float b1,
+                                                  unsigned h) {
+  unsigned d;
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(d) : "v"(a0), "v"(b0), "v"(h));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "+v"(d)
+      : "v"(a1), "v"(b1), "v"(h));
+  return d;
+}
+
+// fp16 hi/lo operands of the 8 products x[j] = a[j] * b[j], j in k-slot
+// order: hi = fp16(fp16(a) * fp16(b)) (one packed multiply per pair), lo =
+// the exact residual x - hi rounded to fp16.  a, b are float32 with their
+// fp16 (round-toward-zero) pairs a16, b16 precomputed in the same order.
+__device__ __forceinline__ void product_hilo(const float a[8], const float b[8],
+                                             const half2_t a16[4], const half2_t b16[4],
+                                             half8_t& hi, half8_t& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned hp = __builtin_bit_cast(unsigned, a16[i] * b16[i]);
+    h[i] = hp;
+    l[i] = residual_pair(a[2 * i], b[2 * i], a[2 * i + 1], b[2 * i + 1], hp);
+  }
+  hi = __builtin_bit_cast(half8_t, h);
+  lo = __builtin_bit_cast(half8_t, l);
+}
+
+__device__ __forceinline__ half2_t pk16(float x, float y) {
+  return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(x, y));
+}
 
 template <bool kMasked>
 __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0, int t_end,
                                                const CodeConsts& cc, State32& st,
                                                const Head32& h, int next, const Lanes32& lo,
-                                               const float us_row[2]) {
+                                               const float us_row[2], const float (&qk)[2][4][8]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int q = lane >> 4;
 
-  // This block's scales into the wave's LDS slots; then reload them for the
-  // next block into the same registers.
-  *reinterpret_cast<float2*>(&sm.sks[wave][2 * lane]) = br.ks;
-  *reinterpret_cast<float2*>(&sm.svs[wave][2 * lane]) = br.vs;
+  // ---- block set-up: scale guards, then this block's scales into LDS ------
   const float lks = fmaxf(br.ks.x, br.ks.y);
   const float lvs = fmaxf(br.vs.x, br.vs.y);
-  load_scales32(br, h, next, lo);
-
-  // A block whose K scales reach kSkMax is scaled down by 2^-e first
-  // (kf), and its scores back up (kun); otherwise both are 1.
+  // A block whose K scales reach kSkMax is scaled down by 2^-e (kf) and its
+  // scores back up (kun); otherwise both are 1.
   float kf = 1.0f, kun = 1.0f;
   if (__builtin_amdgcn_ballot_w64(lks >= kSkMax) != 0) {
     float mx = fmaxf(lks, dpp<kRowRor1>(lks));
@@ -146,38 +192,68 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
     kf = __builtin_ldexpf(1.0f, -e);
     kun = __builtin_ldexpf(1.0f, e);
   }
+  // V prescale 2^sv: set so the largest V scale lands in [2^8, 2^9), moved
+  // only when the block's largest V scale leaves [2^kSvLow, 2^kSvTop) after
+  // scaling (u is rescaled by the change; z does not carry it).
+  if (!st.live || __builtin_amdgcn_ballot_w64(!(lvs < st.vhi)) != 0 ||
+      __builtin_amdgcn_ballot_w64(lvs >= st.vlo) == 0) {
+    float vmx = fmaxf(lvs, dpp<kRowRor1>(lvs));
+    vmx = fmaxf(vmx, dpp<kRowRor2>(vmx));
+    vmx = fmaxf(vmx, dpp<kRowRor4>(vmx));
+    vmx = qblock_max(fmaxf(vmx, dpp<kRowRor8>(vmx)));
+    const int sv_new = prescale_exp(vmx, kSvTop);
+    if (st.live) {
+      const float f = __builtin_ldexpf(1.0f, sv_new - st.sv);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          st.acc[g][t][0] *= f;
+          st.acc[g][t][1] *= f;
+        }
+    }
+    st.sv = sv_new;
+    st.vscale = __builtin_ldexpf(1.0f, sv_new);
+    st.vhi = __builtin_ldexpf(1.0f, kSvTop - sv_new);
+    st.vlo = __builtin_ldexpf(1.0f, kSvLow - sv_new);
+  }
+  {
+    float2 k2 = br.ks, v2 = br.vs;
+    k2.x *= kf;
+    k2.y *= kf;
+    v2.x *= st.vscale;
+    v2.y *= st.vscale;
+    *reinterpret_cast<float2*>(&sm.sks[wave][2 * lane]) = k2;
+    *reinterpret_cast<float2*>(&sm.svs[wave][2 * lane]) = v2;
+  }
+  load_scales32(br, h, next, lo);  // next block's scales into the same registers
   const float us0 = us_row[0] * kun, us1 = us_row[1] * kun;
 
   // ---- S^T = codes^T * q~^T, 4 k-steps of 32 channels, two row tiles ------
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 se[2] = {zero4, zero4}, so[2] = {zero4, zero4};
-  const uint8_t* knext = h.kc + static_cast<long long>(next) * kBB + lo.k_off;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int c0 = ks * 32 + q * 8;
-    f32x4 sa = *reinterpret_cast<const f32x4*>(&sm.sks[wave][c0]);
-    f32x4 sb = *reinterpret_cast<const f32x4*>(&sm.sks[wave][c0 + 4]);
-    sa *= kf;
-    sb *= kf;
+    const f32x4 sa = *reinterpret_cast<const f32x4*>(&sm.sks[wave][c0]);
+    const f32x4 sb = *reinterpret_cast<const f32x4*>(&sm.sks[wave][c0 + 4]);
+    float sk[8];  // k-slot order
+    sk[0] = sa[0]; sk[1] = sa[2]; sk[2] = sa[1]; sk[3] = sa[3];
+    sk[4] = sb[0]; sk[5] = sb[2]; sk[6] = sb[1]; sk[7] = sb[3];
+    half2_t sk16[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sk16[i] = pk16(sk[2 * i], sk[2 * i + 1]);
     half8_t bh[2], bl[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float* qrow = &sm.u.qs[16 * t + n][c0];
-      const f32x4 qa = *reinterpret_cast<const f32x4*>(qrow);
-      const f32x4 qb = *reinterpret_cast<const f32x4*>(qrow + 4);
-      float x[8], xs[8];
+      half2_t q16[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = qa[i] * sa[i];
-        x[i + 4] = qb[i] * sb[i];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xs[j] = x[kSlotByte[j]];
-      split_hilo(xs, bh[t], bl[t]);
+      for (int i = 0; i < 4; ++i) q16[i] = pk16(qk[t][ks][2 * i], qk[t][ks][2 * i + 1]);
+      product_hilo(qk[t][ks], sk, q16, sk16, bh[t], bl[t]);
     }
     half8_t alo, ahi;
     codes_to_half(br.k[ks], cc, alo, ahi);
-    br.k[ks] = *reinterpret_cast<const i32x2*>(knext + ks * 512);  // next block's k-step
+    br.k[ks] = buf_b64(h.kc, lo.k_off + ks * 512, next * kBB);  // next block's k-step
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       se[t] = mfma(alo, bh[t], se[t]);
@@ -209,28 +285,18 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
     lmx[t] = fmaxf(fmaxf(fmaxf(raw[t][0], raw[t][1]), fmaxf(raw[t][2], raw[t][3])),
                    fmaxf(fmaxf(raw[t][4], raw[t][5]), fmaxf(raw[t][6], raw[t][7]))) * us[t];
 
-  // Move the reference of rows that overshoot it by more than kLazy, and the
-  // V prescale when the block's largest V scale leaves [2^kSvLow, 2^kSvTop)
-  // after scaling; both decisions are wave-uniform.
-  const bool move_m =
-      !st.live || __builtin_amdgcn_ballot_w64(lmx[0] > st.m[0] + kLazy ||
-                                              lmx[1] > st.m[1] + kLazy) != 0;
-  const bool move_sv = !st.live || __builtin_amdgcn_ballot_w64(!(lvs < st.vhi)) != 0 ||
-                       __builtin_amdgcn_ballot_w64(lvs >= st.vlo) == 0;
-  if (move_m || move_sv) {
-    float vmx = fmaxf(lvs, dpp<kRowRor1>(lvs));
-    vmx = fmaxf(vmx, dpp<kRowRor2>(vmx));
-    vmx = fmaxf(vmx, dpp<kRowRor4>(vmx));
-    vmx = qblock_max(fmaxf(vmx, dpp<kRowRor8>(vmx)));  // block max over the wave
-    const int sv_new = move_sv ? prescale_exp(vmx, kSvTop) : st.sv;
-    float m_new[2], alpha[2];
+  // Move the reference of rows that overshoot it by more than kLazy (a
+  // wave-uniform decision).
+  if (!st.live || __builtin_amdgcn_ballot_w64(lmx[0] > st.m[0] + kLazy ||
+                                              lmx[1] > st.m[1] + kLazy) != 0) {
+    float alpha[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float mx = qblock_max(lmx[t]);  // row max over the block; finite
-      m_new[t] = st.live ? (mx > st.m[t] + kLazy ? mx : st.m[t]) : mx;
-      alpha[t] = st.live ? fast_exp2(st.m[t] - m_new[t]) : 0.0f;
+      const float m_new = st.live ? (mx > st.m[t] + kLazy ? mx : st.m[t]) : mx;
+      alpha[t] = st.live ? fast_exp2(st.m[t] - m_new) : 0.0f;
       st.z[t] *= alpha[t];
-      st.m[t] = m_new[t];
+      st.m[t] = m_new;
     }
     if (st.live) {
       // acc rows 16t + 4q + i take the factor of score row 16t + 4q + i,
@@ -239,11 +305,9 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
         sm.alp[wave][n] = alpha[0];
         sm.alp[wave][16 + n] = alpha[1];
       }
-      const float f = __builtin_ldexpf(1.0f, sv_new - st.sv);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        f32x4 a = *reinterpret_cast<const f32x4*>(&sm.alp[wave][16 * t + 4 * q]);
-        a *= f;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.alp[wave][16 * t + 4 * q]);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           st.acc[g][t][0] *= a;
@@ -251,47 +315,42 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
         }
       }
     }
-    st.sv = sv_new;
-    st.vhi = __builtin_ldexpf(1.0f, kSvTop - sv_new);
-    st.vlo = __builtin_ldexpf(1.0f, kSvLow - sv_new);
     st.live = true;
   }
 
-  // pt = 2^(s - m + Sv) (the V prescale rides in the exponent); z += sum p
-  float pt[2][8];
-  const float zf = __builtin_ldexpf(1.0f, -st.sv);
+  // p = 2^(s - m) <= 2^kLazy; z += sum p.  pk holds p in k-slot order.
+  float pk[2][8];
+  half2_t p16[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const float shift = static_cast<float>(st.sv) - st.m[t];
+    const float shift = -st.m[t];
+    float pt[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pt[t][j] = fast_exp2(fmaf(raw[t][j], us[t], shift));
-    const float ps = ((pt[t][0] + pt[t][1]) + (pt[t][2] + pt[t][3])) +
-                     ((pt[t][4] + pt[t][5]) + (pt[t][6] + pt[t][7]));
-    st.z[t] = fmaf(ps, zf, st.z[t]);
+    for (int j = 0; j < 8; ++j) pt[j] = fast_exp2(fmaf(raw[t][j], us[t], shift));
+    st.z[t] += ((pt[0] + pt[1]) + (pt[2] + pt[3])) + ((pt[4] + pt[5]) + (pt[6] + pt[7]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pk[t][j] = pt[kSlotByte[j]];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p16[t][i] = pk16(pk[t][2 * i], pk[t][2 * i + 1]);
   }
 
-  // ---- u += p~ x V codes, one value group of 32 features at a time --------
-  const uint8_t* vnext = h.vc + static_cast<long long>(next) * kBB + lo.v_off;
+  // ---- u += p~ x V codes, p~ = p * sV * 2^sv, one value group at a time ---
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const f32x4 va = *reinterpret_cast<const f32x4*>(&sm.svs[wave][g * 32 + q * 8]);
     const f32x4 vb = *reinterpret_cast<const f32x4*>(&sm.svs[wave][g * 32 + q * 8 + 4]);
+    float sv[8];  // k-slot order
+    sv[0] = va[0]; sv[1] = va[2]; sv[2] = va[1]; sv[3] = va[3];
+    sv[4] = vb[0]; sv[5] = vb[2]; sv[6] = vb[1]; sv[7] = vb[3];
+    half2_t sv16[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv16[i] = pk16(sv[2 * i], sv[2 * i + 1]);
     half8_t ah[2], al[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float xt[8], xv[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xt[i] = pt[t][i] * va[i];
-        xt[i + 4] = pt[t][i + 4] * vb[i];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xv[j] = xt[kSlotByte[j]];
-      split_hilo(xv, ah[t], al[t]);
-    }
+    for (int t = 0; t < 2; ++t) product_hilo(pk[t], sv, p16[t], sv16, ah[t], al[t]);
     half8_t be, bo;
     codes_to_half(br.v[g], cc, be, bo);
-    br.v[g] = *reinterpret_cast<const i32x2*>(vnext + g * 128);  // next block's group
+    br.v[g] = buf_b64(h.vc, lo.v_off + g * 128, next * kBB);  // next block's group
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       st.acc[g][t][0] = mfma(ah[t], be, st.acc[g][t][0]);
@@ -329,10 +388,10 @@ attend_mfma_r32_kernel(AttendProblem p) {
   const int rows = p.rows;
   const int nblocks = (p.N + kBlockTokens - 1) / kBlockTokens;
   Head32 h;
-  h.kc = p.k_codes + bh * nblocks * kBB;
-  h.ksc = p.k_scales + bh * nblocks * kBS;
-  h.vc = p.v_codes + bh * nblocks * kBB;
-  h.vsc = p.v_scales + bh * nblocks * kBS;
+  h.kc = head_rsrc(p.k_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
+  h.ksc = head_rsrc(p.k_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
+  h.vc = head_rsrc(p.v_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
+  h.vsc = head_rsrc(p.v_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
 
   const int t_begin = split * p.tokens_per_split;
   const int t_end = min(p.N, t_begin + p.tokens_per_split);
@@ -341,7 +400,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
   const int b_first = b_begin + wave;
   const int b_last = b_first + (b_end - 1 - b_first) / kW * kW;  // valid if b_first < b_end
   const Lanes32 lo = {static_cast<unsigned>(lane * 8), static_cast<unsigned>(q * 512 + n * 8),
-                      static_cast<unsigned>(lane * 2)};
+                      static_cast<unsigned>(lane * 8)};
 
   // The block holding token N-1 is masked when N is not a multiple of 32;
   // the wave that owns it attends it first.  Its loads go out before the
@@ -389,12 +448,26 @@ attend_mfma_r32_kernel(AttendProblem p) {
   }
   __syncthreads();
   const float us_row[2] = {sm.qus[n], sm.qus[16 + n]};
+  // This lane's q values for the whole kernel (rows 16t + n, channels
+  // 32 ks + 8q + (0..7), k-slot order), kept in registers.
+  float qk[2][4][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float* qrow = &sm.u.qs[16 * t + n][ks * 32 + q * 8];
+      const f32x4 qa = *reinterpret_cast<const f32x4*>(qrow);
+      const f32x4 qb = *reinterpret_cast<const f32x4*>(qrow + 4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qk[t][ks][j] = j < 4 ? qa[kSlotByte[j]] : qb[kSlotByte[j] - 4];
+    }
 
   const CodeConsts cc = code_consts();
   State32 st;
   st.m[0] = st.m[1] = -INFINITY;
   st.z[0] = st.z[1] = 0.0f;
   st.sv = 0;
+  st.vscale = 1.0f;
   st.vhi = st.vlo = 0.0f;
   st.live = false;
   {
@@ -407,62 +480,67 @@ attend_mfma_r32_kernel(AttendProblem p) {
 
   if (active) {
     attend_block32<true>(sm, br, first * kBlockTokens, t_end, cc, st, h,
-                         loop_begin <= loop_end ? loop_begin : first, lo, us_row);
+                         loop_begin <= loop_end ? loop_begin : first, lo, us_row, qk);
     for (int b = loop_begin; b <= loop_end; b += kW)
       attend_block32<false>(sm, br, b * kBlockTokens, t_end, cc, st, h, min(b + kW, loop_end),
-                            lo, us_row);
+                            lo, us_row, qk);
   }
   st.z[0] = qblock_sum(st.z[0]);
   st.z[1] = qblock_sum(st.z[1]);
 
-  // ---- merge the waves --------------------------------------------------
-  __syncthreads();  // every wave is done with q (aliased by wu)
-  {
-    const float fu = __builtin_ldexpf(1.0f, -st.sv);
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float2 u2;
-          u2.x = st.acc[g][t][0][i] * fu;
-          u2.y = st.acc[g][t][1][i] * fu;
-          *reinterpret_cast<float2*>(&sm.u.wu[wave][16 * t + 4 * q + i][32 * g + 2 * n]) = u2;
-        }
-    if (q == 0) {
-      sm.wm[wave][n] = st.m[0];
-      sm.wm[wave][16 + n] = st.m[1];
-      sm.wz[wave][n] = st.z[0];
-      sm.wz[wave][16 + n] = st.z[1];
-    }
-  }
-  __syncthreads();
-
+  // ---- merge the waves: two at a time through LDS -------------------------
   // thread -> (row r = tid >> 3, features f0 = 16 (tid & 7) .. +15)
   const int r = tid >> 3;
   const int f0 = (tid & 7) * 16;
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kW; ++w) M = fmaxf(M, sm.wm[w][r]);
-  float Z = 0.0f;
+  const float fu = __builtin_ldexpf(1.0f, -st.sv);
+  __syncthreads();  // every wave is done with q (aliased by wu)
+  if (q == 0) {
+    sm.wm[wave][n] = st.m[0];
+    sm.wm[wave][16 + n] = st.m[1];
+    sm.wz[wave][n] = st.z[0];
+    sm.wz[wave][16 + n] = st.z[1];
+  }
+  float M = -INFINITY, Z = 0.0f;
   float U[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) U[i] = 0.0f;
-  if (M != -INFINITY) {
 #pragma unroll
-    for (int w = 0; w < kW; ++w) {
-      const float mw = sm.wm[w][r];
-      if (mw == -INFINITY) continue;
-      const float e = fast_exp2(mw - M);
-      Z = fmaf(e, sm.wz[w][r], Z);
+  for (int half = 0; half < 2; ++half) {
+    if ((wave >> 1) == half) {  // waves 2 half, 2 half + 1 park their u
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.u.wu[w][r][f0 + 4 * i]);
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) U[4 * i + j] = fmaf(e, a[j], U[4 * i + j]);
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float2 u2;
+            u2.x = st.acc[g][t][0][i] * fu;
+            u2.y = st.acc[g][t][1][i] * fu;
+            *reinterpret_cast<float2*>(
+                &sm.u.wu[wave & 1][16 * t + 4 * q + i][32 * g + 2 * n]) = u2;
+          }
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) M = fmaxf(M, sm.wm[w][r]);
+    }
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) {
+        const float mw = sm.wm[2 * half + w2][r];
+        if (mw == -INFINITY) continue;
+        const float e = fast_exp2(mw - M);
+        Z = fmaf(e, sm.wz[2 * half + w2][r], Z);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.u.wu[w2][r][f0 + 4 * i]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) U[4 * i + j] = fmaf(e, a[j], U[4 * i + j]);
+        }
       }
     }
+    if (half == 0) __syncthreads();  // the first pair is read before the second overwrites it
   }
   const long long row0 = bh * rows;
   if (p.splits == 1) {

@@ -96,11 +96,14 @@ size_t kvq_v_scale_count(int B, int H, int N, int D, int bits, int group); /* B*
 int kvq_attend_auto_splits(int B, int Hkv, int N);
 
 /* Workspace bytes kvq_attend / kvq_attend_f32 need for `num_splits` splits
- * (0 = auto: kvq_attend_auto_splits(B, Hkv, N)).  Holds the
- * per-split partial (m, z, u) of every query row and one arrival counter per
- * (batch, KV head).  A workspace must be ZERO-FILLED once before its first
- * use; every completed call leaves the counters at zero again.  Calls that
- * run at the same time must use different workspaces. */
+ * (0 = auto: kvq_attend_auto_splits(B, Hkv, N)).  Holds one arrival
+ * counter per (batch, KV head), 256 bytes apart at the start, then the
+ * per-split partial (m, z, u) of every query row.  The counters must be zero
+ * when a call starts and every completed call leaves them zero, whatever its
+ * split count: ZERO-FILL a workspace once before its first use, and again
+ * before a call with more (batch, KV head) pairs than any earlier call on it
+ * (its counters would reach into earlier partials).  Calls that run at the
+ * same time must use different workspaces. */
 size_t kvq_attend_workspace_bytes(int B, int Hq, int Hkv, int R, int N, int D, int num_splits);
 
 /* ---- kvq_pack_k / kvq_pack_v ------------------------------------------------

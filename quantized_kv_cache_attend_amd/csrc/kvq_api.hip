@@ -50,14 +50,15 @@ kvq_status hip_status(hipError_t e, const char* what) {
 }  // namespace
 
 WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int R, int D, int splits) {
-  (void)Hkv;
   const size_t rows = static_cast<size_t>(B) * Hq * R;  // every query row once
   WorkspaceLayout w;
-  w.m_off = 0;
+  // The arrival counters come first: where they sit depends on the number of
+  // (batch, KV head) pairs alone, not on the split count or the row shape.
+  w.cnt_off = 0;
+  w.m_off = round_up(sizeof(unsigned) * kCounterStride * static_cast<size_t>(B) * Hkv, 256);
   w.z_off = round_up(w.m_off + sizeof(float) * splits * rows, 256);
   w.u_off = round_up(w.z_off + sizeof(float) * splits * rows, 256);
-  w.cnt_off = round_up(w.u_off + sizeof(float) * splits * rows * D, 256);
-  w.total = round_up(w.cnt_off + sizeof(unsigned) * static_cast<size_t>(B) * Hkv, 256);
+  w.total = round_up(w.u_off + sizeof(float) * splits * rows * D, 256);
   return w;
 }
 

@@ -421,112 +421,33 @@ attend_mfma_r4_kernel(AttendProblem p) {
   }
   __syncthreads();
 
-  // ---- merge the waves: output slot e = tid + j * kThreads -> (row e >> 7,
-  // feature e & 127) -------------------------------------------------------
-  float M[kSlots], Z[kSlots], U[kSlots];
+  // ---- merge the waves: thread -> row r, features f0 .. f0 + kSlots - 1 ----
+  const int e0 = tid * kSlots;
+  const int r = e0 >> 7, f0 = e0 & 127;
+  float M = -INFINITY, Z = 0.0f, U[kSlots];
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int e = min(tid + j * kThreads, kOut - 1);
-    const int r = e >> 7, f = e & 127;
-    float m = -INFINITY;
+  for (int j = 0; j < kSlots; ++j) U[j] = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm.wm[w][r]);
-    float z = 0.0f, u = 0.0f;
-    if (m != -INFINITY) {
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][r]);
+  if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm.wm[w][r];
-        if (mw == -INFINITY) continue;
-        const float x = fast_exp2(mw - m);
-        z = fmaf(x, sm.wz[w][r], z);
-        u = fmaf(x, sm.u.wu[w][r][f], u);
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm.wm[w][r];
+      if (mw == -INFINITY) continue;
+      const float x = fast_exp2(mw - M);
+      Z = fmaf(x, sm.wz[w][r], Z);
+#pragma unroll
+      for (int j = 0; j < kSlots; ++j) U[j] = fmaf(x, sm.u.wu[w][r][f0 + j], U[j]);
     }
-    M[j] = m;
-    Z[j] = z;
-    U[j] = u;
   }
-  const long long row0 = bh * rows;
   if (p.splits == 1) {
+    if (r < rows) {
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j) {
-      const int e = tid + j * kThreads;
-      if (e < kOut && (e >> 7) < rows) p.out[(row0 + (e >> 7)) * kD + (e & 127)] = U[j] / Z[j];
+      for (int j = 0; j < kSlots; ++j) p.out[(bh * rows + r) * kD + f0 + j] = U[j] / Z;
     }
     return;
   }
-
-  // Fused combine: the last workgroup of this head to arrive merges all
-  // splits.  Partials are written with device-scope stores (written through
-  // to the device coherence point, so no cache flush is needed), each thread
-  // waits for its stores to be acknowledged, and only then does thread 0
-  // take a ticket.  The last arriver reads the partials with device-scope
-  // loads.  (A device-scope release/acquire fence would instead write back
-  // and invalidate the whole L2 of the XCD, once per workgroup.)
-  const long long total_rows = static_cast<long long>(p.B) * p.Hkv * rows;
-#pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int e = tid + j * kThreads;
-    const int r = e >> 7, f = e & 127;
-    if (e < kOut && r < rows) {
-      const long long prow = split * total_rows + row0 + r;
-      __hip_atomic_store(&p.part_u[prow * kD + f], U[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (f == 0) {
-        __hip_atomic_store(&p.part_m[prow], M[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.part_z[prow], Z[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above are acknowledged
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&p.counters[bh], 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = prev == static_cast<unsigned>(p.splits - 1);
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  // Online merge over the splits, eight at a time so the loads of a batch
-  // are all in flight together.
-#pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int e = tid + j * kThreads;
-    const int r = e >> 7, f = e & 127;
-    if (e < kOut && r < rows) {
-      const long long prow = row0 + r;
-      float Mg = -INFINITY, Zg = 0.0f, Vg = 0.0f;
-      for (int s0 = 0; s0 < p.splits; s0 += 8) {
-        float ms[8], zs[8], us[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int sidx = s0 + i < p.splits ? s0 + i : s0;
-          const long long pr = sidx * total_rows + prow;
-          ms[i] = __hip_atomic_load(&p.part_m[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          zs[i] = __hip_atomic_load(&p.part_z[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          us[i] = __hip_atomic_load(&p.part_u[pr * kD + f], __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-          if (s0 + i >= p.splits) ms[i] = -INFINITY;
-        }
-        float mb = Mg;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mb = fmaxf(mb, ms[i]);
-        if (mb == -INFINITY) continue;
-        const float a = fast_exp2(Mg - mb);  // 0 while nothing merged yet
-        Zg *= a;
-        Vg *= a;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (ms[i] == -INFINITY) continue;
-          const float x = fast_exp2(ms[i] - mb);
-          Zg = fmaf(x, zs[i], Zg);
-          Vg = fmaf(x, us[i], Vg);
-        }
-        Mg = mb;
-      }
-      p.out[prow * kD + f] = Vg / Zg;
-    }
-  }
-  if (tid == 0) __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  split_combine<kSlots, kSlots, 0>(p, split, bh, r, f0, U, M, Z, &sm.last);
 }
 
 }  // namespace

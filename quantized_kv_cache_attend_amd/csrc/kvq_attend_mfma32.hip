@@ -489,9 +489,9 @@ attend_mfma_r32_kernel(AttendProblem p) {
   st.z[1] = qblock_sum(st.z[1]);
 
   // ---- merge the waves: two at a time through LDS -------------------------
-  // thread -> (row r = tid >> 3, features f0 = 16 (tid & 7) .. +15)
+  // thread -> (row r = tid >> 3, features f0 + 32 i + (0..3), f0 = 4 (tid & 7))
   const int r = tid >> 3;
-  const int f0 = (tid & 7) * 16;
+  const int f0 = (tid & 7) * 4;
   const float fu = __builtin_ldexpf(1.0f, -st.sv);
   __syncthreads();  // every wave is done with q (aliased by wu)
   if (q == 0) {
@@ -534,7 +534,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
         Z = fmaf(e, sm.wz[2 * half + w2][r], Z);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.u.wu[w2][r][f0 + 4 * i]);
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.u.wu[w2][r][f0 + 32 * i]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) U[4 * i + j] = fmaf(e, a[j], U[4 * i + j]);
         }
@@ -550,84 +550,13 @@ attend_mfma_r32_kernel(AttendProblem p) {
         f32x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = U[4 * i + j] / Z;
-        *reinterpret_cast<f32x4*>(&p.out[(row0 + r) * kD + f0 + 4 * i]) = o;
+        *reinterpret_cast<f32x4*>(&p.out[(row0 + r) * kD + f0 + 32 * i]) = o;
       }
     }
     return;
   }
 
-  // Fused combine (as in the 4-row kernel): device-scope partial stores, a
-  // wait for their acknowledgement, a device-scope ticket, and the last
-  // workgroup of the head merges every split with device-scope loads.
-  const long long total_rows = static_cast<long long>(p.B) * p.Hkv * rows;
-  if (r < rows) {
-    const long long prow = split * total_rows + row0 + r;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      __hip_atomic_store(&p.part_u[prow * kD + f0 + i], U[i], __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    if ((tid & 7) == 0) {
-      __hip_atomic_store(&p.part_m[prow], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.part_z[prow], Z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above are acknowledged
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&p.counters[bh], 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = prev == static_cast<unsigned>(p.splits - 1);
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  if (r < rows) {
-    // Online merge over the splits, four at a time so a batch's loads are in
-    // flight together.
-    const long long prow = row0 + r;
-    float Mg = -INFINITY, Zg = 0.0f, V[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) V[i] = 0.0f;
-    for (int s0 = 0; s0 < p.splits; s0 += 4) {
-      float ms[4], zs[4], us[4][16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int sidx = s0 + j < p.splits ? s0 + j : s0;
-        const long long pr = sidx * total_rows + prow;
-        ms[j] = __hip_atomic_load(&p.part_m[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        zs[j] = __hip_atomic_load(&p.part_z[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          us[j][i] = __hip_atomic_load(&p.part_u[pr * kD + f0 + i], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-        if (s0 + j >= p.splits) ms[j] = -INFINITY;
-      }
-      float mb = Mg;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mb = fmaxf(mb, ms[j]);
-      if (mb == -INFINITY) continue;
-      const float a = fast_exp2(Mg - mb);  // 0 while nothing merged yet
-      Zg *= a;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) V[i] *= a;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (ms[j] == -INFINITY) continue;
-        const float e = fast_exp2(ms[j] - mb);
-        Zg = fmaf(e, zs[j], Zg);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) V[i] = fmaf(e, us[j][i], V[i]);
-      }
-      Mg = mb;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 o;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = V[4 * i + j] / Zg;
-      *reinterpret_cast<f32x4*>(&p.out[prow * kD + f0 + 4 * i]) = o;
-    }
-  }
-  if (tid == 0) __hip_atomic_store(&p.counters[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  split_combine<16, 4, 32>(p, split, bh, r, f0, U, M, Z, &sm.last);
 }
 
 }  // namespace

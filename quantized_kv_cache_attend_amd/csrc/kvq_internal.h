@@ -35,8 +35,12 @@ struct AttendProblem {
   float* part_m;           // [splits][B*Hkv*rows]
   float* part_z;           // [splits][B*Hkv*rows]
   float* part_u;           // [splits][B*Hkv*rows][D]
-  unsigned* counters;      // [B*Hkv]
+  unsigned* counters;      // [B*Hkv][kCounterStride], one arrival counter per KV head
 };
+
+// Arrival counters sit 256 bytes apart, so the heads' tickets never contend
+// for one memory line.
+constexpr int kCounterStride = 64;
 
 // Workspace carving, shared by the sizing call and the launchers.
 struct WorkspaceLayout {

@@ -1,12 +1,15 @@
 // Device helpers shared by the matrix-core attention kernels: exact fp16
 // code operands, fp16 hi/lo splits of float32 factors, power-of-two
-// prescales and cross-lane reductions on 64-wide waves.  Internal header
-// (each kernel translation unit gets its own copy of these inline helpers).
+// prescales, cross-lane reductions on 64-wide waves and the split combine.
+// Internal header (each kernel translation unit gets its own copy of these
+// inline helpers).
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+
+#include "kvq_internal.h"
 
 namespace kvq {
 namespace {
@@ -136,6 +139,104 @@ __device__ __forceinline__ void split_hilo(const float x[8], half8_t& hi, half8_
   }
   hi = __builtin_bit_cast(half8_t, h);
   lo = __builtin_bit_cast(half8_t, l);
+}
+
+// ---- split combine -----------------------------------------------------------
+// The KV splits of a head merge their partial (m, z, u) rows with the same
+// rescale as the blocks ("two stops of the online accumulation" on the
+// resource-ledger page: partial statistics compose once brought to one
+// reference).  Each workgroup stores its rows with device-scope stores
+// (written through to the device coherence point, so no cache flush is
+// needed), waits until they are acknowledged, and only then takes a ticket
+// from the head's arrival counter; the last to arrive reads every split with
+// device-scope loads, writes the output and resets the counter to 0.  (A
+// device-scope release/acquire fence would instead write back and invalidate
+// the whole L2 of the XCD, once per workgroup.)
+
+// Feature of a thread's slot i: runs of kRun consecutive features kStride
+// apart, from f0 (consecutive lanes then touch neighbouring words).
+template <int kRun, int kStride>
+__device__ __forceinline__ int slot_feature(int f0, int i) {
+  return f0 + (i / kRun) * kStride + i % kRun;
+}
+
+// One workgroup's part of the combine.  Thread: query row r of the head
+// (r >= p.rows takes no part), features slot_feature(f0, i), i < kF, its
+// merged partial U / M / Z; the thread with f0 == 0 also owns the row's m and
+// z.  last: an int of LDS.  Every thread of the workgroup calls this (it
+// holds barriers).
+template <int kF, int kRun, int kStride>
+__device__ __forceinline__ void split_combine(const AttendProblem& p, int split, long long head,
+                                              int r, int f0, const float (&U)[kF], float M,
+                                              float Z, int* last) {
+  const bool mine = r < p.rows;
+  const long long total_rows = static_cast<long long>(p.B) * p.Hkv * p.rows;
+  const long long row = head * p.rows + r;
+  if (mine) {
+    const long long pr = static_cast<long long>(split) * total_rows + row;
+#pragma unroll
+    for (int i = 0; i < kF; ++i)
+      __hip_atomic_store(&p.part_u[pr * p.D + slot_feature<kRun, kStride>(f0, i)], U[i],
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (f0 == 0) {
+      __hip_atomic_store(&p.part_m[pr], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.part_z[pr], Z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above are acknowledged
+  __syncthreads();
+  unsigned* counter = &p.counters[head * kCounterStride];
+  if (threadIdx.x == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    *last = prev == static_cast<unsigned>(p.splits - 1);
+  }
+  __syncthreads();
+  if (!*last) return;
+  if (mine) {
+    // Online merge over the splits, four at a time so a batch's loads are in
+    // flight together.
+    constexpr int kBatch = 4;
+    float Mg = -INFINITY, Zg = 0.0f, V[kF];
+#pragma unroll
+    for (int i = 0; i < kF; ++i) V[i] = 0.0f;
+    for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+      float ms[kBatch], zs[kBatch], us[kBatch][kF];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const long long pr =
+            static_cast<long long>(s0 + j < p.splits ? s0 + j : s0) * total_rows + row;
+        ms[j] = __hip_atomic_load(&p.part_m[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        zs[j] = __hip_atomic_load(&p.part_z[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int i = 0; i < kF; ++i)
+          us[j][i] = __hip_atomic_load(&p.part_u[pr * p.D + slot_feature<kRun, kStride>(f0, i)],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (s0 + j >= p.splits) ms[j] = -INFINITY;
+      }
+      float mb = Mg;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, ms[j]);
+      if (mb == -INFINITY) continue;
+      const float a = fast_exp2(Mg - mb);  // 0 while nothing is merged yet
+      Zg *= a;
+#pragma unroll
+      for (int i = 0; i < kF; ++i) V[i] *= a;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (ms[j] == -INFINITY) continue;
+        const float e = fast_exp2(ms[j] - mb);
+        Zg = fmaf(e, zs[j], Zg);
+#pragma unroll
+        for (int i = 0; i < kF; ++i) V[i] = fmaf(e, us[j][i], V[i]);
+      }
+      Mg = mb;
+    }
+#pragma unroll
+    for (int i = 0; i < kF; ++i) p.out[row * p.D + slot_feature<kRun, kStride>(f0, i)] = V[i] / Zg;
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace

@@ -131,6 +131,12 @@ def test_attend_sm_scale_and_peaky_scores():
         assert max_abs(got, want) <= TOL
 
 
+def _counters(ws, B, Hkv):
+    """The arrival counters: one per (batch, KV head), 256 bytes apart, at the
+    start of the workspace."""
+    return host(ws)[:256 * B * Hkv]
+
+
 @pytest.mark.parametrize("variant", MFMA_VARIANTS)
 def test_attend_deterministic_and_counters_reset(variant):
     w = WORKLOADS["gqa_n4096"]
@@ -141,9 +147,34 @@ def test_attend_deterministic_and_counters_reset(variant):
     a = _run(q, cache, w.N, 4, 32, workspace=ws, variant=variant)
     b = _run(q, cache, w.N, 4, 32, workspace=ws, variant=variant)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    # the arrival counters sit in the last 256-byte-aligned block of the workspace
-    tail = host(ws)[-256:]
-    assert not tail.any()
+    assert not _counters(ws, w.B, w.Hkv).any()  # every call leaves the counters at zero
+
+
+def test_attend_variants_share_one_workspace():
+    """Split paths of every kernel, one after another on one workspace with
+    different split counts and row shapes: the arrival counters sit where the
+    (batch, KV head) count alone puts them, and each call leaves them zero."""
+    w = WORKLOADS["gqa_n4096"]
+    q, k, v = make_qkv(w, 2)
+    announce("attend shared workspace")
+    want = _oracle(q, k, v, 4, 32)
+    cache = _gpu_cache(k, v, 4, 32)
+    ws = kvq.new_workspace(w.B, w.Hq, w.Hkv, w.R, w.N, w.D, 16)
+    for variant, splits in (("valu", 16), ("mfma", 16), ("valu", 3), ("mfma", 5), ("mfma", 0),
+                            ("auto", 0), ("valu", 0)):
+        got = _run(q, cache, w.N, 4, 32, num_splits=splits, workspace=ws, variant=variant)
+        assert max_abs(got, want) <= TOL, (variant, splits)
+        assert not _counters(ws, w.B, w.Hkv).any(), (variant, splits)
+    # 16 query rows per KV head (the 32-row matrix-core kernel), fewer heads:
+    # their counters are a prefix of the zero counters above
+    w2 = Workload("ws32", 2, 16, 2, 2, 1021, 128, ((4, 32),))
+    q2, k2, v2 = make_qkv(w2, 3)
+    want2 = _oracle(q2, k2, v2, 4, 32)
+    cache2 = _gpu_cache(k2, v2, 4, 32)
+    for variant, splits in (("mfma", 7), ("valu", 16), ("mfma", 16), ("auto", 0)):
+        got = _run(q2, cache2, w2.N, 4, 32, num_splits=splits, workspace=ws, variant=variant)
+        assert max_abs(got, want2) <= TOL, (variant, splits)
+        assert not _counters(ws, w2.B, w2.Hkv).any(), (variant, splits)
 
 
 @pytest.mark.parametrize("hq,hkv,r", [(8, 2, 1), (2, 2, 3), (1, 1, 1), (4, 1, 1), (6, 3, 2)])

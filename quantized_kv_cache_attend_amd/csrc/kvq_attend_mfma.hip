@@ -27,9 +27,13 @@
 //     tokens 8q + (0..7) of byte column 16g + n (features 32g + 2n, +1);
 //   K scales of the block's group: 128 floats, channel order;
 //   V scales of the block: [value group][32 tokens].
-// Every load is a contiguous, coalesced global load into VGPRs; no LDS
-// staging, no barriers in the main loop.  Each wave streams its own blocks
-// and keeps the next block's loads in flight while it computes one.
+// Every load is a contiguous, coalesced buffer load into VGPRs; no LDS
+// staging, no barriers before the final merge.  Each wave streams its own
+// blocks through a ring of kDepth register sets: a part of a set is reloaded
+// with the block kDepth ahead as soon as the block in it has consumed that
+// part.  One set is the default: with about one block per wave in flight the
+// whole chip already keeps ~10 MB of loads outstanding, and deeper rings
+// (more registers, a burst of loads at the start) measured slower.
 //
 // Exact code operands.  Each stored nibble c is turned into the fp16 value
 // c - 7 exactly: OR-ing it into the mantissa of 0x6400 gives 1024 + c (low
@@ -41,10 +45,12 @@
 // Float32 factors on fp16 matrix cores.  q~[r][d] = q[r][d] * qscale *
 // sK[d][G] (scores) and p~[r][j] = p[r][j] * sV[j][G'] (values) are split
 // into fp16 hi + lo (round toward zero, then the remainder), so each product
-// carries ~22 significant bits and accumulates in float32.  Before the split
-// each set is multiplied by a power of two that keeps its largest element
-// inside the fp16 range and the lo halves of all elements that matter out of
-// the subnormal range; the factor is exact and divided out in float32.
+// carries ~22 significant bits and accumulates in float32.  Powers of two
+// keep them in the fp16 normal range and are divided out in float32: each
+// query row is prescaled once so its largest |q * qscale| lies in [2^9,
+// 2^10), which keeps q~ below 2^15 for K scales below 32 (a block with a
+// larger K scale is scaled down first), and the V prescale rides in the
+// exponent of p (below).
 //
 // Math per 32-token block, one wave:
 //   S^T[pair][col] = codes^T (A: 16 token pairs x 32 channels per k-step,
@@ -58,32 +64,37 @@
 #include "kvq_layout.h"
 #include "kvq_mfma_common.h"
 
+
 namespace kvq {
 namespace {
 
 #ifndef KVQ_MFMA_WAVES
 #define KVQ_MFMA_WAVES 8
 #endif
+#ifndef KVQ_MFMA_DEPTH
+#define KVQ_MFMA_DEPTH 1
+#endif
 constexpr int kWaves = KVQ_MFMA_WAVES;   // waves per workgroup, one KV head split each
+constexpr int kDepth = KVQ_MFMA_DEPTH;   // blocks in flight per wave
 constexpr int kThreads = kWaves * 64;
 constexpr int kOut = 4 * 128;            // outputs of one KV head: 4 rows x D
 constexpr int kSlots = kOut / kThreads > 0 ? kOut / kThreads : 1;  // outputs per thread
 constexpr int kD = 128;
-constexpr int kBlockBytes = 2048;   // K or V codes of one 32-token block
-constexpr int kBlockScales = 128;   // K or V scales of one block
+constexpr int kBB = 2048;           // K or V code bytes of one 32-token block
+constexpr int kBS = 128;            // K or V scales of one block
 constexpr float kLazy = 6.0f;       // reference moves only past m + kLazy
 // V prescale: max V scale * 2^Sv is set to [2^8, 2^9) and kept while it
 // stays in [2^2, 2^9): with p <= 2^kLazy, p~ < 2^15 fits fp16.
 constexpr int kSvTop = 9;
 constexpr int kSvLow = 2;
+constexpr int kQTop = 10;           // q rows prescaled to max |.| in [2^9, 2^10)
+constexpr float kSkMax = 32.0f;     // K scales below this need no block rescale
 
 struct alignas(16) Smem {
   union {
     _Float16 qt[kWaves][4][2][4][4][8];  // per wave: q~ [kstep][hi|lo][row][kblock][8]
     float wu[kWaves][4][kD];             // per-wave u for the final merge
   } u;
-  float qus[kWaves][4];                  // 2^-S of q~ per row
-  float qs[4][kD];                       // q * qscale, the workgroup's query rows
   float wm[kWaves][4];
   float wz[kWaves][4];
   int last;
@@ -98,48 +109,44 @@ struct BlockRegs {
 };
 
 struct Head {
-  const uint8_t* kc;
-  const float* ksc;
-  const uint8_t* vc;
-  const float* vsc;
+  __amdgpu_buffer_rsrc_t kc, ksc, vc, vsc;
 };
 
-// Loaders of the four parts of one block's operands.  Each part is
-// reloaded for the next block as soon as the current block has consumed it,
-// so about one block of loads stays in flight with a single register set.
+// This lane's byte offsets inside a block (precompute slot d0 = channels
+// 32 ((lane >> 2) & 3) + 8 (lane & 3) .. +7 for the K scales).
 struct Lanes {
-  unsigned k_off, v_off, ks_off, vs_off;  // byte / element offsets of this lane
+  unsigned k, v, ks, vs;
 };
-__device__ __forceinline__ Lanes lane_offsets(int lane, int d0) {
+__device__ __forceinline__ Lanes lane_offsets(int lane) {
   const int n = lane & 15, q = lane >> 4;
+  const int d0 = ((lane >> 2) & 3) * 32 + (lane & 3) * 8;
   return {static_cast<unsigned>(lane * 8), static_cast<unsigned>(q * 512 + n * 8),
-          static_cast<unsigned>(d0), static_cast<unsigned>((n >> 2) * 32 + q * 8)};
+          static_cast<unsigned>(d0 * 4), static_cast<unsigned>(((n >> 2) * 32 + q * 8) * 4)};
 }
-__device__ __forceinline__ void load_ks(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
-  const float* p = h.ksc + static_cast<long long>(blk) * kBlockScales + o.ks_off;
-  r.ks[0] = *reinterpret_cast<const f32x4*>(p);
-  r.ks[1] = *reinterpret_cast<const f32x4*>(p + 4);
+
+// Byte offset of block blk in an array of `bytes`-sized blocks, or kNoBlock.
+__device__ __forceinline__ unsigned block_base(int blk, bool valid, unsigned bytes) {
+  return valid ? static_cast<unsigned>(blk) * bytes : kNoBlock;
 }
-__device__ __forceinline__ void load_k(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
-  const uint8_t* p = h.kc + static_cast<long long>(blk) * kBlockBytes + o.k_off;
+
+// Loaders of the four parts of one block (base: block_base of that array).
+__device__ __forceinline__ void load_ks(BlockRegs& r, const Head& h, unsigned base, const Lanes& o) {
+  r.ks[0] = buf_f4(h.ksc, base + o.ks, 0);
+  r.ks[1] = buf_f4(h.ksc, base + o.ks + 16, 0);
+}
+__device__ __forceinline__ void load_vs(BlockRegs& r, const Head& h, unsigned base, const Lanes& o) {
+  r.vs[0] = buf_f4(h.vsc, base + o.vs, 0);
+  r.vs[1] = buf_f4(h.vsc, base + o.vs + 16, 0);
+}
+__device__ __forceinline__ void load_block(BlockRegs& r, const Head& h, int blk, bool valid,
+                                           const Lanes& o) {
+  load_ks(r, h, block_base(blk, valid, kBS * 4), o);
+  const unsigned cb = block_base(blk, valid, kBB);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.k[i] = *reinterpret_cast<const i32x2*>(p + i * 512);
-}
-__device__ __forceinline__ void load_vs(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
-  const float* p = h.vsc + static_cast<long long>(blk) * kBlockScales + o.vs_off;
-  r.vs[0] = *reinterpret_cast<const f32x4*>(p);
-  r.vs[1] = *reinterpret_cast<const f32x4*>(p + 4);
-}
-__device__ __forceinline__ void load_v(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
-  const uint8_t* p = h.vc + static_cast<long long>(blk) * kBlockBytes + o.v_off;
+  for (int i = 0; i < 4; ++i) r.k[i] = buf_b64(h.kc, cb + o.k + i * 512, 0);
+  load_vs(r, h, block_base(blk, valid, kBS * 4), o);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = *reinterpret_cast<const i32x2*>(p + i * 128);
-}
-__device__ __forceinline__ void load_block(BlockRegs& r, const Head& h, int blk, const Lanes& o) {
-  load_ks(r, h, blk, o);
-  load_k(r, h, blk, o);
-  load_vs(r, h, blk, o);
-  load_v(r, h, blk, o);
+  for (int i = 0; i < 4; ++i) r.v[i] = buf_b64(h.vc, cb + o.v + i * 128, 0);
 }
 
 // Running state of one wave.  Lane (n, q) tracks query row n & 3: m is the
@@ -157,77 +164,84 @@ struct WaveState {
   bool live;  // a block has been folded in
 };
 
-// Attend one 32-token block (tokens tok0 .. tok0+31; with kMasked, those
-// >= t_end are masked out).
-template <bool kMasked>
+// Attend one 32-token block (tokens tok0 .. tok0+31, those >= t_end masked
+// out) held in br, then reload br's parts with block `next` (if has_next;
+// otherwise the loads return zeros without touching memory).
+// qv: this lane's prescaled q values (precompute slot, channel order);
+// us_row: 2^-Sq of score row n & 3.
 __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, int t_end,
                                              const CodeConsts& cc, WaveState& ws, const Head& h,
-                                             int next, const Lanes& lo_) {
+                                             int next, bool has_next, const Lanes& lo_,
+                                             const float (&qv)[8], float us_row) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int q = lane >> 4;
 
-  // q~ of this block's K group: lane (rq, ksq, kbq) = (lane >> 4, (lane >> 2)
-  // & 3, lane & 3) forms channels ksq*32 + kbq*8 .. +7 of row rq, prescaled
-  // per row (the 16 lanes of a row are one DPP row), and parks hi / lo in
-  // this wave's LDS slots in the B-operand order.
+  // q~ = q' * sK of this block's K group: lane (rq, ksq, kbq) = (lane >> 4,
+  // (lane >> 2) & 3, lane & 3) forms channels ksq*32 + kbq*8 .. +7 of row
+  // rq and parks hi / lo in this wave's LDS slots in the B-operand order.
+  // A block whose K scales reach kSkMax is scaled by 2^-e first (kun = 2^e
+  // restores its scores).
+  float kun = 1.0f;
   {
     const int rq = lane >> 4, ksq = (lane >> 2) & 3, kbq = lane & 3;
-    const f32x4 qa = *reinterpret_cast<const f32x4*>(&sm.qs[rq][ksq * 32 + kbq * 8]);
-    const f32x4 qb = *reinterpret_cast<const f32x4*>(&sm.qs[rq][ksq * 32 + kbq * 8 + 4]);
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[i] = qa[i] * br.ks[0][i];
-      x[i + 4] = qb[i] * br.ks[1][i];
+      x[i] = qv[i] * br.ks[0][i];
+      x[i + 4] = qv[i + 4] * br.ks[1][i];
     }
-    float amax = fmaxf(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))),
-                       fmaxf(fmaxf(fabsf(x[4]), fabsf(x[5])), fmaxf(fabsf(x[6]), fabsf(x[7]))));
-    amax = fmaxf(amax, dpp<kRowRor1>(amax));
-    amax = fmaxf(amax, dpp<kRowRor2>(amax));
-    amax = fmaxf(amax, dpp<kRowRor4>(amax));
-    amax = fmaxf(amax, dpp<kRowRor8>(amax));
-    const int sq = prescale_exp(amax, 15);
+    const float lks = fmaxf(fmaxf(fmaxf(br.ks[0][0], br.ks[0][1]), fmaxf(br.ks[0][2], br.ks[0][3])),
+                            fmaxf(fmaxf(br.ks[1][0], br.ks[1][1]), fmaxf(br.ks[1][2], br.ks[1][3])));
+    if (__builtin_amdgcn_ballot_w64(lks >= kSkMax) != 0) {
+      float mx = fmaxf(lks, dpp<kRowRor1>(lks));
+      mx = fmaxf(mx, dpp<kRowRor2>(mx));
+      mx = fmaxf(mx, dpp<kRowRor4>(mx));
+      mx = qblock_max(fmaxf(mx, dpp<kRowRor8>(mx)));
+      const int e = __builtin_amdgcn_frexp_expf(mx);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __builtin_ldexpf(x[i], -e);
+      kun = __builtin_ldexpf(1.0f, e);
+    }
     float xs[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xs[j] = __builtin_ldexpf(x[kSlotByte[j]], sq);
+    for (int j = 0; j < 8; ++j) xs[j] = x[kSlotByte[j]];
     half8_t hi, lo;
     split_hilo(xs, hi, lo);
     *reinterpret_cast<half8_t*>(&sm.u.qt[wave][ksq][0][rq][kbq][0]) = hi;
     *reinterpret_cast<half8_t*>(&sm.u.qt[wave][ksq][1][rq][kbq][0]) = lo;
-    if ((lane & 15) == 0) sm.qus[wave][rq] = __builtin_ldexpf(1.0f, -sq);
   }
-  load_ks(br, h, next, lo_);
+  load_ks(br, h, block_base(next, has_next, kBS * 4), lo_);
 
   // S^T = codes^T * q~^T over 4 k-steps of 32 channels.
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 se = zero4, so = zero4;
   const int part = n >> 3, row = n & 3;
-  const uint8_t* knext = h.kc + static_cast<long long>(next) * kBlockBytes + lo_.k_off;
+  const unsigned kb = block_base(next, has_next, kBB);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     half8_t alo, ahi;
     codes_to_half(br.k[ks], cc, alo, ahi);
-    br.k[ks] = *reinterpret_cast<const i32x2*>(knext + ks * 512);  // next block's k-step
+    br.k[ks] = buf_b64(h.kc, kb + lo_.k + ks * 512, 0);  // next block's k-step
     const half8_t b = *reinterpret_cast<const half8_t*>(&sm.u.qt[wave][ks][part][row][q][0]);
     se = mfma(alo, b, se);
     so = mfma(ahi, b, so);
   }
-  const float us = sm.qus[wave][row];
-  // hi + lo columns: token 8q + t in raw[t], in units of 2^S of q~
+  const float us = us_row * kun;
+  // hi + lo columns: token 8q + t in raw[t], in units of us
   float raw[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     raw[2 * i] = se[i] + dpp<kRowRor8>(se[i]);
     raw[2 * i + 1] = so[i] + dpp<kRowRor8>(so[i]);
   }
-  if (kMasked) {
+  if (tok0 + kBlockTokens > t_end) {  // the block holding token t_end - 1 (wave-uniform)
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       if (tok0 + 8 * q + t >= t_end) raw[t] = -INFINITY;
   }
-  // this lane's max over its 8 tokens, base-2 units (2^-S > 0 commutes with max)
+  // this lane's max over its 8 tokens, base-2 units (us > 0 commutes with max)
   const float lmx =
       fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
             fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7]))) * us;
@@ -237,10 +251,14 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
 
   // Move the reference when any row's block max overshoots it by more than
   // kLazy, the V prescale when the block's largest V scale leaves
-  // [2^kSvLow, 2^kSvTop) after scaling; both decisions are wave-uniform.
-  const bool move_m = !ws.live || __builtin_amdgcn_ballot_w64(lmx > ws.m + kLazy) != 0;
-  const bool move_sv = !ws.live || __builtin_amdgcn_ballot_w64(!(lvs < ws.vhi)) != 0 ||
-                       __builtin_amdgcn_ballot_w64(lvs >= ws.vlo) == 0;
+  // [2^kSvLow, 2^kSvTop) after scaling; both decisions are wave-uniform.  A
+  // block with no token (a ring step past the wave's last block, never the
+  // wave's first step) moves neither and adds p = 0.
+  const bool empty = tok0 >= t_end;
+  const bool move_m =
+      !empty && (!ws.live || __builtin_amdgcn_ballot_w64(lmx > ws.m + kLazy) != 0);
+  const bool move_sv = !empty && (!ws.live || __builtin_amdgcn_ballot_w64(!(lvs < ws.vhi)) != 0 ||
+                                  __builtin_amdgcn_ballot_w64(lvs >= ws.vlo) == 0);
   if (move_m || move_sv) {
     const float mx = qblock_max(lmx);  // row max over the block; finite
     float vmx = fmaxf(lvs, dpp<kRowRor4>(lvs));
@@ -290,15 +308,14 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
     for (int j = 0; j < 8; ++j) xv[j] = xt[kSlotByte[j]];
     split_hilo(xv, ah, al);
   }
-  load_vs(br, h, next, lo_);
+  load_vs(br, h, block_base(next, has_next, kBS * 4), lo_);
 
   // u[4G'+r][f] += p~ x V codes, one feature group of 32 at a time
-  const uint8_t* vnext = h.vc + static_cast<long long>(next) * kBlockBytes + lo_.v_off;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     half8_t be, bo;
     codes_to_half(br.v[g], cc, be, bo);
-    br.v[g] = *reinterpret_cast<const i32x2*>(vnext + g * 128);  // next block's group
+    br.v[g] = buf_b64(h.vc, kb + lo_.v + g * 128, 0);  // next block's group
     ws.acc[g][0] = mfma(ah, be, ws.acc[g][0]);
     ws.acc[g][0] = mfma(al, be, ws.acc[g][0]);
     ws.acc[g][1] = mfma(ah, bo, ws.acc[g][1]);
@@ -318,7 +335,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
 
   // Workgroup -> (KV head, split).  Workgroups are dealt to the 8 XCDs
   // round-robin; keep all splits of a head on one XCD so the head's partials
-  // stay in that XCD's L2 for the combine.
+  // stay close for the combine.
   const int heads = p.B * p.Hkv;
   const int L = blockIdx.x;
   int head, split;
@@ -334,45 +351,55 @@ attend_mfma_r4_kernel(AttendProblem p) {
   const int rows = p.rows;
   const int nblocks = (p.N + kBlockTokens - 1) / kBlockTokens;
   Head h;
-  h.kc = p.k_codes + bh * nblocks * kBlockBytes;
-  h.ksc = p.k_scales + bh * nblocks * kBlockScales;
-  h.vc = p.v_codes + bh * nblocks * kBlockBytes;
-  h.vsc = p.v_scales + bh * nblocks * kBlockScales;
+  h.kc = head_rsrc(p.k_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
+  h.ksc = head_rsrc(p.k_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
+  h.vc = head_rsrc(p.v_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
+  h.vsc = head_rsrc(p.v_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
 
+  // Blocks of this split: [b_begin, b_end); wave w takes b_begin + w + i kWaves,
+  // i = 0 .. cnt - 1.
   const int t_begin = split * p.tokens_per_split;
   const int t_end = min(p.N, t_begin + p.tokens_per_split);
-  // blocks of this split: [b_begin, b_end); wave w takes b_begin + w + 4i
   const int b_begin = t_begin / kBlockTokens;
   const int b_end = t_end > t_begin ? (t_end + kBlockTokens - 1) / kBlockTokens : b_begin;
   const int b_first = b_begin + wave;
-  const int b_last = b_first + (b_end - 1 - b_first) / kWaves * kWaves;  // valid if b_first < b_end
+  const int cnt = b_first < b_end ? (b_end - 1 - b_first) / kWaves + 1 : 0;  // wave-uniform
 
-  // this lane's K-scale slot in the q~ precompute: channels d0 .. d0+7
+  // This lane's query values: row rq = lane >> 4, channels d0 .. d0+7 (its
+  // q~ precompute slot).  Loaded first, so the block loads queue behind them.
+  const int rq = lane >> 4;
   const int d0 = ((lane >> 2) & 3) * 32 + (lane & 3) * 8;
-  const Lanes lo = lane_offsets(lane, d0);
-
-  // The block holding token N-1 is masked when N is not a multiple of 32;
-  // the wave that owns it attends it first, so only the peeled first block
-  // carries masking code.  Its loads go out before the query is staged.
-  const bool active = b_first < b_end;  // wave-uniform
-  const bool partial = (p.N % kBlockTokens) != 0 && b_last == nblocks - 1;
-  const int first = partial ? b_last : b_first;
-  const int loop_begin = partial ? b_first : b_first + kWaves;
-  const int loop_end = partial ? b_last - kWaves : b_last;  // inclusive
-  BlockRegs br;
-  if (active) load_block(br, h, first, lo);
-
-  // q * qscale of the head's query rows into LDS, output slot e = tid +
-  // j * kThreads -> (row e >> 7, channel e & 127).  Rows past `rows` are zero.
-#pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const int e = tid + j * kThreads;
-    if (e < kOut) {
-      const int rq = e >> 7, c = e & 127;
-      sm.qs[rq][c] = rq < rows ? p.q[(bh * rows + rq) * kD + c] * p.qscale : 0.0f;
-    }
+  f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = qa;
+  if (rq < rows) {
+    const float* src = p.q + (bh * rows + rq) * kD + d0;
+    qa = *reinterpret_cast<const f32x4*>(src);
+    qb = *reinterpret_cast<const f32x4*>(src + 4);
   }
-  __syncthreads();
+  const Lanes lo = lane_offsets(lane);
+  BlockRegs br[kDepth];
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j) load_block(br[j], h, b_first + j * kWaves, j < cnt, lo);
+
+  // q * qscale, prescaled per row by 2^Sq so the row's largest element lies in
+  // [2^9, 2^10) (the 16 lanes of a row are one DPP row).
+  float qv[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qv[i] = qa[i] * p.qscale;
+    qv[i + 4] = qb[i] * p.qscale;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(qv[i]));
+  amax = fmaxf(amax, dpp<kRowRor1>(amax));
+  amax = fmaxf(amax, dpp<kRowRor2>(amax));
+  amax = fmaxf(amax, dpp<kRowRor4>(amax));
+  amax = fmaxf(amax, dpp<kRowRor8>(amax));
+  const int sq = prescale_exp(amax, kQTop);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qv[i] = __builtin_ldexpf(qv[i], sq);
+  // 2^-Sq of score row n & 3 (held by lanes 16 (n & 3) ..)
+  const float us_row = __builtin_ldexpf(1.0f, -__shfl(sq, (n & 3) * 16));
 
   const CodeConsts cc = code_consts();
   WaveState ws;
@@ -387,14 +414,18 @@ attend_mfma_r4_kernel(AttendProblem p) {
     for (int g = 0; g < 4; ++g) ws.acc[g][0] = ws.acc[g][1] = zero4;
   }
 
-  if (active) {
-    // One register set: each part of the next block is loaded as soon as
-    // the current block has consumed that part.
-    attend_block<true>(sm, br, first * kBlockTokens, t_end, cc, ws, h,
-                       loop_begin <= loop_end ? loop_begin : first, lo);
-    for (int b = loop_begin; b <= loop_end; b += kWaves)
-      attend_block<false>(sm, br, b * kBlockTokens, t_end, cc, ws, h, min(b + kWaves, loop_end),
-                          lo);
+  // The ring: block i sits in register set i % kDepth; once attended, the set
+  // is refilled with block i + kDepth.  Every step of a round runs (a step
+  // past the wave's last block attends an all-masked block of zeros), so the
+  // number of loads in flight never depends on the path taken.
+  for (int i0 = 0; i0 < cnt; i0 += kDepth) {
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      const int i = i0 + j;
+      const int blk = b_first + i * kWaves;
+      attend_block(sm, br[j], i < cnt ? blk * kBlockTokens : t_end, t_end, cc, ws, h,
+                   blk + kDepth * kWaves, i + kDepth < cnt, lo, qv, us_row);
+    }
   }
   // z of each row: sum this lane's share over the four q-blocks
   ws.z = qblock_sum(ws.z);
@@ -440,10 +471,11 @@ attend_mfma_r4_kernel(AttendProblem p) {
       for (int j = 0; j < kSlots; ++j) U[j] = fmaf(x, sm.u.wu[w][r][f0 + j], U[j]);
     }
   }
+  const long long row0 = bh * rows;
   if (p.splits == 1) {
     if (r < rows) {
 #pragma unroll
-      for (int j = 0; j < kSlots; ++j) p.out[(bh * rows + r) * kD + f0 + j] = U[j] / Z;
+      for (int j = 0; j < kSlots; ++j) p.out[(row0 + r) * kD + f0 + j] = U[j] / Z;
     }
     return;
   }

@@ -75,33 +75,15 @@ struct Regs32 {
   float2 vs;    // V scales 2 lane, 2 lane + 1 of the block ([group][token])
 };
 
-// Buffer descriptors of one KV head's four arrays (SGPRs): loads take a
-// 32-bit lane offset in a VGPR and the block offset in an SGPR, so no 64-bit
-// per-lane address is kept in registers, and an offset past the head's
-// arrays reads zero instead of faulting.
+// Buffer descriptors of one KV head's four arrays (kvq_mfma_common.h): the
+// block offset rides in an SGPR, the lane offset in a VGPR.
 struct Head32 {
   __amdgpu_buffer_rsrc_t kc, ksc, vc, vsc;
 };
 
-// Raw buffer descriptor word 3 for gfx9-family MUBUF loads (32-bit data
-// format, no swizzle, no index stride).
-constexpr int kRawBufferWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, long long bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), kRawBufferWord3);
-}
-
 struct Lanes32 {
   unsigned k_off, v_off, s_off;  // byte offsets of this lane in a block
 };
-
-__device__ __forceinline__ i32x2 buf_b64(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
-  return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
-__device__ __forceinline__ float2 buf_f2(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
-  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
 
 __device__ __forceinline__ void load_scales32(Regs32& r, const Head32& h, int blk,
                                               const Lanes32& o) {

@@ -1,6 +1,7 @@
-// Device helpers shared by the matrix-core attention kernels: exact fp16
-// code operands, fp16 hi/lo splits of float32 factors, power-of-two
-// prescales, cross-lane reductions on 64-wide waves and the split combine.
+// Device helpers shared by the matrix-core attention kernels: buffer loads,
+// exact fp16 code operands, fp16 hi/lo splits of float32 factors,
+// power-of-two prescales, cross-lane reductions on 64-wide waves and the
+// split combine.
 // Internal header (each kernel translation unit gets its own copy of these
 // inline helpers).
 #pragma once
@@ -22,6 +23,29 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ unsigned as_u32(float x) { return __builtin_bit_cast(unsigned, x); }
 __device__ __forceinline__ float as_f32(unsigned x) { return __builtin_bit_cast(float, x); }
+
+// ---- buffer loads ------------------------------------------------------------
+// A buffer descriptor (SGPRs) covers one KV head's array; loads take a 32-bit
+// lane offset in a VGPR (and optionally a wave-uniform offset in an SGPR), so
+// no 64-bit per-lane address is kept in registers.  A lane offset at or past
+// the descriptor's byte count returns zeros without a memory access;
+// kNoBlock is such an offset for any array below 2 GiB.
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, no swizzle
+constexpr unsigned kNoBlock = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRawBufferWord3);
+}
+__device__ __forceinline__ i32x2 buf_b64(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+  return __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ float2 buf_f2(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ f32x4 buf_f4(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

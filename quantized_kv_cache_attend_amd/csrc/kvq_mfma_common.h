@@ -177,11 +177,23 @@ __device__ __forceinline__ void split_hilo(const float x[8], half8_t& hi, half8_
 // device-scope release/acquire fence would instead write back and invalidate
 // the whole L2 of the XCD, once per workgroup.)
 
+// Cache policy of buffer accesses at device scope (gfx9 "sc1"): stores are
+// written through to the device coherence point before they are
+// acknowledged, loads read it, as for device-scope atomic stores and loads.
+constexpr int kCachePolicyDevice = 16;
+
 // Feature of a thread's slot i: runs of kRun consecutive features kStride
 // apart, from f0 (consecutive lanes then touch neighbouring words).
 template <int kRun, int kStride>
 __device__ __forceinline__ int slot_feature(int f0, int i) {
   return f0 + (i / kRun) * kStride + i % kRun;
+}
+
+// Buffer descriptor of the u rows of one head in one split.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t split_rows(const AttendProblem& p, int split,
+                                                             long long total_rows, long long head) {
+  return head_rsrc(p.part_u + (static_cast<long long>(split) * total_rows + head * p.rows) * p.D,
+                   static_cast<long long>(p.rows) * p.D * 4);
 }
 
 // One workgroup's part of the combine.  Thread: query row r of the head
@@ -198,10 +210,23 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
   const long long row = head * p.rows + r;
   if (mine) {
     const long long pr = static_cast<long long>(split) * total_rows + row;
+    if constexpr (kRun % 4 == 0) {
+      // Runs of four features: one 16-byte device-scope store each, so the
+      // eight lanes of a row fill whole memory lines.
+      const __amdgpu_buffer_rsrc_t rs = split_rows(p, split, total_rows, head);
 #pragma unroll
-    for (int i = 0; i < kF; ++i)
-      __hip_atomic_store(&p.part_u[pr * p.D + slot_feature<kRun, kStride>(f0, i)], U[i],
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int j = 0; j < kF / 4; ++j) {
+        const u32x4 w = {as_u32(U[4 * j]), as_u32(U[4 * j + 1]), as_u32(U[4 * j + 2]),
+                         as_u32(U[4 * j + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(
+            w, rs, (r * p.D + slot_feature<kRun, kStride>(f0, 4 * j)) * 4, 0, kCachePolicyDevice);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kF; ++i)
+        __hip_atomic_store(&p.part_u[pr * p.D + slot_feature<kRun, kStride>(f0, i)], U[i],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (f0 == 0) {
       __hip_atomic_store(&p.part_m[pr], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&p.part_z[pr], Z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -232,10 +257,24 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
             static_cast<long long>(s0 + j < p.splits ? s0 + j : s0) * total_rows + row;
         ms[j] = __hip_atomic_load(&p.part_m[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         zs[j] = __hip_atomic_load(&p.part_z[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (kRun % 4 == 0) {
+          const __amdgpu_buffer_rsrc_t rs =
+              split_rows(p, s0 + j < p.splits ? s0 + j : s0, total_rows, head);
 #pragma unroll
-        for (int i = 0; i < kF; ++i)
-          us[j][i] = __hip_atomic_load(&p.part_u[pr * p.D + slot_feature<kRun, kStride>(f0, i)],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int i4 = 0; i4 < kF / 4; ++i4) {
+            const f32x4 x = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rs, (r * p.D + slot_feature<kRun, kStride>(f0, 4 * i4)) * 4, 0,
+                           kCachePolicyDevice));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) us[j][4 * i4 + e] = x[e];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < kF; ++i)
+            us[j][i] = __hip_atomic_load(&p.part_u[pr * p.D + slot_feature<kRun, kStride>(f0, i)],
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         if (s0 + j >= p.splits) ms[j] = -INFINITY;
       }
       float mb = Mg;

@@ -52,18 +52,29 @@ def kv_bytes(w, bits, group):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_mfma_gqa_n4096_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "quantized_kv_cache_attend_amd", "csrc", "kvq_attend_mfma.hip")
+# The sources the measured kernel is compiled from (its file and the shared header).
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_kv_cache_attend_amd", "csrc", f)
+                  for f in ("kvq_attend_mfma.hip", "kvq_mfma_common.h")]
+
+
+def kernel_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per launch of the matrix-core attend kernel from the committed
     counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same
     counter's reading for a copy of known size), or None when the summary is
-    missing or was taken on a different kernel source."""
-    import hashlib
+    missing or was taken on a different kernel source (sha256 over
+    KERNEL_SOURCES)."""
     try:
         text = open(TRAFFIC_FILE, encoding="utf-8").read()
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        src = kernel_source_sha256()
     except OSError:
         return None
     fields = dict(line.split(":", 1) for line in text.splitlines()

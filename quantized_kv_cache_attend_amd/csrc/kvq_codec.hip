@@ -8,10 +8,14 @@
 // tokens inside a channel, V groups along features inside a token.  The byte
 // order in memory is the block layout of kvq_layout.h.
 //
-// Packing runs in two passes: one thread per group computes the scale, then
-// one thread per stored byte quantizes its one or two elements against the
-// scales just written (every byte of the layout is written, padding
-// included).
+// Packing works per (head, 32-token block) when D <= kStageMaxD: a workgroup
+// stages the block's 32 x D inputs in LDS with coalesced loads, computes the
+// block's scales (V always; K when the group divides 32, so its groups lie in
+// the block) and then writes every stored byte of the block (padding
+// included) from LDS.  Otherwise, and for K scales of longer groups, two
+// plain passes run: one thread per group computes the scale, then one thread
+// per stored byte quantizes its one or two elements against the scales just
+// written.
 //
 // Bit-exactness rests on three properties of this translation unit's build:
 // float32 division is IEEE correctly rounded (hipcc's default for HIP,
@@ -145,6 +149,123 @@ __global__ __launch_bounds__(256) void pack_v_codes_kernel(const float* __restri
   codes[tid] = static_cast<uint8_t>(byte);
 }
 
+// ---- block-staged packing --------------------------------------------------
+// Largest head dim staged through LDS: 32 x (D + 1) floats plus the block's
+// scales stay under 64 KB.
+constexpr int kStageMaxD = 256;
+
+// Stage tokens t0 .. t0 + nt - 1 (all D values, one contiguous run of
+// memory) into tile[tl * (D + 1) + f]; the pad word keeps column reads of
+// 32 rows on distinct banks.
+__device__ __forceinline__ void stage_block(const float* __restrict__ src, int nt, int D,
+                                            float* tile) {
+  const int n = nt * D;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int tl = i / D;
+    tile[tl * (D + 1) + (i - tl * D)] = src[i];
+  }
+}
+
+// V: scales and codes of one (head, block).  LDS: tile, then the block's
+// scales [group][32 tokens].
+template <int BITS>
+__global__ __launch_bounds__(256) void pack_v_block_kernel(const float* __restrict__ x,
+                                                           Layout L, float* __restrict__ scales,
+                                                           uint8_t* __restrict__ codes) {
+  extern __shared__ float lds[];
+  const long long bh = blockIdx.x / L.nblocks;
+  const int blk = static_cast<int>(blockIdx.x % L.nblocks);
+  const int t0 = blk * kBlockTokens;
+  const int nt = min(kBlockTokens, L.N - t0);
+  const int stride = L.D + 1;
+  float* tile = lds;
+  float* sc = lds + kBlockTokens * stride;
+  stage_block(x + (bh * L.N + t0) * static_cast<long long>(L.D), nt, L.D, tile);
+  __syncthreads();
+  // One thread per (group G, token tl), token fastest: the token-minor scale
+  // writes coalesce.  Tokens >= N get scale 1, the scale of an all-zero group.
+  float* hs = scales + bh * v_scales_per_head(L) + static_cast<long long>(blk) * L.vgroups * kBlockTokens;
+  for (int i = threadIdx.x; i < L.vgroups * kBlockTokens; i += blockDim.x) {
+    const int G = i / kBlockTokens, tl = i % kBlockTokens;
+    float amax = 0.0f;
+    if (tl < nt) {
+      const int f1 = min(L.D, (G + 1) * L.group);
+      for (int f = G * L.group; f < f1; ++f) amax = fmaxf(amax, fabsf(tile[tl * stride + f]));
+    }
+    const float sv = group_scale<BITS>(amax);
+    sc[i] = sv;
+    hs[i] = sv;
+  }
+  __syncthreads();
+  uint8_t* dst = codes + bh * v_code_bytes_per_head(L) + blk * L.vblock_bytes;
+  for (int r = threadIdx.x; r < L.vblock_bytes; r += blockDim.x) {
+    const int tl = (r / (L.vcols * 8)) * 8 + (r & 7);
+    const int col = (r / 8) % L.vcols;
+    unsigned byte;
+    if (tl >= nt) {
+      byte = BITS == 4 ? Codec<4>::kQmaxInt * 0x11u : Codec<8>::kQmaxInt;
+    } else {
+      auto code = [&](int f) -> unsigned {
+        const float v = f < L.D ? tile[tl * stride + f] : 0.0f;
+        return stored_code<BITS>(v, sc[(f / L.group) * kBlockTokens + tl]);
+      };
+      byte = BITS == 4 ? (code(2 * col) | (code(2 * col + 1) << 4)) : code(col);
+    }
+    dst[r] = static_cast<uint8_t>(byte);
+  }
+}
+
+// K: codes of one (head, block); with kLocalScales (group divides 32) also
+// the block's scales, else they come from pack_k_scales_kernel.  LDS: tile,
+// then the block's scales [group in block][D].
+template <int BITS, bool kLocalScales>
+__global__ __launch_bounds__(256) void pack_k_block_kernel(const float* __restrict__ x,
+                                                           Layout L, float* __restrict__ scales,
+                                                           uint8_t* __restrict__ codes) {
+  extern __shared__ float lds[];
+  const long long bh = blockIdx.x / L.nblocks;
+  const int blk = static_cast<int>(blockIdx.x % L.nblocks);
+  const int t0 = blk * kBlockTokens;
+  const int nt = min(kBlockTokens, L.N - t0);
+  const int stride = L.D + 1;
+  float* tile = lds;
+  float* sk = lds + kBlockTokens * stride;
+  float* hs = scales + bh * k_scales_per_head(L);
+  stage_block(x + (bh * L.N + t0) * static_cast<long long>(L.D), nt, L.D, tile);
+  __syncthreads();
+  if (kLocalScales) {
+    // One thread per (group gi of the block, channel d), channel fastest.
+    // Only groups holding a token < N have a scale row.
+    const int groups = kBlockTokens / L.group;
+    for (int i = threadIdx.x; i < groups * L.D; i += blockDim.x) {
+      const int gi = i / L.D, d = i - gi * L.D;
+      const int tl0 = gi * L.group;
+      if (tl0 >= nt) continue;
+      const int tl1 = min(nt, tl0 + L.group);
+      float amax = 0.0f;
+      for (int tl = tl0; tl < tl1; ++tl) amax = fmaxf(amax, fabsf(tile[tl * stride + d]));
+      const float s = group_scale<BITS>(amax);
+      sk[i] = s;
+      hs[k_scale_index(L, t0 + tl0, d)] = s;
+    }
+    __syncthreads();
+  }
+  uint8_t* dst = codes + bh * k_code_bytes_per_head(L) + blk * L.kblock_bytes;
+  for (int r = threadIdx.x; r < L.kblock_bytes; r += blockDim.x) {
+    const int d = (r / (L.kcols * 8)) * 8 + (r & 7);
+    const int j = (r / 8) % L.kcols;
+    auto code = [&](int tl) -> unsigned {
+      if (tl >= nt || d >= L.D) return Codec<BITS>::kQmaxInt;
+      const float s = kLocalScales ? sk[(tl / L.group) * L.D + d]
+                                   : hs[k_scale_index(L, t0 + tl, d)];
+      return stored_code<BITS>(tile[tl * stride + d], s);
+    };
+    const int tl = BITS == 4 ? 2 * j : j;
+    const unsigned byte = BITS == 4 ? (code(tl) | (code(tl + 1) << 4)) : code(tl);
+    dst[r] = static_cast<uint8_t>(byte);
+  }
+}
+
 // Stored code of element (t, i) given its byte offset within the head.
 template <int BITS>
 __device__ __forceinline__ int load_code(const uint8_t* head, long long byte, int odd) {
@@ -186,6 +307,25 @@ inline unsigned grid_for(long long threads) {
 template <int BITS>
 hipError_t pack_bits(const float* x, long long BH, const Layout& L, bool k_style, uint8_t* codes,
                      float* scales, hipStream_t stream) {
+  if (L.D <= kStageMaxD) {
+    const unsigned grid = static_cast<unsigned>(BH * L.nblocks);
+    const size_t tile = sizeof(float) * kBlockTokens * (L.D + 1);
+    if (!k_style) {
+      const size_t lds = tile + sizeof(float) * L.vgroups * kBlockTokens;
+      hipLaunchKernelGGL(pack_v_block_kernel<BITS>, dim3(grid), dim3(256), lds, stream, x, L,
+                         scales, codes);
+    } else if (kBlockTokens % L.group == 0) {
+      const size_t lds = tile + sizeof(float) * (kBlockTokens / L.group) * L.D;
+      hipLaunchKernelGGL((pack_k_block_kernel<BITS, true>), dim3(grid), dim3(256), lds, stream, x,
+                         L, scales, codes);
+    } else {
+      hipLaunchKernelGGL(pack_k_scales_kernel<BITS>, dim3(grid_for(BH * L.kgroups * L.D)),
+                         dim3(256), 0, stream, x, BH, L, scales);
+      hipLaunchKernelGGL((pack_k_block_kernel<BITS, false>), dim3(grid), dim3(256), tile, stream,
+                         x, L, scales, codes);
+    }
+    return hipGetLastError();
+  }
   if (k_style) {
     hipLaunchKernelGGL(pack_k_scales_kernel<BITS>, dim3(grid_for(BH * L.kgroups * L.D)),
                        dim3(256), 0, stream, x, BH, L, scales);

@@ -58,6 +58,23 @@ def test_pack_crafted(kind, bits):
     _check_pack_dequant(k, k.copy(), bits, 8 if kind == "ties" else 32, kind)
 
 
+@pytest.mark.parametrize("N,D,bits,group", [
+    (100, 300, 4, 32),   # D above the LDS-staged limit: two-pass kernels
+    (77, 256, 4, 64),    # K groups longer than a block: scale pass + staged codes
+    (65, 40, 8, 16),     # two K groups per block, staged scales and codes
+    (33, 8, 4, 2),       # sixteen K groups per block, tiny head dim
+    (50, 24, 4, 6),      # group not dividing the block: scale pass + staged codes
+])
+def test_pack_kernel_paths(N, D, bits, group):
+    """Every packing path (LDS-staged per block, with local or precomputed K
+    scales, and the two-pass fallback) against the oracle, ragged N."""
+    rng = np.random.default_rng(N * 1000 + D)
+    k = rng.standard_normal((2, 2, N, D), dtype=np.float32) * np.float32(2.0)
+    v = rng.standard_normal((2, 2, N, D), dtype=np.float32)
+    k[0, 1, : min(N, 20)] = 0.0
+    _check_pack_dequant(k, v, bits, group, f"paths N={N} D={D}")
+
+
 def test_pack_multi_head_random():
     rng = np.random.default_rng(77)
     k = (rng.standard_normal((3, 5, 333, 64), dtype=np.float32) * np.float32(3.0))

@@ -36,13 +36,23 @@ CFLAGS = [
 ]
 
 
+# Extra flags per source.  The matrix-core attend kernels assume finite
+# inputs (non-finite inputs are outside the library's contract), so maxima
+# need no NaN-quieting canonicalization: -fno-honor-nans.  Infinities stay
+# honoured (masked scores are -inf).
+EXTRA_CFLAGS = {
+    "kvq_attend_mfma.hip": ["-fno-honor-nans"],
+    "kvq_attend_mfma32.hip": ["-fno-honor-nans"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA_CFLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

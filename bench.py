@@ -5,9 +5,10 @@ One step = one ``kvq_attend`` call (the fused path: K/V tile loads, in-register
 decode, scores, online softmax (m, z, u), split combine) over one full
 synthetic packed cache of the chosen workload, with Q, the packed cache, the
 output and the workspace resident in HBM before timing starts.  Packing is
-outside the step, as in the pages' timing scope; it and the decode-all
-baseline (kvq_dequant + kvq_attend_f32) are timed separately and reported
-under "extra".
+outside the step, as in the pages' timing scope; it, the decode-all
+baseline (kvq_dequant + kvq_attend_f32) and a plain streaming read of the
+same byte count (kvq_stream_read, the measured HBM ceiling) are timed
+separately and reported under "extra".
 
 The timed steps rotate over enough distinct copies of the packed cache that
 their total exceeds the 256 MB Infinity Cache, so every step streams its KV
@@ -52,9 +53,11 @@ def kv_bytes(w, bits, group):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_mfma_gqa_n4096_traffic.md")
-# The sources the measured kernel is compiled from (its file and the shared header).
+# The sources the measured kernel is compiled from (its file, the shared header
+# and the build script with its flags).
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_kv_cache_attend_amd", "csrc", f)
-                  for f in ("kvq_attend_mfma.hip", "kvq_mfma_common.h")]
+                  for f in ("kvq_attend_mfma.hip", "kvq_mfma_common.h")] + [
+                      os.path.join(ROOT, "quantized_kv_cache_attend_amd", "build.py")]
 
 
 def kernel_source_sha256():
@@ -260,6 +263,30 @@ def main():
         extra.update({"pack_us": round(pack_us, 1), "decode_all_us": round(dec_us, 1),
                       "decode_all_kv_gbs": round(nbytes / (dec_us * 1e-6) / 1e9, 1)})
         log(f"[bench] pack {pack_us:.1f} us, decode-all baseline {dec_us:.1f} us")
+
+        # Measured ceiling: a plain streaming read (kvq_stream_read) of the
+        # same byte count, rotating over as many buffers as the cache copies.
+        rbytes = (nbytes + 15) // 16 * 16
+        bufs = [torch.zeros(rbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for b in bufs:
+            kvq.stream_read(b, sink)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        reps_r = max(copies, min(args.steps, 2000))
+        a.record(stream)
+        for i in range(reps_r):
+            kvq.stream_read(bufs[i % copies], sink)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        read_us = a.elapsed_time(b_) * 1e3 / reps_r
+        del bufs
+        extra.update({"read_ceiling_us": round(read_us, 3),
+                      "read_ceiling_gbs": round(rbytes / (read_us * 1e-6) / 1e9, 1),
+                      "attend_over_read_ceiling": round(kernel_us / read_us, 3)})
+        log(f"[bench] streaming-read ceiling for the same bytes: {read_us:.2f} us "
+            f"({rbytes / (read_us * 1e-6) / 1e9:.0f} GB/s); attend / ceiling = {kernel_us / read_us:.2f}")
 
     cpu = None
     if not args.no_cpu_baseline:

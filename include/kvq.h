@@ -173,6 +173,16 @@ kvq_status kvq_attend_f32(const float* q, const float* k, const float* v,
                           int num_splits, void* workspace, size_t workspace_bytes, float* out,
                           void* stream);
 
+/* ---- kvq_stream_read ------------------------------------------------------------------
+ * Measurement aid, not part of the method: reads `bytes` (a positive multiple
+ * of 16) at device pointer `data` (16-byte aligned) once, with 16-byte loads
+ * spread over the whole chip, and discards them (`sink`: a device word that is
+ * written only if the XOR of all the data equals an arbitrary constant).  The
+ * fused attend reads every KV byte once ([BKD] "every position is still
+ * read"), so this plain read of the same byte count is its measured HBM
+ * ceiling.  Allocates nothing; asynchronous on `stream`. */
+kvq_status kvq_stream_read(const void* data, size_t bytes, void* sink, void* stream);
+
 /* ---- diagnostics -------------------------------------------------------------------- */
 const char* kvq_status_string(int status);  /* static string, never NULL */
 const char* kvq_last_error(void);           /* message of this thread's last failed call */

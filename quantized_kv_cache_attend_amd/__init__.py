@@ -51,6 +51,7 @@ _SIGNATURES = {
                                                                  _c_size, _c_vp, _c_int, _c_vp]),
     "kvq_attend_f32": (_c_int, [_c_vp] * 3 + [_c_int] * 6 + [_c_float, _c_int, _c_vp, _c_size,
                                                              _c_vp, _c_vp]),
+    "kvq_stream_read": (_c_int, [_c_vp, _c_size, _c_vp, _c_vp]),
     "kvq_status_string": (ctypes.c_char_p, [_c_int]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_abi_version": (_c_int, []),
@@ -216,3 +217,19 @@ def attend_f32(q, k, v, sm_scale=0.0, num_splits=0, workspace=None, out=None):
                               num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
                               _stream(q.device)), "kvq_attend_f32")
     return out
+
+
+def stream_read(data, sink=None):
+    """Read every byte of the device tensor `data` once (kvq_stream_read): the
+    plain streaming-read ceiling the fused attend is measured against.
+    `sink` (a one-word int32 device tensor, allocated if omitted) is written
+    only if the XOR of the data equals an arbitrary constant."""
+    torch = _torch()
+    if not data.is_cuda or not data.is_contiguous():
+        raise ValueError("stream_read needs a contiguous device tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=data.device)
+    nbytes = data.numel() * data.element_size()
+    _check(lib.kvq_stream_read(_ptr(data), nbytes, _ptr(sink), _stream(data.device)),
+           "kvq_stream_read")
+    return sink

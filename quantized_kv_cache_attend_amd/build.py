@@ -1,6 +1,7 @@
 """Build ``libkvq.so`` (all HIP sources under ``csrc/``) for gfx950 with hipcc.
 
-Run ``python -m quantized_kv_cache_attend_amd.build`` or call :func:`build`.
+Run ``python quantized_kv_cache_attend_amd/build.py`` (by path: importing the package
+loads the library) or call :func:`build`.
 Every call compiles from scratch into ``_build/`` at the repository root and
 then replaces ``quantized_kv_cache_attend_amd/libkvq.so``.
 """

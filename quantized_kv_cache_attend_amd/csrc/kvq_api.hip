@@ -337,6 +337,18 @@ kvq_status kvq_attend_f32(const float* q, const float* k, const float* v, int B,
                     "attend_f32 launch");
 }
 
+kvq_status kvq_stream_read(const void* data, size_t bytes, void* sink, void* stream) {
+  if (!data || !sink) return fail(KVQ_ERR_INVALID, "null pointer argument");
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(KVQ_ERR_INVALID, "bytes must be a positive multiple of 16 (got %zu)", bytes);
+  if (!aligned(data, 16) || !aligned(sink, 4))
+    return fail(KVQ_ERR_INVALID, "data must be 16-byte aligned and sink 4-byte aligned");
+  return hip_status(launch_stream_read(data, static_cast<long long>(bytes),
+                                       static_cast<unsigned*>(sink),
+                                       static_cast<hipStream_t>(stream)),
+                    "stream_read launch");
+}
+
 const char* kvq_status_string(int status) {
   switch (status) {
     case KVQ_OK: return "ok";
@@ -350,6 +362,6 @@ const char* kvq_status_string(int status) {
 
 const char* kvq_last_error(void) { return g_last_error; }
 
-int kvq_abi_version(void) { return 2; }
+int kvq_abi_version(void) { return 3; }
 
 }  // extern "C"

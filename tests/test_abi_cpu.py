@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert lib.kvq_abi_version() == 2
+    assert lib.kvq_abi_version() == 3
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.kvq_status_string(st)
 
@@ -122,3 +122,10 @@ def test_attend_f32_rejects_before_launch():
                               None) == kvq.KVQ_ERR_INVALID
     assert lib.kvq_attend_f32(FAKE, FAKE, FAKE, 1, 1, 1, 1, 8, 96, 0.0, 1, None, 0, FAKE2,
                               None) == kvq.KVQ_ERR_UNSUPPORTED
+
+
+def test_stream_read_rejects_bad_arguments():
+    for data, nbytes, sink in ((None, 1024, FAKE2), (FAKE, 1024, None), (FAKE, 0, FAKE2),
+                               (FAKE, 1000, FAKE2), (ctypes.c_void_p(0x10008), 1024, FAKE2)):
+        assert lib.kvq_stream_read(data, nbytes, sink, None) == kvq.KVQ_ERR_INVALID
+

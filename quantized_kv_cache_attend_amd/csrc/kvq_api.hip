@@ -169,8 +169,13 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   return KVQ_OK;
 }
 
+// The matrix-core kernels address a head's arrays with 32-bit buffer
+// offsets: up to 2^20 blocks (2^25 tokens) per head.
+constexpr int kMfmaMaxN = 1 << 25;
+
 bool mfma_eligible(const AttendProblem& p) {
   return p.bits == 4 && p.group == 32 && p.D == 128 && p.rows <= kMfma32MaxRows &&
+         p.N <= kMfmaMaxN &&
          aligned(p.q, 16) && aligned(p.k_codes, 16) && aligned(p.v_codes, 16) &&
          aligned(p.k_scales, 16) && aligned(p.v_scales, 16);
 }
@@ -310,7 +315,8 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
       if (!mfma_eligible(p))
         return fail(KVQ_ERR_UNSUPPORTED,
                     "matrix-core kernels need bits=4, group=32, D=128, <= %d query rows per "
-                    "KV head and 16-byte aligned q and cache arrays", kMfma32MaxRows);
+                    "KV head, N <= %d and 16-byte aligned q and cache arrays", kMfma32MaxRows,
+                    kMfmaMaxN);
       return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
     default:
       return fail(KVQ_ERR_INVALID, "unknown variant %d", variant);

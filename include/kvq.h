@@ -155,7 +155,7 @@ kvq_status kvq_attend(const float* q, const uint8_t* k_codes, const float* k_sca
 
 /* Same contract as kvq_attend with an explicit kernel family.
  * KVQ_VARIANT_MFMA returns KVQ_ERR_UNSUPPORTED unless bits == 4,
- * group == 32, D == 128, (Hq/Hkv)*R <= 32, N <= 2^25 and q and all four
+ * group == 32, D == 128, (Hq/Hkv)*R <= 32, N <= 2^25 - 32 and q and all four
  * cache arrays are 16-byte aligned; KVQ_VARIANT_AUTO picks it whenever those
  * hold. */
 kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,

@@ -170,8 +170,8 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
 }
 
 // The matrix-core kernels address a head's arrays with 32-bit buffer
-// offsets: up to 2^20 blocks (2^25 tokens) per head.
-constexpr int kMfmaMaxN = 1 << 25;
+// offsets below 2^31: fewer than 2^20 blocks of 2 KB per head.
+constexpr int kMfmaMaxN = (1 << 25) - kBlockTokens;
 
 bool mfma_eligible(const AttendProblem& p) {
   return p.bits == 4 && p.group == 32 && p.D == 128 && p.rows <= kMfma32MaxRows &&

@@ -101,7 +101,7 @@ def _attend(**kw):
     (dict(splits=4, ws=ctypes.c_void_p(0x40000000), wsb=64), kvq.KVQ_ERR_WORKSPACE),
     (dict(variant=9), kvq.KVQ_ERR_INVALID),
     (dict(variant=2, bits=8), kvq.KVQ_ERR_UNSUPPORTED),      # matrix-core kernel is 4-bit g32 D128
-    (dict(variant=2, D=128, N=(1 << 25) + 1, out=ctypes.c_void_p(1 << 44)),
+    (dict(variant=2, D=128, N=(1 << 25) - 31, out=ctypes.c_void_p(1 << 44)),
      kvq.KVQ_ERR_UNSUPPORTED),                              # past its 32-bit buffer offsets
 ])
 def test_attend_rejects_before_launch(kw, status):

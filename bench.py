@@ -12,7 +12,10 @@ separately and reported under "extra".
 
 The timed steps rotate over enough distinct copies of the packed cache that
 their total exceeds the 256 MB Infinity Cache, so every step streams its KV
-bytes from HBM.
+bytes from HBM.  By default they are replayed from a HIP graph holding one
+step per cache copy (captured once, checked bit for bit against the eager
+result before timing), so that a ~13 us kernel is not paced by the host's
+per-call launch cost; `--launch eager` times a plain Python loop of calls.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 """
@@ -137,8 +140,11 @@ def cpu_baseline(w, q, k, v, bits, group, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=20000)
+    ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="timed steps replayed from a HIP graph (one step per cache copy) "
+                         "or launched one by one from Python")
     ap.add_argument("--workload", default="gqa_n4096", choices=["gqa_n4096", "gqa_n32768"])
     ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--splits", type=int, default=-1, help="-1: workload default, 0: auto")
@@ -194,6 +200,37 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    ref = out.clone()      # every cache copy holds the same bytes: one expected output
+
+    def eager_steps(n):
+        for i in range(n):
+            step(i)
+
+    run_steps = eager_steps
+    if args.launch == "graph":
+        # One graph node per cache copy, on torch's capture stream (default
+        # priority); the kernel resets its own split counters, so replays need
+        # no memset nodes.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_steps(copies)
+        torch.cuda.synchronize()
+        for rep in range(3):     # replays checked bit for bit, eager work between them
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, ref):
+                raise RuntimeError(f"graph replay {rep} differs from the eager result")
+            eager_steps(1)
+            torch.cuda.synchronize()
+
+        def run_steps(n):
+            for _ in range(n // copies):
+                graph.replay()
+            eager_steps(n % copies)
+        run_steps(args.warmup)
+        torch.cuda.synchronize()
 
     # Timed region: K steps back to back, host clock and stream events.
     e0 = torch.cuda.Event(enable_timing=True)
@@ -201,14 +238,27 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    run_steps(args.steps)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     region_ms = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] wall {ms_per_step * 1e3:.2f} us/step, stream events {region_ms * 1e3:.2f} us/step")
+    if not torch.equal(out, ref):
+        raise RuntimeError("timed steps changed the output")
+    log(f"[bench] {args.launch}: wall {ms_per_step * 1e3:.2f} us/step, "
+        f"stream events {region_ms * 1e3:.2f} us/step")
+
+    eager_us = None
+    if args.launch == "graph":
+        # For comparison: the same steps launched one by one from Python.
+        n_e = min(args.steps, 2000)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        eager_steps(n_e)
+        torch.cuda.synchronize()
+        eager_us = (time.perf_counter() - t1) * 1e6 / n_e
+        log(f"[bench] eager Python loop: {eager_us:.2f} us/step")
 
     # Per-launch duration: an event pair around each call (same stream).
     n_ev = min(args.steps, 400)
@@ -232,6 +282,9 @@ def main():
     extra = {"wall_us_per_step": round(ms_per_step * 1e3, 3),
              "stream_event_us_per_step": round(region_ms * 1e3, 3),
              "per_launch_event_us_median": round(launch_us, 3),
+             "launch": (f"HIP graph of {copies} steps, replayed" if args.launch == "graph"
+                        else "eager Python loop"),
+             "eager_wall_us_per_step": None if eager_us is None else round(eager_us, 3),
              "cache_copies": copies, "splits": splits or "auto",
              "variant": args.variant, "output_finite": finite}
 
@@ -269,18 +322,28 @@ def main():
         rbytes = (nbytes + 15) // 16 * 16
         bufs = [torch.zeros(rbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
-        for b in bufs:
-            kvq.stream_read(b, sink)
+        def reads():
+            for b in bufs:
+                kvq.stream_read(b, sink)
+        reads()
+        torch.cuda.synchronize()
+        read_pass = reads
+        if args.launch == "graph":      # launched the same way as the timed steps
+            rgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(rgraph):
+                reads()
+            read_pass = rgraph.replay
+        n_pass = max(1, min(args.steps, 2000) // copies)
+        read_pass()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b_ = torch.cuda.Event(enable_timing=True)
-        reps_r = max(copies, min(args.steps, 2000))
         a.record(stream)
-        for i in range(reps_r):
-            kvq.stream_read(bufs[i % copies], sink)
+        for _ in range(n_pass):
+            read_pass()
         b_.record(stream)
         torch.cuda.synchronize()
-        read_us = a.elapsed_time(b_) * 1e3 / reps_r
+        read_us = a.elapsed_time(b_) * 1e3 / (n_pass * copies)
         del bufs
         extra.update({"read_ceiling_us": round(read_us, 3),
                       "read_ceiling_gbs": round(rbytes / (read_us * 1e-6) / 1e9, 1),

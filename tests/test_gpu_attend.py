@@ -177,6 +177,48 @@ def test_attend_variants_share_one_workspace():
         assert not _counters(ws, w2.B, w2.Hkv).any(), (variant, splits)
 
 
+@pytest.mark.parametrize("variant,shape,splits", [
+    ("mfma", (8, 32, 8, 1, 4096), 0), ("mfma", (2, 16, 2, 2, 1021), 7),
+    ("valu", (8, 32, 8, 1, 4096), 0)])
+def test_attend_graph_replay(variant, shape, splits):
+    """Calls captured in a HIP graph (two per graph, sharing one workspace, as
+    a serving loop or the timed bench steps would launch them) give the eager
+    result bit for bit on every replay, with eager work and host syncs in
+    between; the split counters stay reset."""
+    import torch
+    B, Hq, Hkv, R, N = shape
+    w = Workload("graph", B, Hq, Hkv, R, N, 128, ((4, 32),))
+    q, k, v = make_qkv(w, 4)
+    announce(f"attend graph replay {variant} {shape} splits={splits}")
+    cache = _gpu_cache(k, v, 4, 32)
+    qd = dev(q)
+    q2 = qd.flip(-1).contiguous()
+    ws = kvq.new_workspace(B, Hq, Hkv, R, N, 128, splits)
+    o1, o2 = torch.empty_like(qd), torch.empty_like(qd)
+
+    def calls():
+        kvq.attend(qd, *cache, N, 4, 32, num_splits=splits, workspace=ws, out=o1, variant=variant)
+        kvq.attend(q2, *cache, N, 4, 32, num_splits=splits, workspace=ws, out=o2, variant=variant)
+    calls()
+    torch.cuda.synchronize()
+    e1, e2 = o1.clone(), o2.clone()
+    assert max_abs(host(e1), _oracle(q, k, v, 4, 32)) <= TOL
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o1.fill_(float("nan"))
+        o2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, e1) and torch.equal(o2, e2), rep
+        assert not _counters(ws, B, Hkv).any(), rep
+        kvq.attend(q2, *cache, N, 4, 32, num_splits=splits, workspace=ws, out=o1, variant=variant)
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("hq,hkv,r", [(8, 2, 1), (2, 2, 3), (1, 1, 1), (4, 1, 1), (6, 3, 2)])
 @pytest.mark.parametrize("n", [1, 7, 35, 1021, 4097])
 def test_attend_mfma_ragged_and_gqa_shapes(hq, hkv, r, n):

@@ -286,6 +286,35 @@ def store_v(codes: np.ndarray, scales: np.ndarray, n: int, d: int, bits: int, gr
 
 
 # ---------------------------------------------------------------------------
+# A cache that grows by decode steps
+# ---------------------------------------------------------------------------
+
+def cache_after(k: np.ndarray, v: np.ndarray, n: int, capacity: int, bits: int, group: int):
+    """The packed cache, in the block layout for ``capacity`` tokens, once the
+    first ``n`` tokens of K and V ``[..., N, D]`` have been appended to it.
+
+    [RL] "prefill and decode": a decode step reads the cached K/V and appends
+    its new position.  Reading: the cache of n tokens is the packed tensor of
+    those n tokens ([KPG] "what a byte holds"), its short groups zero-padded
+    ([KPG] "why grouping needs both direction and length"), laid out for the
+    capacity; positions past n are zeros before quantization, so they hold
+    the zero code with scale 1 where a whole group is empty.
+    Parity: pinned in tests/test_oracle_cache.py (equality with plain packing
+    at n = capacity; the byte formula of the layout read back independently;
+    a token-by-token append that requantizes the open K group).
+    """
+    _check_format(bits, group)
+    lead, d = k.shape[:-2], k.shape[-1]
+    kp = np.zeros(lead + (capacity, d), np.float32)
+    vp = np.zeros(lead + (capacity, d), np.float32)
+    kp[..., :n, :] = k[..., :n, :]
+    vp[..., :n, :] = v[..., :n, :]
+    kc, ks = store_k(*pack_k(kp, bits, group), capacity, d, bits, group)
+    vc, vs = store_v(*pack_v(vp, bits, group), capacity, d, bits, group)
+    return kc, ks, vc, vs
+
+
+# ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
 

@@ -127,6 +127,48 @@ kvq_status kvq_dequant_k(const uint8_t* codes, const float* scales, int B, int H
 kvq_status kvq_dequant_v(const uint8_t* codes, const float* scales, int B, int H, int N, int D,
                          int bits, int group, float* out, void* stream);
 
+/* ---- growing cache: kvq_cache_clear, kvq_append, kvq_attend_cache -------------
+ * A decode step reads the cached K/V and appends its new position ([RL]
+ * "prefill and decode").  A cache sized for `capacity` tokens uses the
+ * layouts above with N = capacity (sizes: kvq_k_code_bytes(B, H, capacity,
+ * ...) etc.).  After n tokens it holds exactly the bytes kvq_pack_k/_v write
+ * for those n tokens zero-padded to `capacity` ([KPG] "why grouping needs
+ * both direction and length": short groups are padded with zeros): positions
+ * past n hold the zero code, and K groups past the last token and V groups
+ * of tokens past n have scale 1.  V groups lie inside one token, so a new
+ * token's V is packed on its own; K groups run along tokens, so the open K
+ * group (the one holding token n-1 while n % group != 0) is requantized from
+ * float32 whenever tokens join it, its earlier tokens' K taken from k_tail.
+ *
+ * kvq_cache_clear: the empty cache (n = 0): every stored code qmax, every
+ *   scale 1.  k_tail needs no initialization.
+ * kvq_append: append T >= 1 tokens k_new, v_new [B][H][T][D] float32 after
+ *   the first N >= 0 tokens (N + T <= capacity).  k_tail [B][H][group][D]
+ *   float32, slot t % group = K of token t of the open group: read for the
+ *   open group's earlier tokens and rewritten for the new open group, so it
+ *   must be the tail the previous appends left (unused when N % group == 0).
+ *   The cache must hold the state of N tokens (kvq_cache_clear, then appends
+ *   of N tokens in total; a prompt can be appended in one call).  Bit-exact:
+ *   afterwards the arrays equal the pack of all N + T tokens as above.  The
+ *   new rows must not overlap the cache arrays; calls on one cache must be
+ *   ordered (one stream).
+ * kvq_attend_cache: kvq_attend_variant over the first N tokens of a cache
+ *   laid out for `capacity` >= N tokens whose positions past N are in the
+ *   empty state above (as kvq_cache_clear + kvq_append leave them).  The
+ *   matrix-core limits of kvq_attend_variant apply with capacity in place
+ *   of N; capacity == N is exactly kvq_attend_variant. */
+kvq_status kvq_cache_clear(int B, int H, int capacity, int D, int bits, int group,
+                           uint8_t* k_codes, float* k_scales, uint8_t* v_codes, float* v_scales,
+                           void* stream);
+kvq_status kvq_append(const float* k_new, const float* v_new, int B, int H, int N, int T,
+                      int capacity, int D, int bits, int group, uint8_t* k_codes, float* k_scales,
+                      uint8_t* v_codes, float* v_scales, float* k_tail, void* stream);
+kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float* k_scales,
+                            const uint8_t* v_codes, const float* v_scales, int B, int Hq, int Hkv,
+                            int R, int N, int capacity, int D, int bits, int group,
+                            float sm_scale, int num_splits, void* workspace,
+                            size_t workspace_bytes, float* out, int variant, void* stream);
+
 /* ---- kvq_attend ---------------------------------------------------------------
  * out[b][hq][r][:] = softmax_j(sm_scale * q[b][hq][r] . k_j) v_j over all N
  * tokens of KV head hq / (Hq/Hkv), with k_j, v_j decoded from the packed

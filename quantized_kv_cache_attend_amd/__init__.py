@@ -49,6 +49,10 @@ _SIGNATURES = {
                                                          _c_vp, _c_vp]),
     "kvq_attend_variant": (_c_int, [_c_vp] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_vp,
                                                                  _c_size, _c_vp, _c_int, _c_vp]),
+    "kvq_cache_clear": (_c_int, [_c_int] * 6 + [_c_vp] * 5),
+    "kvq_append": (_c_int, [_c_vp] * 2 + [_c_int] * 8 + [_c_vp] * 6),
+    "kvq_attend_cache": (_c_int, [_c_vp] * 5 + [_c_int] * 9 + [_c_float, _c_int, _c_vp, _c_size,
+                                                               _c_vp, _c_int, _c_vp]),
     "kvq_attend_f32": (_c_int, [_c_vp] * 3 + [_c_int] * 6 + [_c_float, _c_int, _c_vp, _c_size,
                                                              _c_vp, _c_vp]),
     "kvq_stream_read": (_c_int, [_c_vp, _c_size, _c_vp, _c_vp]),
@@ -180,9 +184,23 @@ def dequant_v(codes, scales, N, D, bits=4, group=32, out=None):
     return _dequant(lib.kvq_dequant_v, codes, scales, N, D, bits, group, out)
 
 
+def _check_cache(arrays, B, H, cap, D, bits, group):
+    """The four packed arrays hold at least the layout's elements for `cap` tokens."""
+    for t, shape, name in zip(arrays, packed_shapes(B, H, cap, D, bits, group),
+                              ("k_codes", "k_scales", "v_codes", "v_scales")):
+        need = 1
+        for n in shape:
+            need *= n
+        if t.numel() < need:
+            raise ValueError(f"{name} holds {t.numel()} elements, the layout for {cap} tokens "
+                             f"needs {need}")
+
+
 def attend(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scale=0.0,
-           num_splits=0, workspace=None, out=None, variant="auto"):
-    """Fused attention of q [B,Hq,R,D] over the packed cache (KV heads = k_codes.shape[1])."""
+           num_splits=0, workspace=None, out=None, variant="auto", capacity=None):
+    """Fused attention of q [B,Hq,R,D] over the first N tokens of the packed
+    cache (KV heads = k_codes.shape[1]); `capacity`: the tokens the cache
+    layout is sized for (default N; a cache grown by append())."""
     torch = _torch()
     _need(q, torch.float32, "q")
     for t, n, dt in ((k_codes, "k_codes", torch.uint8), (k_scales, "k_scales", torch.float32),
@@ -190,16 +208,66 @@ def attend(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scal
         _need(t, dt, n)
     B, Hq, R, D = q.shape
     Hkv = k_codes.shape[1]
+    cap = N if capacity is None else capacity
+    if bits in (4, 8) and group >= 2 and N >= 1 and cap >= N:
+        _check_cache((k_codes, k_scales, v_codes, v_scales), B, Hkv, cap, D, bits, group)
     if workspace is None:
         workspace = new_workspace(B, Hq, Hkv, R, N, D, num_splits, device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    _check(lib.kvq_attend_variant(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
-                                  _ptr(v_scales), B, Hq, Hkv, R, N, D, bits, group,
-                                  float(sm_scale), num_splits, _ptr(workspace),
-                                  workspace.numel(), _ptr(out), VARIANTS[variant],
-                                  _stream(q.device)), "kvq_attend")
+    if capacity is None:
+        _check(lib.kvq_attend_variant(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                      _ptr(v_scales), B, Hq, Hkv, R, N, D, bits, group,
+                                      float(sm_scale), num_splits, _ptr(workspace),
+                                      workspace.numel(), _ptr(out), VARIANTS[variant],
+                                      _stream(q.device)), "kvq_attend")
+    else:
+        _check(lib.kvq_attend_cache(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                    _ptr(v_scales), B, Hq, Hkv, R, N, capacity, D, bits, group,
+                                    float(sm_scale), num_splits, _ptr(workspace),
+                                    workspace.numel(), _ptr(out), VARIANTS[variant],
+                                    _stream(q.device)), "kvq_attend_cache")
     return out
+
+
+# --- growing cache (decode steps) -------------------------------------------------------
+
+def new_cache(B, H, capacity, D, bits=4, group=32, device="cuda"):
+    """An empty packed cache for `capacity` tokens (kvq_cache_clear) and its
+    float32 K tail: (k_codes, k_scales, v_codes, v_scales, k_tail)."""
+    torch = _torch()
+    kcs, kss, vcs, vss = packed_shapes(B, H, capacity, D, bits, group)
+    kc = torch.empty(kcs, dtype=torch.uint8, device=device)
+    ks = torch.empty(kss, dtype=torch.float32, device=device)
+    vc = torch.empty(vcs, dtype=torch.uint8, device=device)
+    vs = torch.empty(vss, dtype=torch.float32, device=device)
+    tail = torch.zeros((B, H, group, D), dtype=torch.float32, device=device)
+    _check(lib.kvq_cache_clear(B, H, capacity, D, bits, group, _ptr(kc), _ptr(ks), _ptr(vc),
+                               _ptr(vs), _stream(kc.device)), "kvq_cache_clear")
+    return kc, ks, vc, vs, tail
+
+
+def append(k_new, v_new, N, cache, capacity, bits=4, group=32):
+    """Append k_new, v_new [B,H,T,D] float32 after the first N tokens of
+    `cache` (the tuple new_cache returns) laid out for `capacity` tokens."""
+    torch = _torch()
+    _need(k_new, torch.float32, "k_new")
+    _need(v_new, torch.float32, "v_new")
+    if k_new.shape != v_new.shape or k_new.dim() != 4:
+        raise ValueError("k_new and v_new must both be [B, H, T, D]")
+    kc, ks, vc, vs, tail = cache
+    for t, n, dt in ((kc, "k_codes", torch.uint8), (ks, "k_scales", torch.float32),
+                     (vc, "v_codes", torch.uint8), (vs, "v_scales", torch.float32),
+                     (tail, "k_tail", torch.float32)):
+        _need(t, dt, n)
+    B, H, T, D = k_new.shape
+    if bits in (4, 8) and group >= 2 and capacity >= 1:
+        _check_cache((kc, ks, vc, vs), B, H, capacity, D, bits, group)
+        if tail.numel() < B * H * group * D:
+            raise ValueError(f"k_tail must hold [B, H, group, D] = {(B, H, group, D)}")
+    _check(lib.kvq_append(_ptr(k_new), _ptr(v_new), B, H, N, T, capacity, D, bits, group,
+                          _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), _ptr(tail),
+                          _stream(k_new.device)), "kvq_append")
 
 
 def attend_f32(q, k, v, sm_scale=0.0, num_splits=0, workspace=None, out=None):

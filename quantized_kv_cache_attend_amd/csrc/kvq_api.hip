@@ -84,9 +84,10 @@ int auto_splits(int B, int Hkv, int N) {
 
 // Shared validation of the attention calls.  `bits` == 32 marks the
 // float32-cache path.
+// `cap`: tokens the packed layout is sized for (>= N; N for the float32 cache).
 kvq_status check_attend(const float* q, const void* k, const void* ks, const void* v,
-                        const void* vs, int B, int Hq, int Hkv, int R, int N, int D, int bits,
-                        int group, float sm_scale, int num_splits, void* workspace,
+                        const void* vs, int B, int Hq, int Hkv, int R, int N, int cap, int D,
+                        int bits, int group, float sm_scale, int num_splits, void* workspace,
                         size_t workspace_bytes, float* out, AttendProblem* p) {
   if (!q || !k || !v || !out || (bits != 32 && (!ks || !vs)))
     return fail(KVQ_ERR_INVALID, "null pointer argument");
@@ -94,6 +95,7 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
     return fail(KVQ_ERR_INVALID, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d R=%d N=%d D=%d)", B, Hq,
                 Hkv, R, N, D);
   if (Hq % Hkv) return fail(KVQ_ERR_INVALID, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (cap < N) return fail(KVQ_ERR_INVALID, "capacity=%d < N=%d", cap, N);
   if (bits != 32 && !format_ok(bits, group))
     return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
                 group);
@@ -116,7 +118,7 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   if (bits == 32) {
     kb = vb = sizeof(float) * static_cast<size_t>(BH) * N * D;
   } else {
-    const Layout L = make_layout(N, D, bits, group);
+    const Layout L = make_layout(cap, D, bits, group);
     kb = static_cast<size_t>(BH * k_code_bytes_per_head(L));
     vb = static_cast<size_t>(BH * v_code_bytes_per_head(L));
     ksb = sizeof(float) * static_cast<size_t>(BH * k_scales_per_head(L));
@@ -153,6 +155,7 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   p->Hkv = Hkv;
   p->R = R;
   p->N = N;
+  p->cap = cap;
   p->D = D;
   p->rows = rows;
   p->bits = bits;
@@ -175,7 +178,7 @@ constexpr int kMfmaMaxN = (1 << 25) - kBlockTokens;
 
 bool mfma_eligible(const AttendProblem& p) {
   return p.bits == 4 && p.group == 32 && p.D == 128 && p.rows <= kMfma32MaxRows &&
-         p.N <= kMfmaMaxN &&
+         p.cap <= kMfmaMaxN &&
          aligned(p.q, 16) && aligned(p.k_codes, 16) && aligned(p.v_codes, 16) &&
          aligned(p.k_scales, 16) && aligned(p.v_scales, 16);
 }
@@ -295,14 +298,75 @@ kvq_status kvq_dequant_v(const uint8_t* codes, const float* scales, int B, int H
                     "dequant_v launch");
 }
 
-kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,
-                              const uint8_t* v_codes, const float* v_scales, int B, int Hq,
-                              int Hkv, int R, int N, int D, int bits, int group, float sm_scale,
-                              int num_splits, void* workspace, size_t workspace_bytes,
-                              float* out, int variant, void* stream) {
+kvq_status kvq_cache_clear(int B, int H, int capacity, int D, int bits, int group,
+                           uint8_t* k_codes, float* k_scales, uint8_t* v_codes, float* v_scales,
+                           void* stream) {
+  if (!k_codes || !k_scales || !v_codes || !v_scales)
+    return fail(KVQ_ERR_INVALID, "null pointer argument");
+  if (B < 1 || H < 1 || capacity < 1 || D < 1)
+    return fail(KVQ_ERR_INVALID, "sizes must be >= 1 (B=%d H=%d capacity=%d D=%d)", B, H,
+                capacity, D);
+  if (!format_ok(bits, group))
+    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
+                group);
+  if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
+    return fail(KVQ_ERR_INVALID, "float arrays must be 4-byte aligned");
+  return hip_status(launch_cache_clear(B, H, capacity, D, bits, group, k_codes, k_scales, v_codes,
+                                       v_scales, static_cast<hipStream_t>(stream)),
+                    "cache_clear launch");
+}
+
+kvq_status kvq_append(const float* k_new, const float* v_new, int B, int H, int N, int T,
+                      int capacity, int D, int bits, int group, uint8_t* k_codes, float* k_scales,
+                      uint8_t* v_codes, float* v_scales, float* k_tail, void* stream) {
+  if (!k_new || !v_new || !k_codes || !k_scales || !v_codes || !v_scales || !k_tail)
+    return fail(KVQ_ERR_INVALID, "null pointer argument");
+  if (B < 1 || H < 1 || T < 1 || D < 1 || N < 0)
+    return fail(KVQ_ERR_INVALID, "sizes must be >= 1, N >= 0 (B=%d H=%d N=%d T=%d D=%d)", B, H,
+                N, T, D);
+  if (capacity < 1 || static_cast<long long>(N) + T > capacity)
+    return fail(KVQ_ERR_INVALID, "N + T = %lld exceeds capacity=%d",
+                static_cast<long long>(N) + T, capacity);
+  if (!format_ok(bits, group))
+    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
+                group);
+  if (!aligned(k_new, 4) || !aligned(v_new, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4) ||
+      !aligned(k_tail, 4))
+    return fail(KVQ_ERR_INVALID, "float arrays must be 4-byte aligned");
+  const long long BH = static_cast<long long>(B) * H;
+  const Layout L = make_layout(capacity, D, bits, group);
+  const size_t new_bytes = sizeof(float) * static_cast<size_t>(BH) * T * D;
+  const size_t tail_bytes = sizeof(float) * static_cast<size_t>(BH) * group * D;
+  const void* ins[2] = {k_new, v_new};
+  const void* outs[5] = {k_codes, k_scales, v_codes, v_scales, k_tail};
+  const size_t out_bytes[5] = {static_cast<size_t>(BH * k_code_bytes_per_head(L)),
+                               sizeof(float) * static_cast<size_t>(BH * k_scales_per_head(L)),
+                               static_cast<size_t>(BH * v_code_bytes_per_head(L)),
+                               sizeof(float) * static_cast<size_t>(BH * v_scales_per_head(L)),
+                               tail_bytes};
+  for (int a = 0; a < 5; ++a) {
+    for (int b = 0; b < 2; ++b)
+      if (overlaps(outs[a], out_bytes[a], ins[b], new_bytes))
+        return fail(KVQ_ERR_INVALID, "the new K/V rows overlap a cache array");
+    for (int b = a + 1; b < 5; ++b)
+      if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b]))
+        return fail(KVQ_ERR_INVALID, "cache arrays overlap");
+  }
+  return hip_status(launch_append(k_new, v_new, B, H, N, T, capacity, D, bits, group, k_codes,
+                                  k_scales, v_codes, v_scales, k_tail,
+                                  static_cast<hipStream_t>(stream)),
+                    "append launch");
+}
+
+kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float* k_scales,
+                            const uint8_t* v_codes, const float* v_scales, int B, int Hq, int Hkv,
+                            int R, int N, int capacity, int D, int bits, int group,
+                            float sm_scale, int num_splits, void* workspace,
+                            size_t workspace_bytes, float* out, int variant, void* stream) {
   AttendProblem p;
-  kvq_status st = check_attend(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N, D, bits,
-                               group, sm_scale, num_splits, workspace, workspace_bytes, out, &p);
+  kvq_status st = check_attend(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N, capacity,
+                               D, bits, group, sm_scale, num_splits, workspace, workspace_bytes,
+                               out, &p);
   if (st != KVQ_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
@@ -323,6 +387,16 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
   }
 }
 
+kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,
+                              const uint8_t* v_codes, const float* v_scales, int B, int Hq,
+                              int Hkv, int R, int N, int D, int bits, int group, float sm_scale,
+                              int num_splits, void* workspace, size_t workspace_bytes,
+                              float* out, int variant, void* stream) {
+  return kvq_attend_cache(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N, N, D, bits,
+                          group, sm_scale, num_splits, workspace, workspace_bytes, out, variant,
+                          stream);
+}
+
 kvq_status kvq_attend(const float* q, const uint8_t* k_codes, const float* k_scales,
                       const uint8_t* v_codes, const float* v_scales, int B, int Hq, int Hkv,
                       int R, int N, int D, int bits, int group, float sm_scale, int num_splits,
@@ -336,7 +410,7 @@ kvq_status kvq_attend_f32(const float* q, const float* k, const float* v, int B,
                           int R, int N, int D, float sm_scale, int num_splits, void* workspace,
                           size_t workspace_bytes, float* out, void* stream) {
   AttendProblem p;
-  kvq_status st = check_attend(q, k, nullptr, v, nullptr, B, Hq, Hkv, R, N, D, 32, 1, sm_scale,
+  kvq_status st = check_attend(q, k, nullptr, v, nullptr, B, Hq, Hkv, R, N, N, D, 32, 1, sm_scale,
                                num_splits, workspace, workspace_bytes, out, &p);
   if (st != KVQ_OK) return st;
   return hip_status(launch_attend_valu(p, static_cast<hipStream_t>(stream)),
@@ -368,6 +442,6 @@ const char* kvq_status_string(int status) {
 
 const char* kvq_last_error(void) { return g_last_error; }
 
-int kvq_abi_version(void) { return 3; }
+int kvq_abi_version(void) { return 4; }
 
 }  // extern "C"

@@ -349,7 +349,8 @@ attend_mfma_r4_kernel(AttendProblem p) {
   }
   const long long bh = head;
   const int rows = p.rows;
-  const int nblocks = (p.N + kBlockTokens - 1) / kBlockTokens;
+  // Per-head strides follow the layout's capacity; only blocks below N are read.
+  const int nblocks = (p.cap + kBlockTokens - 1) / kBlockTokens;
   Head h;
   h.kc = head_rsrc(p.k_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
   h.ksc = head_rsrc(p.k_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);

@@ -368,7 +368,8 @@ attend_mfma_r32_kernel(AttendProblem p) {
   }
   const long long bh = head;
   const int rows = p.rows;
-  const int nblocks = (p.N + kBlockTokens - 1) / kBlockTokens;
+  // Per-head strides follow the layout's capacity; only blocks below N are read.
+  const int nblocks = (p.cap + kBlockTokens - 1) / kBlockTokens;
   Head32 h;
   h.kc = head_rsrc(p.k_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
   h.ksc = head_rsrc(p.k_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
@@ -388,7 +389,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
   // the wave that owns it attends it first.  Its loads go out before the
   // query rows are staged.
   const bool active = b_first < b_end;
-  const bool partial = (p.N % kBlockTokens) != 0 && b_last == nblocks - 1;
+  const bool partial = (p.N % kBlockTokens) != 0 && b_last == (p.N - 1) / kBlockTokens;
   const int first = partial ? b_last : b_first;
   const int loop_begin = partial ? b_first : b_first + kW;
   const int loop_end = partial ? b_last - kW : b_last;  // inclusive

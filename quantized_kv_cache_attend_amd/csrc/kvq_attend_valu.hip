@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   const long long bh = static_cast<long long>(blockIdx.z) * p.Hkv + blockIdx.y;
   const int t_begin = split * p.tokens_per_split;
   const int t_end = min(p.N, t_begin + p.tokens_per_split);
-  const Layout L = make_layout(p.N, p.D, SRC == 32 ? 8 : SRC, SRC == 32 ? 2 : p.group);
+  const Layout L = make_layout(p.cap, p.D, SRC == 32 ? 8 : SRC, SRC == 32 ? 2 : p.group);
 
   // Query rows of this KV head are contiguous in q: [bh*rows, bh*rows + rows).
   for (int i = tid; i < rows * D; i += kThreads)

@@ -304,6 +304,105 @@ inline unsigned grid_for(long long threads) {
   return static_cast<unsigned>((threads + 255) / 256);
 }
 
+// ---- growing cache --------------------------------------------------------
+// A decode step reads the cached K/V and appends the new position
+// ("给长前缀列一张有单位的资源账本", "prefill and decode").  Here the cache
+// after n tokens holds exactly the packed form of those n tokens
+// zero-padded to the layout's capacity, i.e. what the pack kernels give for
+// that input: an empty cache is all zero codes with scale 1 (the all-zero
+// group of the format), V groups lie inside one token so a new token's V is
+// packed on its own, and a K group spans `group` tokens of one channel, so
+// the open group (the one holding token n - 1 when the group is not full)
+// is requantized from float32 on every append, with the K values of its
+// earlier tokens taken from the tail the appends keep.
+
+// Empty state: every stored code the zero code, every scale 1.
+__global__ __launch_bounds__(256) void cache_clear_kernel(uint8_t* __restrict__ kc, long long nkc,
+                                                          float* __restrict__ ks, long long nks,
+                                                          uint8_t* __restrict__ vc, long long nvc,
+                                                          float* __restrict__ vs, long long nvs,
+                                                          uint8_t zero_code) {
+  const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+  const long long first = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (long long i = first; i < nkc; i += stride) kc[i] = zero_code;
+  for (long long i = first; i < nvc; i += stride) vc[i] = zero_code;
+  for (long long i = first; i < nks; i += stride) ks[i] = 1.0f;
+  for (long long i = first; i < nvs; i += stride) vs[i] = 1.0f;
+}
+
+// Append tokens [N, N + T) of every head.  Threads [0, BH*D): one K channel
+// (head, d) each, walking the K groups the new tokens touch; the rest: one
+// V group (head, new token, feature group) each.  A K thread owns its
+// channel's tail column, so it reads the open group's earlier tokens before
+// it overwrites slots with the tokens of the new open group.
+template <int BITS>
+__global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ k_new,
+                                                     const float* __restrict__ v_new,
+                                                     long long BH, Layout L, int N, int T,
+                                                     uint8_t* __restrict__ k_codes,
+                                                     float* __restrict__ k_scales,
+                                                     uint8_t* __restrict__ v_codes,
+                                                     float* __restrict__ v_scales,
+                                                     float* __restrict__ k_tail) {
+  const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const long long nk = BH * L.D;
+  const int n1 = N + T;
+  const int g = L.group;
+  constexpr int kStep = BITS == 4 ? 2 : 1;  // tokens (K) or features (V) per byte
+  if (tid < nk) {
+    const int d = static_cast<int>(tid % L.D);
+    const long long bh = tid / L.D;
+    const float* src = k_new + bh * T * static_cast<long long>(L.D) + d;
+    float* tail = k_tail + bh * g * static_cast<long long>(L.D) + d;
+    uint8_t* codes = k_codes + bh * k_code_bytes_per_head(L);
+    float* scales = k_scales + bh * k_scales_per_head(L);
+    const int tpad = L.nblocks * kBlockTokens;  // tokens that have stored codes
+    auto value = [&](int t) -> float {
+      return t < N ? tail[static_cast<long long>(t % g) * L.D]
+                   : src[static_cast<long long>(t - N) * L.D];
+    };
+    for (int g0 = N / g * g; g0 < n1; g0 += g) {
+      const int gend = min(g0 + g, n1);
+      float amax = 0.0f;
+      for (int t = g0; t < gend; ++t) amax = fmaxf(amax, fabsf(value(t)));
+      const float s = group_scale<BITS>(amax);
+      scales[k_scale_index(L, g0, d)] = s;
+      auto code = [&](int t) -> unsigned {
+        return t < n1 ? stored_code<BITS>(value(t), s) : Codec<BITS>::kQmaxInt;
+      };
+      const int tend = min(g0 + g, tpad);
+      for (int t = g0; t < tend; t += kStep) {
+        const unsigned byte = BITS == 4 ? (code(t) | (code(t + 1) << 4)) : code(t);
+        codes[k_code_byte(L, t, d)] = static_cast<uint8_t>(byte);
+      }
+    }
+    for (int t = max(N, n1 / g * g); t < n1; ++t)
+      tail[static_cast<long long>(t % g) * L.D] = src[static_cast<long long>(t - N) * L.D];
+    return;
+  }
+  const long long i = tid - nk;
+  if (i >= BH * T * L.vgroups) return;
+  const int G = static_cast<int>(i % L.vgroups);
+  const long long rest = i / L.vgroups;
+  const int j = static_cast<int>(rest % T);
+  const long long bh = rest / T;
+  const int t = N + j;
+  const float* src = v_new + (bh * T + j) * static_cast<long long>(L.D);
+  const int f0 = G * g, f1 = min(L.D, f0 + g);
+  float amax = 0.0f;
+  for (int f = f0; f < f1; ++f) amax = fmaxf(amax, fabsf(src[f]));
+  const float s = group_scale<BITS>(amax);
+  v_scales[bh * v_scales_per_head(L) + v_scale_index(L, t, f0)] = s;
+  uint8_t* codes = v_codes + bh * v_code_bytes_per_head(L);
+  auto code = [&](int f) -> unsigned {
+    return f < L.D ? stored_code<BITS>(src[f], s) : Codec<BITS>::kQmaxInt;
+  };
+  for (int f = f0; f < f0 + g; f += kStep) {
+    const unsigned byte = BITS == 4 ? (code(f) | (code(f + 1) << 4)) : code(f);
+    codes[v_code_byte(L, t, f)] = static_cast<uint8_t>(byte);
+  }
+}
+
 template <int BITS>
 hipError_t pack_bits(const float* x, long long BH, const Layout& L, bool k_style, uint8_t* codes,
                      float* scales, hipStream_t stream) {
@@ -349,6 +448,37 @@ hipError_t launch_pack(const float* x, int B, int H, int N, int D, int bits, int
   const Layout L = make_layout(N, D, bits, group);
   return bits == 4 ? pack_bits<4>(x, BH, L, k_style, codes, scales, stream)
                    : pack_bits<8>(x, BH, L, k_style, codes, scales, stream);
+}
+
+hipError_t launch_cache_clear(int B, int H, int cap, int D, int bits, int group, uint8_t* k_codes,
+                              float* k_scales, uint8_t* v_codes, float* v_scales,
+                              hipStream_t stream) {
+  const long long BH = static_cast<long long>(B) * H;
+  const Layout L = make_layout(cap, D, bits, group);
+  const uint8_t zero = bits == 4 ? 0x77 : 0x7F;  // stored code qmax (both nibbles for 4-bit)
+  const long long most = BH * (k_code_bytes_per_head(L) > v_code_bytes_per_head(L)
+                                   ? k_code_bytes_per_head(L)
+                                   : v_code_bytes_per_head(L));
+  const unsigned grid = most > 4096LL * 256 ? 4096u : grid_for(most);
+  hipLaunchKernelGGL(cache_clear_kernel, dim3(grid), dim3(256), 0, stream, k_codes,
+                     BH * k_code_bytes_per_head(L), k_scales, BH * k_scales_per_head(L), v_codes,
+                     BH * v_code_bytes_per_head(L), v_scales, BH * v_scales_per_head(L), zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const float* k_new, const float* v_new, int B, int H, int N, int T,
+                         int cap, int D, int bits, int group, uint8_t* k_codes, float* k_scales,
+                         uint8_t* v_codes, float* v_scales, float* k_tail, hipStream_t stream) {
+  const long long BH = static_cast<long long>(B) * H;
+  const Layout L = make_layout(cap, D, bits, group);
+  const unsigned grid = grid_for(BH * D + BH * T * static_cast<long long>(L.vgroups));
+  if (bits == 4)
+    hipLaunchKernelGGL(append_kernel<4>, dim3(grid), dim3(256), 0, stream, k_new, v_new, BH, L, N,
+                       T, k_codes, k_scales, v_codes, v_scales, k_tail);
+  else
+    hipLaunchKernelGGL(append_kernel<8>, dim3(grid), dim3(256), 0, stream, k_new, v_new, BH, L, N,
+                       T, k_codes, k_scales, v_codes, v_scales, k_tail);
+  return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const float* scales, int B, int H, int N, int D,

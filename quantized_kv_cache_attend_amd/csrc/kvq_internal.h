@@ -26,6 +26,7 @@ struct AttendProblem {
   const float* v_f32;
   float* out;              // [B][Hq][R][D]
   int B, Hq, Hkv, R, N, D;
+  int cap;                 // tokens the packed layout is sized for (>= N; N for float32)
   int rows;                // (Hq / Hkv) * R: query rows sharing one KV head
   int bits, group;         // 4/8 and group; bits == 32 marks the float32 cache
   float qscale;            // sm_scale * log2(e)
@@ -51,6 +52,16 @@ WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int R, int D, int split
 // Launchers (host functions; return the launch's hipError_t).
 hipError_t launch_pack(const float* x, int B, int H, int N, int D, int bits, int group,
                        bool k_style, uint8_t* codes, float* scales, hipStream_t stream);
+// Empty-cache state (every code the zero code, every scale 1) and the
+// decode-step append of T tokens after the first N of a cache laid out for
+// `cap` tokens; k_tail [B*H][group][D] keeps the float32 K of the tokens of
+// the open K group.
+hipError_t launch_cache_clear(int B, int H, int cap, int D, int bits, int group, uint8_t* k_codes,
+                              float* k_scales, uint8_t* v_codes, float* v_scales,
+                              hipStream_t stream);
+hipError_t launch_append(const float* k_new, const float* v_new, int B, int H, int N, int T,
+                         int cap, int D, int bits, int group, uint8_t* k_codes, float* k_scales,
+                         uint8_t* v_codes, float* v_scales, float* k_tail, hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* codes, const float* scales, int B, int H, int N, int D,
                           int bits, int group, bool k_style, float* out, hipStream_t stream);
 hipError_t launch_attend_valu(const AttendProblem& p, hipStream_t stream);

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert lib.kvq_abi_version() == 3
+    assert lib.kvq_abi_version() == 4
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.kvq_status_string(st)
 
@@ -131,3 +131,55 @@ def test_stream_read_rejects_bad_arguments():
                                (FAKE, 1000, FAKE2), (ctypes.c_void_p(0x10008), 1024, FAKE2)):
         assert lib.kvq_stream_read(data, nbytes, sink, None) == kvq.KVQ_ERR_INVALID
 
+
+
+def _attend_cache(N, capacity, **kw):
+    a = dict(q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, D=32, variant=0, out=FAKE2)
+    a.update(kw)
+    return lib.kvq_attend_cache(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], 1, 4, 2, 1, N,
+                                capacity, a["D"], 4, 32, 0.0, 1, None, 0, a["out"], a["variant"],
+                                None)
+
+
+def test_attend_cache_rejects_before_launch():
+    assert _attend_cache(64, 63) == kvq.KVQ_ERR_INVALID               # capacity < N
+    assert _attend_cache(64, 64, q=None) == kvq.KVQ_ERR_INVALID
+    assert _attend_cache(0, 64) == kvq.KVQ_ERR_INVALID
+    # matrix-core limits apply to the capacity (the per-head buffer extent)
+    assert _attend_cache(64, (1 << 25) - 31, D=128, variant=2,
+                         out=ctypes.c_void_p(1 << 44)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_last_error()
+
+
+def _append(**kw):
+    a = dict(k=FAKE, v=FAKE, B=1, H=2, N=5, T=3, cap=16, D=8, bits=4, group=8,
+             kc=ctypes.c_void_p(1 << 30), ks=ctypes.c_void_p(2 << 30), vc=ctypes.c_void_p(3 << 30),
+             vs=ctypes.c_void_p(4 << 30), tail=ctypes.c_void_p(5 << 30))
+    a.update(kw)
+    return lib.kvq_append(a["k"], a["v"], a["B"], a["H"], a["N"], a["T"], a["cap"], a["D"],
+                          a["bits"], a["group"], a["kc"], a["ks"], a["vc"], a["vs"], a["tail"],
+                          None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(k=None), dict(tail=None), dict(vs=None),
+    dict(T=0), dict(N=-1), dict(B=0), dict(D=0),
+    dict(N=14, T=3),                                   # past the capacity
+    dict(cap=0, N=0, T=1),
+    dict(bits=6), dict(group=5),
+    dict(k=ctypes.c_void_p(0x10002)),                  # misaligned float pointer
+    dict(tail=ctypes.c_void_p((1 << 30) + 64)),        # tail inside the K codes
+    dict(k=ctypes.c_void_p(3 << 30)),                  # new rows inside the V codes
+])
+def test_append_rejects_before_launch(kw):
+    assert _append(**kw) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_last_error()
+
+
+def test_cache_clear_rejects_before_launch():
+    ptrs = [ctypes.c_void_p(i << 30) for i in (1, 2, 3, 4)]
+    assert lib.kvq_cache_clear(1, 1, 0, 8, 4, 8, *ptrs, None) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_cache_clear(1, 1, 16, 8, 4, 9, *ptrs, None) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_cache_clear(1, 1, 16, 8, 4, 8, None, *ptrs[1:], None) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_cache_clear(1, 1, 16, 8, 4, 8, ptrs[0], ctypes.c_void_p((2 << 30) + 2),
+                               *ptrs[2:], None) == kvq.KVQ_ERR_INVALID

@@ -351,6 +351,67 @@ def main():
         log(f"[bench] streaming-read ceiling for the same bytes: {read_us:.2f} us "
             f"({rbytes / (read_us * 1e-6) / 1e9:.0f} GB/s); attend / ceiling = {kernel_us / read_us:.2f}")
 
+        # Decode loop on a growing cache laid out for all N tokens: a prompt
+        # of N - 80 tokens in one append, then one-token steps (kvq_append +
+        # kvq_attend_cache over the tokens so far), 16 untimed, 64 timed with
+        # events around each call (eager: each step's N differs).  The last step attends all N tokens and
+        # must equal the full-cache call above bit for bit.
+        n_warm, n_timed = 16, 64
+        prompt = w.N - n_warm - n_timed
+        if prompt >= 1:
+            cache = kvq.new_cache(w.B, w.Hkv, w.N, w.D, bits, group, device=dev)
+            kp, vp = kd[:, :, :prompt].contiguous(), vd[:, :, :prompt].contiguous()
+            p0 = torch.cuda.Event(enable_timing=True)
+            p1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            p0.record(stream)
+            kvq.append(kp, vp, 0, cache, w.N, bits, group)
+            p1.record(stream)
+            torch.cuda.synchronize()
+            prompt_us = p0.elapsed_time(p1) * 1e3
+            del kp, vp
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                  for _ in range(n_timed)]
+            k_steps = [kd[:, :, i:i + 1].contiguous() for i in range(prompt, w.N)]
+            v_steps = [vd[:, :, i:i + 1].contiguous() for i in range(prompt, w.N)]
+            dec_out = torch.empty_like(qd)
+            torch.cuda.synchronize()
+            # Queue the loop behind a few ms of unrelated reads so the host
+            # enqueues every step before the GPU reaches them: the events
+            # then time the GPU work, not the pace of the Python calls.
+            blocker = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+            for _ in range(128):
+                kvq.stream_read(blocker, sink)
+            for i, n in enumerate(range(prompt, w.N)):
+                e = ev[i - n_warm] if i >= n_warm else None
+                if e:
+                    e[0].record(stream)
+                kvq.append(k_steps[i], v_steps[i], n, cache, w.N, bits, group)
+                if e:
+                    e[1].record(stream)
+                kvq.attend(qd, *cache[:4], n + 1, bits, group, num_splits=splits, workspace=ws,
+                           out=dec_out, variant=args.variant, capacity=w.N)
+                if e:
+                    e[2].record(stream)
+            torch.cuda.synchronize()
+            full = kvq.attend(qd, kc, ks, vc, vs, w.N, bits, group, num_splits=splits,
+                              workspace=ws, variant=args.variant)
+            torch.cuda.synchronize()
+            app = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e3
+            att = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
+            extra["decode_step"] = {
+                "tokens": f"{w.N - n_timed + 1}..{w.N}",
+                "prompt_append_us": round(prompt_us, 1),
+                "prompt_tokens": prompt,
+                "append_us_median": round(float(np.median(app)), 3),
+                "attend_us_median": round(float(np.median(att)), 3),
+                "last_step_equals_full_cache_attend": bool(torch.equal(dec_out, full)),
+            }
+            log(f"[bench] decode steps: append {np.median(app):.2f} us + attend "
+                f"{np.median(att):.2f} us (medians of {n_timed}); last step == full-cache attend: "
+                f"{extra['decode_step']['last_step_equals_full_cache_attend']}")
+            del cache, blocker
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host ...")

@@ -330,54 +330,91 @@ __global__ __launch_bounds__(256) void cache_clear_kernel(uint8_t* __restrict__ 
   for (long long i = first; i < nvs; i += stride) vs[i] = 1.0f;
 }
 
-// Append tokens [N, N + T) of every head.  Threads [0, BH*D): one K channel
-// (head, d) each, walking the K groups the new tokens touch; the rest: one
-// V group (head, new token, feature group) each.  A K thread owns its
-// channel's tail column, so it reads the open group's earlier tokens before
-// it overwrites slots with the tokens of the new open group.
+// Append tokens [N, N + T) of every head.  Threads [0, BH*ng*D): one K
+// group of one channel each (head, touched group gi < ng, channel d; d
+// fastest), ng = the number of token groups the new tokens touch; the rest:
+// one V group (head, new token, feature group) each.  Only the first
+// touched group reads the tail (its tokens below N).  The tokens of the new
+// open group are written to the tail by the thread of the last group when
+// no other thread of its channel reads the tail in the same launch (it is
+// the first group itself, or the first group starts at N); otherwise
+// append_tail_kernel writes them after this kernel.  Groups of up to
+// kRegGroup elements are loaded into registers in one go (independent
+// loads, one memory round trip); longer groups are walked element by
+// element.
+constexpr int kRegGroup = 32;
+
 template <int BITS>
 __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ k_new,
                                                      const float* __restrict__ v_new,
                                                      long long BH, Layout L, int N, int T,
+                                                     int ng, bool tail_here,
                                                      uint8_t* __restrict__ k_codes,
                                                      float* __restrict__ k_scales,
                                                      uint8_t* __restrict__ v_codes,
                                                      float* __restrict__ v_scales,
                                                      float* __restrict__ k_tail) {
   const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const long long nk = BH * L.D;
+  const long long nk = BH * ng * L.D;
   const int n1 = N + T;
   const int g = L.group;
   constexpr int kStep = BITS == 4 ? 2 : 1;  // tokens (K) or features (V) per byte
+  constexpr unsigned kZero = Codec<BITS>::kQmaxInt;
   if (tid < nk) {
-    const int d = static_cast<int>(tid % L.D);
-    const long long bh = tid / L.D;
-    const float* src = k_new + bh * T * static_cast<long long>(L.D) + d;
-    float* tail = k_tail + bh * g * static_cast<long long>(L.D) + d;
+    const long long D = L.D;
+    const int d = static_cast<int>(tid % D);
+    const long long rest = tid / D;
+    const int gi = static_cast<int>(rest % ng);
+    const long long bh = rest / ng;
+    const int g0 = (N / g + gi) * g;             // first token of this group
+    const float* src = k_new + bh * T * D + d;
+    float* tail = k_tail + bh * g * D + d;
+    const int cnt = min(g0 + g, n1) - g0;        // tokens of the group that hold values
+    const int ncode = min(g0 + g, L.nblocks * kBlockTokens) - g0;  // ... that have codes
+    const bool write_tail = tail_here && n1 % g != 0 && gi == ng - 1;
+    const int t_tail = max(N, g0);               // first token of the new tail (if written)
+    float* scale = k_scales + bh * k_scales_per_head(L) + k_scale_index(L, g0, d);
     uint8_t* codes = k_codes + bh * k_code_bytes_per_head(L);
-    float* scales = k_scales + bh * k_scales_per_head(L);
-    const int tpad = L.nblocks * kBlockTokens;  // tokens that have stored codes
-    auto value = [&](int t) -> float {
-      return t < N ? tail[static_cast<long long>(t % g) * L.D]
-                   : src[static_cast<long long>(t - N) * L.D];
+    // K of token g0 + i (its tail slot is i, g0 being a multiple of g).
+    auto value = [&](int i) -> float {
+      const int t = g0 + i;
+      return t < N ? tail[i * D] : src[(t - N) * D];
     };
-    for (int g0 = N / g * g; g0 < n1; g0 += g) {
-      const int gend = min(g0 + g, n1);
+    if (g <= kRegGroup) {
+      float x[kRegGroup];
+#pragma unroll
+      for (int i = 0; i < kRegGroup; ++i) x[i] = i < cnt ? value(i) : 0.0f;
       float amax = 0.0f;
-      for (int t = g0; t < gend; ++t) amax = fmaxf(amax, fabsf(value(t)));
+#pragma unroll
+      for (int i = 0; i < kRegGroup; ++i) amax = fmaxf(amax, fabsf(x[i]));
       const float s = group_scale<BITS>(amax);
-      scales[k_scale_index(L, g0, d)] = s;
-      auto code = [&](int t) -> unsigned {
-        return t < n1 ? stored_code<BITS>(value(t), s) : Codec<BITS>::kQmaxInt;
-      };
-      const int tend = min(g0 + g, tpad);
-      for (int t = g0; t < tend; t += kStep) {
-        const unsigned byte = BITS == 4 ? (code(t) | (code(t + 1) << 4)) : code(t);
-        codes[k_code_byte(L, t, d)] = static_cast<uint8_t>(byte);
+      *scale = s;
+#pragma unroll
+      for (int i = 0; i < kRegGroup; i += kStep) {
+        if (i < ncode) {
+          unsigned byte = i < cnt ? stored_code<BITS>(x[i], s) : kZero;
+          if (BITS == 4) byte |= (i + 1 < cnt ? stored_code<BITS>(x[i + 1], s) : kZero) << 4;
+          codes[k_code_byte(L, g0 + i, d)] = static_cast<uint8_t>(byte);
+        }
       }
+      if (write_tail) {
+#pragma unroll
+        for (int i = 0; i < kRegGroup; ++i)
+          if (i < cnt && g0 + i >= t_tail) tail[i * D] = x[i];
+      }
+      return;
     }
-    for (int t = max(N, n1 / g * g); t < n1; ++t)
-      tail[static_cast<long long>(t % g) * L.D] = src[static_cast<long long>(t - N) * L.D];
+    float amax = 0.0f;
+    for (int i = 0; i < cnt; ++i) amax = fmaxf(amax, fabsf(value(i)));
+    const float s = group_scale<BITS>(amax);
+    *scale = s;
+    auto code = [&](int i) -> unsigned { return i < cnt ? stored_code<BITS>(value(i), s) : kZero; };
+    for (int i = 0; i < ncode; i += kStep) {
+      const unsigned byte = BITS == 4 ? (code(i) | (code(i + 1) << 4)) : code(i);
+      codes[k_code_byte(L, g0 + i, d)] = static_cast<uint8_t>(byte);
+    }
+    if (write_tail)
+      for (int t = t_tail; t < n1; ++t) tail[(t - g0) * D] = src[(t - N) * D];
     return;
   }
   const long long i = tid - nk;
@@ -388,19 +425,52 @@ __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ k
   const long long bh = rest / T;
   const int t = N + j;
   const float* src = v_new + (bh * T + j) * static_cast<long long>(L.D);
-  const int f0 = G * g, f1 = min(L.D, f0 + g);
-  float amax = 0.0f;
-  for (int f = f0; f < f1; ++f) amax = fmaxf(amax, fabsf(src[f]));
-  const float s = group_scale<BITS>(amax);
-  v_scales[bh * v_scales_per_head(L) + v_scale_index(L, t, f0)] = s;
+  const int f0 = G * g;
+  const int cnt = min(L.D, f0 + g) - f0;  // features of the group inside D
+  v_scales += bh * v_scales_per_head(L) + v_scale_index(L, t, f0);
   uint8_t* codes = v_codes + bh * v_code_bytes_per_head(L);
-  auto code = [&](int f) -> unsigned {
-    return f < L.D ? stored_code<BITS>(src[f], s) : Codec<BITS>::kQmaxInt;
-  };
-  for (int f = f0; f < f0 + g; f += kStep) {
-    const unsigned byte = BITS == 4 ? (code(f) | (code(f + 1) << 4)) : code(f);
-    codes[v_code_byte(L, t, f)] = static_cast<uint8_t>(byte);
+  if (g <= kRegGroup) {
+    float x[kRegGroup];
+#pragma unroll
+    for (int f = 0; f < kRegGroup; ++f) x[f] = f < cnt ? src[f0 + f] : 0.0f;
+    float amax = 0.0f;
+#pragma unroll
+    for (int f = 0; f < kRegGroup; ++f) amax = fmaxf(amax, fabsf(x[f]));
+    const float s = group_scale<BITS>(amax);
+    *v_scales = s;
+#pragma unroll
+    for (int f = 0; f < kRegGroup; f += kStep) {
+      if (f < g) {
+        unsigned byte = f < cnt ? stored_code<BITS>(x[f], s) : kZero;
+        if (BITS == 4) byte |= (f + 1 < cnt ? stored_code<BITS>(x[f + 1], s) : kZero) << 4;
+        codes[v_code_byte(L, t, f0 + f)] = static_cast<uint8_t>(byte);
+      }
+    }
+    return;
   }
+  float amax = 0.0f;
+  for (int f = 0; f < cnt; ++f) amax = fmaxf(amax, fabsf(src[f0 + f]));
+  const float s = group_scale<BITS>(amax);
+  *v_scales = s;
+  auto code = [&](int f) -> unsigned { return f < cnt ? stored_code<BITS>(src[f0 + f], s) : kZero; };
+  for (int f = 0; f < g; f += kStep) {
+    const unsigned byte = BITS == 4 ? (code(f) | (code(f + 1) << 4)) : code(f);
+    codes[v_code_byte(L, t, f0 + f)] = static_cast<uint8_t>(byte);
+  }
+}
+
+// The new open group's tokens [n1 - n1 % g, n1) into the tail, one thread
+// per (head, channel), after append_kernel has read the old tail.
+__global__ __launch_bounds__(256) void append_tail_kernel(const float* __restrict__ k_new,
+                                                          long long BH, int D, int N, int T,
+                                                          int g, float* __restrict__ k_tail) {
+  const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (tid >= BH * D) return;
+  const int d = static_cast<int>(tid % D);
+  const long long bh = tid / D;
+  const int n1 = N + T;
+  for (int t = n1 / g * g; t < n1; ++t)
+    k_tail[(bh * g + t % g) * D + d] = k_new[(bh * T + (t - N)) * D + d];
 }
 
 template <int BITS>
@@ -471,13 +541,22 @@ hipError_t launch_append(const float* k_new, const float* v_new, int B, int H, i
                          uint8_t* v_codes, float* v_scales, float* k_tail, hipStream_t stream) {
   const long long BH = static_cast<long long>(B) * H;
   const Layout L = make_layout(cap, D, bits, group);
-  const unsigned grid = grid_for(BH * D + BH * T * static_cast<long long>(L.vgroups));
+  const int n1 = N + T;
+  const int ng = (n1 + group - 1) / group - N / group;  // token groups the new tokens touch
+  // The tail is rewritten in the same launch unless the first touched group
+  // reads it (N inside a group) while a later group is the new open one.
+  const bool tail_here = ng == 1 || N % group == 0;
+  const unsigned grid =
+      grid_for(BH * ng * static_cast<long long>(D) + BH * T * static_cast<long long>(L.vgroups));
   if (bits == 4)
     hipLaunchKernelGGL(append_kernel<4>, dim3(grid), dim3(256), 0, stream, k_new, v_new, BH, L, N,
-                       T, k_codes, k_scales, v_codes, v_scales, k_tail);
+                       T, ng, tail_here, k_codes, k_scales, v_codes, v_scales, k_tail);
   else
     hipLaunchKernelGGL(append_kernel<8>, dim3(grid), dim3(256), 0, stream, k_new, v_new, BH, L, N,
-                       T, k_codes, k_scales, v_codes, v_scales, k_tail);
+                       T, ng, tail_here, k_codes, k_scales, v_codes, v_scales, k_tail);
+  if (!tail_here && n1 % group != 0)
+    hipLaunchKernelGGL(append_tail_kernel, dim3(grid_for(BH * D)), dim3(256), 0, stream, k_new, BH,
+                       D, N, T, group, k_tail);
   return hipGetLastError();
 }
 

@@ -337,7 +337,22 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-def attend_dense(q, k_hat, v_hat, sm_scale=None, trace=None):
+def causal_mask(n: int, r: int) -> np.ndarray:
+    """Which of ``n`` cached tokens each of ``r`` queries may read when the
+    queries are the sequence's last ``r`` positions (a prefill chunk or a
+    multi-token decode step): query ``i`` sits at position ``n - r + i`` and
+    reads token ``j`` iff ``j <= n - r + i``.  ``[r, n]`` bool.
+
+    [RL] "prefill and decode" (a causal kernel reads only the keys at or
+    before each query) and [TOS] opening section (its queries read every
+    position, which does not stand in for a causal prefill).  Reading: the
+    chunk is aligned to the end of the cache; when ``n < r`` the first
+    ``r - n`` queries read nothing.
+    """
+    return np.arange(n)[None, :] <= (n - r + np.arange(r))[:, None]
+
+
+def attend_dense(q, k_hat, v_hat, sm_scale=None, trace=None, causal=False):
     """Dense ``softmax(Q K^T * sm_scale) V`` in float64.
 
     ``q`` is ``[B, Hq, R, D]``; ``k_hat``/``v_hat`` are ``[B, Hkv, N, D]``
@@ -348,8 +363,12 @@ def attend_dense(q, k_hat, v_hat, sm_scale=None, trace=None):
     to rounding order: [BKD] "Compare equivalent representations first" (the
     dense decode-all path) and [RL] "why FlashAttention need not keep the whole
     heat map" (the row output is sum_j exp(s_j) v_j / sum_j exp(s_j), shifted
-    by the max for stability).  No mask: the queries read every KV position
-    ([TOS] opening section).
+    by the max for stability).  No mask by default: the queries read every
+    KV position ([TOS] opening section).  ``causal``: query ``i`` of the R
+    per head reads only the tokens ``causal_mask`` allows; masked positions
+    enter neither the max nor the sum, and a row with no legal key returns
+    zeros ([RL] "why FlashAttention need not keep the whole heat map": such a
+    row is handled explicitly, never as NaN).
 
     ``trace`` (optional dict) receives the byte sizes of the named work arrays
     ([BKD] "Which arrays shrink?").
@@ -360,8 +379,15 @@ def attend_dense(q, k_hat, v_hat, sm_scale=None, trace=None):
     v64 = np.asarray(v_hat, dtype=np.float64)
     rows = _gqa_rows(np.asarray(q, dtype=np.float64), k64.shape[1])
     scores = np.matmul(rows, np.swapaxes(k64, -1, -2)) * scale
-    weights = np.exp(scores - scores.max(axis=-1, keepdims=True))
-    out = np.matmul(weights, v64) / weights.sum(axis=-1, keepdims=True)
+    if causal:
+        r = q.shape[2]
+        visible = np.tile(causal_mask(k64.shape[2], r), (rows.shape[2] // r, 1))
+        scores = np.where(visible, scores, -np.inf)
+    mx = scores.max(axis=-1, keepdims=True)
+    mx = np.where(np.isfinite(mx), mx, 0.0)          # rows with no legal key
+    weights = np.exp(scores - mx)
+    den = weights.sum(axis=-1, keepdims=True)
+    out = np.matmul(weights, v64) / np.where(den > 0, den, 1.0)
     if trace is not None:
         trace["decoded_kv_bytes"] = int(np.asarray(k_hat).nbytes + np.asarray(v_hat).nbytes)
         trace["score_bytes"] = int(scores.nbytes)
@@ -383,7 +409,9 @@ def merge_blocks(score_blocks, value_blocks, rescale_z=True, rescale_u=True):
         u_new = a*u_old + exp(block scores - m_new) @ block V
         output = u / z
     starting from m = -inf, z = u = 0.  Empty blocks are skipped, so
-    -inf - (-inf) is never formed ([RL] same section).  ``rescale_z`` and
+    -inf - (-inf) is never formed ([RL] same section).  Masked scores are
+    -inf: they add nothing to the max or the sums, and a row that has seen
+    no legal key yet stays at (-inf, 0, 0) and ends as zeros.  ``rescale_z`` and
     ``rescale_u`` exist only for the ablation the pages ask for ([BKD] "Use
     the failure to choose the next question", [TOS] "exercises"): dropping
     either rescale must break the result.
@@ -403,19 +431,20 @@ def merge_blocks(score_blocks, value_blocks, rescale_z=True, rescale_u=True):
             a = np.zeros_like(blk_max)
         else:
             m_new = np.maximum(m, blk_max)
-            a = np.exp(m - m_new)
-        p = np.exp(s_blk - m_new[..., None])
+            a = np.exp(m - np.where(np.isfinite(m_new), m_new, 0.0))
+        ref = np.where(np.isfinite(m_new), m_new, 0.0)   # rows with no legal key yet
+        p = np.exp(s_blk - ref[..., None])
         z = (a * z if rescale_z else z) + p.sum(axis=-1)
         u = (a[..., None] * u if rescale_u else u) + np.matmul(p[..., None, :], v_blk)[..., 0, :]
         m = m_new
         states.append((m.copy(), z.copy(), u.copy()))
     if m is None:
         raise ValueError("no non-empty block: a row with no key is undefined")
-    return u / z[..., None], states
+    return u / np.where(z > 0, z, 1.0)[..., None], states
 
 
 def attend_blocked(q, k_hat, v_hat, block, sm_scale=None, rescale_z=True,
-                   rescale_u=True, trace=None):
+                   rescale_u=True, trace=None, causal=False):
     """Blocked attention: score ``block`` tokens at a time and merge them with
     :func:`merge_blocks`.  Same inputs and output as :func:`attend_dense`.
 
@@ -423,7 +452,7 @@ def attend_blocked(q, k_hat, v_hat, block, sm_scale=None, rescale_z=True,
     and [TOS] "exercises" (a block length such as 7 that does not divide N:
     the last block is shorter).  Decoding is elementwise, so slicing a block
     of an already decoded cache gives the same values as decoding that block
-    from its codes.
+    from its codes.  ``causal``: scores outside ``causal_mask`` are -inf.
     """
     d = q.shape[-1]
     scale = default_scale(d) if sm_scale is None else float(sm_scale)
@@ -431,10 +460,14 @@ def attend_blocked(q, k_hat, v_hat, block, sm_scale=None, rescale_z=True,
     v64 = np.asarray(v_hat, dtype=np.float64)
     rows = _gqa_rows(np.asarray(q, dtype=np.float64), k64.shape[1])
     n = k64.shape[-2]
+    visible = np.tile(causal_mask(n, q.shape[2]), (rows.shape[2] // q.shape[2], 1))
     score_blocks, value_blocks = [], []
     for start in range(0, n, block):
         k_blk = k64[..., start:start + block, :]
-        score_blocks.append(np.matmul(rows, np.swapaxes(k_blk, -1, -2)) * scale)
+        s_blk = np.matmul(rows, np.swapaxes(k_blk, -1, -2)) * scale
+        if causal:
+            s_blk = np.where(visible[:, start:start + block], s_blk, -np.inf)
+        score_blocks.append(s_blk)
         value_blocks.append(v64[..., None, start:start + block, :])
         if trace is not None and start == 0:
             kb = np.asarray(k_hat)[..., start:start + block, :]
@@ -500,7 +533,8 @@ def attend_split(q, k_hat, v_hat, num_splits, sm_scale=None):
     return (big_u / big_z[..., None]).reshape(q.shape)
 
 
-def attend_packed(q, k_codes, k_scales, v_codes, v_scales, n, bits, group, sm_scale=None):
+def attend_packed(q, k_codes, k_scales, v_codes, v_scales, n, bits, group, sm_scale=None,
+                  causal=False):
     """The oracle of the fused path: decode the whole packed cache to float32
     ([KPG] "what a byte holds"), promote to float64 and run dense attention
     ([BKD] "Compare equivalent representations first")."""
@@ -509,7 +543,7 @@ def attend_packed(q, k_codes, k_scales, v_codes, v_scales, n, bits, group, sm_sc
     shape = (b, hkv, n, d)
     k_hat = dequant_k(k_codes, k_scales, shape, bits, group)
     v_hat = dequant_v(v_codes, v_scales, shape, bits, group)
-    return attend_dense(q, k_hat, v_hat, sm_scale)
+    return attend_dense(q, k_hat, v_hat, sm_scale, causal=causal)
 
 
 # ---------------------------------------------------------------------------

@@ -81,6 +81,12 @@ typedef enum kvq_variant {
                             fp16 matrix cores on exact codes */
 } kvq_variant;
 
+/* Flags of kvq_attend_cache. */
+typedef enum kvq_attend_flags {
+  KVQ_ATTEND_CAUSAL = 1  /* the R queries of each head are the sequence's last R positions:
+                            query r (position N-R+r) reads tokens j <= N-R+r */
+} kvq_attend_flags;
+
 /* ---- host-only sizing (no device work, never fails) ------------------------
  * Byte / element counts of the packed arrays; 0 if an argument is invalid
  * (size < 1, bits not 4 or 8, group odd or < 2). */
@@ -156,7 +162,14 @@ kvq_status kvq_dequant_v(const uint8_t* codes, const float* scales, int B, int H
  *   laid out for `capacity` >= N tokens whose positions past N are in the
  *   empty state above (as kvq_cache_clear + kvq_append leave them).  The
  *   matrix-core limits of kvq_attend_variant apply with capacity in place
- *   of N; capacity == N is exactly kvq_attend_variant. */
+ *   of N; capacity == N and flags == 0 is exactly kvq_attend_variant.
+ *   flags: 0 or KVQ_ATTEND_CAUSAL, a causal chunk (a prefill chunk or a
+ *   multi-token decode step whose R queries were just appended): query r of
+ *   each head reads only tokens j <= N-R+r; masked tokens enter neither the
+ *   running max nor the sums, and a query with no legal key (N-R+r < 0)
+ *   gets zeros ([RL] "why FlashAttention need not keep the whole heat
+ *   map").  With R == 1 the flag changes nothing.  With R > 1 it runs on the
+ *   general kernel (KVQ_VARIANT_MFMA returns KVQ_ERR_UNSUPPORTED). */
 kvq_status kvq_cache_clear(int B, int H, int capacity, int D, int bits, int group,
                            uint8_t* k_codes, float* k_scales, uint8_t* v_codes, float* v_scales,
                            void* stream);
@@ -167,7 +180,8 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
                             const uint8_t* v_codes, const float* v_scales, int B, int Hq, int Hkv,
                             int R, int N, int capacity, int D, int bits, int group,
                             float sm_scale, int num_splits, void* workspace,
-                            size_t workspace_bytes, float* out, int variant, void* stream);
+                            size_t workspace_bytes, float* out, int variant, int flags,
+                            void* stream);
 
 /* ---- kvq_attend ---------------------------------------------------------------
  * out[b][hq][r][:] = softmax_j(sm_scale * q[b][hq][r] . k_j) v_j over all N

@@ -52,7 +52,7 @@ _SIGNATURES = {
     "kvq_cache_clear": (_c_int, [_c_int] * 6 + [_c_vp] * 5),
     "kvq_append": (_c_int, [_c_vp] * 2 + [_c_int] * 8 + [_c_vp] * 6),
     "kvq_attend_cache": (_c_int, [_c_vp] * 5 + [_c_int] * 9 + [_c_float, _c_int, _c_vp, _c_size,
-                                                               _c_vp, _c_int, _c_vp]),
+                                                               _c_vp, _c_int, _c_int, _c_vp]),
     "kvq_attend_f32": (_c_int, [_c_vp] * 3 + [_c_int] * 6 + [_c_float, _c_int, _c_vp, _c_size,
                                                              _c_vp, _c_vp]),
     "kvq_stream_read": (_c_int, [_c_vp, _c_size, _c_vp, _c_vp]),
@@ -67,6 +67,7 @@ for _name, (_res, _args) in _SIGNATURES.items():
 
 KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP, KVQ_ERR_WORKSPACE = 0, -1, -2, -3, -4
 VARIANTS = {"auto": 0, "valu": 1, "mfma": 2}
+KVQ_ATTEND_CAUSAL = 1
 
 
 class KvqError(RuntimeError):
@@ -197,10 +198,11 @@ def _check_cache(arrays, B, H, cap, D, bits, group):
 
 
 def attend(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scale=0.0,
-           num_splits=0, workspace=None, out=None, variant="auto", capacity=None):
+           num_splits=0, workspace=None, out=None, variant="auto", capacity=None, causal=False):
     """Fused attention of q [B,Hq,R,D] over the first N tokens of the packed
     cache (KV heads = k_codes.shape[1]); `capacity`: the tokens the cache
-    layout is sized for (default N; a cache grown by append())."""
+    layout is sized for (default N; a cache grown by append()); `causal`: the
+    R queries are the last R positions and read only tokens up to their own."""
     torch = _torch()
     _need(q, torch.float32, "q")
     for t, n, dt in ((k_codes, "k_codes", torch.uint8), (k_scales, "k_scales", torch.float32),
@@ -215,7 +217,7 @@ def attend(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scal
         workspace = new_workspace(B, Hq, Hkv, R, N, D, num_splits, device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    if capacity is None:
+    if capacity is None and not causal:
         _check(lib.kvq_attend_variant(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                       _ptr(v_scales), B, Hq, Hkv, R, N, D, bits, group,
                                       float(sm_scale), num_splits, _ptr(workspace),
@@ -223,10 +225,11 @@ def attend(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scal
                                       _stream(q.device)), "kvq_attend")
     else:
         _check(lib.kvq_attend_cache(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
-                                    _ptr(v_scales), B, Hq, Hkv, R, N, capacity, D, bits, group,
+                                    _ptr(v_scales), B, Hq, Hkv, R, N, cap, D, bits, group,
                                     float(sm_scale), num_splits, _ptr(workspace),
                                     workspace.numel(), _ptr(out), VARIANTS[variant],
-                                    _stream(q.device)), "kvq_attend_cache")
+                                    KVQ_ATTEND_CAUSAL if causal else 0, _stream(q.device)),
+               "kvq_attend_cache")
     return out
 
 

@@ -156,6 +156,7 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   p->R = R;
   p->N = N;
   p->cap = cap;
+  p->causal = 0;
   p->D = D;
   p->rows = rows;
   p->bits = bits;
@@ -362,20 +363,28 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
                             const uint8_t* v_codes, const float* v_scales, int B, int Hq, int Hkv,
                             int R, int N, int capacity, int D, int bits, int group,
                             float sm_scale, int num_splits, void* workspace,
-                            size_t workspace_bytes, float* out, int variant, void* stream) {
+                            size_t workspace_bytes, float* out, int variant, int flags,
+                            void* stream) {
   AttendProblem p;
   kvq_status st = check_attend(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N, capacity,
                                D, bits, group, sm_scale, num_splits, workspace, workspace_bytes,
                                out, &p);
   if (st != KVQ_OK) return st;
+  if (flags & ~KVQ_ATTEND_CAUSAL) return fail(KVQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  // One query per head reads every token under the causal rule too.
+  p.causal = (flags & KVQ_ATTEND_CAUSAL) && R > 1;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
     case KVQ_VARIANT_AUTO:
-      if (mfma_eligible(p)) return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
+      if (!p.causal && mfma_eligible(p))
+        return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
       return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
     case KVQ_VARIANT_VALU:
       return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
     case KVQ_VARIANT_MFMA:
+      if (p.causal)
+        return fail(KVQ_ERR_UNSUPPORTED,
+                    "causal chunks of R > 1 queries run on the general kernel (variant VALU)");
       if (!mfma_eligible(p))
         return fail(KVQ_ERR_UNSUPPORTED,
                     "matrix-core kernels need bits=4, group=32, D=128, <= %d query rows per "
@@ -393,7 +402,7 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
                               int num_splits, void* workspace, size_t workspace_bytes,
                               float* out, int variant, void* stream) {
   return kvq_attend_cache(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N, N, D, bits,
-                          group, sm_scale, num_splits, workspace, workspace_bytes, out, variant,
+                          group, sm_scale, num_splits, workspace, workspace_bytes, out, variant, 0,
                           stream);
 }
 
@@ -442,6 +451,6 @@ const char* kvq_status_string(int status) {
 
 const char* kvq_last_error(void) { return g_last_error; }
 
-int kvq_abi_version(void) { return 4; }
+int kvq_abi_version(void) { return 5; }
 
 }  // extern "C"

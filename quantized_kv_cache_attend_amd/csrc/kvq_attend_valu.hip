@@ -96,11 +96,13 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
     }
     __syncthreads();
 
-    // Scores of every (row, token); tokens past N are masked out (-inf).
+    // Scores of every (row, token); tokens past N are masked out (-inf), and
+    // in a causal chunk so are the tokens after the row's query position
+    // (row r is query r % R of its head, at position N - R + r % R).
     for (int i = tid; i < rows * kTile; i += kThreads) {
       const int r = i / kTile, j = i % kTile;
       float s = -INFINITY;
-      if (j < tn) {
+      if (j < tn && (!p.causal || t0 + j <= p.N - p.R + r % p.R)) {
         s = 0.0f;
 #pragma unroll 8
         for (int d = 0; d < D; ++d) s = fmaf(sQ[r][d], sK[j][d], s);
@@ -119,11 +121,14 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
 #pragma unroll
       for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
       const float m_old = live ? sM[r] : 0.0f;
-      // The tile holds at least one real token, so m_new is finite and
-      // neither exponent below can be (-inf) - (-inf).
+      // Without a causal mask the tile holds a real token for every row, so
+      // m_new is finite.  A causal row that has seen no legal key yet keeps
+      // m = -inf (and z = u = 0): its exponents are taken against 0 so that
+      // (-inf) - (-inf) is never formed.
       const float m_new = fmaxf(m_old, mx);
-      const float pj = exp2f(s - m_new);
-      const float alpha = exp2f(m_old - m_new);
+      const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+      const float pj = exp2f(s - m_ref);
+      const float alpha = exp2f(m_old - m_ref);
       float sum = pj;
 #pragma unroll
       for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
@@ -161,7 +166,8 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
       const int idx = tid + i * kThreads;
       if (idx < rows * D) {
         const int r = idx / D;
-        p.out[(row0 + r) * D + idx % D] = acc[i] / sZ[r];
+        // z = 0 only for a causal row with no legal key: its output is 0.
+        p.out[(row0 + r) * D + idx % D] = sZ[r] > 0.0f ? acc[i] / sZ[r] : 0.0f;
       }
     }
   } else {
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttendProblem p) {
     z = fmaf(w, p.part_z[s * total_rows + row], z);
     u = fmaf(w, p.part_u[s * total_rows * p.D + tid], u);
   }
-  p.out[tid] = u / z;
+  p.out[tid] = z > 0.0f ? u / z : 0.0f;  // no split saw a legal key: 0
 }
 
 template <int D>

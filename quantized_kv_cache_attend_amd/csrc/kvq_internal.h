@@ -27,6 +27,7 @@ struct AttendProblem {
   float* out;              // [B][Hq][R][D]
   int B, Hq, Hkv, R, N, D;
   int cap;                 // tokens the packed layout is sized for (>= N; N for float32)
+  int causal;              // 1: row r is query r % R at position N - R + r % R (R > 1)
   int rows;                // (Hq / Hkv) * R: query rows sharing one KV head
   int bits, group;         // 4/8 and group; bits == 32 marks the float32 cache
   float qscale;            // sm_scale * log2(e)

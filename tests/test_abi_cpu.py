@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert lib.kvq_abi_version() == 4
+    assert lib.kvq_abi_version() == 5
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.kvq_status_string(st)
 
@@ -134,11 +134,11 @@ def test_stream_read_rejects_bad_arguments():
 
 
 def _attend_cache(N, capacity, **kw):
-    a = dict(q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, D=32, variant=0, out=FAKE2)
+    a = dict(q=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, D=32, variant=0, out=FAKE2, flags=0, R=1)
     a.update(kw)
-    return lib.kvq_attend_cache(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], 1, 4, 2, 1, N,
+    return lib.kvq_attend_cache(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], 1, 4, 2, a["R"], N,
                                 capacity, a["D"], 4, 32, 0.0, 1, None, 0, a["out"], a["variant"],
-                                None)
+                                a["flags"], None)
 
 
 def test_attend_cache_rejects_before_launch():
@@ -147,6 +147,10 @@ def test_attend_cache_rejects_before_launch():
     assert _attend_cache(0, 64) == kvq.KVQ_ERR_INVALID
     # matrix-core limits apply to the capacity (the per-head buffer extent)
     assert _attend_cache(64, (1 << 25) - 31, D=128, variant=2,
+                         out=ctypes.c_void_p(1 << 44)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _attend_cache(64, 64, flags=2) == kvq.KVQ_ERR_INVALID      # unknown flag
+    # causal chunks of several queries run on the general kernel only
+    assert _attend_cache(64, 64, D=128, R=2, variant=2, flags=1,
                          out=ctypes.c_void_p(1 << 44)) == kvq.KVQ_ERR_UNSUPPORTED
     assert lib.kvq_last_error()
 

@@ -376,15 +376,11 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
   const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
     case KVQ_VARIANT_AUTO:
-      if (!p.causal && mfma_eligible(p))
-        return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
+      if (mfma_eligible(p)) return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
       return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
     case KVQ_VARIANT_VALU:
       return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
     case KVQ_VARIANT_MFMA:
-      if (p.causal)
-        return fail(KVQ_ERR_UNSUPPORTED,
-                    "causal chunks of R > 1 queries run on the general kernel (variant VALU)");
       if (!mfma_eligible(p))
         return fail(KVQ_ERR_UNSUPPORTED,
                     "matrix-core kernels need bits=4, group=32, D=128, <= %d query rows per "

@@ -168,11 +168,15 @@ struct WaveState {
 // out) held in br, then reload br's parts with block `next` (if has_next;
 // otherwise the loads return zeros without touching memory).
 // qv: this lane's prescaled q values (precompute slot, channel order);
-// us_row: 2^-Sq of score row n & 3.
+// us_row: 2^-Sq of score row n & 3.  kCausal: also mask the tokens after
+// lim, the position of score row n & 3's query; a row that has seen no
+// legal key keeps m = -inf and its exponents are taken against 0, so
+// (-inf) - (-inf) is never formed.
+template <bool kCausal>
 __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, int t_end,
                                              const CodeConsts& cc, WaveState& ws, const Head& h,
                                              int next, bool has_next, const Lanes& lo_,
-                                             const float (&qv)[8], float us_row) {
+                                             const float (&qv)[8], float us_row, int lim) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
@@ -236,10 +240,10 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
     raw[2 * i] = se[i] + dpp<kRowRor8>(se[i]);
     raw[2 * i + 1] = so[i] + dpp<kRowRor8>(so[i]);
   }
-  if (tok0 + kBlockTokens > t_end) {  // the block holding token t_end - 1 (wave-uniform)
+  if (kCausal || tok0 + kBlockTokens > t_end) {  // the block holding token t_end - 1 (wave-uniform)
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      if (tok0 + 8 * q + t >= t_end) raw[t] = -INFINITY;
+      if (tok0 + 8 * q + t >= t_end || (kCausal && tok0 + 8 * q + t > lim)) raw[t] = -INFINITY;
   }
   // this lane's max over its 8 tokens, base-2 units (us > 0 commutes with max)
   const float lmx =
@@ -260,13 +264,14 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
   const bool move_sv = !empty && (!ws.live || __builtin_amdgcn_ballot_w64(!(lvs < ws.vhi)) != 0 ||
                                   __builtin_amdgcn_ballot_w64(lvs >= ws.vlo) == 0);
   if (move_m || move_sv) {
-    const float mx = qblock_max(lmx);  // row max over the block; finite
+    const float mx = qblock_max(lmx);  // row max over the block (finite unless kCausal)
     float vmx = fmaxf(lvs, dpp<kRowRor4>(lvs));
     vmx = qblock_max(fmaxf(vmx, dpp<kRowRor8>(vmx)));  // block max over the wave
     const float m_new = ws.live ? (mx > ws.m + kLazy ? mx : ws.m) : mx;
     const int sv_new = move_sv ? prescale_exp(vmx, kSvTop) : ws.sv;
     if (ws.live) {
-      const float alpha = fast_exp2(ws.m - m_new);
+      // a row still without a legal key (kCausal) has z = u = 0: factor 0
+      const float alpha = kCausal && m_new == -INFINITY ? 0.0f : fast_exp2(ws.m - m_new);
       ws.z *= alpha;
       const float t = __builtin_ldexpf(1.0f, sv_new - ws.sv);
       const float a0 = as_f32(__builtin_amdgcn_readlane(static_cast<int>(as_u32(alpha)), 0));
@@ -288,7 +293,7 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
   }
 
   // pt = 2^(s - m + Sv) (the V prescale rides in the exponent), z += sum p
-  const float shift = static_cast<float>(ws.sv) - ws.m;
+  const float shift = static_cast<float>(ws.sv) - (kCausal && ws.m == -INFINITY ? 0.0f : ws.m);
   float pt[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) pt[t] = fast_exp2(fmaf(raw[t], us, shift));
@@ -323,6 +328,8 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
   }
 }
 
+// kCausal: a causal chunk (row r is query r % R at position N - R + r % R).
+template <bool kCausal>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 attend_mfma_r4_kernel(AttendProblem p) {
   __shared__ Smem sm;
@@ -415,6 +422,9 @@ attend_mfma_r4_kernel(AttendProblem p) {
     for (int g = 0; g < 4; ++g) ws.acc[g][0] = ws.acc[g][1] = zero4;
   }
 
+  // Causal limit of this lane's score row n & 3.
+  const int lim = p.N - p.R + (n & 3) % p.R;
+
   // The ring: block i sits in register set i % kDepth; once attended, the set
   // is refilled with block i + kDepth.  Every step of a round runs (a step
   // past the wave's last block attends an all-masked block of zeros), so the
@@ -424,8 +434,8 @@ attend_mfma_r4_kernel(AttendProblem p) {
     for (int j = 0; j < kDepth; ++j) {
       const int i = i0 + j;
       const int blk = b_first + i * kWaves;
-      attend_block(sm, br[j], i < cnt ? blk * kBlockTokens : t_end, t_end, cc, ws, h,
-                   blk + kDepth * kWaves, i + kDepth < cnt, lo, qv, us_row);
+      attend_block<kCausal>(sm, br[j], i < cnt ? blk * kBlockTokens : t_end, t_end, cc, ws, h,
+                            blk + kDepth * kWaves, i + kDepth < cnt, lo, qv, us_row, lim);
     }
   }
   // z of each row: sum this lane's share over the four q-blocks
@@ -476,7 +486,8 @@ attend_mfma_r4_kernel(AttendProblem p) {
   if (p.splits == 1) {
     if (r < rows) {
 #pragma unroll
-      for (int j = 0; j < kSlots; ++j) p.out[(row0 + r) * kD + f0 + j] = U[j] / Z;
+      for (int j = 0; j < kSlots; ++j)  // Z = 0: a causal row with no legal key
+        p.out[(row0 + r) * kD + f0 + j] = Z > 0.0f ? U[j] / Z : 0.0f;
     }
     return;
   }
@@ -492,7 +503,10 @@ int mfma_tokens_per_split(int N, int splits) {
 
 hipError_t launch_attend_mfma(const AttendProblem& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
-  hipLaunchKernelGGL(attend_mfma_r4_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+  if (p.causal)
+    hipLaunchKernelGGL(attend_mfma_r4_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attend_mfma_r4_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

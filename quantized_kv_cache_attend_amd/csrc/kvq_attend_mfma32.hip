@@ -148,11 +148,16 @@ __device__ __forceinline__ half2_t pk16(float x, float y) {
   return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(x, y));
 }
 
-template <bool kMasked>
+// kMasked: mask tokens >= t_end; kCausal (implies kMasked): also mask, for
+// score row 16t + n, the tokens after its query's position lim[t], and keep
+// rows that have seen no legal key at m = -inf (exponents then taken
+// against 0, so (-inf) - (-inf) is never formed).
+template <bool kMasked, bool kCausal>
 __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0, int t_end,
                                                const CodeConsts& cc, State32& st,
                                                const Head32& h, int next, const Lanes32& lo,
-                                               const float us_row[2], const float (&qk)[2][4][8]) {
+                                               const float us_row[2], const float (&qk)[2][4][8],
+                                               const int (&lim)[2]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
@@ -257,7 +262,8 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
     if (kMasked) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (tok0 + 8 * q + j >= t_end) raw[t][j] = -INFINITY;
+        if (tok0 + 8 * q + j >= t_end || (kCausal && tok0 + 8 * q + j > lim[t]))
+          raw[t][j] = -INFINITY;
     }
   }
   const float us[2] = {us0, us1};
@@ -274,9 +280,10 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
     float alpha[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float mx = qblock_max(lmx[t]);  // row max over the block; finite
+      const float mx = qblock_max(lmx[t]);  // row max over the block (finite unless kCausal)
       const float m_new = st.live ? (mx > st.m[t] + kLazy ? mx : st.m[t]) : mx;
       alpha[t] = st.live ? fast_exp2(st.m[t] - m_new) : 0.0f;
+      if (kCausal && m_new == -INFINITY) alpha[t] = 0.0f;  // still no legal key: z = u = 0
       st.z[t] *= alpha[t];
       st.m[t] = m_new;
     }
@@ -305,7 +312,7 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
   half2_t p16[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const float shift = -st.m[t];
+    const float shift = kCausal && st.m[t] == -INFINITY ? 0.0f : -st.m[t];
     float pt[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) pt[j] = fast_exp2(fmaf(raw[t][j], us[t], shift));
@@ -343,6 +350,9 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
   }
 }
 
+// kCausal: a causal chunk (row r is query r % R at position N - R + r % R);
+// every block runs the masked path.
+template <bool kCausal>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attend_mfma_r32_kernel(AttendProblem p) {
   __shared__ Smem32 sm;
@@ -461,12 +471,15 @@ attend_mfma_r32_kernel(AttendProblem p) {
       for (int t = 0; t < 2; ++t) st.acc[g][t][0] = st.acc[g][t][1] = zero4;
   }
 
+  // Causal limit of this lane's score rows 16t + n.
+  const int lim[2] = {p.N - p.R + n % p.R, p.N - p.R + (16 + n) % p.R};
   if (active) {
-    attend_block32<true>(sm, br, first * kBlockTokens, t_end, cc, st, h,
-                         loop_begin <= loop_end ? loop_begin : first, lo, us_row, qk);
+    attend_block32<true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
+                                  loop_begin <= loop_end ? loop_begin : first, lo, us_row, qk,
+                                  lim);
     for (int b = loop_begin; b <= loop_end; b += kW)
-      attend_block32<false>(sm, br, b * kBlockTokens, t_end, cc, st, h, min(b + kW, loop_end),
-                            lo, us_row, qk);
+      attend_block32<kCausal, kCausal>(sm, br, b * kBlockTokens, t_end, cc, st, h,
+                                       min(b + kW, loop_end), lo, us_row, qk, lim);
   }
   st.z[0] = qblock_sum(st.z[0]);
   st.z[1] = qblock_sum(st.z[1]);
@@ -532,7 +545,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
       for (int i = 0; i < 4; ++i) {
         f32x4 o;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = U[4 * i + j] / Z;
+        for (int j = 0; j < 4; ++j) o[j] = Z > 0.0f ? U[4 * i + j] / Z : 0.0f;  // Z = 0: no key
         *reinterpret_cast<f32x4*>(&p.out[(row0 + r) * kD + f0 + 32 * i]) = o;
       }
     }
@@ -546,7 +559,10 @@ attend_mfma_r32_kernel(AttendProblem p) {
 
 hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
-  hipLaunchKernelGGL(attend_mfma_r32_kernel, dim3(grid), dim3(kT), 0, stream, p);
+  if (p.causal)
+    hipLaunchKernelGGL(attend_mfma_r32_kernel<true>, dim3(grid), dim3(kT), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attend_mfma_r32_kernel<false>, dim3(grid), dim3(kT), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -296,7 +296,8 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
       Mg = mb;
     }
 #pragma unroll
-    for (int i = 0; i < kF; ++i) p.out[row * p.D + slot_feature<kRun, kStride>(f0, i)] = V[i] / Zg;
+    for (int i = 0; i < kF; ++i)  // Zg = 0 only for a causal row with no legal key: 0
+      p.out[row * p.D + slot_feature<kRun, kStride>(f0, i)] = Zg > 0.0f ? V[i] / Zg : 0.0f;
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

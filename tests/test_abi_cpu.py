@@ -149,9 +149,7 @@ def test_attend_cache_rejects_before_launch():
     assert _attend_cache(64, (1 << 25) - 31, D=128, variant=2,
                          out=ctypes.c_void_p(1 << 44)) == kvq.KVQ_ERR_UNSUPPORTED
     assert _attend_cache(64, 64, flags=2) == kvq.KVQ_ERR_INVALID      # unknown flag
-    # causal chunks of several queries run on the general kernel only
-    assert _attend_cache(64, 64, D=128, R=2, variant=2, flags=1,
-                         out=ctypes.c_void_p(1 << 44)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _attend_cache(64, 64, flags=-1) == kvq.KVQ_ERR_INVALID
     assert lib.kvq_last_error()
 
 

@@ -18,15 +18,23 @@ kvq = pytest.importorskip("quantized_kv_cache_attend_amd")
 TOL = 1e-4
 
 
-@pytest.mark.parametrize("variant", ["valu", "auto"])
+MFMA_OK = {(4, 32, 128)}   # (bits, group, D) the matrix-core kernels take (<= 32 rows)
+
+
+@pytest.mark.parametrize("variant", ["valu", "mfma", "auto"])
 @pytest.mark.parametrize("B,hq,hkv,r,n,d,bits,group", [
-    (2, 8, 2, 4, 100, 128, 4, 32),
+    (2, 8, 2, 4, 100, 128, 4, 32),      # 16 rows per KV head: 32-row kernel
     (1, 4, 1, 8, 5, 64, 8, 8),          # N < R: queries 0..2 have no legal key
     (2, 4, 4, 3, 1021, 32, 4, 8),
     (1, 2, 1, 16, 40, 128, 4, 32),      # 32 rows per KV head
-    (1, 8, 8, 2, 4097, 128, 4, 32),
+    (1, 8, 8, 2, 4097, 128, 4, 32),     # 2 rows: 4-row kernel
+    (1, 2, 2, 4, 3, 128, 4, 32),        # 4-row kernel, N < R
+    (2, 4, 1, 8, 70, 128, 4, 32),       # 32 rows, the mask spans two 32-token blocks
+    (1, 4, 2, 2, 33, 128, 4, 32),       # 4 rows, tokens 32.. in a second block
 ])
 def test_causal_chunk(B, hq, hkv, r, n, d, bits, group, variant):
+    if variant == "mfma" and (bits, group, d) not in MFMA_OK:
+        pytest.skip("outside the matrix-core kernels' format")
     w = Workload("causal", B, hq, hkv, r, n, d, ((bits, group),))
     q, k, v = make_qkv(w, 5)
     announce(f"causal B={B} hq={hq} hkv={hkv} R={r} N={n} D={d} {bits}b g{group} {variant}")
@@ -42,6 +50,21 @@ def test_causal_chunk(B, hq, hkv, r, n, d, bits, group, variant):
         assert np.isfinite(got).all(), splits
         assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
         assert (got[:, :, empty] == 0).all()
+
+
+@pytest.mark.parametrize("hq,hkv,r", [(8, 2, 2), (8, 1, 4)])
+def test_causal_matrix_core_equals_general_kernel(hq, hkv, r):
+    """Both kernel families on one causal problem agree within the split
+    tolerance (a different summation order only)."""
+    w = Workload("causal_x", 2, hq, hkv, r, 1500, 128, ((4, 32),))
+    q, k, v = make_qkv(w, 8)
+    announce(f"causal mfma vs valu hq={hq} hkv={hkv} R={r}")
+    gk, gks = kvq.pack_k(dev(k), 4, 32)
+    gv, gvs = kvq.pack_v(dev(v), 4, 32)
+    qd = dev(q)
+    a = host(kvq.attend(qd, gk, gks, gv, gvs, w.N, 4, 32, variant="mfma", causal=True))
+    b = host(kvq.attend(qd, gk, gks, gv, gvs, w.N, 4, 32, variant="valu", causal=True))
+    assert max_abs(a, b) <= 2e-5
 
 
 def test_single_query_causal_is_the_unmasked_call():

@@ -22,6 +22,7 @@ Prints ONE JSON line on stdout; diagnostics go to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -411,6 +412,40 @@ def main():
                 f"{np.median(att):.2f} us (medians of {n_timed}); last step == full-cache attend: "
                 f"{extra['decode_step']['last_step_equals_full_cache_attend']}")
             del cache, blocker
+
+        # A causal multi-token step on the same cache: R_c = 4 new queries per
+        # head (the last 4 positions; GQA makes 4 * Hq/Hkv rows per KV head),
+        # against the same queries without the mask.  Events around 200
+        # calls rotating over the cache copies, enqueued behind a blocker.
+        r_c = 4
+        qc = torch.from_numpy(make_qkv(dataclasses.replace(w, R=r_c), 1, n=1)[0]).to(dev)
+        out_c = torch.empty_like(qc)
+        ws_c = kvq.new_workspace(w.B, w.Hq, w.Hkv, r_c, w.N, w.D, 0, device=dev)
+        timings = {}
+        for causal in (True, False):
+            kvq.attend(qc, *caches[0], w.N, bits, group, workspace=ws_c, out=out_c,
+                       causal=causal)
+            torch.cuda.synchronize()
+            blocker = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+            for _ in range(64):
+                kvq.stream_read(blocker, sink)
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            for i in range(200):
+                kvq.attend(qc, *caches[i % copies], w.N, bits, group, workspace=ws_c, out=out_c,
+                           causal=causal)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            timings[causal] = c0.elapsed_time(c1) * 1e3 / 200
+            del blocker
+        extra["causal_step"] = {
+            "queries_per_head": r_c, "rows_per_kv_head": r_c * w.Hq // w.Hkv,
+            "causal_us": round(timings[True], 3), "unmasked_us": round(timings[False], 3),
+            "causal_kv_gbs": round(nbytes / (timings[True] * 1e-6) / 1e9, 1),
+        }
+        log(f"[bench] causal step of {r_c} queries per head: {timings[True]:.2f} us "
+            f"(unmasked {timings[False]:.2f} us)")
 
     cpu = None
     if not args.no_cpu_baseline:

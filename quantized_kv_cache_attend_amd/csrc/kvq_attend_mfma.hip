@@ -176,7 +176,8 @@ template <bool kCausal>
 __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, int t_end,
                                              const CodeConsts& cc, WaveState& ws, const Head& h,
                                              int next, bool has_next, const Lanes& lo_,
-                                             const float (&qv)[8], float us_row, int lim) {
+                                             const float (&qv)[8], float us_row, int lim,
+                                             int lim_lo) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
@@ -240,7 +241,9 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
     raw[2 * i] = se[i] + dpp<kRowRor8>(se[i]);
     raw[2 * i + 1] = so[i] + dpp<kRowRor8>(so[i]);
   }
-  if (kCausal || tok0 + kBlockTokens > t_end) {  // the block holding token t_end - 1 (wave-uniform)
+  // The block holding token t_end - 1, or (kCausal) one holding a token past
+  // N - R that some query may not read; wave-uniform.
+  if (tok0 + kBlockTokens > t_end || (kCausal && tok0 + kBlockTokens - 1 > lim_lo)) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       if (tok0 + 8 * q + t >= t_end || (kCausal && tok0 + 8 * q + t > lim)) raw[t] = -INFINITY;
@@ -435,7 +438,8 @@ attend_mfma_r4_kernel(AttendProblem p) {
       const int i = i0 + j;
       const int blk = b_first + i * kWaves;
       attend_block<kCausal>(sm, br[j], i < cnt ? blk * kBlockTokens : t_end, t_end, cc, ws, h,
-                            blk + kDepth * kWaves, i + kDepth < cnt, lo, qv, us_row, lim);
+                            blk + kDepth * kWaves, i + kDepth < cnt, lo, qv, us_row, lim,
+                            p.N - p.R);
     }
   }
   // z of each row: sum this lane's share over the four q-blocks

@@ -351,7 +351,8 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
 }
 
 // kCausal: a causal chunk (row r is query r % R at position N - R + r % R);
-// every block runs the masked path.
+// every block runs the masked path (a second, unmasked copy of the block
+// code in the loop spills registers).
 template <bool kCausal>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attend_mfma_r32_kernel(AttendProblem p) {

@@ -546,6 +546,33 @@ def attend_packed(q, k_codes, k_scales, v_codes, v_scales, n, bits, group, sm_sc
     return attend_dense(q, k_hat, v_hat, sm_scale, causal=causal)
 
 
+def attend_window(q, k, v, window, bits, group, sm_scale=None, causal=False):
+    """Attention over a mixed cache: the oldest ``N - window`` tokens packed,
+    the most recent ``window`` tokens kept in float32.
+
+    [KPG] "exercises and common mistakes" announces the study of leaving
+    limited high-precision room to the most recent tokens, keeping the same
+    packed format, and "accuracy and space on the same input" builds the
+    early / late biased inputs for it.  Reading: the packed part is the
+    packed tensor of the first ``N - window`` tokens on their own (its last
+    short group zero-padded, as for any length), the window tokens enter
+    attention unquantized, and attention runs over all N tokens in float64
+    ([BKD] "Compare equivalent representations first").
+    Parity: pinned in tests/test_oracle_window.py (window 0 is the packed
+    path, window N the float32 path, and the decoded cache is the packed
+    prefix followed by the raw window).
+    """
+    n, d = k.shape[-2], k.shape[-1]
+    npk = n - window
+    k_hat = np.array(k, dtype=np.float32)
+    v_hat = np.array(v, dtype=np.float32)
+    if npk > 0:
+        shape = k.shape[:-2] + (npk, d)
+        k_hat[..., :npk, :] = dequant_k(*pack_k(k[..., :npk, :], bits, group), shape, bits, group)
+        v_hat[..., :npk, :] = dequant_v(*pack_v(v[..., :npk, :], bits, group), shape, bits, group)
+    return attend_dense(q, k_hat, v_hat, sm_scale, causal=causal)
+
+
 # ---------------------------------------------------------------------------
 # Byte ledgers and error measures
 # ---------------------------------------------------------------------------

@@ -220,6 +220,24 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
                               float sm_scale, int num_splits, void* workspace,
                               size_t workspace_bytes, float* out, int variant, void* stream);
 
+/* ---- kvq_attend_window ------------------------------------------------------------
+ * Attention over a mixed cache: N >= 0 packed tokens (the first N tokens of
+ * a cache laid out for `capacity` >= max(N, 1) tokens, as kvq_attend_cache
+ * reads them) followed by the W >= 1 most recent tokens kept in float32,
+ * k_win, v_win [B][Hkv][W][D] ([KPG] "exercises and common mistakes": high
+ * precision reserved for the most recent tokens, the packed format
+ * unchanged).  The N + W tokens are attended as one sequence: q, out,
+ * sm_scale, splits, workspace (sized for N + W tokens) and flags
+ * (KVQ_ATTEND_CAUSAL: positions counted over N + W) as in kvq_attend_cache.
+ * Runs on the general kernel; a decode loop moves the window's oldest
+ * tokens into the packed cache with kvq_append. */
+kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float* k_scales,
+                             const uint8_t* v_codes, const float* v_scales, const float* k_win,
+                             const float* v_win, int B, int Hq, int Hkv, int R, int N, int W,
+                             int capacity, int D, int bits, int group, float sm_scale,
+                             int num_splits, void* workspace, size_t workspace_bytes, float* out,
+                             int flags, void* stream);
+
 /* ---- kvq_attend_f32 -------------------------------------------------------------
  * The same attention over an unquantized float32 cache k, v [B][Hkv][N][D]:
  * the float32-cache reference of [BKD] "Compare equivalent representations

@@ -53,6 +53,8 @@ _SIGNATURES = {
     "kvq_append": (_c_int, [_c_vp] * 2 + [_c_int] * 8 + [_c_vp] * 6),
     "kvq_attend_cache": (_c_int, [_c_vp] * 5 + [_c_int] * 9 + [_c_float, _c_int, _c_vp, _c_size,
                                                                _c_vp, _c_int, _c_int, _c_vp]),
+    "kvq_attend_window": (_c_int, [_c_vp] * 7 + [_c_int] * 10 + [_c_float, _c_int, _c_vp,
+                                                                _c_size, _c_vp, _c_int, _c_vp]),
     "kvq_attend_f32": (_c_int, [_c_vp] * 3 + [_c_int] * 6 + [_c_float, _c_int, _c_vp, _c_size,
                                                              _c_vp, _c_vp]),
     "kvq_stream_read": (_c_int, [_c_vp, _c_size, _c_vp, _c_vp]),
@@ -230,6 +232,37 @@ def attend(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scal
                                     workspace.numel(), _ptr(out), VARIANTS[variant],
                                     KVQ_ATTEND_CAUSAL if causal else 0, _stream(q.device)),
                "kvq_attend_cache")
+    return out
+
+
+def attend_window(q, k_codes, k_scales, v_codes, v_scales, k_win, v_win, N, bits=4, group=32,
+                  capacity=None, sm_scale=0.0, num_splits=0, workspace=None, out=None,
+                  causal=False):
+    """Attention over N packed tokens followed by the W = k_win.shape[2]
+    most recent tokens in float32 (k_win, v_win [B,Hkv,W,D])."""
+    torch = _torch()
+    _need(q, torch.float32, "q")
+    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (k_scales, "k_scales", torch.float32),
+                     (v_codes, "v_codes", torch.uint8), (v_scales, "v_scales", torch.float32),
+                     (k_win, "k_win", torch.float32), (v_win, "v_win", torch.float32)):
+        _need(t, dt, n)
+    B, Hq, R, D = q.shape
+    Hkv, W = k_win.shape[1], k_win.shape[2]
+    if tuple(k_win.shape) != (B, Hkv, W, D) or k_win.shape != v_win.shape:
+        raise ValueError("k_win and v_win must both be [B, Hkv, W, D]")
+    cap = max(N, 1) if capacity is None else capacity
+    if bits in (4, 8) and group >= 2 and cap >= max(N, 1):
+        _check_cache((k_codes, k_scales, v_codes, v_scales), B, Hkv, cap, D, bits, group)
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, R, N + W, D, num_splits, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.kvq_attend_window(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                 _ptr(v_scales), _ptr(k_win), _ptr(v_win), B, Hq, Hkv, R, N, W,
+                                 cap, D, bits, group, float(sm_scale), num_splits,
+                                 _ptr(workspace), workspace.numel(), _ptr(out),
+                                 KVQ_ATTEND_CAUSAL if causal else 0, _stream(q.device)),
+           "kvq_attend_window")
     return out
 
 

@@ -84,18 +84,21 @@ int auto_splits(int B, int Hkv, int N) {
 
 // Shared validation of the attention calls.  `bits` == 32 marks the
 // float32-cache path.
-// `cap`: tokens the packed layout is sized for (>= N; N for the float32 cache).
+// `cap`: tokens the packed layout is sized for (>= the n_packed tokens read
+// from it; N for the float32 cache).  N counts every token attended.
 kvq_status check_attend(const float* q, const void* k, const void* ks, const void* v,
                         const void* vs, int B, int Hq, int Hkv, int R, int N, int cap, int D,
                         int bits, int group, float sm_scale, int num_splits, void* workspace,
-                        size_t workspace_bytes, float* out, AttendProblem* p) {
+                        size_t workspace_bytes, float* out, AttendProblem* p, int n_packed = -1) {
+  if (n_packed < 0) n_packed = N;
   if (!q || !k || !v || !out || (bits != 32 && (!ks || !vs)))
     return fail(KVQ_ERR_INVALID, "null pointer argument");
   if (B < 1 || Hq < 1 || Hkv < 1 || R < 1 || N < 1 || D < 1)
     return fail(KVQ_ERR_INVALID, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d R=%d N=%d D=%d)", B, Hq,
                 Hkv, R, N, D);
   if (Hq % Hkv) return fail(KVQ_ERR_INVALID, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  if (cap < N) return fail(KVQ_ERR_INVALID, "capacity=%d < N=%d", cap, N);
+  if (cap < n_packed || cap < 1)
+    return fail(KVQ_ERR_INVALID, "capacity=%d < %d packed tokens", cap, n_packed);
   if (bits != 32 && !format_ok(bits, group))
     return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
                 group);
@@ -157,6 +160,8 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   p->N = N;
   p->cap = cap;
   p->causal = 0;
+  p->k_win = p->v_win = nullptr;
+  p->W = 0;
   p->D = D;
   p->rows = rows;
   p->bits = bits;
@@ -392,6 +397,36 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
   }
 }
 
+kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float* k_scales,
+                             const uint8_t* v_codes, const float* v_scales, const float* k_win,
+                             const float* v_win, int B, int Hq, int Hkv, int R, int N, int W,
+                             int capacity, int D, int bits, int group, float sm_scale,
+                             int num_splits, void* workspace, size_t workspace_bytes, float* out,
+                             int flags, void* stream) {
+  if (!k_win || !v_win) return fail(KVQ_ERR_INVALID, "null pointer argument");
+  if (N < 0 || W < 1 || static_cast<long long>(N) + W > 0x7fffffff)
+    return fail(KVQ_ERR_INVALID, "need N >= 0 packed tokens and W >= 1 window tokens (N=%d W=%d)",
+                N, W);
+  if (!aligned(k_win, 4) || !aligned(v_win, 4))
+    return fail(KVQ_ERR_INVALID, "float arrays must be 4-byte aligned");
+  if (flags & ~KVQ_ATTEND_CAUSAL) return fail(KVQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  AttendProblem p;
+  kvq_status st = check_attend(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N + W,
+                               capacity, D, bits, group, sm_scale, num_splits, workspace,
+                               workspace_bytes, out, &p, N);
+  if (st != KVQ_OK) return st;
+  const size_t out_bytes = sizeof(float) * static_cast<size_t>(B) * Hq * R * D;
+  const size_t win_bytes = sizeof(float) * static_cast<size_t>(B) * Hkv * W * D;
+  if (overlaps(out, out_bytes, k_win, win_bytes) || overlaps(out, out_bytes, v_win, win_bytes))
+    return fail(KVQ_ERR_INVALID, "out overlaps the window");
+  p.k_win = k_win;
+  p.v_win = v_win;
+  p.W = W;
+  p.causal = (flags & KVQ_ATTEND_CAUSAL) && R > 1;
+  return hip_status(launch_attend_valu(p, static_cast<hipStream_t>(stream)),
+                    "attend_window launch");
+}
+
 kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,
                               const uint8_t* v_codes, const float* v_scales, int B, int Hq,
                               int Hkv, int R, int N, int D, int bits, int group, float sm_scale,
@@ -447,6 +482,6 @@ const char* kvq_status_string(int status) {
 
 const char* kvq_last_error(void) { return g_last_error; }
 
-int kvq_abi_version(void) { return 5; }
+int kvq_abi_version(void) { return 6; }
 
 }  // extern "C"

@@ -29,11 +29,13 @@ constexpr int kThreads = 256;
 constexpr int kTile = 32;
 
 // Decoded K (token n, channel d) and V (token n, feature f) of head bh:
-// fl32((stored - qmax) * scale), addressed through the block layout.
+// fl32((stored - qmax) * scale), addressed through the block layout; the
+// tokens of a recent-token window (n >= N - W) come from its float32 rows.
 template <int SRC>
 __device__ __forceinline__ float decode_k(const AttendProblem& p, const Layout& L, long long bh,
                                           int d, int n) {
   if (SRC == 32) return p.k_f32[(bh * p.N + n) * p.D + d];
+  if (n >= p.N - p.W) return p.k_win[(bh * p.W + (n - (p.N - p.W))) * p.D + d];
   const unsigned b = p.k_codes[bh * k_code_bytes_per_head(L) + k_code_byte(L, n, d)];
   const int c = SRC == 4 ? static_cast<int>((n & 1) ? (b >> 4) : (b & 15u)) - 7
                          : static_cast<int>(b) - 127;
@@ -44,6 +46,7 @@ template <int SRC>
 __device__ __forceinline__ float decode_v(const AttendProblem& p, const Layout& L, long long bh,
                                           int n, int f) {
   if (SRC == 32) return p.v_f32[(bh * p.N + n) * p.D + f];
+  if (n >= p.N - p.W) return p.v_win[(bh * p.W + (n - (p.N - p.W))) * p.D + f];
   const unsigned b = p.v_codes[bh * v_code_bytes_per_head(L) + v_code_byte(L, n, f)];
   const int c = SRC == 4 ? static_cast<int>((f & 1) ? (b >> 4) : (b & 15u)) - 7
                          : static_cast<int>(b) - 127;

@@ -28,6 +28,11 @@ struct AttendProblem {
   int B, Hq, Hkv, R, N, D;
   int cap;                 // tokens the packed layout is sized for (>= N; N for float32)
   int causal;              // 1: row r is query r % R at position N - R + r % R (R > 1)
+  // Recent-token window (general kernel only): tokens [N - W, N) are read
+  // from float32 k_win / v_win [B*Hkv][W][D] instead of the packed cache.
+  const float* k_win;
+  const float* v_win;
+  int W;
   int rows;                // (Hq / Hkv) * R: query rows sharing one KV head
   int bits, group;         // 4/8 and group; bits == 32 marks the float32 cache
   float qscale;            // sm_scale * log2(e)

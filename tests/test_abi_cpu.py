@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert lib.kvq_abi_version() == 5
+    assert lib.kvq_abi_version() == 6
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.kvq_status_string(st)
 
@@ -185,3 +185,22 @@ def test_cache_clear_rejects_before_launch():
     assert lib.kvq_cache_clear(1, 1, 16, 8, 4, 8, None, *ptrs[1:], None) == kvq.KVQ_ERR_INVALID
     assert lib.kvq_cache_clear(1, 1, 16, 8, 4, 8, ptrs[0], ctypes.c_void_p((2 << 30) + 2),
                                *ptrs[2:], None) == kvq.KVQ_ERR_INVALID
+
+
+def _attend_window(**kw):
+    a = dict(q=FAKE, kw=ctypes.c_void_p(3 << 30), vw=ctypes.c_void_p(4 << 30), N=64, W=8,
+             cap=64, flags=0, out=FAKE2)
+    a.update(kw)
+    return lib.kvq_attend_window(a["q"], FAKE, FAKE, FAKE, FAKE, a["kw"], a["vw"], 1, 4, 2, 1,
+                                 a["N"], a["W"], a["cap"], 32, 4, 32, 0.0, 1, None, 0, a["out"],
+                                 a["flags"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(kw=None), dict(vw=None), dict(W=0), dict(N=-1), dict(cap=63), dict(cap=0, N=0),
+    dict(flags=4), dict(kw=ctypes.c_void_p((3 << 30) + 2)),
+    dict(out=ctypes.c_void_p((4 << 30) + 64)),          # out inside the V window
+])
+def test_attend_window_rejects_before_launch(kw):
+    assert _attend_window(**kw) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_last_error()

@@ -1,0 +1,69 @@
+"""GPU parity of the mixed cache (kvq_attend_window): N packed tokens plus the
+W most recent in float32, against the oracle's attend_window (<= 1e-4),
+including the causal chunk, an empty packed part, and a decode loop that
+moves the window's oldest token into a growing packed cache."""
+import numpy as np
+import pytest
+
+from oracle import kvq_oracle as O
+from workloads import Workload, make_qkv
+
+from gpu_helpers import announce, dev, host, max_abs
+
+pytestmark = pytest.mark.gpu
+
+kvq = pytest.importorskip("quantized_kv_cache_attend_amd")
+
+TOL = 1e-4
+
+
+@pytest.mark.parametrize("B,hq,hkv,r,n,w,d,bits,group,causal", [
+    (2, 8, 2, 1, 500, 16, 128, 4, 32, False),
+    (1, 4, 1, 4, 1021, 64, 32, 4, 8, False),
+    (1, 2, 2, 8, 300, 33, 64, 8, 8, True),
+    (2, 4, 2, 4, 0, 40, 128, 4, 32, False),     # no packed token at all
+    (1, 2, 1, 2, 4096, 1, 128, 4, 32, True),
+])
+def test_attend_window(B, hq, hkv, r, n, w, d, bits, group, causal):
+    wl = Workload("win", B, hq, hkv, r, n + w, d, ((bits, group),))
+    q, k, v = make_qkv(wl, 9)
+    announce(f"attend_window B={B} hq={hq} hkv={hkv} R={r} N={n} W={w} D={d} {bits}b g{group} "
+             f"causal={causal}")
+    want = O.attend_window(q, k, v, w, bits, group, causal=causal)
+    cap = max(n, 1)
+    kp = np.zeros((B, hkv, cap, d), np.float32)
+    vp = np.zeros((B, hkv, cap, d), np.float32)
+    kp[:, :, :n], vp[:, :, :n] = k[:, :, :n], v[:, :, :n]
+    kc, ks = kvq.pack_k(dev(kp), bits, group)
+    vc, vs = kvq.pack_v(dev(vp), bits, group)
+    kw, vw = dev(k[:, :, n:]), dev(v[:, :, n:])
+    for splits in (1, 3, 0):
+        got = host(kvq.attend_window(dev(q), kc, ks, vc, vs, kw, vw, n, bits, group,
+                                     capacity=cap, num_splits=splits, causal=causal))
+        assert np.isfinite(got).all()
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
+
+
+def test_decode_loop_with_window():
+    """Each step: the new token joins the float32 window; once it holds W
+    tokens the oldest moves into the packed cache (kvq_append)."""
+    B, hq, hkv, d, cap, W = 1, 4, 2, 128, 160, 8
+    wl = Workload("loop", B, hq, hkv, 1, cap + W, d, ((4, 32),))
+    q, k, v = make_qkv(wl, 10)
+    announce("decode loop with an 8-token window")
+    cache = kvq.new_cache(B, hkv, cap, d, 4, 32)
+    kd, vd, qd = dev(k), dev(v), dev(q)
+    n_packed = 0
+    for t in range(1, 150):                      # t tokens so far
+        w = min(t, W)
+        if t > W:                                # token t - W - 1 leaves the window
+            j = t - W - 1
+            kvq.append(kd[:, :, j:j + 1].contiguous(), vd[:, :, j:j + 1].contiguous(), n_packed,
+                       cache, cap, 4, 32)
+            n_packed += 1
+        if t % 37 == 0 or t in (1, 8, 9, 149):
+            got = host(kvq.attend_window(qd, *cache[:4], kd[:, :, t - w:t].contiguous(),
+                                         vd[:, :, t - w:t].contiguous(), n_packed, 4, 32,
+                                         capacity=cap))
+            want = O.attend_window(q, k[:, :, :t], v[:, :, :t], w, 4, 32)
+            assert max_abs(got, want) <= TOL, (t, max_abs(got, want))

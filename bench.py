@@ -447,6 +447,36 @@ def main():
         log(f"[bench] causal step of {r_c} queries per head: {timings[True]:.2f} us "
             f"(unmasked {timings[False]:.2f} us)")
 
+        # The mixed cache: the 64 most recent tokens in float32, the rest
+        # packed (kvq_attend_window, general kernel), same queries.
+        win = 64
+        kpre = kvq.pack_k(kd[:, :, :w.N - win].contiguous(), bits, group)
+        vpre = kvq.pack_v(vd[:, :, :w.N - win].contiguous(), bits, group)
+        kw, vw = kd[:, :, w.N - win:].contiguous(), vd[:, :, w.N - win:].contiguous()
+        out_w = torch.empty_like(qd)
+
+        def window_call():
+            kvq.attend_window(qd, *kpre, *vpre, kw, vw, w.N - win, bits, group, workspace=ws,
+                              out=out_w, num_splits=splits)
+        window_call()
+        torch.cuda.synchronize()
+        blocker = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+        for _ in range(64):
+            kvq.stream_read(blocker, sink)
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        n_w = 20
+        w0.record(stream)
+        for _ in range(n_w):
+            window_call()
+        w1.record(stream)
+        torch.cuda.synchronize()
+        win_us = w0.elapsed_time(w1) * 1e3 / n_w
+        extra["window_step"] = {"float32_window_tokens": win, "us": round(win_us, 2),
+                                "kernel": "general (VALU)"}
+        log(f"[bench] mixed cache (last {win} tokens float32): {win_us:.1f} us")
+        del blocker, kpre, vpre, kw, vw
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host ...")

@@ -11,9 +11,13 @@ same recipe through the library's kernels (pack, fused attend, and the
 float32-cache attend as the reference) at any size.
 
     python -m quantized_kv_cache_attend_amd.accuracy [--n 128 512 4096] [--d 32 128]
+        [--window 0 16 64]
 
 prints one markdown table (mean relative L2 per format, length, head dim and
-distribution) and, with --json, the per-input values.
+distribution) and, with --json, the per-input values.  --window adds the
+mixed cache the same page announces as its next study ("exercises and
+common mistakes": high precision kept for the most recent tokens): the last
+W tokens in float32 (kvq_attend_window), the rest packed.
 """
 from __future__ import annotations
 
@@ -44,9 +48,11 @@ def packed_bytes_per_head(n: int, d: int, bits: int, group: int) -> int:
 
 
 def study(lengths, dims, seeds=(0, 1, 2), dists=DISTS, formats=FORMATS, queries=4,
-          device="cuda"):
+          device="cuda", windows=(0,)):
     """Per-input relative L2 errors on the GPU.  Returns a list of dicts
-    (n, d, dist, seed, bits, group, rel_l2, packed_bytes)."""
+    (n, d, dist, seed, bits, group, window, rel_l2, packed_bytes); window W > 0:
+    the last W tokens stay float32 (packed_bytes then counts them at 4 bytes
+    per element)."""
     import torch
 
     import quantized_kv_cache_attend_amd as kvq
@@ -63,29 +69,42 @@ def study(lengths, dims, seeds=(0, 1, 2), dists=DISTS, formats=FORMATS, queries=
                     qd, kd, vd = (torch.from_numpy(a).to(device) for a in (q, k, v))
                     ref = kvq.attend_f32(qd, kd, vd).cpu().numpy()
                     for bits, group in formats:
-                        kc, ks = kvq.pack_k(kd, bits, group)
-                        vc, vs = kvq.pack_v(vd, bits, group)
-                        out = kvq.attend(qd, kc, ks, vc, vs, n, bits, group).cpu().numpy()
-                        rows.append({"n": n, "d": d, "dist": dist, "seed": seed, "bits": bits,
-                                     "group": group, "rel_l2": rel_l2(out, ref),
-                                     "packed_bytes": packed_bytes_per_head(n, d, bits, group)})
+                        for win in windows:
+                            if win >= n:
+                                continue
+                            npk = n - win
+                            kc, ks = kvq.pack_k(kd[:, :, :npk].contiguous(), bits, group)
+                            vc, vs = kvq.pack_v(vd[:, :, :npk].contiguous(), bits, group)
+                            if win:
+                                out = kvq.attend_window(qd, kc, ks, vc, vs,
+                                                        kd[:, :, npk:].contiguous(),
+                                                        vd[:, :, npk:].contiguous(), npk, bits,
+                                                        group)
+                            else:
+                                out = kvq.attend(qd, kc, ks, vc, vs, n, bits, group)
+                            nbytes = packed_bytes_per_head(npk, d, bits, group) + 8 * win * d
+                            rows.append({"n": n, "d": d, "dist": dist, "seed": seed,
+                                         "bits": bits, "group": group, "window": win,
+                                         "rel_l2": rel_l2(out.cpu().numpy(), ref),
+                                         "packed_bytes": nbytes})
     return rows
 
 
 def table(rows) -> str:
-    """Mean over seeds, one line per (n, d, dist), one column per format."""
+    """Mean over seeds, one line per (n, d, dist, window), one column per format."""
     fmts = sorted({(r["bits"], r["group"]) for r in rows}, key=lambda f: (f[0], f[1]))
-    keys = sorted({(r["n"], r["d"], r["dist"]) for r in rows},
-                  key=lambda k: (k[0], k[1], DISTS.index(k[2]) if k[2] in DISTS else 9))
-    head = "| N | D | keys | " + " | ".join(f"{b}-bit g{g}" for b, g in fmts) + " |"
-    lines = [head, "|" + "---|" * (3 + len(fmts))]
-    for n, d, dist in keys:
+    keys = sorted({(r["n"], r["d"], r["dist"], r["window"]) for r in rows},
+                  key=lambda k: (k[0], k[1], DISTS.index(k[2]) if k[2] in DISTS else 9, k[3]))
+    head = "| N | D | keys | float32 window | " + " | ".join(f"{b}-bit g{g}" for b, g in fmts) + " |"
+    lines = [head, "|" + "---|" * (4 + len(fmts))]
+    for n, d, dist, win in keys:
         cells = []
         for b, g in fmts:
             vals = [r["rel_l2"] for r in rows
-                    if (r["n"], r["d"], r["dist"], r["bits"], r["group"]) == (n, d, dist, b, g)]
-            cells.append(f"{100 * np.mean(vals):.3f} %")
-        lines.append(f"| {n} | {d} | {dist} | " + " | ".join(cells) + " |")
+                    if (r["n"], r["d"], r["dist"], r["window"], r["bits"], r["group"]) ==
+                    (n, d, dist, win, b, g)]
+            cells.append(f"{100 * np.mean(vals):.3f} %" if vals else "-")
+        lines.append(f"| {n} | {d} | {dist} | {win} | " + " | ".join(cells) + " |")
     return "\n".join(lines)
 
 
@@ -95,9 +114,11 @@ def main(argv=None):
     ap.add_argument("--n", type=int, nargs="+", default=[128, 512, 4096, 32768])
     ap.add_argument("--d", type=int, nargs="+", default=[32, 128])
     ap.add_argument("--seeds", type=int, nargs="+", default=[0, 1, 2])
+    ap.add_argument("--window", type=int, nargs="+", default=[0],
+                    help="float32 windows of the most recent tokens (0: fully packed)")
     ap.add_argument("--json", help="write the per-input values here")
     args = ap.parse_args(argv)
-    rows = study(args.n, args.d, tuple(args.seeds))
+    rows = study(args.n, args.d, tuple(args.seeds), windows=tuple(args.window))
     print(table(rows))
     if args.json:
         with open(args.json, "w", encoding="utf-8") as f:

@@ -38,3 +38,21 @@ def test_study_matches_oracle():
         mean[(b, g)] = np.mean([r["rel_l2"] for r in rows
                                 if (r["bits"], r["group"], r["dist"]) == (b, g, "clean")])
     assert mean[(8, 8)] < mean[(8, 32)] < mean[(4, 8)] < mean[(4, 32)]
+
+
+def test_window_study_matches_oracle():
+    """The mixed cache in the study: per-input errors equal the oracle's
+    attend_window errors, and a 16-token float32 window cuts the error of
+    late-biased inputs."""
+    from quantized_kv_cache_attend_amd import accuracy
+    announce("accuracy study with windows")
+    rows = accuracy.study([512], [32], dists=("late", "early"), formats=((4, 32),),
+                          windows=(0, 16))
+    for r in rows:
+        w = Workload("acc", 1, 1, 1, 4, r["n"], r["d"], ((4, 32),))
+        q, k, v = make_qkv(w, r["seed"], r["dist"])
+        want = O.rel_l2(O.attend_window(q, k, v, r["window"], 4, 32), O.attend_dense(q, k, v))
+        assert abs(r["rel_l2"] - want) <= 1e-4 * want + 1e-6, r
+    late = {win: np.mean([r["rel_l2"] for r in rows if (r["dist"], r["window"]) == ("late", win)])
+            for win in (0, 16)}
+    assert late[16] < 0.5 * late[0]

@@ -96,3 +96,25 @@ def test_multi_token_step_on_a_growing_cache():
         kc, ks, vc, vs = oracle_pack(k[:, :, :n], v[:, :, :n], 4, 32)
         want = O.attend_packed(q, kc, ks, vc, vs, n, 4, 32, causal=True)
         assert max_abs(got, want) <= TOL, (n, max_abs(got, want))
+
+
+@pytest.mark.parametrize("name,r,splits", [("gqa_n4096", 4, 0), ("gqa_n32768", 4, 16)])
+def test_causal_full_size_sampled(name, r, splits):
+    """The full-size caches with a causal chunk of R queries per head (the
+    shapes bench.py times for the causal step), on the matrix-core kernels;
+    the oracle recomputes sampled KV heads."""
+    import dataclasses
+    from workloads import WORKLOADS
+    w = dataclasses.replace(WORKLOADS[name], R=r)
+    q, k, v = make_qkv(w, 11)
+    announce(f"causal full size {name} R={r} splits={splits}")
+    gk, gks = kvq.pack_k(dev(k), 4, 32)
+    gv, gvs = kvq.pack_v(dev(v), 4, 32)
+    got = host(kvq.attend(dev(q), gk, gks, gv, gvs, w.N, 4, 32, num_splits=splits,
+                          variant="mfma", causal=True))
+    rep = w.Hq // w.Hkv
+    for b, h in ((0, 0), (w.B - 1, w.Hkv - 1)):
+        qs = q[b:b + 1, h * rep:(h + 1) * rep]
+        kc, ks, vc, vs = oracle_pack(k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], 4, 32)
+        want = O.attend_packed(qs, kc, ks, vc, vs, w.N, 4, 32, causal=True)
+        assert max_abs(got[b:b + 1, h * rep:(h + 1) * rep], want) <= TOL, (b, h)

@@ -67,3 +67,23 @@ def test_decode_loop_with_window():
                                          capacity=cap))
             want = O.attend_window(q, k[:, :, :t], v[:, :, :t], w, 4, 32)
             assert max_abs(got, want) <= TOL, (t, max_abs(got, want))
+
+
+def test_window_full_size_sampled():
+    """The C4-size mixed cache bench.py times (the last 64 tokens float32),
+    sampled KV heads against the oracle."""
+    from workloads import WORKLOADS
+    w = WORKLOADS["gqa_n4096"]
+    q, k, v = make_qkv(w, 12)
+    win = 64
+    npk = w.N - win
+    announce("window full size gqa_n4096 W=64")
+    kc, ks = kvq.pack_k(dev(k[:, :, :npk]), 4, 32)
+    vc, vs = kvq.pack_v(dev(v[:, :, :npk]), 4, 32)
+    got = host(kvq.attend_window(dev(q), kc, ks, vc, vs, dev(k[:, :, npk:]), dev(v[:, :, npk:]),
+                                 npk, 4, 32))
+    rep = w.Hq // w.Hkv
+    for b, h in ((0, 0), (3, 5), (7, 7)):
+        qs = q[b:b + 1, h * rep:(h + 1) * rep]
+        want = O.attend_window(qs, k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], win, 4, 32)
+        assert max_abs(got[b:b + 1, h * rep:(h + 1) * rep], want) <= TOL, (b, h)

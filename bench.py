@@ -454,9 +454,11 @@ def main():
         vpre = kvq.pack_v(vd[:, :, :w.N - win].contiguous(), bits, group)
         kw, vw = kd[:, :, w.N - win:].contiguous(), vd[:, :, w.N - win:].contiguous()
         out_w = torch.empty_like(qd)
+        ws_w = kvq.new_workspace(w.B, w.Hq, w.Hkv, w.R, w.N, w.D,
+                                 (splits or kvq.auto_splits(w.B, w.Hkv, w.N)) + 1, device=dev)
 
-        def window_call():
-            kvq.attend_window(qd, *kpre, *vpre, kw, vw, w.N - win, bits, group, workspace=ws,
+        def window_call():  # one workspace slot more than the splits: the fused form
+            kvq.attend_window(qd, *kpre, *vpre, kw, vw, w.N - win, bits, group, workspace=ws_w,
                               out=out_w, num_splits=splits)
         window_call()
         torch.cuda.synchronize()
@@ -473,9 +475,10 @@ def main():
         torch.cuda.synchronize()
         win_us = w0.elapsed_time(w1) * 1e3 / n_w
         extra["window_step"] = {"float32_window_tokens": win, "us": round(win_us, 2),
-                                "kernel": "general (VALU)"}
+                                "form": "window partial (general kernel) + matrix-core attend "
+                                        "merging it in its combine"}
         log(f"[bench] mixed cache (last {win} tokens float32): {win_us:.1f} us")
-        del blocker, kpre, vpre, kw, vw
+        del blocker, kpre, vpre, kw, vw, ws_w
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -162,6 +162,9 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   p->causal = 0;
   p->k_win = p->v_win = nullptr;
   p->W = 0;
+  p->pos_end = N;
+  p->part0 = 0;
+  p->extra_parts = 0;
   p->D = D;
   p->rows = rows;
   p->bits = bits;
@@ -419,12 +422,51 @@ kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float
   const size_t win_bytes = sizeof(float) * static_cast<size_t>(B) * Hkv * W * D;
   if (overlaps(out, out_bytes, k_win, win_bytes) || overlaps(out, out_bytes, v_win, win_bytes))
     return fail(KVQ_ERR_INVALID, "out overlaps the window");
+  p.causal = (flags & KVQ_ATTEND_CAUSAL) && R > 1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // Fused form: the packed tokens on a matrix-core kernel, whose fused
+  // combine also merges one extra partial slot: the window's (m, z, u),
+  // written just before by the general kernel over the W float32 tokens
+  // (stream order makes it complete and visible when the combine reads it).
+  if (N >= 1) {
+    AttendProblem pm = p;
+    pm.N = N;
+    pm.pos_end = N + W;
+    if (mfma_eligible(pm)) {
+      const bool wide = pm.rows > kMfmaMaxRows;
+      const int S = num_splits ? num_splits
+                               : (wide ? mfma32_auto_splits(B, Hkv, N) : mfma_auto_splits(B, Hkv, N));
+      const WorkspaceLayout wl = workspace_layout(B, Hq, Hkv, R, D, S + 1);
+      if (S + 1 <= 65535 && workspace && workspace_bytes >= wl.total) {
+        char* ws = static_cast<char*>(workspace);
+        pm.splits = S;
+        pm.extra_parts = 1;
+        pm.tokens_per_split = mfma_tokens_per_split(N, S);
+        pm.part_m = reinterpret_cast<float*>(ws + wl.m_off);
+        pm.part_z = reinterpret_cast<float*>(ws + wl.z_off);
+        pm.part_u = reinterpret_cast<float*>(ws + wl.u_off);
+        pm.counters = reinterpret_cast<unsigned*>(ws + wl.cnt_off);
+        AttendProblem pw = pm;  // the window: W float32 tokens, positions local to it
+        pw.bits = 32;
+        pw.group = 1;
+        pw.k_f32 = k_win;
+        pw.v_f32 = v_win;
+        pw.N = pw.cap = pw.pos_end = W;
+        pw.splits = 1;
+        pw.tokens_per_split = W;
+        pw.part0 = S;
+        pw.extra_parts = 0;
+        hipError_t e = launch_attend_valu(pw, s);
+        if (e == hipSuccess) e = wide ? launch_attend_mfma32(pm, s) : launch_attend_mfma(pm, s);
+        return hip_status(e, "attend_window (fused) launch");
+      }
+    }
+  }
   p.k_win = k_win;
   p.v_win = v_win;
   p.W = W;
-  p.causal = (flags & KVQ_ATTEND_CAUSAL) && R > 1;
-  return hip_status(launch_attend_valu(p, static_cast<hipStream_t>(stream)),
-                    "attend_window launch");
+  return hip_status(launch_attend_valu(p, s), "attend_window launch");
 }
 
 kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,

@@ -426,7 +426,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
   }
 
   // Causal limit of this lane's score row n & 3.
-  const int lim = p.N - p.R + (n & 3) % p.R;
+  const int lim = p.pos_end - p.R + (n & 3) % p.R;
 
   // The ring: block i sits in register set i % kDepth; once attended, the set
   // is refilled with block i + kDepth.  Every step of a round runs (a step
@@ -439,7 +439,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
       const int blk = b_first + i * kWaves;
       attend_block<kCausal>(sm, br[j], i < cnt ? blk * kBlockTokens : t_end, t_end, cc, ws, h,
                             blk + kDepth * kWaves, i + kDepth < cnt, lo, qv, us_row, lim,
-                            p.N - p.R);
+                            p.pos_end - p.R);
     }
   }
   // z of each row: sum this lane's share over the four q-blocks
@@ -487,7 +487,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
     }
   }
   const long long row0 = bh * rows;
-  if (p.splits == 1) {
+  if (p.splits + p.extra_parts == 1) {
     if (r < rows) {
 #pragma unroll
       for (int j = 0; j < kSlots; ++j)  // Z = 0: a causal row with no legal key

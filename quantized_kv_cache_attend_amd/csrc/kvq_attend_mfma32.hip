@@ -473,7 +473,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
   }
 
   // Causal limit of this lane's score rows 16t + n.
-  const int lim[2] = {p.N - p.R + n % p.R, p.N - p.R + (16 + n) % p.R};
+  const int lim[2] = {p.pos_end - p.R + n % p.R, p.pos_end - p.R + (16 + n) % p.R};
   if (active) {
     attend_block32<true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
                                   loop_begin <= loop_end ? loop_begin : first, lo, us_row, qk,
@@ -540,7 +540,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
     if (half == 0) __syncthreads();  // the first pair is read before the second overwrites it
   }
   const long long row0 = bh * rows;
-  if (p.splits == 1) {
+  if (p.splits + p.extra_parts == 1) {
     if (r < rows) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

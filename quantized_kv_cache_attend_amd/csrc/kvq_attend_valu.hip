@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
     for (int i = tid; i < rows * kTile; i += kThreads) {
       const int r = i / kTile, j = i % kTile;
       float s = -INFINITY;
-      if (j < tn && (!p.causal || t0 + j <= p.N - p.R + r % p.R)) {
+      if (j < tn && (!p.causal || t0 + j <= p.pos_end - p.R + r % p.R)) {
         s = 0.0f;
 #pragma unroll 8
         for (int d = 0; d < D; ++d) s = fmaf(sQ[r][d], sK[j][d], s);
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   }
 
   const long long row0 = bh * rows;
-  if (p.splits == 1) {
+  if (p.splits == 1 && p.part0 == 0) {
 #pragma unroll
     for (int i = 0; i < kAcc; ++i) {
       const int idx = tid + i * kThreads;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
     }
   } else {
     const long long total_rows = static_cast<long long>(p.B) * p.Hkv * rows;
-    const long long base = static_cast<long long>(split) * total_rows + row0;
+    const long long base = static_cast<long long>(split + p.part0) * total_rows + row0;
 #pragma unroll
     for (int i = 0; i < kAcc; ++i) {
       const int idx = tid + i * kThreads;

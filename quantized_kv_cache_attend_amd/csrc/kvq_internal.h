@@ -27,7 +27,11 @@ struct AttendProblem {
   float* out;              // [B][Hq][R][D]
   int B, Hq, Hkv, R, N, D;
   int cap;                 // tokens the packed layout is sized for (>= N; N for float32)
-  int causal;              // 1: row r is query r % R at position N - R + r % R (R > 1)
+  int causal;              // 1: row r is query r % R at position pos_end - R + r % R (R > 1)
+  int pos_end;             // position after the last query (N unless a window follows)
+  int part0;               // first partial slot this launch writes (splits > 1 or part0 > 0)
+  int extra_parts;         // slots splits .. splits + extra_parts - 1 were written by an
+                           // earlier launch and join the combine
   // Recent-token window (general kernel only): tokens [N - W, N) are read
   // from float32 k_win / v_win [B*Hkv][W][D] instead of the packed cache.
   const float* k_win;

@@ -249,17 +249,18 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
     float Mg = -INFINITY, Zg = 0.0f, V[kF];
 #pragma unroll
     for (int i = 0; i < kF; ++i) V[i] = 0.0f;
-    for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+    const int parts = p.splits + p.extra_parts;  // extra slots: written by an earlier launch
+    for (int s0 = 0; s0 < parts; s0 += kBatch) {
       float ms[kBatch], zs[kBatch], us[kBatch][kF];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const long long pr =
-            static_cast<long long>(s0 + j < p.splits ? s0 + j : s0) * total_rows + row;
+            static_cast<long long>(s0 + j < parts ? s0 + j : s0) * total_rows + row;
         ms[j] = __hip_atomic_load(&p.part_m[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         zs[j] = __hip_atomic_load(&p.part_z[pr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if constexpr (kRun % 4 == 0) {
           const __amdgpu_buffer_rsrc_t rs =
-              split_rows(p, s0 + j < p.splits ? s0 + j : s0, total_rows, head);
+              split_rows(p, s0 + j < parts ? s0 + j : s0, total_rows, head);
 #pragma unroll
           for (int i4 = 0; i4 < kF / 4; ++i4) {
             const f32x4 x = __builtin_bit_cast(
@@ -275,7 +276,7 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
             us[j][i] = __hip_atomic_load(&p.part_u[pr * p.D + slot_feature<kRun, kStride>(f0, i)],
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        if (s0 + j >= p.splits) ms[j] = -INFINITY;
+        if (s0 + j >= parts) ms[j] = -INFINITY;
       }
       float mb = Mg;
 #pragma unroll

@@ -44,6 +44,31 @@ def test_attend_window(B, hq, hkv, r, n, w, d, bits, group, causal):
         assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
 
 
+@pytest.mark.parametrize("hq,hkv,r,causal", [(32, 8, 1, False), (16, 2, 2, True), (8, 8, 4, True)])
+def test_fused_window_equals_general_kernel(hq, hkv, r, causal):
+    """The fused form (window partial + matrix-core combine) against the
+    general kernel on the same call (a workspace one slot too small forces
+    the latter), and both against the oracle."""
+    B, n, w, D = 2, 2000, 48, 128
+    wl = Workload("fused", B, hq, hkv, r, n + w, D, ((4, 32),))
+    q, k, v = make_qkv(wl, 13)
+    announce(f"window fused vs general hq={hq} hkv={hkv} R={r} causal={causal}")
+    want = O.attend_window(q, k, v, w, 4, 32, causal=causal)
+    kc, ks = kvq.pack_k(dev(k[:, :, :n]), 4, 32)
+    vc, vs = kvq.pack_v(dev(v[:, :, :n]), 4, 32)
+    kw, vw, qd = dev(k[:, :, n:]), dev(v[:, :, n:]), dev(q)
+    for splits in (1, 3, 0):
+        fused = host(kvq.attend_window(qd, kc, ks, vc, vs, kw, vw, n, 4, 32, num_splits=splits,
+                                       causal=causal))
+        assert max_abs(fused, want) <= TOL, (splits, max_abs(fused, want))
+        if splits:  # exactly `splits` slots: no room for the window's, so the general kernel runs
+            small = kvq.new_workspace(B, hq, hkv, r, n + w, D, splits)
+            general = host(kvq.attend_window(qd, kc, ks, vc, vs, kw, vw, n, 4, 32,
+                                             num_splits=splits, workspace=small, causal=causal))
+            assert max_abs(fused, general) <= 2e-5, splits
+            assert max_abs(general, want) <= TOL, splits
+
+
 def test_decode_loop_with_window():
     """Each step: the new token joins the float32 window; once it holds W
     tokens the oldest moves into the packed cache (kvq_append)."""

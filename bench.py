@@ -371,46 +371,56 @@ def main():
             torch.cuda.synchronize()
             prompt_us = p0.elapsed_time(p1) * 1e3
             del kp, vp
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                  for _ in range(n_timed)]
             k_steps = [kd[:, :, i:i + 1].contiguous() for i in range(prompt, w.N)]
             v_steps = [vd[:, :, i:i + 1].contiguous() for i in range(prompt, w.N)]
             dec_out = torch.empty_like(qd)
             torch.cuda.synchronize()
-            # Queue the loop behind a few ms of unrelated reads so the host
-            # enqueues every step before the GPU reaches them: the events
-            # then time the GPU work, not the pace of the Python calls.
+            # Queue the loops behind a few ms of unrelated reads so the host
+            # enqueues every step before the GPU reaches them: one event pair
+            # then times back-to-back GPU work, not the pace of the Python
+            # calls (an event pair around one small kernel costs several us).
             blocker = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
-            for _ in range(128):
-                kvq.stream_read(blocker, sink)
+
+            def queue_blocker():
+                for _ in range(128):
+                    kvq.stream_read(blocker, sink)
+            queue_blocker()
+            d0 = torch.cuda.Event(enable_timing=True)
+            d1 = torch.cuda.Event(enable_timing=True)
             for i, n in enumerate(range(prompt, w.N)):
-                e = ev[i - n_warm] if i >= n_warm else None
-                if e:
-                    e[0].record(stream)
+                if i == n_warm:
+                    d0.record(stream)
                 kvq.append(k_steps[i], v_steps[i], n, cache, w.N, bits, group)
-                if e:
-                    e[1].record(stream)
                 kvq.attend(qd, *cache[:4], n + 1, bits, group, num_splits=splits, workspace=ws,
                            out=dec_out, variant=args.variant, capacity=w.N)
-                if e:
-                    e[2].record(stream)
+            d1.record(stream)
             torch.cuda.synchronize()
+            step_us = d0.elapsed_time(d1) * 1e3 / n_timed
             full = kvq.attend(qd, kc, ks, vc, vs, w.N, bits, group, num_splits=splits,
                               workspace=ws, variant=args.variant)
             torch.cuda.synchronize()
-            app = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e3
-            att = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
+            same = bool(torch.equal(dec_out, full))
+            # the same number of back-to-back attends alone (all N tokens)
+            queue_blocker()
+            d0.record(stream)
+            for _ in range(n_timed):
+                kvq.attend(qd, *cache[:4], w.N, bits, group, num_splits=splits, workspace=ws,
+                           out=dec_out, variant=args.variant, capacity=w.N)
+            d1.record(stream)
+            torch.cuda.synchronize()
+            attend_us = d0.elapsed_time(d1) * 1e3 / n_timed
             extra["decode_step"] = {
                 "tokens": f"{w.N - n_timed + 1}..{w.N}",
                 "prompt_append_us": round(prompt_us, 1),
                 "prompt_tokens": prompt,
-                "append_us_median": round(float(np.median(app)), 3),
-                "attend_us_median": round(float(np.median(att)), 3),
-                "last_step_equals_full_cache_attend": bool(torch.equal(dec_out, full)),
+                "step_us": round(step_us, 3),
+                "attend_only_us": round(attend_us, 3),
+                "append_us": round(step_us - attend_us, 3),
+                "last_step_equals_full_cache_attend": same,
             }
-            log(f"[bench] decode steps: append {np.median(app):.2f} us + attend "
-                f"{np.median(att):.2f} us (medians of {n_timed}); last step == full-cache attend: "
-                f"{extra['decode_step']['last_step_equals_full_cache_attend']}")
+            log(f"[bench] decode steps: {step_us:.2f} us per one-token append + attend, attend "
+                f"alone {attend_us:.2f} us (back to back, {n_timed} steps); last step == "
+                f"full-cache attend: {same}")
             del cache, blocker
 
         # A causal multi-token step on the same cache: R_c = 4 new queries per

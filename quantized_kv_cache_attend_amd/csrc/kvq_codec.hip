@@ -459,6 +459,85 @@ __global__ __launch_bounds__(256) void append_kernel(const float* __restrict__ k
   }
 }
 
+// One-token append (a decode step), with each group spread over lanes: a
+// lane holds one stored byte (two elements for 4-bit, one for 8-bit), the
+// group's largest magnitude is a max over its kLanes = group / (elements per
+// byte) neighbouring lanes (a power of two <= 64, so a group never straddles
+// a wavefront), and every lane quantizes its own one or two elements.
+// Threads [0, BH*D*kLanes): K, lane = token slot of the open group (fastest)
+// and channel; the rest: V, lane = byte column of the new token's row.
+// Same arithmetic as the general kernel (group_scale, stored_code), so the
+// bytes are the same.
+template <int BITS>
+__global__ __launch_bounds__(256) void append_one_kernel(const float* __restrict__ k_new,
+                                                         const float* __restrict__ v_new,
+                                                         long long BH, Layout L, int N,
+                                                         int lanes_log2,
+                                                         uint8_t* __restrict__ k_codes,
+                                                         float* __restrict__ k_scales,
+                                                         uint8_t* __restrict__ v_codes,
+                                                         float* __restrict__ v_scales,
+                                                         float* __restrict__ k_tail) {
+  constexpr int kStep = BITS == 4 ? 2 : 1;
+  constexpr unsigned kZero = Codec<BITS>::kQmaxInt;
+  const int lanes = 1 << lanes_log2;  // bytes (lanes) per group
+  const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int D = L.D, g = L.group;
+  const long long nk = BH * D * lanes;
+  const bool k_part = tid < nk;
+  const long long i = k_part ? tid : tid - nk;
+  const int slot = static_cast<int>(i & (lanes - 1));
+  const long long rest = i >> lanes_log2;
+  float x[kStep];
+  long long bh;
+  int d = 0, t0 = 0, f0 = 0;
+  bool live;
+  if (k_part) {
+    d = static_cast<int>(rest % D);
+    bh = rest / D;
+    const int g0 = N / g * g;  // the open group
+    t0 = g0 + kStep * slot;
+    live = true;
+    const float* tail = k_tail + bh * g * static_cast<long long>(D) + d;
+#pragma unroll
+    for (int e = 0; e < kStep; ++e) {
+      const int t = t0 + e;
+      x[e] = t < N ? tail[static_cast<long long>(t - g0) * D]
+                   : (t == N ? k_new[bh * D + d] : 0.0f);
+    }
+  } else {
+    const int cols = L.dpad / kStep;  // byte columns of one token row
+    f0 = kStep * static_cast<int>(rest % (cols >> lanes_log2) * lanes + slot);
+    bh = rest / (cols >> lanes_log2);
+    live = bh < BH;
+#pragma unroll
+    for (int e = 0; e < kStep; ++e)
+      x[e] = live && f0 + e < D ? v_new[bh * D + f0 + e] : 0.0f;
+  }
+  float amax = fabsf(x[0]);
+  if (BITS == 4) amax = fmaxf(amax, fabsf(x[kStep - 1]));
+  for (int o = lanes >> 1; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (!live) return;
+  const float s = group_scale<BITS>(amax);
+  if (k_part) {
+    const int g0 = N / g * g;
+    if (slot == 0) k_scales[bh * k_scales_per_head(L) + k_scale_index(L, g0, d)] = s;
+    if (t0 < L.nblocks * kBlockTokens) {
+      unsigned byte = t0 <= N ? stored_code<BITS>(x[0], s) : kZero;
+      if (BITS == 4) byte |= (t0 + 1 <= N ? stored_code<BITS>(x[1], s) : kZero) << 4;
+      k_codes[bh * k_code_bytes_per_head(L) + k_code_byte(L, t0, d)] = static_cast<uint8_t>(byte);
+    }
+    // the new token joins the tail unless it completes its group
+    if ((N + 1) % g != 0 && t0 <= N && N < t0 + kStep)
+      k_tail[(bh * g + N % g) * static_cast<long long>(D) + d] = x[N - t0];
+  } else {
+    if (slot == 0) v_scales[bh * v_scales_per_head(L) + v_scale_index(L, N, f0)] = s;
+    unsigned byte = f0 < D ? stored_code<BITS>(x[0], s) : kZero;
+    if (BITS == 4) byte |= (f0 + 1 < D ? stored_code<BITS>(x[1], s) : kZero) << 4;
+    v_codes[bh * v_code_bytes_per_head(L) + v_code_byte(L, N, f0)] = static_cast<uint8_t>(byte);
+  }
+}
+
 // The new open group's tokens [n1 - n1 % g, n1) into the tail, one thread
 // per (head, channel), after append_kernel has read the old tail.
 __global__ __launch_bounds__(256) void append_tail_kernel(const float* __restrict__ k_new,
@@ -541,6 +620,22 @@ hipError_t launch_append(const float* k_new, const float* v_new, int B, int H, i
                          uint8_t* v_codes, float* v_scales, float* k_tail, hipStream_t stream) {
   const long long BH = static_cast<long long>(B) * H;
   const Layout L = make_layout(cap, D, bits, group);
+  const int per_byte = bits == 4 ? 2 : 1;
+  const int lanes = group / per_byte;  // bytes per group
+  if (T == 1 && lanes <= 64 && (lanes & (lanes - 1)) == 0) {
+    int lanes_log2 = 0;
+    while ((1 << lanes_log2) < lanes) ++lanes_log2;
+    const long long threads = BH * D * lanes + BH * (L.dpad / per_byte);
+    if (bits == 4)
+      hipLaunchKernelGGL(append_one_kernel<4>, dim3(grid_for(threads)), dim3(256), 0, stream,
+                         k_new, v_new, BH, L, N, lanes_log2, k_codes, k_scales, v_codes, v_scales,
+                         k_tail);
+    else
+      hipLaunchKernelGGL(append_one_kernel<8>, dim3(grid_for(threads)), dim3(256), 0, stream,
+                         k_new, v_new, BH, L, N, lanes_log2, k_codes, k_scales, v_codes, v_scales,
+                         k_tail);
+    return hipGetLastError();
+  }
   const int n1 = N + T;
   const int ng = (n1 + group - 1) / group - N / group;  // token groups the new tokens touch
   // The tail is rewritten in the same launch unless the first touched group

@@ -103,3 +103,19 @@ def test_attend_cache_prefix(variant, hq, hkv, r):
             got_s = kvq.attend(qd, *cache[:4], n, 4, 32, num_splits=s, variant=variant,
                                capacity=cap)
             assert max_abs(host(got_s), want) <= TOL, (n, s)
+
+
+@pytest.mark.parametrize("bits,group,d", [
+    (4, 32, 128), (8, 32, 40), (8, 8, 24), (4, 8, 13), (4, 64, 128), (8, 64, 64), (4, 128, 32),
+    (8, 6, 24),                                   # 6 per group: the general kernel
+])
+def test_single_token_appends_bit_exact(bits, group, d):
+    """A run of one-token appends (the decode step's lane-parallel kernel
+    where the group's byte count is a power of two <= 64), checked after
+    every call, from an empty cache through several groups and blocks."""
+    cap = 75
+    k = np.random.default_rng(3).standard_normal((2, 3, cap, d), dtype=np.float32)
+    v = np.random.default_rng(4).standard_normal((2, 3, cap, d), dtype=np.float32)
+    announce(f"single-token appends {bits}b g{group} d={d}")
+    for n, cache in _grow(k, v, cap, bits, group, [1] * cap):
+        _check_state(k, v, n, cap, bits, group, cache)

@@ -276,7 +276,7 @@ def test_attend_mfma32_ragged_and_gqa_shapes(hq, hkv, r, n):
 @pytest.mark.parametrize("dist", ["clean", "early", "late"])
 @pytest.mark.parametrize("scale_k", [False, True])
 def test_attend_mfma32_peaky_and_channel_scaled(dist, scale_k):
-    """C5-like heads (8 GQA heads x 4 queries per KV head) with biased keys and
+    """Heads shaped like the 32768-token workload (8 GQA heads x 4 queries per KV head), biased keys and
     log-uniform K channel scales."""
     w = Workload("peaky32", 2, 16, 2, 4, 4096, 128, ((4, 32),), k_channel_scale=scale_k)
     q, k, v = make_qkv(w, 7, dist)

@@ -95,7 +95,7 @@ def test_decode_loop_with_window():
 
 
 def test_window_full_size_sampled():
-    """The C4-size mixed cache bench.py times (the last 64 tokens float32),
+    """The 8 x 4096-token mixed cache bench.py times (the last 64 tokens float32),
     sampled KV heads against the oracle."""
     from workloads import WORKLOADS
     w = WORKLOADS["gqa_n4096"]

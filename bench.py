@@ -159,7 +159,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by (batch, KV head) with no exchange; see the design notes)",
+              "(the attention shards by (batch, KV head) with no exchange; one GPU shows its share)",
               file=sys.stderr)
         sys.exit(2)
 

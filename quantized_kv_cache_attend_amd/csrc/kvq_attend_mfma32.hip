@@ -350,9 +350,13 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
   }
 }
 
-// kCausal: a causal chunk (row r is query r % R at position N - R + r % R);
-// every block runs the masked path (a second, unmasked copy of the block
-// code in the loop spills registers).
+// kCausal: a causal chunk (row r is query r % R at position pos_end - R +
+// r % R).  Only tokens past pos_end - R can be masked; they lie in at most
+// two consecutive blocks (R <= 32), which belong to different waves and are
+// each the last block of its wave.  So the masked block of a wave is the one
+// it attends first, and its loop runs the unmasked path: every row reads
+// every token there, which also gives a row still without a legal key its
+// first one.
 template <bool kCausal>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attend_mfma_r32_kernel(AttendProblem p) {
@@ -400,7 +404,8 @@ attend_mfma_r32_kernel(AttendProblem p) {
   // the wave that owns it attends it first.  Its loads go out before the
   // query rows are staged.
   const bool active = b_first < b_end;
-  const bool partial = (p.N % kBlockTokens) != 0 && b_last == (p.N - 1) / kBlockTokens;
+  const bool partial = ((p.N % kBlockTokens) != 0 && b_last == (p.N - 1) / kBlockTokens) ||
+                       (kCausal && (b_last + 1) * kBlockTokens - 1 > p.pos_end - p.R);
   const int first = partial ? b_last : b_first;
   const int loop_begin = partial ? b_first : b_first + kW;
   const int loop_end = partial ? b_last - kW : b_last;  // inclusive
@@ -479,8 +484,8 @@ attend_mfma_r32_kernel(AttendProblem p) {
                                   loop_begin <= loop_end ? loop_begin : first, lo, us_row, qk,
                                   lim);
     for (int b = loop_begin; b <= loop_end; b += kW)
-      attend_block32<kCausal, kCausal>(sm, br, b * kBlockTokens, t_end, cc, st, h,
-                                       min(b + kW, loop_end), lo, us_row, qk, lim);
+      attend_block32<false, false>(sm, br, b * kBlockTokens, t_end, cc, st, h,
+                                   min(b + kW, loop_end), lo, us_row, qk, lim);
   }
   st.z[0] = qblock_sum(st.z[0]);
   st.z[1] = qblock_sum(st.z[1]);

@@ -113,33 +113,40 @@ struct State32 {
   bool live;
 };
 
-// Packed fp16 pair of exact residuals a.x*b.x - h.lo, a.y*b.y - h.hi, each
-// computed by one fused multiply-add and rounded once to fp16
-// (v_fma_mixlo_f16 / v_fma_mixhi_f16 widen the fp16 operand internally).
-__device__ __forceinline__ unsigned residual_pair(float a0, float b0, float a1, float b1,
-                                                  unsigned h) {
-  unsigned d;
-  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,0,1]" : "=v"(d) : "v"(a0), "v"(b0), "v"(h));
-  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
-      : "+v"(d)
-      : "v"(a1), "v"(b1), "v"(h));
-  return d;
-}
-
 // fp16 hi/lo operands of the 8 products x[j] = a[j] * b[j], j in k-slot
 // order: hi = fp16(fp16(a) * fp16(b)) (one packed multiply per pair), lo =
-// the exact residual x - hi rounded to fp16.  a, b are float32 with their
-// fp16 (round-toward-zero) pairs a16, b16 precomputed in the same order.
+// the residual x - hi, from one fused multiply-add per value rounded once to
+// fp16 (v_fma_mixlo_f16 / v_fma_mixhi_f16 widen the fp16 hi internally).
+// a, b are float32 with their fp16 (round-toward-zero) pairs a16, b16
+// precomputed in the same order.  The eight mix instructions are one asm
+// statement with early-clobber outputs (no output shares a register with an
+// input), ending with s_nop 1: the compiler's hazard tracking does not see
+// inside inline asm, and a matrix-core instruction reading a VGPR that a
+// VALU instruction just wrote needs two wait states.
 __device__ __forceinline__ void product_hilo(const float a[8], const float b[8],
                                              const half2_t a16[4], const half2_t b16[4],
                                              half8_t& hi, half8_t& lo) {
   u32x4 h, l;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const unsigned hp = __builtin_bit_cast(unsigned, a16[i] * b16[i]);
-    h[i] = hp;
-    l[i] = residual_pair(a[2 * i], b[2 * i], a[2 * i + 1], b[2 * i + 1], hp);
-  }
+  for (int i = 0; i < 4; ++i) h[i] = __builtin_bit_cast(unsigned, a16[i] * b16[i]);
+  unsigned l0, l1, l2, l3;
+  asm("v_fma_mixlo_f16 %0, %4, %5, -%20 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %6, %7, -%20 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %1, %8, %9, -%21 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %10, %11, -%21 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %2, %12, %13, -%22 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %2, %14, %15, -%22 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %3, %16, %17, -%23 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %3, %18, %19, -%23 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3)
+      : "v"(a[0]), "v"(b[0]), "v"(a[1]), "v"(b[1]), "v"(a[2]), "v"(b[2]), "v"(a[3]), "v"(b[3]),
+        "v"(a[4]), "v"(b[4]), "v"(a[5]), "v"(b[5]), "v"(a[6]), "v"(b[6]), "v"(a[7]), "v"(b[7]),
+        "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]));
+  l[0] = l0;
+  l[1] = l1;
+  l[2] = l2;
+  l[3] = l3;
   hi = __builtin_bit_cast(half8_t, h);
   lo = __builtin_bit_cast(half8_t, l);
 }
@@ -152,7 +159,7 @@ __device__ __forceinline__ half2_t pk16(float x, float y) {
 // score row 16t + n, the tokens after its query's position lim[t], and keep
 // rows that have seen no legal key at m = -inf (exponents then taken
 // against 0, so (-inf) - (-inf) is never formed).
-template <bool kMasked, bool kCausal>
+template <int kTiles, bool kMasked, bool kCausal>
 __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0, int t_end,
                                                const CodeConsts& cc, State32& st,
                                                const Head32& h, int next, const Lanes32& lo,
@@ -194,7 +201,7 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < kTiles; ++t) {
           st.acc[g][t][0] *= f;
           st.acc[g][t][1] *= f;
         }
@@ -232,7 +239,7 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
     for (int i = 0; i < 4; ++i) sk16[i] = pk16(sk[2 * i], sk[2 * i + 1]);
     half8_t bh[2], bl[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kTiles; ++t) {
       half2_t q16[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) q16[i] = pk16(qk[t][ks][2 * i], qk[t][ks][2 * i + 1]);
@@ -242,7 +249,7 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
     codes_to_half(br.k[ks], cc, alo, ahi);
     br.k[ks] = buf_b64(h.kc, lo.k_off + ks * 512, next * kBB);  // next block's k-step
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kTiles; ++t) {
       se[t] = mfma(alo, bh[t], se[t]);
       se[t] = mfma(alo, bl[t], se[t]);
       so[t] = mfma(ahi, bh[t], so[t]);
@@ -253,7 +260,7 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
   // raw[t][j]: row 16t + n, token 8q + j, in units of 2^Sq(row) (x kf)
   float raw[2][8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       raw[t][2 * i] = se[t][i];
@@ -269,17 +276,17 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
   const float us[2] = {us0, us1};
   float lmx[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < kTiles; ++t)
     lmx[t] = fmaxf(fmaxf(fmaxf(raw[t][0], raw[t][1]), fmaxf(raw[t][2], raw[t][3])),
                    fmaxf(fmaxf(raw[t][4], raw[t][5]), fmaxf(raw[t][6], raw[t][7]))) * us[t];
 
   // Move the reference of rows that overshoot it by more than kLazy (a
   // wave-uniform decision).
   if (!st.live || __builtin_amdgcn_ballot_w64(lmx[0] > st.m[0] + kLazy ||
-                                              lmx[1] > st.m[1] + kLazy) != 0) {
+                                              (kTiles > 1 && lmx[1] > st.m[1] + kLazy)) != 0) {
     float alpha[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kTiles; ++t) {
       const float mx = qblock_max(lmx[t]);  // row max over the block (finite unless kCausal)
       const float m_new = st.live ? (mx > st.m[t] + kLazy ? mx : st.m[t]) : mx;
       alpha[t] = st.live ? fast_exp2(st.m[t] - m_new) : 0.0f;
@@ -292,10 +299,10 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
       // owned by lanes n = 4q + i: exchange through this wave's LDS slot.
       if (q == 0) {
         sm.alp[wave][n] = alpha[0];
-        sm.alp[wave][16 + n] = alpha[1];
+        if (kTiles > 1) sm.alp[wave][16 + n] = alpha[1];
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < kTiles; ++t) {
         const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.alp[wave][16 * t + 4 * q]);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -311,7 +318,7 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
   float pk[2][8];
   half2_t p16[2][4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kTiles; ++t) {
     const float shift = kCausal && st.m[t] == -INFINITY ? 0.0f : -st.m[t];
     float pt[8];
 #pragma unroll
@@ -336,12 +343,12 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
     for (int i = 0; i < 4; ++i) sv16[i] = pk16(sv[2 * i], sv[2 * i + 1]);
     half8_t ah[2], al[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) product_hilo(pk[t], sv, p16[t], sv16, ah[t], al[t]);
+    for (int t = 0; t < kTiles; ++t) product_hilo(pk[t], sv, p16[t], sv16, ah[t], al[t]);
     half8_t be, bo;
     codes_to_half(br.v[g], cc, be, bo);
     br.v[g] = buf_b64(h.vc, lo.v_off + g * 128, next * kBB);  // next block's group
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kTiles; ++t) {
       st.acc[g][t][0] = mfma(ah[t], be, st.acc[g][t][0]);
       st.acc[g][t][0] = mfma(al[t], be, st.acc[g][t][0]);
       st.acc[g][t][1] = mfma(ah[t], bo, st.acc[g][t][1]);
@@ -350,14 +357,15 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
   }
 }
 
-// kCausal: a causal chunk (row r is query r % R at position pos_end - R +
+// kTiles: 16-row tiles of query rows (1 for up to 16 rows per KV head, 2
+// for up to 32).  kCausal: a causal chunk (row r is query r % R at position pos_end - R +
 // r % R).  Only tokens past pos_end - R can be masked; they lie in at most
 // two consecutive blocks (R <= 32), which belong to different waves and are
 // each the last block of its wave.  So the masked block of a wave is the one
 // it attends first, and its loop runs the unmasked path: every row reads
 // every token there, which also gives a row still without a legal key its
 // first one.
-template <bool kCausal>
+template <int kTiles, bool kCausal>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attend_mfma_r32_kernel(AttendProblem p) {
   __shared__ Smem32 sm;
@@ -446,12 +454,12 @@ attend_mfma_r32_kernel(AttendProblem p) {
     if ((tid & 7) == 0) sm.qus[r] = __builtin_ldexpf(1.0f, -sq);
   }
   __syncthreads();
-  const float us_row[2] = {sm.qus[n], sm.qus[16 + n]};
+  const float us_row[2] = {sm.qus[n], kTiles > 1 ? sm.qus[16 + n] : 1.0f};
   // This lane's q values for the whole kernel (rows 16t + n, channels
   // 32 ks + 8q + (0..7), k-slot order), kept in registers.
   float qk[2][4][8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < kTiles; ++t)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const float* qrow = &sm.u.qs[16 * t + n][ks * 32 + q * 8];
@@ -474,21 +482,21 @@ attend_mfma_r32_kernel(AttendProblem p) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) st.acc[g][t][0] = st.acc[g][t][1] = zero4;
+      for (int t = 0; t < kTiles; ++t) st.acc[g][t][0] = st.acc[g][t][1] = zero4;
   }
 
   // Causal limit of this lane's score rows 16t + n.
   const int lim[2] = {p.pos_end - p.R + n % p.R, p.pos_end - p.R + (16 + n) % p.R};
   if (active) {
-    attend_block32<true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
+    attend_block32<kTiles, true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
                                   loop_begin <= loop_end ? loop_begin : first, lo, us_row, qk,
                                   lim);
     for (int b = loop_begin; b <= loop_end; b += kW)
-      attend_block32<false, false>(sm, br, b * kBlockTokens, t_end, cc, st, h,
+      attend_block32<kTiles, false, false>(sm, br, b * kBlockTokens, t_end, cc, st, h,
                                    min(b + kW, loop_end), lo, us_row, qk, lim);
   }
   st.z[0] = qblock_sum(st.z[0]);
-  st.z[1] = qblock_sum(st.z[1]);
+  if (kTiles > 1) st.z[1] = qblock_sum(st.z[1]);
 
   // ---- merge the waves: two at a time through LDS -------------------------
   // thread -> (row r = tid >> 3, features f0 + 32 i + (0..3), f0 = 4 (tid & 7))
@@ -498,9 +506,9 @@ attend_mfma_r32_kernel(AttendProblem p) {
   __syncthreads();  // every wave is done with q (aliased by wu)
   if (q == 0) {
     sm.wm[wave][n] = st.m[0];
-    sm.wm[wave][16 + n] = st.m[1];
+    sm.wm[wave][16 + n] = kTiles > 1 ? st.m[1] : -INFINITY;  // rows 16..31: none with one tile
     sm.wz[wave][n] = st.z[0];
-    sm.wz[wave][16 + n] = st.z[1];
+    sm.wz[wave][16 + n] = kTiles > 1 ? st.z[1] : 0.0f;
   }
   float M = -INFINITY, Z = 0.0f;
   float U[16];
@@ -512,7 +520,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < kTiles; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float2 u2;
@@ -565,10 +573,18 @@ attend_mfma_r32_kernel(AttendProblem p) {
 
 hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
-  if (p.causal)
-    hipLaunchKernelGGL(attend_mfma_r32_kernel<true>, dim3(grid), dim3(kT), 0, stream, p);
-  else
-    hipLaunchKernelGGL(attend_mfma_r32_kernel<false>, dim3(grid), dim3(kT), 0, stream, p);
+  // One 16-row tile when the KV head has at most 16 query rows.
+  if (p.rows <= 16) {
+    if (p.causal)
+      hipLaunchKernelGGL((attend_mfma_r32_kernel<1, true>), dim3(grid), dim3(kT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attend_mfma_r32_kernel<1, false>), dim3(grid), dim3(kT), 0, stream, p);
+  } else {
+    if (p.causal)
+      hipLaunchKernelGGL((attend_mfma_r32_kernel<2, true>), dim3(grid), dim3(kT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attend_mfma_r32_kernel<2, false>), dim3(grid), dim3(kT), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

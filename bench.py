@@ -490,6 +490,35 @@ def main():
         log(f"[bench] mixed cache (last {win} tokens float32): {win_us:.1f} us")
         del blocker, kpre, vpre, kw, vw, ws_w
 
+        # The other formats on the same cache shape (the general kernel):
+        # 8-bit group 32 and 4-bit group 8, KV GB/s of their own byte counts.
+        fmt = {}
+        for fb, fg in ((8, 32), (4, 8)):
+            fkc, fks = kvq.pack_k(kd, fb, fg)
+            fvc, fvs = kvq.pack_v(vd, fb, fg)
+            fbytes = kv_bytes(w, fb, fg)
+
+            def fcall():
+                kvq.attend(qd, fkc, fks, fvc, fvs, w.N, fb, fg, workspace=ws, out=out,
+                           num_splits=splits)
+            fcall()
+            torch.cuda.synchronize()
+            f0 = torch.cuda.Event(enable_timing=True)
+            f1 = torch.cuda.Event(enable_timing=True)
+            nf = 20
+            f0.record(stream)
+            for _ in range(nf):
+                fcall()
+            f1.record(stream)
+            torch.cuda.synchronize()
+            fus = f0.elapsed_time(f1) * 1e3 / nf
+            fmt[f"{fb}bit_g{fg}"] = {"us": round(fus, 2), "kv_bytes": fbytes,
+                                     "kv_gbs": round(fbytes / (fus * 1e-6) / 1e9, 1)}
+            del fkc, fks, fvc, fvs
+        extra["other_formats"] = fmt
+        log("[bench] other formats (general kernel): " +
+            ", ".join(f"{k} {v['us']:.1f} us ({v['kv_gbs']:.0f} GB/s)" for k, v in fmt.items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host ...")

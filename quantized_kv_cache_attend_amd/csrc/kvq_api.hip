@@ -172,7 +172,9 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(static_cast<float>(D));
   p->qscale = scale * kLog2e;
   p->splits = splits;
-  p->tokens_per_split = static_cast<int>((N + splits - 1) / splits);
+  p->tokens_per_split =
+      static_cast<int>(round_up((static_cast<long long>(N) + splits - 1) / splits, kBlockTokens));
+  p->codes_aligned = bits != 32 && aligned(k, 4) && aligned(v, 4);
   char* ws = static_cast<char*>(workspace);
   p->part_m = splits > 1 ? reinterpret_cast<float*>(ws + wl.m_off) : nullptr;
   p->part_z = splits > 1 ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;

@@ -53,6 +53,88 @@ __device__ __forceinline__ float decode_v(const AttendProblem& p, const Layout& 
   return static_cast<float>(c) * p.v_scales[bh * v_scales_per_head(L) + v_scale_index(L, n, f)];
 }
 
+// Tokens of 32-token block blk (t0 = 32 blk) into sK / sV, reading the
+// block's code bytes as 4-byte words (every thread decodes whole words: K,
+// one channel quad of two token columns; V, one token quad of one byte
+// column): the packed tokens below min(t_end, t_win) decoded, the tokens of
+// a recent-token window [t_win, t_end) left alone (another loop writes
+// them), every other token 0.  Same values as decode_k / decode_v:
+// fl32((stored - qmax) * scale).
+// ks_row[tl]: offset of token t0 + tl's K scale row ((t0 + tl) / group * D),
+// fgrp[f]: value group of feature f < D (f / group); both precomputed in LDS
+// so the decode does no integer division.
+template <int D, int SRC>
+__device__ __forceinline__ void decode_block(const AttendProblem& p, const Layout& L, long long bh,
+                                             int blk, int t_end, int t_win, float (*sK)[D + 1],
+                                             float (*sV)[D], const int* ks_row,
+                                             const int* fgrp) {
+  constexpr int kQmax = SRC == 4 ? 7 : 127;
+  constexpr int kKcols = kTile * SRC / 8;  // K byte columns per channel octet
+  const int t0 = blk * kTile;
+  const int t_pk = min(t_end, t_win);
+  auto window = [&](int tl) { return t0 + tl >= t_win && t0 + tl < t_end; };
+  const int tid = threadIdx.x;
+  const unsigned* kw = reinterpret_cast<const unsigned*>(
+      p.k_codes + bh * k_code_bytes_per_head(L) + static_cast<long long>(blk) * L.kblock_bytes);
+  const float* ks = p.k_scales + bh * k_scales_per_head(L);
+  for (int w = tid; w < L.kblock_bytes / 4; w += kThreads) {
+    const unsigned word = kw[w];
+    const int run = w >> 1;  // 8-byte run (octet o, column j)
+    const int o = run / kKcols, j = run % kKcols;
+    const int d0 = 8 * o + 4 * (w & 1);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int d = d0 + b;
+      if (d >= D) break;
+      const unsigned byte = (word >> (8 * b)) & 255u;
+      if (SRC == 4) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int tl = 2 * j + h;
+          if (window(tl)) continue;
+          const int c = static_cast<int>(h ? byte >> 4 : byte & 15u) - kQmax;
+          sK[tl][d] = t0 + tl < t_pk ? static_cast<float>(c) * ks[ks_row[tl] + d] : 0.0f;
+        }
+      } else {
+        if (window(j)) continue;
+        const int c = static_cast<int>(byte) - kQmax;
+        sK[j][d] = t0 + j < t_pk ? static_cast<float>(c) * ks[ks_row[j] + d] : 0.0f;
+      }
+    }
+  }
+  const unsigned* vw = reinterpret_cast<const unsigned*>(
+      p.v_codes + bh * v_code_bytes_per_head(L) + static_cast<long long>(blk) * L.vblock_bytes);
+  const float* vs = p.v_scales + bh * v_scales_per_head(L) +
+                    static_cast<long long>(blk) * L.vgroups * kTile;  // [group][32 tokens]
+  for (int w = tid; w < L.vblock_bytes / 4; w += kThreads) {
+    const unsigned word = vw[w];
+    const int run = w >> 1;  // 8-byte run (token octet o < 4, column f)
+    const int o = (run >= L.vcols) + (run >= 2 * L.vcols) + (run >= 3 * L.vcols);
+    const int col = run - o * L.vcols;
+    const int tq = 8 * o + 4 * (w & 1);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int tl = tq + b;
+      if (window(tl)) continue;
+      const bool live = t0 + tl < t_pk;
+      const unsigned byte = (word >> (8 * b)) & 255u;
+      if (SRC == 4) {
+        const int f = 2 * col;
+        if (f >= D) continue;
+        const float s = live ? vs[fgrp[f] * kTile + tl] : 0.0f;
+        sV[tl][f] = live ? static_cast<float>(static_cast<int>(byte & 15u) - kQmax) * s : 0.0f;
+        if (f + 1 < D)
+          sV[tl][f + 1] = live ? static_cast<float>(static_cast<int>(byte >> 4) - kQmax) * s : 0.0f;
+      } else {
+        if (col >= D) continue;
+        sV[tl][col] = live ? static_cast<float>(static_cast<int>(byte) - kQmax) *
+                                 vs[fgrp[col] * kTile + tl]
+                           : 0.0f;
+      }
+    }
+  }
+}
+
 template <int D, int SRC>
 __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) {
   constexpr int kAcc = kMaxRows * D / kThreads;  // u accumulators per thread
@@ -61,6 +143,8 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   __shared__ float sV[kTile][D];
   __shared__ float sP[kMaxRows][kTile + 1];
   __shared__ float sM[kMaxRows], sZ[kMaxRows], sA[kMaxRows];
+  __shared__ int sKsRow[kTile];     // K scale row offset of each token of the tile
+  __shared__ int sFgrp[D];          // value group of each feature below D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -79,6 +163,8 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
     sM[r] = -INFINITY;
     sZ[r] = 0.0f;
   }
+  if (SRC != 32)
+    for (int f = tid; f < D; f += kThreads) sFgrp[f] = f / p.group;
   float acc[kAcc];
 #pragma unroll
   for (int i = 0; i < kAcc; ++i) acc[i] = 0.0f;
@@ -86,16 +172,34 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
 
   for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
     const int tn = min(kTile, t_end - t0);
-    // Decode the tile.  K: the 8 channels of an octet fastest, then the
-    // token (one 8-byte run of the block layout per token column); V: the
-    // feature fastest.
-    for (int i = tid; i < kTile * D; i += kThreads) {
-      const int j = (i >> 3) % kTile, d = (i / (8 * kTile)) * 8 + (i & 7);
-      sK[j][d] = j < tn ? decode_k<SRC>(p, L, bh, d, t0 + j) : 0.0f;
-    }
-    for (int i = tid; i < kTile * D; i += kThreads) {
-      const int f = i % D, j = i / D;
-      sV[j][f] = j < tn ? decode_v<SRC>(p, L, bh, t0 + j, f) : 0.0f;
+    const int t_win = p.N - p.W;  // first token of a recent-token window (N without one)
+    if (SRC != 32 && p.codes_aligned && t0 < t_win) {
+      // Tiles start on block boundaries: decode the packed block word by
+      // word, then the window's float32 rows of the tile (disjoint tokens).
+      if (tid < kTile) sKsRow[tid] = (t0 + tid) / p.group * D;
+      __syncthreads();
+      decode_block<D, SRC>(p, L, bh, t0 / kTile, t_end, t_win, sK, sV, sKsRow, sFgrp);
+      if (t0 + kTile > t_win) {
+        for (int i = tid; i < kTile * D; i += kThreads) {
+          const int j = i / D, d = i % D;
+          if (t0 + j >= t_win && j < tn) {
+            sK[j][d] = decode_k<SRC>(p, L, bh, d, t0 + j);
+            sV[j][d] = decode_v<SRC>(p, L, bh, t0 + j, d);
+          }
+        }
+      }
+    } else {
+      // Element by element.  K: the 8 channels of an octet fastest, then the
+      // token (one 8-byte run of the block layout per token column); V: the
+      // feature fastest.
+      for (int i = tid; i < kTile * D; i += kThreads) {
+        const int j = (i >> 3) % kTile, d = (i / (8 * kTile)) * 8 + (i & 7);
+        sK[j][d] = j < tn ? decode_k<SRC>(p, L, bh, d, t0 + j) : 0.0f;
+      }
+      for (int i = tid; i < kTile * D; i += kThreads) {
+        const int f = i % D, j = i / D;
+        sV[j][f] = j < tn ? decode_v<SRC>(p, L, bh, t0 + j, f) : 0.0f;
+      }
     }
     __syncthreads();
 
@@ -150,6 +254,9 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
     // (here) are rescaled by the same alpha.
 #pragma unroll
     for (int i = 0; i < kAcc; ++i) {
+      // Slots past rows * D hold nothing for any thread: leave the loop (a
+      // uniform exit, so the unrolled slots of the few-row case cost nothing).
+      if (i * kThreads >= rows * D) break;
       const int idx = tid + i * kThreads;
       if (idx < rows * D) {
         const int r = idx / D, f = idx % D;

@@ -41,7 +41,8 @@ struct AttendProblem {
   int bits, group;         // 4/8 and group; bits == 32 marks the float32 cache
   float qscale;            // sm_scale * log2(e)
   int splits;              // >= 1
-  int tokens_per_split;    // ceil(N / splits), rounded as the kernel requires
+  int tokens_per_split;    // ceil(N / splits), rounded up to whole 32-token blocks
+  int codes_aligned;       // both code arrays 4-byte aligned (word loads of whole blocks)
   // Workspace views (valid when splits > 1).
   float* part_m;           // [splits][B*Hkv*rows]
   float* part_z;           // [splits][B*Hkv*rows]

@@ -490,34 +490,59 @@ def main():
         log(f"[bench] mixed cache (last {win} tokens float32): {win_us:.1f} us")
         del blocker, kpre, vpre, kw, vw, ws_w
 
-        # The other formats on the same cache shape (the general kernel):
-        # 8-bit group 32 and 4-bit group 8, KV GB/s of their own byte counts.
+        # The other formats on the same cache shape: 8-bit group 32 (the
+        # matrix-core kernels) and 4-bit group 8 (the general kernel), KV GB/s
+        # of their own byte counts, timed like the main step (rotating cache
+        # copies past the Infinity Cache, launched the same way).
         fmt = {}
         for fb, fg in ((8, 32), (4, 8)):
-            fkc, fks = kvq.pack_k(kd, fb, fg)
-            fvc, fvs = kvq.pack_v(vd, fb, fg)
             fbytes = kv_bytes(w, fb, fg)
+            fcopies = max(2, math.ceil(3 * MALL_BYTES / fbytes))
+            fk0, fks0 = kvq.pack_k(kd, fb, fg)
+            fv0, fvs0 = kvq.pack_v(vd, fb, fg)
+            fcaches = [(fk0, fks0, fv0, fvs0)] + [tuple(t.clone() for t in (fk0, fks0, fv0, fvs0))
+                                                  for _ in range(fcopies - 1)]
+            fout = torch.empty_like(qd)
 
-            def fcall():
-                kvq.attend(qd, fkc, fks, fvc, fvs, w.N, fb, fg, workspace=ws, out=out,
-                           num_splits=splits)
-            fcall()
+            def fpass():
+                for c in fcaches:
+                    kvq.attend(qd, *c, w.N, fb, fg, workspace=ws, out=fout, num_splits=splits)
+            fpass()
             torch.cuda.synchronize()
+            fref = fout.clone()
+            run_f = fpass
+            if args.launch == "graph":
+                fgraph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(fgraph):
+                    fpass()
+                torch.cuda.synchronize()
+                fout.fill_(float("nan"))
+                fgraph.replay()
+                torch.cuda.synchronize()
+                if not torch.equal(fout, fref):
+                    raise RuntimeError(f"{fb}-bit g{fg} graph replay differs from the eager result")
+                run_f = fgraph.replay
+            n_f = max(2, 400 // fcopies)
             f0 = torch.cuda.Event(enable_timing=True)
             f1 = torch.cuda.Event(enable_timing=True)
-            nf = 20
             f0.record(stream)
-            for _ in range(nf):
-                fcall()
+            for _ in range(n_f):
+                run_f()
             f1.record(stream)
             torch.cuda.synchronize()
-            fus = f0.elapsed_time(f1) * 1e3 / nf
+            fus = f0.elapsed_time(f1) * 1e3 / (n_f * fcopies)
             fmt[f"{fb}bit_g{fg}"] = {"us": round(fus, 2), "kv_bytes": fbytes,
-                                     "kv_gbs": round(fbytes / (fus * 1e-6) / 1e9, 1)}
-            del fkc, fks, fvc, fvs
+                                     "kv_gbs": round(fbytes / (fus * 1e-6) / 1e9, 1),
+                                     "hbm_frac": round(fbytes / (fus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                     "kernel": "matrix-core" if (fb, fg) == (8, 32) else "general",
+                                     "cache_copies": fcopies}
+            del fcaches, fk0, fks0, fv0, fvs0, fout
+            if args.launch == "graph":
+                del fgraph
         extra["other_formats"] = fmt
-        log("[bench] other formats (general kernel): " +
-            ", ".join(f"{k} {v['us']:.1f} us ({v['kv_gbs']:.0f} GB/s)" for k, v in fmt.items()))
+        log("[bench] other formats: " +
+            ", ".join(f"{k} ({v['kernel']}) {v['us']:.1f} us ({v['kv_gbs']:.0f} GB/s)"
+                      for k, v in fmt.items()))
 
     cpu = None
     if not args.no_cpu_baseline:

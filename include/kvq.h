@@ -77,8 +77,8 @@ typedef enum kvq_status {
 typedef enum kvq_variant {
   KVQ_VARIANT_AUTO = 0,  /* what kvq_attend uses */
   KVQ_VARIANT_VALU = 1,  /* any supported format: decode a tile to float32 in LDS */
-  KVQ_VARIANT_MFMA = 2   /* 4-bit, group 32, D = 128, <= 32 query rows per KV head:
-                            fp16 matrix cores on exact codes */
+  KVQ_VARIANT_MFMA = 2   /* 4- or 8-bit, group 32, D = 128, <= 32 query rows per KV
+                            head: fp16 matrix cores on exact codes */
 } kvq_variant;
 
 /* Flags of kvq_attend_cache. */
@@ -168,8 +168,8 @@ kvq_status kvq_dequant_v(const uint8_t* codes, const float* scales, int B, int H
  *   each head reads only tokens j <= N-R+r; masked tokens enter neither the
  *   running max nor the sums, and a query with no legal key (N-R+r < 0)
  *   gets zeros ([RL] "why FlashAttention need not keep the whole heat
- *   map").  With R == 1 the flag changes nothing.  With R > 1 it runs on the
- *   general kernel (KVQ_VARIANT_MFMA returns KVQ_ERR_UNSUPPORTED). */
+ *   map").  With R == 1 the flag changes nothing.  Every kernel family
+ *   takes the flag. */
 kvq_status kvq_cache_clear(int B, int H, int capacity, int D, int bits, int group,
                            uint8_t* k_codes, float* k_scales, uint8_t* v_codes, float* v_scales,
                            void* stream);
@@ -210,10 +210,10 @@ kvq_status kvq_attend(const float* q, const uint8_t* k_codes, const float* k_sca
                       float* out, void* stream);
 
 /* Same contract as kvq_attend with an explicit kernel family.
- * KVQ_VARIANT_MFMA returns KVQ_ERR_UNSUPPORTED unless bits == 4,
- * group == 32, D == 128, (Hq/Hkv)*R <= 32, N <= 2^25 - 32 and q and all four
- * cache arrays are 16-byte aligned; KVQ_VARIANT_AUTO picks it whenever those
- * hold. */
+ * KVQ_VARIANT_MFMA returns KVQ_ERR_UNSUPPORTED unless bits is 4 or 8,
+ * group == 32, D == 128, (Hq/Hkv)*R <= 32, N <= 2^25 - 32 (4-bit) or
+ * N <= 2^24 - 32 (8-bit) and q and all four cache arrays are 16-byte
+ * aligned; KVQ_VARIANT_AUTO picks it whenever those hold. */
 kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,
                               const uint8_t* v_codes, const float* v_scales,
                               int B, int Hq, int Hkv, int R, int N, int D, int bits, int group,

@@ -184,12 +184,14 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
 }
 
 // The matrix-core kernels address a head's arrays with 32-bit buffer
-// offsets below 2^31: fewer than 2^20 blocks of 2 KB per head.
+// offsets below 2^31: fewer than 2^20 blocks of 2 KB (4-bit) or 2^19 blocks
+// of 4 KB (8-bit) per head.
 constexpr int kMfmaMaxN = (1 << 25) - kBlockTokens;
+constexpr int kMfmaMaxN8 = (1 << 24) - kBlockTokens;
 
 bool mfma_eligible(const AttendProblem& p) {
-  return p.bits == 4 && p.group == 32 && p.D == 128 && p.rows <= kMfma32MaxRows &&
-         p.cap <= kMfmaMaxN &&
+  return (p.bits == 4 || p.bits == 8) && p.group == 32 && p.D == 128 &&
+         p.rows <= kMfma32MaxRows && p.cap <= (p.bits == 8 ? kMfmaMaxN8 : kMfmaMaxN) &&
          aligned(p.q, 16) && aligned(p.k_codes, 16) && aligned(p.v_codes, 16) &&
          aligned(p.k_scales, 16) && aligned(p.v_scales, 16);
 }
@@ -393,9 +395,9 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
     case KVQ_VARIANT_MFMA:
       if (!mfma_eligible(p))
         return fail(KVQ_ERR_UNSUPPORTED,
-                    "matrix-core kernels need bits=4, group=32, D=128, <= %d query rows per "
-                    "KV head, N <= %d and 16-byte aligned q and cache arrays", kMfma32MaxRows,
-                    kMfmaMaxN);
+                    "matrix-core kernels need bits=4|8, group=32, D=128, <= %d query rows per "
+                    "KV head, N <= %d (4-bit) or %d (8-bit) and 16-byte aligned q and cache "
+                    "arrays", kMfma32MaxRows, kMfmaMaxN, kMfmaMaxN8);
       return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
     default:
       return fail(KVQ_ERR_INVALID, "unknown variant %d", variant);

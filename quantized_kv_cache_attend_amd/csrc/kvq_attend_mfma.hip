@@ -80,7 +80,9 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kOut = 4 * 128;            // outputs of one KV head: 4 rows x D
 constexpr int kSlots = kOut / kThreads > 0 ? kOut / kThreads : 1;  // outputs per thread
 constexpr int kD = 128;
-constexpr int kBB = 2048;           // K or V code bytes of one 32-token block
+// K or V code bytes of one 32-token block (4-bit: 2 KB, 8-bit: 4 KB)
+template <int kBits>
+constexpr int kBB = 512 * kBits;
 constexpr int kBS = 128;            // K or V scales of one block
 constexpr float kLazy = 6.0f;       // reference moves only past m + kLazy
 // V prescale: max V scale * 2^Sv is set to [2^8, 2^9) and kept while it
@@ -101,9 +103,10 @@ struct alignas(16) Smem {
 };
 
 // One block's operands, as loaded by one lane.
+template <int kBits>
 struct BlockRegs {
-  i32x2 k[4];   // K codes, k-step 0..3
-  i32x2 v[4];   // V codes, feature group 0..3
+  typename CodeOps<kBits>::words k[4];  // K codes, k-step 0..3
+  typename CodeOps<kBits>::words v[4];  // V codes, feature group 0..3
   f32x4 ks[2];  // K scales of channels d0 .. d0+7 (precompute slot)
   f32x4 vs[2];  // V scales of value group n >> 2, tokens 8q .. 8q+7
 };
@@ -113,15 +116,24 @@ struct Head {
 };
 
 // This lane's byte offsets inside a block (precompute slot d0 = channels
-// 32 ((lane >> 2) & 3) + 8 (lane & 3) .. +7 for the K scales).
+// 32 ((lane >> 2) & 3) + 8 (lane & 3) .. +7 for the K scales).  A lane reads
+// 2 * kBits code bytes per k-step (K) or feature group (V): channels
+// 32 ks + 8q .. +7 of tokens 2n, 2n + 1, and tokens 8q .. 8q+7 of features
+// 32 g + 2n, +1; kKStep and kVStep are the strides between them.
+template <int kBits>
+constexpr int kKStep = 128 * kBits;
+template <int kBits>
+constexpr int kVStep = 32 * kBits;
 struct Lanes {
   unsigned k, v, ks, vs;
 };
+template <int kBits>
 __device__ __forceinline__ Lanes lane_offsets(int lane) {
   const int n = lane & 15, q = lane >> 4;
   const int d0 = ((lane >> 2) & 3) * 32 + (lane & 3) * 8;
-  return {static_cast<unsigned>(lane * 8), static_cast<unsigned>(q * 512 + n * 8),
-          static_cast<unsigned>(d0 * 4), static_cast<unsigned>(((n >> 2) * 32 + q * 8) * 4)};
+  return {static_cast<unsigned>(lane * 2 * kBits),
+          static_cast<unsigned>(q * 128 * kBits + n * 2 * kBits), static_cast<unsigned>(d0 * 4),
+          static_cast<unsigned>(((n >> 2) * 32 + q * 8) * 4)};
 }
 
 // Byte offset of block blk in an array of `bytes`-sized blocks, or kNoBlock.
@@ -130,23 +142,28 @@ __device__ __forceinline__ unsigned block_base(int blk, bool valid, unsigned byt
 }
 
 // Loaders of the four parts of one block (base: block_base of that array).
-__device__ __forceinline__ void load_ks(BlockRegs& r, const Head& h, unsigned base, const Lanes& o) {
+template <int kBits>
+__device__ __forceinline__ void load_ks(BlockRegs<kBits>& r, const Head& h, unsigned base,
+                                        const Lanes& o) {
   r.ks[0] = buf_f4(h.ksc, base + o.ks, 0);
   r.ks[1] = buf_f4(h.ksc, base + o.ks + 16, 0);
 }
-__device__ __forceinline__ void load_vs(BlockRegs& r, const Head& h, unsigned base, const Lanes& o) {
+template <int kBits>
+__device__ __forceinline__ void load_vs(BlockRegs<kBits>& r, const Head& h, unsigned base,
+                                        const Lanes& o) {
   r.vs[0] = buf_f4(h.vsc, base + o.vs, 0);
   r.vs[1] = buf_f4(h.vsc, base + o.vs + 16, 0);
 }
-__device__ __forceinline__ void load_block(BlockRegs& r, const Head& h, int blk, bool valid,
+template <int kBits>
+__device__ __forceinline__ void load_block(BlockRegs<kBits>& r, const Head& h, int blk, bool valid,
                                            const Lanes& o) {
   load_ks(r, h, block_base(blk, valid, kBS * 4), o);
-  const unsigned cb = block_base(blk, valid, kBB);
+  const unsigned cb = block_base(blk, valid, kBB<kBits>);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.k[i] = buf_b64(h.kc, cb + o.k + i * 512, 0);
+  for (int i = 0; i < 4; ++i) r.k[i] = CodeOps<kBits>::load(h.kc, cb + o.k + i * kKStep<kBits>, 0);
   load_vs(r, h, block_base(blk, valid, kBS * 4), o);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = buf_b64(h.vc, cb + o.v + i * 128, 0);
+  for (int i = 0; i < 4; ++i) r.v[i] = CodeOps<kBits>::load(h.vc, cb + o.v + i * kVStep<kBits>, 0);
 }
 
 // Running state of one wave.  Lane (n, q) tracks query row n & 3: m is the
@@ -172,9 +189,10 @@ struct WaveState {
 // lim, the position of score row n & 3's query; a row that has seen no
 // legal key keeps m = -inf and its exponents are taken against 0, so
 // (-inf) - (-inf) is never formed.
-template <bool kCausal>
-__device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, int t_end,
-                                             const CodeConsts& cc, WaveState& ws, const Head& h,
+template <int kBits, bool kCausal>
+__device__ __forceinline__ void attend_block(Smem& sm, BlockRegs<kBits>& br, int tok0, int t_end,
+                                             const typename CodeOps<kBits>::consts& cc,
+                                             WaveState& ws, const Head& h,
                                              int next, bool has_next, const Lanes& lo_,
                                              const float (&qv)[8], float us_row, int lim,
                                              int lim_lo) {
@@ -223,12 +241,12 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 se = zero4, so = zero4;
   const int part = n >> 3, row = n & 3;
-  const unsigned kb = block_base(next, has_next, kBB);
+  const unsigned kb = block_base(next, has_next, kBB<kBits>);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    half8_t alo, ahi;
-    codes_to_half(br.k[ks], cc, alo, ahi);
-    br.k[ks] = buf_b64(h.kc, kb + lo_.k + ks * 512, 0);  // next block's k-step
+    half8_t alo, ahi;  // tokens 2n and 2n + 1
+    CodeOps<kBits>::to_half(br.k[ks], cc, alo, ahi);
+    br.k[ks] = CodeOps<kBits>::load(h.kc, kb + lo_.k + ks * kKStep<kBits>, 0);  // next block's k-step
     const half8_t b = *reinterpret_cast<const half8_t*>(&sm.u.qt[wave][ks][part][row][q][0]);
     se = mfma(alo, b, se);
     so = mfma(ahi, b, so);
@@ -321,9 +339,9 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
   // u[4G'+r][f] += p~ x V codes, one feature group of 32 at a time
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    half8_t be, bo;
-    codes_to_half(br.v[g], cc, be, bo);
-    br.v[g] = buf_b64(h.vc, kb + lo_.v + g * 128, 0);  // next block's group
+    half8_t be, bo;  // features 32g + 2n and 32g + 2n + 1
+    CodeOps<kBits>::to_half(br.v[g], cc, be, bo);
+    br.v[g] = CodeOps<kBits>::load(h.vc, kb + lo_.v + g * kVStep<kBits>, 0);  // next block's group
     ws.acc[g][0] = mfma(ah, be, ws.acc[g][0]);
     ws.acc[g][0] = mfma(al, be, ws.acc[g][0]);
     ws.acc[g][1] = mfma(ah, bo, ws.acc[g][1]);
@@ -332,7 +350,7 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs& br, int tok0, 
 }
 
 // kCausal: a causal chunk (row r is query r % R at position N - R + r % R).
-template <bool kCausal>
+template <int kBits, bool kCausal>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 attend_mfma_r4_kernel(AttendProblem p) {
   __shared__ Smem sm;
@@ -362,9 +380,11 @@ attend_mfma_r4_kernel(AttendProblem p) {
   // Per-head strides follow the layout's capacity; only blocks below N are read.
   const int nblocks = (p.cap + kBlockTokens - 1) / kBlockTokens;
   Head h;
-  h.kc = head_rsrc(p.k_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
+  h.kc = head_rsrc(p.k_codes + bh * nblocks * kBB<kBits>,
+                   static_cast<long long>(nblocks) * kBB<kBits>);
   h.ksc = head_rsrc(p.k_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
-  h.vc = head_rsrc(p.v_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
+  h.vc = head_rsrc(p.v_codes + bh * nblocks * kBB<kBits>,
+                   static_cast<long long>(nblocks) * kBB<kBits>);
   h.vsc = head_rsrc(p.v_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
 
   // Blocks of this split: [b_begin, b_end); wave w takes b_begin + w + i kWaves,
@@ -386,8 +406,8 @@ attend_mfma_r4_kernel(AttendProblem p) {
     qa = *reinterpret_cast<const f32x4*>(src);
     qb = *reinterpret_cast<const f32x4*>(src + 4);
   }
-  const Lanes lo = lane_offsets(lane);
-  BlockRegs br[kDepth];
+  const Lanes lo = lane_offsets<kBits>(lane);
+  BlockRegs<kBits> br[kDepth];
 #pragma unroll
   for (int j = 0; j < kDepth; ++j) load_block(br[j], h, b_first + j * kWaves, j < cnt, lo);
 
@@ -412,7 +432,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
   // 2^-Sq of score row n & 3 (held by lanes 16 (n & 3) ..)
   const float us_row = __builtin_ldexpf(1.0f, -__shfl(sq, (n & 3) * 16));
 
-  const CodeConsts cc = code_consts();
+  const typename CodeOps<kBits>::consts cc = CodeOps<kBits>::make();
   WaveState ws;
   ws.m = -INFINITY;
   ws.z = 0.0f;
@@ -437,7 +457,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
     for (int j = 0; j < kDepth; ++j) {
       const int i = i0 + j;
       const int blk = b_first + i * kWaves;
-      attend_block<kCausal>(sm, br[j], i < cnt ? blk * kBlockTokens : t_end, t_end, cc, ws, h,
+      attend_block<kBits, kCausal>(sm, br[j], i < cnt ? blk * kBlockTokens : t_end, t_end, cc, ws, h,
                             blk + kDepth * kWaves, i + kDepth < cnt, lo, qv, us_row, lim,
                             p.pos_end - p.R);
     }
@@ -505,12 +525,22 @@ int mfma_tokens_per_split(int N, int splits) {
   return (per + kBlockTokens - 1) / kBlockTokens * kBlockTokens;
 }
 
+template <int kBits>
+void launch_r4(const AttendProblem& p, unsigned grid, hipStream_t stream) {
+  if (p.causal)
+    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, p);
+}
+
 hipError_t launch_attend_mfma(const AttendProblem& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
-  if (p.causal)
-    hipLaunchKernelGGL(attend_mfma_r4_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, p);
+  if (p.bits == 8)
+    launch_r4<8>(p, grid, stream);
   else
-    hipLaunchKernelGGL(attend_mfma_r4_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, p);
+    launch_r4<4>(p, grid, stream);
   return hipGetLastError();
 }
 

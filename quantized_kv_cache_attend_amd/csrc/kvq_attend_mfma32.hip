@@ -44,7 +44,12 @@ constexpr int kW = 4;            // waves per workgroup
 constexpr int kT = kW * 64;      // threads per workgroup
 constexpr int kR = 32;           // query rows per KV head (padded)
 constexpr int kD = 128;
-constexpr int kBB = 2048;        // K or V code bytes of one 32-token block
+template <int kBits>
+constexpr int kBB = 512 * kBits; // K or V code bytes of one 32-token block
+template <int kBits>
+constexpr int kKStep = 128 * kBits;  // lane code bytes: K k-step stride
+template <int kBits>
+constexpr int kVStep = 32 * kBits;   //   and V value-group stride
 constexpr int kBS = 128;         // K or V scales of one block
 constexpr int kQStride = 132;    // LDS row of q: 4 words of padding keep the
                                  // 16 rows read by a quarter-wave on distinct banks
@@ -68,9 +73,10 @@ struct alignas(16) Smem32 {
   int last;
 };
 
+template <int kBits>
 struct Regs32 {
-  i32x2 k[4];   // K codes, k-step 0..3
-  i32x2 v[4];   // V codes, value group 0..3
+  typename CodeOps<kBits>::words k[4];  // K codes, k-step 0..3
+  typename CodeOps<kBits>::words v[4];  // V codes, value group 0..3
   float2 ks;    // K scales 2 lane, 2 lane + 1 of the block
   float2 vs;    // V scales 2 lane, 2 lane + 1 of the block ([group][token])
 };
@@ -85,18 +91,22 @@ struct Lanes32 {
   unsigned k_off, v_off, s_off;  // byte offsets of this lane in a block
 };
 
-__device__ __forceinline__ void load_scales32(Regs32& r, const Head32& h, int blk,
+template <int kBits>
+__device__ __forceinline__ void load_scales32(Regs32<kBits>& r, const Head32& h, int blk,
                                               const Lanes32& o) {
   r.ks = buf_f2(h.ksc, o.s_off, blk * kBS * 4);
   r.vs = buf_f2(h.vsc, o.s_off, blk * kBS * 4);
 }
-__device__ __forceinline__ void load_block32(Regs32& r, const Head32& h, int blk,
+template <int kBits>
+__device__ __forceinline__ void load_block32(Regs32<kBits>& r, const Head32& h, int blk,
                                              const Lanes32& o) {
   load_scales32(r, h, blk, o);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.k[i] = buf_b64(h.kc, o.k_off + i * 512, blk * kBB);
+  for (int i = 0; i < 4; ++i)
+    r.k[i] = CodeOps<kBits>::load(h.kc, o.k_off + i * kKStep<kBits>, blk * kBB<kBits>);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = buf_b64(h.vc, o.v_off + i * 128, blk * kBB);
+  for (int i = 0; i < 4; ++i)
+    r.v[i] = CodeOps<kBits>::load(h.vc, o.v_off + i * kVStep<kBits>, blk * kBB<kBits>);
 }
 
 // Running state of one wave.  Lane (n, q) owns score rows 16t + n (t = 0, 1):
@@ -159,9 +169,10 @@ __device__ __forceinline__ half2_t pk16(float x, float y) {
 // score row 16t + n, the tokens after its query's position lim[t], and keep
 // rows that have seen no legal key at m = -inf (exponents then taken
 // against 0, so (-inf) - (-inf) is never formed).
-template <int kTiles, bool kMasked, bool kCausal>
-__device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0, int t_end,
-                                               const CodeConsts& cc, State32& st,
+template <int kBits, int kTiles, bool kMasked, bool kCausal>
+__device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, int tok0, int t_end,
+                                               const typename CodeOps<kBits>::consts& cc,
+                                               State32& st,
                                                const Head32& h, int next, const Lanes32& lo,
                                                const float us_row[2], const float (&qk)[2][4][8],
                                                const int (&lim)[2]) {
@@ -245,9 +256,10 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
       for (int i = 0; i < 4; ++i) q16[i] = pk16(qk[t][ks][2 * i], qk[t][ks][2 * i + 1]);
       product_hilo(qk[t][ks], sk, q16, sk16, bh[t], bl[t]);
     }
-    half8_t alo, ahi;
-    codes_to_half(br.k[ks], cc, alo, ahi);
-    br.k[ks] = buf_b64(h.kc, lo.k_off + ks * 512, next * kBB);  // next block's k-step
+    half8_t alo, ahi;  // tokens 2n and 2n + 1
+    CodeOps<kBits>::to_half(br.k[ks], cc, alo, ahi);
+    br.k[ks] = CodeOps<kBits>::load(h.kc, lo.k_off + ks * kKStep<kBits>,
+                                    next * kBB<kBits>);  // next block's k-step
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       se[t] = mfma(alo, bh[t], se[t]);
@@ -344,9 +356,10 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
     half8_t ah[2], al[2];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) product_hilo(pk[t], sv, p16[t], sv16, ah[t], al[t]);
-    half8_t be, bo;
-    codes_to_half(br.v[g], cc, be, bo);
-    br.v[g] = buf_b64(h.vc, lo.v_off + g * 128, next * kBB);  // next block's group
+    half8_t be, bo;  // features 32g + 2n and 32g + 2n + 1
+    CodeOps<kBits>::to_half(br.v[g], cc, be, bo);
+    br.v[g] = CodeOps<kBits>::load(h.vc, lo.v_off + g * kVStep<kBits>,
+                                   next * kBB<kBits>);  // next block's group
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       st.acc[g][t][0] = mfma(ah[t], be, st.acc[g][t][0]);
@@ -365,7 +378,7 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32& br, int tok0,
 // it attends first, and its loop runs the unmasked path: every row reads
 // every token there, which also gives a row still without a legal key its
 // first one.
-template <int kTiles, bool kCausal>
+template <int kBits, int kTiles, bool kCausal>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attend_mfma_r32_kernel(AttendProblem p) {
   __shared__ Smem32 sm;
@@ -394,9 +407,11 @@ attend_mfma_r32_kernel(AttendProblem p) {
   // Per-head strides follow the layout's capacity; only blocks below N are read.
   const int nblocks = (p.cap + kBlockTokens - 1) / kBlockTokens;
   Head32 h;
-  h.kc = head_rsrc(p.k_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
+  h.kc = head_rsrc(p.k_codes + bh * nblocks * kBB<kBits>,
+                   static_cast<long long>(nblocks) * kBB<kBits>);
   h.ksc = head_rsrc(p.k_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
-  h.vc = head_rsrc(p.v_codes + bh * nblocks * kBB, static_cast<long long>(nblocks) * kBB);
+  h.vc = head_rsrc(p.v_codes + bh * nblocks * kBB<kBits>,
+                   static_cast<long long>(nblocks) * kBB<kBits>);
   h.vsc = head_rsrc(p.v_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
 
   const int t_begin = split * p.tokens_per_split;
@@ -405,7 +420,10 @@ attend_mfma_r32_kernel(AttendProblem p) {
   const int b_end = t_end > t_begin ? (t_end + kBlockTokens - 1) / kBlockTokens : b_begin;
   const int b_first = b_begin + wave;
   const int b_last = b_first + (b_end - 1 - b_first) / kW * kW;  // valid if b_first < b_end
-  const Lanes32 lo = {static_cast<unsigned>(lane * 8), static_cast<unsigned>(q * 512 + n * 8),
+  // Code bytes of lane (n, q): K channels 32 ks + 8q .. +7 of tokens 2n, 2n + 1;
+  // V tokens 8q .. 8q+7 of features 32 g + 2n, +1 (2 * kBits bytes each).
+  const Lanes32 lo = {static_cast<unsigned>(lane * 2 * kBits),
+                      static_cast<unsigned>(q * 128 * kBits + n * 2 * kBits),
                       static_cast<unsigned>(lane * 8)};
 
   // The block holding token N-1 is masked when N is not a multiple of 32;
@@ -417,7 +435,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
   const int first = partial ? b_last : b_first;
   const int loop_begin = partial ? b_first : b_first + kW;
   const int loop_end = partial ? b_last - kW : b_last;  // inclusive
-  Regs32 br;
+  Regs32<kBits> br;
   if (active) load_block32(br, h, first, lo);
 
   // q * qscale into LDS, each row prescaled by 2^Sq so its largest element
@@ -469,7 +487,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
       for (int j = 0; j < 8; ++j) qk[t][ks][j] = j < 4 ? qa[kSlotByte[j]] : qb[kSlotByte[j] - 4];
     }
 
-  const CodeConsts cc = code_consts();
+  const typename CodeOps<kBits>::consts cc = CodeOps<kBits>::make();
   State32 st;
   st.m[0] = st.m[1] = -INFINITY;
   st.z[0] = st.z[1] = 0.0f;
@@ -488,11 +506,11 @@ attend_mfma_r32_kernel(AttendProblem p) {
   // Causal limit of this lane's score rows 16t + n.
   const int lim[2] = {p.pos_end - p.R + n % p.R, p.pos_end - p.R + (16 + n) % p.R};
   if (active) {
-    attend_block32<kTiles, true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
+    attend_block32<kBits, kTiles, true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
                                   loop_begin <= loop_end ? loop_begin : first, lo, us_row, qk,
                                   lim);
     for (int b = loop_begin; b <= loop_end; b += kW)
-      attend_block32<kTiles, false, false>(sm, br, b * kBlockTokens, t_end, cc, st, h,
+      attend_block32<kBits, kTiles, false, false>(sm, br, b * kBlockTokens, t_end, cc, st, h,
                                    min(b + kW, loop_end), lo, us_row, qk, lim);
   }
   st.z[0] = qblock_sum(st.z[0]);
@@ -571,19 +589,29 @@ attend_mfma_r32_kernel(AttendProblem p) {
 
 }  // namespace
 
+template <int kBits, int kTiles>
+void launch_r32(const AttendProblem& p, unsigned grid, hipStream_t stream) {
+  if (p.causal)
+    hipLaunchKernelGGL((attend_mfma_r32_kernel<kBits, kTiles, true>), dim3(grid), dim3(kT), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((attend_mfma_r32_kernel<kBits, kTiles, false>), dim3(grid), dim3(kT), 0,
+                       stream, p);
+}
+
 hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
   // One 16-row tile when the KV head has at most 16 query rows.
-  if (p.rows <= 16) {
-    if (p.causal)
-      hipLaunchKernelGGL((attend_mfma_r32_kernel<1, true>), dim3(grid), dim3(kT), 0, stream, p);
+  if (p.bits == 8) {
+    if (p.rows <= 16)
+      launch_r32<8, 1>(p, grid, stream);
     else
-      hipLaunchKernelGGL((attend_mfma_r32_kernel<1, false>), dim3(grid), dim3(kT), 0, stream, p);
+      launch_r32<8, 2>(p, grid, stream);
   } else {
-    if (p.causal)
-      hipLaunchKernelGGL((attend_mfma_r32_kernel<2, true>), dim3(grid), dim3(kT), 0, stream, p);
+    if (p.rows <= 16)
+      launch_r32<4, 1>(p, grid, stream);
     else
-      hipLaunchKernelGGL((attend_mfma_r32_kernel<2, false>), dim3(grid), dim3(kT), 0, stream, p);
+      launch_r32<4, 2>(p, grid, stream);
   }
   return hipGetLastError();
 }

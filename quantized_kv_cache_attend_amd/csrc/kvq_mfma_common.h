@@ -129,6 +129,70 @@ __device__ __forceinline__ void codes_to_half(i32x2 w, const CodeConsts& k, half
   hi = __builtin_bit_cast(half8_t, h);
 }
 
+// 8-bit codes: sixteen code bytes, two rows of 8 (bytes 0..7 and 8..15) ->
+// fp16 (c - 127) operands first / second, in the same k-slot order (b0, b2,
+// b1, b3, b4, b6, b5, b7) as codes_to_half.  One byte permute places two
+// codes under the exponent byte 0x64 (fp16 1024 + c, exact for c < 1024),
+// one packed add removes the bias.
+struct CodeConsts8 {
+  unsigned sel_even, sel_odd, magic;
+};
+__device__ __forceinline__ CodeConsts8 code_consts8() {
+  // v_perm_b32 selectors over {magic (bytes 4..7), word (bytes 0..3)}:
+  // (byte 0 | 0x64 << 8 | byte 2 << 16 | 0x64 << 24) and the same for bytes 1, 3.
+  return {in_vgpr(0x04020400u), in_vgpr(0x04030401u), in_vgpr(0x64646464u)};
+}
+__device__ __forceinline__ void codes8_to_half(u32x4 w, const CodeConsts8& k, half8_t& first,
+                                               half8_t& second) {
+  // (Each value goes through a scalar: __builtin_bit_cast of a vector
+  // element compiles to wrong code with this compiler.)
+  const half2_t bias = {(_Float16)-1151.0f, (_Float16)-1151.0f};
+  const unsigned src[4] = {w.x, w.y, w.z, w.w};
+  unsigned out[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned e = __builtin_amdgcn_perm(k.magic, src[i], k.sel_even);
+    const unsigned o = __builtin_amdgcn_perm(k.magic, src[i], k.sel_odd);
+    out[2 * i] = __builtin_bit_cast(unsigned, __builtin_bit_cast(half2_t, e) + bias);
+    out[2 * i + 1] = __builtin_bit_cast(unsigned, __builtin_bit_cast(half2_t, o) + bias);
+  }
+  const u32x4 a = {out[0], out[1], out[2], out[3]};
+  const u32x4 b = {out[4], out[5], out[6], out[7]};
+  first = __builtin_bit_cast(half8_t, a);
+  second = __builtin_bit_cast(half8_t, b);
+}
+
+// Code bytes of one lane's operand pair per format: 8 bytes hold two
+// 4-bit rows (low and high nibbles), 16 bytes two 8-bit rows.
+template <int kBits>
+struct CodeOps;
+template <>
+struct CodeOps<4> {
+  typedef i32x2 words;
+  typedef CodeConsts consts;
+  static __device__ __forceinline__ consts make() { return code_consts(); }
+  static __device__ __forceinline__ words load(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+    return buf_b64(r, voff, soff);
+  }
+  static __device__ __forceinline__ void to_half(words w, const consts& k, half8_t& a,
+                                                 half8_t& b) {
+    codes_to_half(w, k, a, b);
+  }
+};
+template <>
+struct CodeOps<8> {
+  typedef u32x4 words;
+  typedef CodeConsts8 consts;
+  static __device__ __forceinline__ consts make() { return code_consts8(); }
+  static __device__ __forceinline__ words load(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  }
+  static __device__ __forceinline__ void to_half(words w, const consts& k, half8_t& a,
+                                                 half8_t& b) {
+    codes8_to_half(w, k, a, b);
+  }
+};
+
 // k-slot j of a converted operand holds byte kSlotByte[j] of the 8 read.
 __device__ constexpr int kSlotByte[8] = {0, 2, 1, 3, 4, 6, 5, 7};
 

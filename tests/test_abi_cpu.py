@@ -100,7 +100,11 @@ def _attend(**kw):
     (dict(splits=4), kvq.KVQ_ERR_WORKSPACE),                 # no workspace
     (dict(splits=4, ws=ctypes.c_void_p(0x40000000), wsb=64), kvq.KVQ_ERR_WORKSPACE),
     (dict(variant=9), kvq.KVQ_ERR_INVALID),
-    (dict(variant=2, bits=8), kvq.KVQ_ERR_UNSUPPORTED),      # matrix-core kernel is 4-bit g32 D128
+    (dict(variant=2, bits=8), kvq.KVQ_ERR_UNSUPPORTED),      # matrix-core kernels: D = 128 only
+    (dict(variant=2, D=128, group=8, out=ctypes.c_void_p(1 << 44)),
+     kvq.KVQ_ERR_UNSUPPORTED),                              # and group 32 only
+    (dict(variant=2, D=128, bits=8, N=(1 << 24) - 31, out=ctypes.c_void_p(1 << 44)),
+     kvq.KVQ_ERR_UNSUPPORTED),                              # 8-bit: 4 KB blocks, half the tokens
     (dict(variant=2, D=128, N=(1 << 25) - 31, out=ctypes.c_void_p(1 << 44)),
      kvq.KVQ_ERR_UNSUPPORTED),                              # past its 32-bit buffer offsets
 ])

@@ -149,6 +149,9 @@ def main():
     ap.add_argument("--workload", default="gqa_n4096", choices=["gqa_n4096", "gqa_n32768"])
     ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--splits", type=int, default=-1, help="-1: workload default, 0: auto")
+    ap.add_argument("--bits", type=int, default=0, choices=[0, 4, 8],
+                    help="code width of the timed cache (0: the workload's, 4)")
+    ap.add_argument("--group", type=int, default=0, help="group length (0: the workload's, 32)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -172,6 +175,8 @@ def main():
 
     w = WORKLOADS[args.workload]
     bits, group = w.formats[0]
+    default_format = not args.bits and not args.group
+    bits, group = args.bits or bits, args.group or group
     splits = w.num_splits if args.splits < 0 else args.splits
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -550,9 +555,10 @@ def main():
         cpu = cpu_baseline(w, q, k, v, bits, group, args.cpu_seconds)
         log(f"[bench] oracle {cpu['value']:.3f} GB/s ({cpu['sample']})")
 
-    traffic = measured_traffic() if args.variant in ("auto", "mfma") and w.name == "gqa_n4096" else None
+    traffic = (measured_traffic() if args.variant in ("auto", "mfma") and w.name == "gqa_n4096"
+               and default_format else None)
     result = {
-        "metric": METRIC,
+        "metric": METRIC if default_format else METRIC.replace("4-bit", f"{bits}-bit g{group}"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -562,7 +568,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4+f32",
+        "dtype": f"u{bits}+f32",
         "data": "synthetic (seeded N(0,1) float32 Q/K/V, packed on the GPU)",
         "config": {"workload": w.name, "batch": w.B, "n_tokens": w.N, "hq": w.Hq, "hkv": w.Hkv,
                    "queries_per_head": w.R, "head_dim": w.D, "bits": bits, "group": group,

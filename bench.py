@@ -549,6 +549,45 @@ def main():
             ", ".join(f"{k} ({v['kernel']}) {v['us']:.1f} us ({v['kv_gbs']:.0f} GB/s)"
                       for k, v in fmt.items()))
 
+        # The single-head workloads (128 / 512 / 1024 tokens, D = 32, every
+        # format they name): per-call time of one fused attend, graph-launched
+        # back to back.  These are latency-bound (a few KB of cache).
+        small = {}
+        for sname in ("single_n128", "single_n512", "single_n1024"):
+            sw = WORKLOADS[sname]
+            sq, sk_, sv_ = make_qkv(sw, 0)
+            sqd, skd, svd = (torch.from_numpy(a).to(dev) for a in (sq, sk_, sv_))
+            for sb, sg in sw.formats:
+                sc = kvq.pack_k(skd, sb, sg) + kvq.pack_v(svd, sb, sg)
+                sws = kvq.new_workspace(sw.B, sw.Hq, sw.Hkv, sw.R, sw.N, sw.D, 0, device=dev)
+                sout = torch.empty_like(sqd)
+
+                def scalls(n):
+                    for _ in range(n):
+                        kvq.attend(sqd, *sc, sw.N, sb, sg, workspace=sws, out=sout)
+                scalls(1)
+                torch.cuda.synchronize()
+                n_s, reps_s = 50, 10
+                srun = lambda: scalls(n_s)  # noqa: E731
+                if args.launch == "graph":
+                    sgraph = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(sgraph):
+                        scalls(n_s)
+                    srun = sgraph.replay
+                srun()
+                torch.cuda.synchronize()
+                s0 = torch.cuda.Event(enable_timing=True)
+                s1 = torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                for _ in range(reps_s):
+                    srun()
+                s1.record(stream)
+                torch.cuda.synchronize()
+                small[f"{sname}_{sb}bit_g{sg}"] = round(s0.elapsed_time(s1) * 1e3 / (n_s * reps_s), 2)
+        extra["single_head_us_per_call"] = small
+        log("[bench] single-head workloads (us per call): " +
+            ", ".join(f"{k} {v:.2f}" for k, v in small.items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host ...")

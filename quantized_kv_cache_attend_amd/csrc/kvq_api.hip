@@ -70,12 +70,13 @@ namespace {
 
 int auto_splits(int B, int Hkv, int N) {
   // About 512 workgroups: two per compute unit, all resident at once, so
-  // every KV byte's load can be in flight early; and no split shorter than
-  // 512 tokens, so each workgroup streams at least two 256-token tiles and
-  // overlaps the second tile's loads with the first tile's math.
+  // every KV byte's load can be in flight early.  A split is at least one
+  // 32-token tile: a workgroup walks its tiles one after another (each a
+  // load, a decode and the math, ~4 us), so a short cache on few heads is
+  // fastest spread one tile per workgroup.
   const long long heads = static_cast<long long>(B) * Hkv;
   const long long want = (512 + heads - 1) / heads;
-  const long long cap = (N + 511) / 512;
+  const long long cap = (N + kBlockTokens - 1) / kBlockTokens;
   long long s = want < cap ? want : cap;
   if (s < 1) s = 1;
   if (s > 1024) s = 1024;

@@ -305,17 +305,40 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttendProblem p) {
   const long long tid = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
   if (tid >= total_rows * p.D) return;
   const long long row = tid / p.D;
-  float big_m = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) big_m = fmaxf(big_m, p.part_m[s * total_rows + row]);
-  float z = 0.0f, u = 0.0f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float m = p.part_m[s * total_rows + row];
-    if (m == -INFINITY) continue;
-    const float w = exp2f(m - big_m);
-    z = fmaf(w, p.part_z[s * total_rows + row], z);
-    u = fmaf(w, p.part_u[s * total_rows * p.D + tid], u);
+  // One pass in batches of kBatch splits, whose loads are all issued before
+  // any is used; the running (M, Z, U) moves to each batch's max with the
+  // same rescale.
+  constexpr int kBatch = 8;
+  float M = -INFINITY, Z = 0.0f, U = 0.0f;
+  for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+    float ms[kBatch], zs[kBatch], us[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const long long s = min(s0 + j, p.splits - 1);
+      ms[j] = p.part_m[s * total_rows + row];
+      zs[j] = p.part_z[s * total_rows + row];
+      us[j] = p.part_u[s * total_rows * p.D + tid];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (s0 + j >= p.splits) ms[j] = -INFINITY;
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, ms[j]);
+    if (mb == -INFINITY) continue;  // no split so far saw a legal key
+    const float a = exp2f(M - mb);  // 0 while nothing is merged yet
+    Z *= a;
+    U *= a;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (ms[j] == -INFINITY) continue;
+      const float w = exp2f(ms[j] - mb);
+      Z = fmaf(w, zs[j], Z);
+      U = fmaf(w, us[j], U);
+    }
+    M = mb;
   }
-  p.out[tid] = z > 0.0f ? u / z : 0.0f;  // no split saw a legal key: 0
+  p.out[tid] = Z > 0.0f ? U / Z : 0.0f;  // no split saw a legal key: 0
 }
 
 template <int D>

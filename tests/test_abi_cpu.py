@@ -64,8 +64,9 @@ def test_sizes_reject_bad_format():
 def test_auto_splits_and_workspace():
     # about 512 workgroups, never splits shorter than 512 tokens
     assert lib.kvq_attend_auto_splits(8, 8, 4096) == 8
-    assert lib.kvq_attend_auto_splits(1, 1, 128) == 1
-    assert lib.kvq_attend_auto_splits(1, 1, 1024) == 2
+    assert lib.kvq_attend_auto_splits(1, 1, 128) == 4       # one 32-token tile per split
+    assert lib.kvq_attend_auto_splits(1, 1, 1024) == 32
+    assert lib.kvq_attend_auto_splits(1, 1, 31) == 1
     assert lib.kvq_attend_auto_splits(1, 1, 1 << 20) == 512
     assert lib.kvq_attend_auto_splits(16, 8, 32768) == 4
     w1 = lib.kvq_attend_workspace_bytes(8, 32, 8, 1, 4096, 128, 8)

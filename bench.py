@@ -470,9 +470,10 @@ def main():
         kw, vw = kd[:, :, w.N - win:].contiguous(), vd[:, :, w.N - win:].contiguous()
         out_w = torch.empty_like(qd)
         ws_w = kvq.new_workspace(w.B, w.Hq, w.Hkv, w.R, w.N, w.D,
-                                 (splits or kvq.auto_splits(w.B, w.Hkv, w.N)) + 1, device=dev)
+                                 (splits or kvq.auto_splits(w.B, w.Hkv, w.N)) + win // 32,
+                                 device=dev)
 
-        def window_call():  # one workspace slot more than the splits: the fused form
+        def window_call():  # a workspace slot per 32 window tokens beyond the splits: fused form
             kvq.attend_window(qd, *kpre, *vpre, kw, vw, w.N - win, bits, group, workspace=ws_w,
                               out=out_w, num_splits=splits)
         window_call()

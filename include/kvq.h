@@ -230,13 +230,15 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
  * sm_scale, splits, workspace (sized for N + W tokens) and flags
  * (KVQ_ATTEND_CAUSAL: positions counted over N + W) as in kvq_attend_cache.
  * When the packed part suits the matrix-core kernels (KVQ_VARIANT_MFMA's
- * conditions with capacity for N) and the workspace holds S + 1 split slots
- * (kvq_attend_workspace_bytes(B, Hq, Hkv, R, N + W, D, S + 1); S = num_splits,
- * or the matrix-core kernel's own automatic count, at most
- * kvq_attend_auto_splits(B, Hkv, N)), the call is fused: the general kernel
- * writes the window's partial (m, z, u) into slot S, then the matrix-core
- * kernel attends the packed tokens and its combine merges that slot with
- * its S splits.  Otherwise the general kernel reads both parts.  A decode
+ * conditions with capacity for N) and the workspace holds S + P split slots,
+ * 1 <= P <= ceil(W / 32) (kvq_attend_workspace_bytes(B, Hq, Hkv, R, N + W, D,
+ * S + P); S = num_splits, or the matrix-core kernel's own automatic count, at
+ * most kvq_attend_auto_splits(B, Hkv, N)), the call is fused: the general
+ * kernel writes the window's partial (m, z, u) into slots S .. S + P - 1 (P
+ * the largest count the workspace holds: one workgroup per 32 window tokens
+ * at P = ceil(W / 32)), then the matrix-core kernel attends the packed tokens
+ * and its combine merges those slots with its S splits.  Otherwise the
+ * general kernel reads both parts.  A decode
  * loop moves the window's oldest tokens into the packed cache with
  * kvq_append. */
 kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float* k_scales,

@@ -253,8 +253,8 @@ def attend_window(q, k_codes, k_scales, v_codes, v_scales, k_win, v_win, N, bits
     cap = max(N, 1) if capacity is None else capacity
     if bits in (4, 8) and group >= 2 and cap >= max(N, 1):
         _check_cache((k_codes, k_scales, v_codes, v_scales), B, Hkv, cap, D, bits, group)
-    if workspace is None:  # one slot more than the splits: room for the fused form
-        slots = (num_splits or auto_splits(B, Hkv, N + W)) + 1
+    if workspace is None:  # a slot per 32 window tokens beyond the splits: the fused form
+        slots = (num_splits or auto_splits(B, Hkv, N + W)) + (W + 31) // 32
         workspace = new_workspace(B, Hq, Hkv, R, N + W, D, slots, device=q.device)
     if out is None:
         out = torch.empty_like(q)

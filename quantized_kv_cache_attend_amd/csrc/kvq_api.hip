@@ -431,9 +431,10 @@ kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
   // Fused form: the packed tokens on a matrix-core kernel, whose fused
-  // combine also merges one extra partial slot: the window's (m, z, u),
-  // written just before by the general kernel over the W float32 tokens
-  // (stream order makes it complete and visible when the combine reads it).
+  // combine also merges P extra partial slots: the window's (m, z, u),
+  // written just before by the general kernel over the W float32 tokens,
+  // one workgroup per 32 tokens when the workspace has the slots (stream
+  // order makes them complete and visible when the combine reads them).
   if (N >= 1) {
     AttendProblem pm = p;
     pm.N = N;
@@ -442,11 +443,15 @@ kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float
       const bool wide = pm.rows > kMfmaMaxRows;
       const int S = num_splits ? num_splits
                                : (wide ? mfma32_auto_splits(B, Hkv, N) : mfma_auto_splits(B, Hkv, N));
-      const WorkspaceLayout wl = workspace_layout(B, Hq, Hkv, R, D, S + 1);
-      if (S + 1 <= 65535 && workspace && workspace_bytes >= wl.total) {
+      int P = (W + kBlockTokens - 1) / kBlockTokens;  // window parts wanted
+      while (P > 1 && (S + P > 65535 || !workspace ||
+                       workspace_bytes < workspace_layout(B, Hq, Hkv, R, D, S + P).total))
+        --P;
+      const WorkspaceLayout wl = workspace_layout(B, Hq, Hkv, R, D, S + P);
+      if (S + P <= 65535 && workspace && workspace_bytes >= wl.total) {
         char* ws = static_cast<char*>(workspace);
         pm.splits = S;
-        pm.extra_parts = 1;
+        pm.extra_parts = P;
         pm.tokens_per_split = mfma_tokens_per_split(N, S);
         pm.part_m = reinterpret_cast<float*>(ws + wl.m_off);
         pm.part_z = reinterpret_cast<float*>(ws + wl.z_off);
@@ -458,8 +463,8 @@ kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float
         pw.k_f32 = k_win;
         pw.v_f32 = v_win;
         pw.N = pw.cap = pw.pos_end = W;
-        pw.splits = 1;
-        pw.tokens_per_split = W;
+        pw.splits = P;
+        pw.tokens_per_split = (W + P - 1) / P;
         pw.part0 = S;
         pw.extra_parts = 0;
         hipError_t e = launch_attend_valu(pw, s);

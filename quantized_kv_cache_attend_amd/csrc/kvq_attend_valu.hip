@@ -361,7 +361,9 @@ hipError_t launch_attend_valu(const AttendProblem& p, hipStream_t stream) {
     case 64: e = launch_valu_d<64>(p, stream); break;
     default: e = launch_valu_d<128>(p, stream); break;
   }
-  if (e != hipSuccess || p.splits == 1) return e;
+  // part0 > 0: the partials are extra slots of a later matrix-core call,
+  // whose fused combine merges them.
+  if (e != hipSuccess || p.splits == 1 || p.part0 != 0) return e;
   return launch_combine(p, stream);
 }
 

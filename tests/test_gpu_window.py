@@ -46,9 +46,10 @@ def test_attend_window(B, hq, hkv, r, n, w, d, bits, group, causal):
 
 @pytest.mark.parametrize("hq,hkv,r,causal", [(32, 8, 1, False), (16, 2, 2, True), (8, 8, 4, True)])
 def test_fused_window_equals_general_kernel(hq, hkv, r, causal):
-    """The fused form (window partial + matrix-core combine) against the
-    general kernel on the same call (a workspace one slot too small forces
-    the latter), and both against the oracle."""
+    """The fused form (window partials + matrix-core combine; the 48-token
+    window in two parts, or in one when the workspace has a single extra
+    slot) against the general kernel on the same call (a workspace with no
+    extra slot forces the latter), and all against the oracle."""
     B, n, w, D = 2, 2000, 48, 128
     wl = Workload("fused", B, hq, hkv, r, n + w, D, ((4, 32),))
     q, k, v = make_qkv(wl, 13)
@@ -67,6 +68,13 @@ def test_fused_window_equals_general_kernel(hq, hkv, r, causal):
                                              num_splits=splits, workspace=small, causal=causal))
             assert max_abs(fused, general) <= 2e-5, splits
             assert max_abs(general, want) <= TOL, splits
+            # one slot more: the fused form with the whole window in one part
+            # (the default workspace has one per 32 window tokens, here 2)
+            one = kvq.new_workspace(B, hq, hkv, r, n + w, D, splits + 1)
+            fused1 = host(kvq.attend_window(qd, kc, ks, vc, vs, kw, vw, n, 4, 32,
+                                            num_splits=splits, workspace=one, causal=causal))
+            assert max_abs(fused1, fused) <= 2e-5, splits
+            assert max_abs(fused1, want) <= TOL, splits
 
 
 def test_decode_loop_with_window():

@@ -233,12 +233,12 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
  * conditions with capacity for N) and the workspace holds S + P split slots,
  * 1 <= P <= ceil(W / 32) (kvq_attend_workspace_bytes(B, Hq, Hkv, R, N + W, D,
  * S + P); S = num_splits, or the matrix-core kernel's own automatic count, at
- * most kvq_attend_auto_splits(B, Hkv, N)), the call is fused: the general
- * kernel writes the window's partial (m, z, u) into slots S .. S + P - 1 (P
- * the largest count the workspace holds: one workgroup per 32 window tokens
- * at P = ceil(W / 32)), then the matrix-core kernel attends the packed tokens
- * and its combine merges those slots with its S splits.  Otherwise the
- * general kernel reads both parts.  A decode
+ * most kvq_attend_auto_splits(B, Hkv, N)), the call is fused into one
+ * matrix-core launch: per KV head, S workgroups attend the packed tokens and
+ * P more the window tokens (P the largest count the workspace holds: one
+ * workgroup per 32 window tokens at P = ceil(W / 32)), and the split combine
+ * merges all S + P partials.  Otherwise the general kernel reads both
+ * parts.  A decode
  * loop moves the window's oldest tokens into the packed cache with
  * kvq_append. */
 kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float* k_scales,

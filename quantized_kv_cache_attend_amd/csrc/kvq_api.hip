@@ -163,6 +163,8 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   p->causal = 0;
   p->k_win = p->v_win = nullptr;
   p->W = 0;
+  p->win_parts = 0;
+  p->win_per_part = 0;
   p->pos_end = N;
   p->part0 = 0;
   p->extra_parts = 0;
@@ -430,11 +432,10 @@ kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float
   p.causal = (flags & KVQ_ATTEND_CAUSAL) && R > 1;
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
-  // Fused form: the packed tokens on a matrix-core kernel, whose fused
-  // combine also merges P extra partial slots: the window's (m, z, u),
-  // written just before by the general kernel over the W float32 tokens,
-  // one workgroup per 32 tokens when the workspace has the slots (stream
-  // order makes them complete and visible when the combine reads them).
+  // Fused form, one launch of a matrix-core kernel: S workgroups per head
+  // attend the packed tokens and P more attend the W float32 window tokens
+  // (one per 32 tokens when the workspace has the slots); the fused combine
+  // merges all S + P partials.
   if (N >= 1) {
     AttendProblem pm = p;
     pm.N = N;
@@ -450,25 +451,18 @@ kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float
       const WorkspaceLayout wl = workspace_layout(B, Hq, Hkv, R, D, S + P);
       if (S + P <= 65535 && workspace && workspace_bytes >= wl.total) {
         char* ws = static_cast<char*>(workspace);
-        pm.splits = S;
-        pm.extra_parts = P;
+        pm.splits = S + P;  // S packed splits, then P window parts
+        pm.win_parts = P;
+        pm.win_per_part = (W + P - 1) / P;
+        pm.k_win = k_win;
+        pm.v_win = v_win;
+        pm.W = W;
         pm.tokens_per_split = mfma_tokens_per_split(N, S);
         pm.part_m = reinterpret_cast<float*>(ws + wl.m_off);
         pm.part_z = reinterpret_cast<float*>(ws + wl.z_off);
         pm.part_u = reinterpret_cast<float*>(ws + wl.u_off);
         pm.counters = reinterpret_cast<unsigned*>(ws + wl.cnt_off);
-        AttendProblem pw = pm;  // the window: W float32 tokens, positions local to it
-        pw.bits = 32;
-        pw.group = 1;
-        pw.k_f32 = k_win;
-        pw.v_f32 = v_win;
-        pw.N = pw.cap = pw.pos_end = W;
-        pw.splits = P;
-        pw.tokens_per_split = (W + P - 1) / P;
-        pw.part0 = S;
-        pw.extra_parts = 0;
-        hipError_t e = launch_attend_valu(pw, s);
-        if (e == hipSuccess) e = wide ? launch_attend_mfma32(pm, s) : launch_attend_mfma(pm, s);
+        const hipError_t e = wide ? launch_attend_mfma32(pm, s) : launch_attend_mfma(pm, s);
         return hip_status(e, "attend_window (fused) launch");
       }
     }

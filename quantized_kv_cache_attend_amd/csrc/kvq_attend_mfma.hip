@@ -96,6 +96,7 @@ struct alignas(16) Smem {
   union {
     _Float16 qt[kWaves][4][2][4][4][8];  // per wave: q~ [kstep][hi|lo][row][kblock][8]
     float wu[kWaves][4][kD];             // per-wave u for the final merge
+    WinSmem<4> win;                      // a recent-token window part
   } u;
   float wm[kWaves][4];
   float wz[kWaves][4];
@@ -350,7 +351,10 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs<kBits>& br, int
 }
 
 // kCausal: a causal chunk (row r is query r % R at position N - R + r % R).
-template <int kBits, bool kCausal>
+// kWindow: the last p.win_parts workgroups of each head attend recent-token
+// window parts (a separate instantiation, so the plain kernel's block loop
+// is compiled without that path).
+template <int kBits, bool kCausal, bool kWindow>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 attend_mfma_r4_kernel(AttendProblem p) {
   __shared__ Smem sm;
@@ -377,6 +381,16 @@ attend_mfma_r4_kernel(AttendProblem p) {
   }
   const long long bh = head;
   const int rows = p.rows;
+  const int packed_splits = p.splits - p.win_parts;
+  if (kWindow && split >= packed_splits) {  // a window part (the whole workgroup)
+    const int e0 = tid * kSlots;
+    const int r = e0 >> 7, f0 = e0 & 127;
+    float U[kSlots], M, Z;
+    window_part<4, kThreads, kSlots, kSlots, 0>(p, sm.u.win, bh, split - packed_splits, r, f0, U,
+                                                M, Z);
+    split_combine<kSlots, kSlots, 0>(p, split, bh, r, f0, U, M, Z, &sm.last);
+    return;
+  }
   // Per-head strides follow the layout's capacity; only blocks below N are read.
   const int nblocks = (p.cap + kBlockTokens - 1) / kBlockTokens;
   Head h;
@@ -525,22 +539,23 @@ int mfma_tokens_per_split(int N, int splits) {
   return (per + kBlockTokens - 1) / kBlockTokens * kBlockTokens;
 }
 
-template <int kBits>
+template <int kBits, bool kWindow>
 void launch_r4(const AttendProblem& p, unsigned grid, hipStream_t stream) {
   if (p.causal)
-    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, true>), dim3(grid), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, true, kWindow>), dim3(grid), dim3(kThreads),
+                       0, stream, p);
   else
-    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, false>), dim3(grid), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, false, kWindow>), dim3(grid), dim3(kThreads),
+                       0, stream, p);
 }
 
 hipError_t launch_attend_mfma(const AttendProblem& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
+  const bool win = p.win_parts > 0;
   if (p.bits == 8)
-    launch_r4<8>(p, grid, stream);
+    win ? launch_r4<8, true>(p, grid, stream) : launch_r4<8, false>(p, grid, stream);
   else
-    launch_r4<4>(p, grid, stream);
+    win ? launch_r4<4, true>(p, grid, stream) : launch_r4<4, false>(p, grid, stream);
   return hipGetLastError();
 }
 

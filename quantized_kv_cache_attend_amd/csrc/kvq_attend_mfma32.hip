@@ -63,6 +63,7 @@ struct alignas(16) Smem32 {
   union {
     float qs[kR][kQStride];      // q * qscale * 2^Sq(row)
     float wu[2][kR][kD];         // u of two waves at a time, for the merge
+    WinSmem<kR> win;             // a recent-token window part
   } u;
   float sks[kW][kBS];            // this block's K scales (per wave), channel order
   float svs[kW][kBS];            // this block's V scales (per wave), [group][token]
@@ -378,7 +379,10 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
 // it attends first, and its loop runs the unmasked path: every row reads
 // every token there, which also gives a row still without a legal key its
 // first one.
-template <int kBits, int kTiles, bool kCausal>
+// kWindow: the last p.win_parts workgroups of each head attend recent-token
+// window parts (a separate instantiation, so the plain kernel's block loop is
+// compiled without that path).
+template <int kBits, int kTiles, bool kCausal, bool kWindow>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attend_mfma_r32_kernel(AttendProblem p) {
   __shared__ Smem32 sm;
@@ -404,6 +408,14 @@ attend_mfma_r32_kernel(AttendProblem p) {
   }
   const long long bh = head;
   const int rows = p.rows;
+  const int packed_splits = p.splits - p.win_parts;
+  if (kWindow && split >= packed_splits) {  // a window part (the whole workgroup)
+    const int r = tid >> 3, f0 = (tid & 7) * 4;
+    float U[16], M, Z;
+    window_part<kR, kT, 16, 4, 32>(p, sm.u.win, bh, split - packed_splits, r, f0, U, M, Z);
+    split_combine<16, 4, 32>(p, split, bh, r, f0, U, M, Z, &sm.last);
+    return;
+  }
   // Per-head strides follow the layout's capacity; only blocks below N are read.
   const int nblocks = (p.cap + kBlockTokens - 1) / kBlockTokens;
   Head32 h;
@@ -591,12 +603,22 @@ attend_mfma_r32_kernel(AttendProblem p) {
 
 template <int kBits, int kTiles>
 void launch_r32(const AttendProblem& p, unsigned grid, hipStream_t stream) {
-  if (p.causal)
-    hipLaunchKernelGGL((attend_mfma_r32_kernel<kBits, kTiles, true>), dim3(grid), dim3(kT), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((attend_mfma_r32_kernel<kBits, kTiles, false>), dim3(grid), dim3(kT), 0,
-                       stream, p);
+  const bool win = p.win_parts > 0;
+  if (p.causal) {
+    if (win)
+      hipLaunchKernelGGL((attend_mfma_r32_kernel<kBits, kTiles, true, true>), dim3(grid),
+                         dim3(kT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attend_mfma_r32_kernel<kBits, kTiles, true, false>), dim3(grid),
+                         dim3(kT), 0, stream, p);
+  } else {
+    if (win)
+      hipLaunchKernelGGL((attend_mfma_r32_kernel<kBits, kTiles, false, true>), dim3(grid),
+                         dim3(kT), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attend_mfma_r32_kernel<kBits, kTiles, false, false>), dim3(grid),
+                         dim3(kT), 0, stream, p);
+  }
 }
 
 hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream) {

@@ -32,11 +32,16 @@ struct AttendProblem {
   int part0;               // first partial slot this launch writes (splits > 1 or part0 > 0)
   int extra_parts;         // slots splits .. splits + extra_parts - 1 were written by an
                            // earlier launch and join the combine
-  // Recent-token window (general kernel only): tokens [N - W, N) are read
-  // from float32 k_win / v_win [B*Hkv][W][D] instead of the packed cache.
+  // Recent-token window, float32 k_win / v_win [B*Hkv][W][D].  General
+  // kernel: tokens [N - W, N) are read from it instead of the packed cache.
+  // Matrix-core kernels (win_parts > 0): the W window tokens follow the N
+  // packed ones; the last win_parts of the `splits` workgroups of a head
+  // attend win_per_part window tokens each instead of packed blocks.
   const float* k_win;
   const float* v_win;
   int W;
+  int win_parts;
+  int win_per_part;
   int rows;                // (Hq / Hkv) * R: query rows sharing one KV head
   int bits, group;         // 4/8 and group; bits == 32 marks the float32 cache
   float qscale;            // sm_scale * log2(e)

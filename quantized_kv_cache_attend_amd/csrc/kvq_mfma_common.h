@@ -368,5 +368,128 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
     __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---- recent-token window parts -------------------------------------------------
+// A mixed cache ([RL] "prefill and decode": the newest tokens kept in
+// float32 beside the packed ones) attended in one launch: the last
+// p.win_parts workgroups of each head take the W float32 window tokens
+// (positions N .. N + W - 1) in parts of p.win_per_part instead of packed
+// blocks, run the same online softmax over them, kWinTile tokens at a time
+// through LDS, and join the split combine with their partial (m, z, u) like
+// any other split.  The work is small (W is a few dozen tokens) and runs
+// beside the packed splits' streaming.
+constexpr int kWinD = 128;    // head dimension of the matrix-core kernels
+constexpr int kWinTile = 8;   // window tokens per LDS tile
+
+template <int kRowsPad>
+struct WinSmem {
+  float q[kRowsPad][kWinD + 4];  // q * qscale (padded rows: distinct banks)
+  float k[kWinTile][kWinD + 4];
+  float v[kWinTile][kWinD];
+  float s[kRowsPad][kWinTile + 1];  // scores, then p
+  float m[kRowsPad], z[kRowsPad], a[kRowsPad];
+};
+
+// Window part `part` of head `head` into this thread's slots: query row r,
+// features slot_feature<kRun, kStride>(f0, i), i < kF (the caller's
+// split_combine mapping).  Every thread of the workgroup calls it (it holds
+// barriers); on return U, M, Z hold the part's u, m, z of row r (m = -inf,
+// z = u = 0 for a row with no legal token in the part).
+template <int kRowsPad, int kThreadsWG, int kF, int kRun, int kStride>
+__device__ __forceinline__ void window_part(const AttendProblem& p, WinSmem<kRowsPad>& ws,
+                                            long long head, int part, int r, int f0,
+                                            float (&U)[kF], float& M, float& Z) {
+  constexpr int kTPD = kThreadsWG / (kRowsPad * kWinTile);  // threads per score dot product
+  static_assert(kTPD * kRowsPad * kWinTile == kThreadsWG && (kTPD & (kTPD - 1)) == 0 &&
+                    kTPD <= 64, "one power-of-two group of lanes per (row, token) score");
+  const int tid = threadIdx.x;
+  const int rows = p.rows;
+  const int t_lo = part * p.win_per_part;
+  const int t_hi = min(p.W, t_lo + p.win_per_part);
+  for (int i = tid; i < kRowsPad * kWinD; i += kThreadsWG) {
+    const int rr = i / kWinD, d = i % kWinD;
+    ws.q[rr][d] = rr < rows ? p.q[(head * rows + rr) * kWinD + d] * p.qscale : 0.0f;
+  }
+  for (int rr = tid; rr < kRowsPad; rr += kThreadsWG) {
+    ws.m[rr] = -INFINITY;
+    ws.z[rr] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < kF; ++i) U[i] = 0.0f;
+  const float* kw = p.k_win + head * p.W * kWinD;
+  const float* vw = p.v_win + head * p.W * kWinD;
+  // causal limit of a row: its query sits at pos_end - R + r % R
+  const int lim0 = p.pos_end - p.R;
+  for (int t0 = t_lo; t0 < t_hi; t0 += kWinTile) {
+    __syncthreads();  // the previous tile is consumed (first tile: q, m, z are written)
+    for (int i = tid; i < kWinTile * kWinD / 4; i += kThreadsWG) {
+      const int j = i / (kWinD / 4), d = (i % (kWinD / 4)) * 4;
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = kk;
+      if (t0 + j < t_hi) {
+        kk = *reinterpret_cast<const f32x4*>(kw + static_cast<long long>(t0 + j) * kWinD + d);
+        vv = *reinterpret_cast<const f32x4*>(vw + static_cast<long long>(t0 + j) * kWinD + d);
+      }
+      *reinterpret_cast<f32x4*>(&ws.k[j][d]) = kk;
+      *reinterpret_cast<f32x4*>(&ws.v[j][d]) = vv;
+    }
+    __syncthreads();
+    {  // score of (row rr, token j): kTPD consecutive lanes, then a lane-group sum
+      const int dot = tid / kTPD, sub = tid % kTPD;
+      const int rr = dot / kWinTile, j = dot % kWinTile;
+      float acc = 0.0f;
+#pragma unroll 4
+      for (int d = sub * 4; d < kWinD; d += 4 * kTPD) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&ws.q[rr][d]);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&ws.k[j][d]);
+        acc = fmaf(a[0], b[0], acc);
+        acc = fmaf(a[1], b[1], acc);
+        acc = fmaf(a[2], b[2], acc);
+        acc = fmaf(a[3], b[3], acc);
+      }
+#pragma unroll
+      for (int o = kTPD / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      if (sub == 0) {
+        const int t = t0 + j;
+        const bool ok = rr < rows && t < t_hi && (!p.causal || p.N + t <= lim0 + rr % p.R);
+        ws.s[rr][j] = ok ? acc : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // online softmax of each row over the tile: both z and u move by alpha;
+    // a row with no legal token so far keeps m = -inf (exponents against 0)
+    for (int rr = tid; rr < kRowsPad; rr += kThreadsWG) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kWinTile; ++j) mx = fmaxf(mx, ws.s[rr][j]);
+      const float m_old = ws.m[rr];
+      const float m_new = fmaxf(m_old, mx);
+      const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+      float sum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kWinTile; ++j) {
+        const float pj = fast_exp2(ws.s[rr][j] - m_ref);
+        ws.s[rr][j] = pj;
+        sum += pj;
+      }
+      const float alpha = fast_exp2(m_old - m_ref);
+      ws.z[rr] = fmaf(alpha, ws.z[rr], sum);
+      ws.m[rr] = m_new;
+      ws.a[rr] = alpha;
+    }
+    __syncthreads();
+    const float alpha = ws.a[r];
+#pragma unroll
+    for (int i = 0; i < kF; ++i) {
+      const int f = slot_feature<kRun, kStride>(f0, i);
+      float add = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kWinTile; ++j) add = fmaf(ws.s[r][j], ws.v[j][f], add);
+      U[i] = fmaf(alpha, U[i], add);
+    }
+  }
+  __syncthreads();
+  M = ws.m[r];
+  Z = ws.z[r];
+}
+
 }  // namespace
 }  // namespace kvq

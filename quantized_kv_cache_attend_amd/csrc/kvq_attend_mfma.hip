@@ -1,5 +1,5 @@
-// Matrix-core fused attention for the 4-bit, group-32, D=128 packed cache
-// with at most 4 query rows per KV head (GQA group x queries <= 4).
+// Matrix-core fused attention for the 4- or 8-bit, group-32, D=128 packed
+// cache with at most 4 query rows per KV head (GQA group x queries <= 4).
 //
 // Method: the blocked online softmax of "Block KV decoding: less workspace,
 // more time" (huhohoo.com/en/docs/llm/kv-block-decode-cost), section "Do not
@@ -25,6 +25,9 @@
 //     2n+1 high nibble), k-step ks = 0..3;
 //   V block (2 KB): lane (n, q) reads 8 bytes at q*512 + g*128 + 8n =
 //     tokens 8q + (0..7) of byte column 16g + n (features 32g + 2n, +1);
+//   8-bit codes (4 KB blocks): the same lane reads 16 bytes at twice those
+//     offsets, the same two rows one byte per code (the first 8 bytes the
+//     row of the low nibble above, the next 8 the other);
 //   K scales of the block's group: 128 floats, channel order;
 //   V scales of the block: [value group][32 tokens].
 // Every load is a contiguous, coalesced buffer load into VGPRs; no LDS

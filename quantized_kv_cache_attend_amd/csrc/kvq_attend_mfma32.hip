@@ -1,6 +1,6 @@
-// Matrix-core fused attention for the 4-bit, group-32, D=128 packed cache
-// with 5 to 32 query rows per KV head (GQA group x queries), rows padded to
-// 32 so both products fill whole 16x16 matrix-core tiles.
+// Matrix-core fused attention for the 4- or 8-bit, group-32, D=128 packed
+// cache with 5 to 32 query rows per KV head (GQA group x queries), rows
+// padded to 16 or 32 so both products fill whole 16x16 matrix-core tiles.
 //
 // Method: the blocked online softmax of "Block KV decoding: less workspace,
 // more time" (huhohoo.com/en/docs/llm/kv-block-decode-cost), section "Do not

@@ -166,8 +166,6 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   p->win_parts = 0;
   p->win_per_part = 0;
   p->pos_end = N;
-  p->part0 = 0;
-  p->extra_parts = 0;
   p->D = D;
   p->rows = rows;
   p->bits = bits;

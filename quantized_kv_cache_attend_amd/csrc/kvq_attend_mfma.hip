@@ -524,7 +524,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
     }
   }
   const long long row0 = bh * rows;
-  if (p.splits + p.extra_parts == 1) {
+  if (p.splits == 1) {
     if (r < rows) {
 #pragma unroll
       for (int j = 0; j < kSlots; ++j)  // Z = 0: a causal row with no legal key

@@ -583,7 +583,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
     if (half == 0) __syncthreads();  // the first pair is read before the second overwrites it
   }
   const long long row0 = bh * rows;
-  if (p.splits + p.extra_parts == 1) {
+  if (p.splits == 1) {
     if (r < rows) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   }
 
   const long long row0 = bh * rows;
-  if (p.splits == 1 && p.part0 == 0) {
+  if (p.splits == 1) {
 #pragma unroll
     for (int i = 0; i < kAcc; ++i) {
       const int idx = tid + i * kThreads;
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
     }
   } else {
     const long long total_rows = static_cast<long long>(p.B) * p.Hkv * rows;
-    const long long base = static_cast<long long>(split + p.part0) * total_rows + row0;
+    const long long base = static_cast<long long>(split) * total_rows + row0;
 #pragma unroll
     for (int i = 0; i < kAcc; ++i) {
       const int idx = tid + i * kThreads;
@@ -361,9 +361,7 @@ hipError_t launch_attend_valu(const AttendProblem& p, hipStream_t stream) {
     case 64: e = launch_valu_d<64>(p, stream); break;
     default: e = launch_valu_d<128>(p, stream); break;
   }
-  // part0 > 0: the partials are extra slots of a later matrix-core call,
-  // whose fused combine merges them.
-  if (e != hipSuccess || p.splits == 1 || p.part0 != 0) return e;
+  if (e != hipSuccess || p.splits == 1) return e;
   return launch_combine(p, stream);
 }
 

@@ -29,9 +29,6 @@ struct AttendProblem {
   int cap;                 // tokens the packed layout is sized for (>= N; N for float32)
   int causal;              // 1: row r is query r % R at position pos_end - R + r % R (R > 1)
   int pos_end;             // position after the last query (N unless a window follows)
-  int part0;               // first partial slot this launch writes (splits > 1 or part0 > 0)
-  int extra_parts;         // slots splits .. splits + extra_parts - 1 were written by an
-                           // earlier launch and join the combine
   // Recent-token window, float32 k_win / v_win [B*Hkv][W][D].  General
   // kernel: tokens [N - W, N) are read from it instead of the packed cache.
   // Matrix-core kernels (win_parts > 0): the W window tokens follow the N

@@ -313,7 +313,7 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
     float Mg = -INFINITY, Zg = 0.0f, V[kF];
 #pragma unroll
     for (int i = 0; i < kF; ++i) V[i] = 0.0f;
-    const int parts = p.splits + p.extra_parts;  // extra slots: written by an earlier launch
+    const int parts = p.splits;
     for (int s0 = 0; s0 < parts; s0 += kBatch) {
       float ms[kBatch], zs[kBatch], us[kBatch][kF];
 #pragma unroll

@@ -63,20 +63,26 @@ __device__ __forceinline__ float decode_v(const AttendProblem& p, const Layout& 
 // ks_row[tl]: offset of token t0 + tl's K scale row ((t0 + tl) / group * D),
 // fgrp[f]: value group of feature f < D (f / group); both precomputed in LDS
 // so the decode does no integer division.
-template <int D, int SRC>
+// kStaged: the block's K scale rows and V scales were copied to LDS (kss,
+// vss; ks_row then counts from the first staged row), else they are read
+// from the cache arrays.  kFull: every token of the block is packed and
+// attended (no window token, none past the split), so no token is tested.
+template <int D, int SRC, bool kStaged, bool kFull>
 __device__ __forceinline__ void decode_block(const AttendProblem& p, const Layout& L, long long bh,
                                              int blk, int t_end, int t_win, float (*sK)[D + 1],
                                              float (*sV)[D], const int* ks_row,
-                                             const int* fgrp) {
+                                             const int* fgrp, const float* kss,
+                                             const float* vss) {
   constexpr int kQmax = SRC == 4 ? 7 : 127;
   constexpr int kKcols = kTile * SRC / 8;  // K byte columns per channel octet
   const int t0 = blk * kTile;
   const int t_pk = min(t_end, t_win);
-  auto window = [&](int tl) { return t0 + tl >= t_win && t0 + tl < t_end; };
+  auto window = [&](int tl) { return !kFull && t0 + tl >= t_win && t0 + tl < t_end; };
+  auto packed = [&](int tl) { return kFull || t0 + tl < t_pk; };
   const int tid = threadIdx.x;
   const unsigned* kw = reinterpret_cast<const unsigned*>(
       p.k_codes + bh * k_code_bytes_per_head(L) + static_cast<long long>(blk) * L.kblock_bytes);
-  const float* ks = p.k_scales + bh * k_scales_per_head(L);
+  const float* ks = kStaged ? kss : p.k_scales + bh * k_scales_per_head(L);
   for (int w = tid; w < L.kblock_bytes / 4; w += kThreads) {
     const unsigned word = kw[w];
     const int run = w >> 1;  // 8-byte run (octet o, column j)
@@ -93,19 +99,20 @@ __device__ __forceinline__ void decode_block(const AttendProblem& p, const Layou
           const int tl = 2 * j + h;
           if (window(tl)) continue;
           const int c = static_cast<int>(h ? byte >> 4 : byte & 15u) - kQmax;
-          sK[tl][d] = t0 + tl < t_pk ? static_cast<float>(c) * ks[ks_row[tl] + d] : 0.0f;
+          sK[tl][d] = packed(tl) ? static_cast<float>(c) * ks[ks_row[tl] + d] : 0.0f;
         }
       } else {
         if (window(j)) continue;
         const int c = static_cast<int>(byte) - kQmax;
-        sK[j][d] = t0 + j < t_pk ? static_cast<float>(c) * ks[ks_row[j] + d] : 0.0f;
+        sK[j][d] = packed(j) ? static_cast<float>(c) * ks[ks_row[j] + d] : 0.0f;
       }
     }
   }
   const unsigned* vw = reinterpret_cast<const unsigned*>(
       p.v_codes + bh * v_code_bytes_per_head(L) + static_cast<long long>(blk) * L.vblock_bytes);
-  const float* vs = p.v_scales + bh * v_scales_per_head(L) +
-                    static_cast<long long>(blk) * L.vgroups * kTile;  // [group][32 tokens]
+  const float* vs = kStaged ? vss
+                           : p.v_scales + bh * v_scales_per_head(L) +
+                                 static_cast<long long>(blk) * L.vgroups * kTile;  // [group][32 tokens]
   for (int w = tid; w < L.vblock_bytes / 4; w += kThreads) {
     const unsigned word = vw[w];
     const int run = w >> 1;  // 8-byte run (token octet o < 4, column f)
@@ -116,7 +123,7 @@ __device__ __forceinline__ void decode_block(const AttendProblem& p, const Layou
     for (int b = 0; b < 4; ++b) {
       const int tl = tq + b;
       if (window(tl)) continue;
-      const bool live = t0 + tl < t_pk;
+      const bool live = packed(tl);
       const unsigned byte = (word >> (8 * b)) & 255u;
       if (SRC == 4) {
         const int f = 2 * col;
@@ -145,6 +152,15 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   __shared__ float sM[kMaxRows], sZ[kMaxRows], sA[kMaxRows];
   __shared__ int sKsRow[kTile];     // K scale row offset of each token of the tile
   __shared__ int sFgrp[D];          // value group of each feature below D
+  // Groups of at least kStageMinGroup: a block's K scales span at most
+  // kStageKRows rows and its V scales at most kStageVGroups groups; they are
+  // copied to LDS once per tile (two contiguous runs) instead of being read
+  // per decoded element.
+  constexpr int kStageMinGroup = 8;
+  constexpr int kStageKRows = 5;
+  constexpr int kStageVGroups = (D + kStageMinGroup - 1) / kStageMinGroup;
+  __shared__ float sKss[kStageKRows * D];
+  __shared__ float sVss[kStageVGroups * kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -176,9 +192,30 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
     if (SRC != 32 && p.codes_aligned && t0 < t_win) {
       // Tiles start on block boundaries: decode the packed block word by
       // word, then the window's float32 rows of the tile (disjoint tokens).
-      if (tid < kTile) sKsRow[tid] = (t0 + tid) / p.group * D;
+      const bool staged = p.group >= kStageMinGroup;  // uniform
+      if (staged) {
+        const int row0 = t0 / p.group;
+        const int row1 = min((t0 + kTile - 1) / p.group, L.kgroups - 1);
+        const float* kr = p.k_scales + bh * k_scales_per_head(L) + static_cast<long long>(row0) * D;
+        for (int i = tid; i < (row1 - row0 + 1) * D; i += kThreads) sKss[i] = kr[i];
+        const float* vr = p.v_scales + bh * v_scales_per_head(L) +
+                          static_cast<long long>(t0 / kTile) * L.vgroups * kTile;
+        for (int i = tid; i < L.vgroups * kTile; i += kThreads) sVss[i] = vr[i];
+        if (tid < kTile) sKsRow[tid] = (min((t0 + tid) / p.group, row1) - row0) * D;
+      } else if (tid < kTile) {
+        sKsRow[tid] = (t0 + tid) / p.group * D;
+      }
       __syncthreads();
-      decode_block<D, SRC>(p, L, bh, t0 / kTile, t_end, t_win, sK, sV, sKsRow, sFgrp);
+      const bool full = t0 + kTile <= min(t_end, t_win);  // uniform
+      if (staged && full)
+        decode_block<D, SRC, true, true>(p, L, bh, t0 / kTile, t_end, t_win, sK, sV, sKsRow,
+                                         sFgrp, sKss, sVss);
+      else if (staged)
+        decode_block<D, SRC, true, false>(p, L, bh, t0 / kTile, t_end, t_win, sK, sV, sKsRow,
+                                          sFgrp, sKss, sVss);
+      else
+        decode_block<D, SRC, false, false>(p, L, bh, t0 / kTile, t_end, t_win, sK, sV, sKsRow,
+                                           sFgrp, nullptr, nullptr);
       if (t0 + kTile > t_win) {
         for (int i = tid; i < kTile * D; i += kThreads) {
           const int j = i / D, d = i % D;

@@ -145,7 +145,7 @@ __device__ __forceinline__ void decode_block(const AttendProblem& p, const Layou
 template <int D, int SRC>
 __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) {
   constexpr int kAcc = kMaxRows * D / kThreads;  // u accumulators per thread
-  __shared__ float sQ[kMaxRows][D];
+  __shared__ float sQ[kMaxRows][D + 1];  // padded: rows read together sit on distinct banks
   __shared__ float sK[kTile][D + 1];
   __shared__ float sV[kTile][D];
   __shared__ float sP[kMaxRows][kTile + 1];
@@ -247,9 +247,14 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
       const int r = i / kTile, j = i % kTile;
       float s = -INFINITY;
       if (j < tn && (!p.causal || t0 + j <= p.pos_end - p.R + r % p.R)) {
-        s = 0.0f;
+        // four independent partial sums (no single dependent chain of D FMAs)
+        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 8
-        for (int d = 0; d < D; ++d) s = fmaf(sQ[r][d], sK[j][d], s);
+        for (int d = 0; d < D; d += 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s4[e] = fmaf(sQ[r][d + e], sK[j][d + e], s4[e]);
+        }
+        s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
       }
       sP[r][j] = s;
     }
@@ -297,9 +302,13 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
       const int idx = tid + i * kThreads;
       if (idx < rows * D) {
         const int r = idx / D, f = idx % D;
-        float add = 0.0f;
+        float a2[2] = {0.0f, 0.0f};
 #pragma unroll 8
-        for (int j = 0; j < kTile; ++j) add = fmaf(sP[r][j], sV[j][f], add);
+        for (int j = 0; j < kTile; j += 2) {
+          a2[0] = fmaf(sP[r][j], sV[j][f], a2[0]);
+          a2[1] = fmaf(sP[r][j + 1], sV[j + 1][f], a2[1]);
+        }
+        const float add = a2[0] + a2[1];
         acc[i] = fmaf(sA[r], acc[i], add);
       }
     }

@@ -63,6 +63,49 @@ __device__ __forceinline__ float decode_v(const AttendProblem& p, const Layout& 
 // ks_row[tl]: offset of token t0 + tl's K scale row ((t0 + tl) / group * D),
 // fgrp[f]: value group of feature f < D (f / group); both precomputed in LDS
 // so the decode does no integer division.
+// Merge of one output (row, element e of the out / part_u arrays) over all
+// splits: M = max_s m_s, Z = sum_s 2^(m_s - M) z_s, U = sum_s 2^(m_s - M)
+// u_s, read with device-scope loads in batches of kBatch splits whose loads
+// are all issued before use; splits that saw no legal token (m = -inf) are
+// skipped and a row no split saw gets 0.
+__device__ __forceinline__ float merge_splits(const AttendProblem& p, long long total_rows,
+                                              long long row, long long e) {
+  constexpr int kBatch = 8;
+  float M = -INFINITY, Z = 0.0f, U = 0.0f;
+  for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+    float ms[kBatch], zs[kBatch], us[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const long long s = min(s0 + j, p.splits - 1);
+      ms[j] = __hip_atomic_load(&p.part_m[s * total_rows + row], __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+      zs[j] = __hip_atomic_load(&p.part_z[s * total_rows + row], __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+      us[j] = __hip_atomic_load(&p.part_u[s * total_rows * p.D + e], __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (s0 + j >= p.splits) ms[j] = -INFINITY;
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, ms[j]);
+    if (mb == -INFINITY) continue;
+    const float a = exp2f(M - mb);  // 0 while nothing is merged yet
+    Z *= a;
+    U *= a;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (ms[j] == -INFINITY) continue;
+      const float w = exp2f(ms[j] - mb);
+      Z = fmaf(w, zs[j], Z);
+      U = fmaf(w, us[j], U);
+    }
+    M = mb;
+  }
+  return Z > 0.0f ? U / Z : 0.0f;
+}
+
 // kStaged: the block's K scale rows and V scales were copied to LDS (kss,
 // vss; ks_row then counts from the first staged row), else they are read
 // from the cache arrays.  kFull: every token of the block is packed and
@@ -151,6 +194,7 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   __shared__ float sP[kMaxRows][kTile + 1];
   __shared__ float sM[kMaxRows], sZ[kMaxRows], sA[kMaxRows];
   __shared__ int sKsRow[kTile];     // K scale row offset of each token of the tile
+  __shared__ int sLast;             // this workgroup is the last split of its head to finish
   __shared__ int sFgrp[D];          // value group of each feature below D
   // Groups of at least kStageMinGroup: a block's K scales span at most
   // kStageKRows rows and its V scales at most kStageVGroups groups; they are
@@ -326,65 +370,43 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
         p.out[(row0 + r) * D + idx % D] = sZ[r] > 0.0f ? acc[i] / sZ[r] : 0.0f;
       }
     }
-  } else {
-    const long long total_rows = static_cast<long long>(p.B) * p.Hkv * rows;
-    const long long base = static_cast<long long>(split) * total_rows + row0;
-#pragma unroll
-    for (int i = 0; i < kAcc; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < rows * D) p.part_u[base * D + idx] = acc[i];
-    }
-    for (int r = tid; r < rows; r += kThreads) {
-      p.part_m[base + r] = sM[r];
-      p.part_z[base + r] = sZ[r];
-    }
+    return;
   }
-}
-
-// Merge the per-split (m, z, u) of one row ([RL] "two stops of the online
-// accumulation": partial statistics compose once brought to one base):
-//   M = max_s m_s,  Z = sum_s 2^(m_s - M) z_s,  U = sum_s 2^(m_s - M) u_s.
-// Splits that saw no token carry m = -inf and are skipped.  One thread per
-// (row, feature).
-__global__ __launch_bounds__(kThreads) void combine_kernel(AttendProblem p) {
-  const long long total_rows = static_cast<long long>(p.B) * p.Hkv * p.rows;
-  const long long tid = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
-  if (tid >= total_rows * p.D) return;
-  const long long row = tid / p.D;
-  // One pass in batches of kBatch splits, whose loads are all issued before
-  // any is used; the running (M, Z, U) moves to each batch's max with the
-  // same rescale.
-  constexpr int kBatch = 8;
-  float M = -INFINITY, Z = 0.0f, U = 0.0f;
-  for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
-    float ms[kBatch], zs[kBatch], us[kBatch];
+  // Several splits: store this split's partial (m, z, u) with device-scope
+  // stores, wait until they are acknowledged, take a ticket from the head's
+  // arrival counter; the last split to arrive merges them all ([RL] "two
+  // stops of the online accumulation") and resets the counter.
+  const long long total_rows = static_cast<long long>(p.B) * p.Hkv * rows;
+  const long long base = static_cast<long long>(split) * total_rows + row0;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const long long s = min(s0 + j, p.splits - 1);
-      ms[j] = p.part_m[s * total_rows + row];
-      zs[j] = p.part_z[s * total_rows + row];
-      us[j] = p.part_u[s * total_rows * p.D + tid];
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      if (s0 + j >= p.splits) ms[j] = -INFINITY;
-    float mb = M;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, ms[j]);
-    if (mb == -INFINITY) continue;  // no split so far saw a legal key
-    const float a = exp2f(M - mb);  // 0 while nothing is merged yet
-    Z *= a;
-    U *= a;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (ms[j] == -INFINITY) continue;
-      const float w = exp2f(ms[j] - mb);
-      Z = fmaf(w, zs[j], Z);
-      U = fmaf(w, us[j], U);
-    }
-    M = mb;
+  for (int i = 0; i < kAcc; ++i) {
+    if (i * kThreads >= rows * D) break;
+    const int idx = tid + i * kThreads;
+    if (idx < rows * D)
+      __hip_atomic_store(&p.part_u[base * D + idx], acc[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
-  p.out[tid] = Z > 0.0f ? U / Z : 0.0f;  // no split saw a legal key: 0
+  for (int r = tid; r < rows; r += kThreads) {
+    __hip_atomic_store(&p.part_m[base + r], sM[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.part_z[base + r], sZ[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above are acknowledged
+  __syncthreads();
+  unsigned* counter = &p.counters[bh * kCounterStride];
+  if (tid == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sLast = prev == static_cast<unsigned>(p.splits - 1);
+  }
+  __syncthreads();
+  if (!sLast) return;
+#pragma unroll
+  for (int i = 0; i < kAcc; ++i) {
+    if (i * kThreads >= rows * D) break;
+    const int idx = tid + i * kThreads;
+    if (idx < rows * D) p.out[row0 * D + idx] = merge_splits(p, total_rows, row0 + idx / D, row0 * D + idx);
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D>
@@ -407,15 +429,7 @@ hipError_t launch_attend_valu(const AttendProblem& p, hipStream_t stream) {
     case 64: e = launch_valu_d<64>(p, stream); break;
     default: e = launch_valu_d<128>(p, stream); break;
   }
-  if (e != hipSuccess || p.splits == 1) return e;
-  return launch_combine(p, stream);
-}
-
-hipError_t launch_combine(const AttendProblem& p, hipStream_t stream) {
-  const long long n = static_cast<long long>(p.B) * p.Hkv * p.rows * p.D;
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace kvq

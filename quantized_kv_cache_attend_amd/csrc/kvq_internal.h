@@ -86,7 +86,6 @@ constexpr int kMfmaMaxRows = 4;
 constexpr int kMfma32MaxRows = 32;
 int mfma_tokens_per_split(int N, int splits);
 hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream);
-hipError_t launch_combine(const AttendProblem& p, hipStream_t stream);
 hipError_t launch_stream_read(const void* data, long long bytes, unsigned* sink,
                               hipStream_t stream);
 

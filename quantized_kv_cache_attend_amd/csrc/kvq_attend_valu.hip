@@ -1,7 +1,7 @@
 // General fused attention over the packed cache, plain float32 VALU
 // arithmetic.  Serves every supported format (4/8-bit, any even group,
 // D in {32, 64, 128}, up to 64 query rows per KV head) and the float32-cache
-// path; the 4-bit group-32 D=128 hot case has a matrix-core kernel of its own.
+// path; the 4- and 8-bit group-32 D=128 cases have matrix-core kernels.
 //
 // Method, from "Block KV decoding: less workspace, more time"
 // (huhohoo.com/en/docs/llm/kv-block-decode-cost), section "Do not average
@@ -18,7 +18,8 @@
 // kTile tokens is decoded to float32 in LDS (the exact value
 // fl32((stored - qmax) * scale) the decode-all path produces), shared by
 // all query rows of the KV head (every GQA head and query), then scored,
-// folded into (m, z) and into u.
+// folded into (m, z) and into u.  With several splits the last workgroup of
+// a head to finish merges all of them (a ticket per head).
 #include "kvq_internal.h"
 #include "kvq_layout.h"
 

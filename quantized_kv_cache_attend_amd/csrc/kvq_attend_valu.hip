@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   constexpr int kAcc = kMaxRows * D / kThreads;  // u accumulators per thread
   __shared__ float sQ[kMaxRows][D + 1];  // padded: rows read together sit on distinct banks
   __shared__ float sK[kTile][D + 1];
-  __shared__ float sV[kTile][D];
+  __shared__ __align__(16) float sV[kTile][D];
   __shared__ float sP[kMaxRows][kTile + 1];
   __shared__ float sM[kMaxRows], sZ[kMaxRows], sA[kMaxRows];
   __shared__ int sKsRow[kTile];     // K scale row offset of each token of the tile
@@ -229,6 +229,9 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   float acc[kAcc];
 #pragma unroll
   for (int i = 0; i < kAcc; ++i) acc[i] = 0.0f;
+  // float32 cache with both arrays 16-byte aligned: vector row loads
+  const bool f32_vec = SRC == 32 && ((reinterpret_cast<uintptr_t>(p.k_f32) |
+                                      reinterpret_cast<uintptr_t>(p.v_f32)) & 15) == 0;
   __syncthreads();
 
   for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
@@ -269,6 +272,23 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
             sV[j][d] = decode_v<SRC>(p, L, bh, t0 + j, d);
           }
         }
+      }
+    } else if (SRC == 32 && f32_vec) {
+      // Float32 cache rows, 16-byte aligned: whole rows with 16-byte loads.
+      const float* krow = p.k_f32 + (bh * p.N + t0) * D;
+      const float* vrow = p.v_f32 + (bh * p.N + t0) * D;
+      for (int i = tid; i < kTile * (D / 4); i += kThreads) {
+        const int j = i / (D / 4), d = (i % (D / 4)) * 4;
+        float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
+        if (j < tn) {
+          kk = *reinterpret_cast<const float4*>(krow + j * D + d);
+          vv = *reinterpret_cast<const float4*>(vrow + j * D + d);
+        }
+        sK[j][d] = kk.x;
+        sK[j][d + 1] = kk.y;
+        sK[j][d + 2] = kk.z;
+        sK[j][d + 3] = kk.w;
+        *reinterpret_cast<float4*>(&sV[j][d]) = vv;
       }
     } else {
       // Element by element.  K: the 8 channels of an octet fastest, then the

@@ -319,9 +319,20 @@ def main():
             kvq.dequant_v(vc, vs, w.N, w.D, bits, group, out=vf)
             kvq.attend_f32(qd, kf, vf, num_splits=splits, workspace=ws, out=out)
         dec_us = timed(decode_all, reps)
+
+        def dequant_only():
+            kvq.dequant_k(kc, ks, w.N, w.D, bits, group, out=kf)
+            kvq.dequant_v(vc, vs, w.N, w.D, bits, group, out=vf)
+        deq_us = timed(dequant_only, reps)
+        # HBM bytes of decode-all: read the packed cache, write and read back
+        # the float32 K and V.
+        f32_bytes = 2 * kd.numel() * 4
         extra.update({"pack_us": round(pack_us, 1), "decode_all_us": round(dec_us, 1),
-                      "decode_all_kv_gbs": round(nbytes / (dec_us * 1e-6) / 1e9, 1)})
-        log(f"[bench] pack {pack_us:.1f} us, decode-all baseline {dec_us:.1f} us")
+                      "decode_all_dequant_us": round(deq_us, 1),
+                      "decode_all_kv_gbs": round(nbytes / (dec_us * 1e-6) / 1e9, 1),
+                      "decode_all_hbm_bytes": nbytes + 2 * f32_bytes})
+        log(f"[bench] pack {pack_us:.1f} us, decode-all baseline {dec_us:.1f} us "
+            f"(dequant {deq_us:.1f} us + float32 attend {dec_us - deq_us:.1f} us)")
 
         # Measured ceiling: a plain streaming read (kvq_stream_read) of the
         # same byte count, rotating over as many buffers as the cache copies.

@@ -127,7 +127,8 @@ kvq_status kvq_pack_v(const float* v, int B, int H, int N, int D, int bits, int 
  * Decode the whole packed cache back to float32 [B][H][N][D], cropping the
  * padding: out = fl32((stored - qmax) * scale), one float32 multiply ([KPG]
  * "what a byte holds").  The decode-everything half of the baseline in
- * [BKD] "Compare equivalent representations first". */
+ * [BKD] "Compare equivalent representations first".  N * D must be below
+ * 2^32 (KVQ_ERR_UNSUPPORTED otherwise). */
 kvq_status kvq_dequant_k(const uint8_t* codes, const float* scales, int B, int H, int N, int D,
                          int bits, int group, float* out, void* stream);
 kvq_status kvq_dequant_v(const uint8_t* codes, const float* scales, int B, int H, int N, int D,

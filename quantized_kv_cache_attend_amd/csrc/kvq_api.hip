@@ -300,6 +300,8 @@ kvq_status kvq_dequant_k(const uint8_t* codes, const float* scales, int B, int H
                          int bits, int group, float* out, void* stream) {
   const kvq_status st = codec_check(codes, scales, out, B, H, N, D, bits, group);
   if (st != KVQ_OK) return st;
+  if (static_cast<long long>(N) * D >= (1LL << 32))
+    return fail(KVQ_ERR_UNSUPPORTED, "dequant of N * D >= 2^32 elements per head (N=%d D=%d)", N, D);
   return hip_status(launch_dequant(codes, scales, B, H, N, D, bits, group, true, out,
                                    static_cast<hipStream_t>(stream)),
                     "dequant_k launch");
@@ -309,6 +311,8 @@ kvq_status kvq_dequant_v(const uint8_t* codes, const float* scales, int B, int H
                          int bits, int group, float* out, void* stream) {
   const kvq_status st = codec_check(codes, scales, out, B, H, N, D, bits, group);
   if (st != KVQ_OK) return st;
+  if (static_cast<long long>(N) * D >= (1LL << 32))
+    return fail(KVQ_ERR_UNSUPPORTED, "dequant of N * D >= 2^32 elements per head (N=%d D=%d)", N, D);
   return hip_status(launch_dequant(codes, scales, B, H, N, D, bits, group, false, out,
                                    static_cast<hipStream_t>(stream)),
                     "dequant_v launch");

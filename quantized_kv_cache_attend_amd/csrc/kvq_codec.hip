@@ -277,17 +277,19 @@ __device__ __forceinline__ int load_code(const uint8_t* head, long long byte, in
 // Decode to the original [B][H][N][D] layout, one thread per output element
 // (d fastest, so the float32 stores coalesce).  fl32((stored - qmax) * s):
 // the integer difference is exact in float32, the multiply rounds once.
+// Grid: x over the N * D elements of one head (32-bit index arithmetic),
+// y * z over the heads.
 template <int BITS, bool K_STYLE>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ scales,
                                                       long long BH, Layout L,
                                                       float* __restrict__ out) {
-  const long long tid = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (tid >= BH * L.N * static_cast<long long>(L.D)) return;
-  const int d = static_cast<int>(tid % L.D);
-  const long long rest = tid / L.D;
-  const int n = static_cast<int>(rest % L.N);
-  const long long bh = rest / L.N;
+  const unsigned e = blockIdx.x * 256u + threadIdx.x;
+  const long long bh = static_cast<long long>(blockIdx.z) * gridDim.y + blockIdx.y;
+  if (bh >= BH || e >= static_cast<unsigned>(L.N) * static_cast<unsigned>(L.D)) return;
+  const int n = static_cast<int>(e / static_cast<unsigned>(L.D));
+  const int d = static_cast<int>(e - static_cast<unsigned>(n) * static_cast<unsigned>(L.D));
+  const long long tid = bh * L.N * static_cast<long long>(L.D) + e;
   int c;
   float s;
   if (K_STYLE) {
@@ -298,6 +300,55 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     s = scales[bh * v_scales_per_head(L) + v_scale_index(L, n, d)];
   }
   out[tid] = static_cast<float>(c - Codec<BITS>::kQmaxInt) * s;
+}
+
+// The same decode, four consecutive features of one token per thread (D a
+// multiple of 4; code, scale and output arrays 4-, 16- and 16-byte
+// aligned): one 16-byte store, K's four code bytes in one 4-byte load and
+// its four scales in one 16-byte load.
+template <int BITS, bool K_STYLE>
+__global__ __launch_bounds__(256) void dequant4_kernel(const uint8_t* __restrict__ codes,
+                                                       const float* __restrict__ scales,
+                                                       long long BH, Layout L,
+                                                       float* __restrict__ out) {
+  const unsigned e = blockIdx.x * 256u + threadIdx.x;  // quad index inside the head
+  const long long bh = static_cast<long long>(blockIdx.z) * gridDim.y + blockIdx.y;
+  const unsigned quads = static_cast<unsigned>(L.D) / 4;
+  if (bh >= BH || e >= static_cast<unsigned>(L.N) * quads) return;
+  const int n = static_cast<int>(e / quads);
+  const int d = static_cast<int>(e - static_cast<unsigned>(n) * quads) * 4;
+  constexpr int kQ = Codec<BITS>::kQmaxInt;
+  int c[4];
+  float s[4];
+  if (K_STYLE) {
+    // channels d .. d+3 sit in one 4-byte half of an 8-byte run
+    const unsigned w = *reinterpret_cast<const unsigned*>(
+        codes + bh * k_code_bytes_per_head(L) + k_code_byte(L, n, d));
+    const int sh = BITS == 4 ? 4 * (n & 1) : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      c[i] = static_cast<int>((w >> (8 * i + sh)) & (BITS == 4 ? 15u : 255u));
+    const float4 sc = *reinterpret_cast<const float4*>(
+        scales + bh * k_scales_per_head(L) + k_scale_index(L, n, d));
+    s[0] = sc.x;
+    s[1] = sc.y;
+    s[2] = sc.z;
+    s[3] = sc.w;
+  } else {
+    const uint8_t* head = codes + bh * v_code_bytes_per_head(L);
+    const float* vs = scales + bh * v_scales_per_head(L);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = load_code<BITS>(head, v_code_byte(L, n, d + i), (d + i) & 1);
+      s[i] = vs[v_scale_index(L, n, d + i)];
+    }
+  }
+  float4 o;
+  o.x = static_cast<float>(c[0] - kQ) * s[0];
+  o.y = static_cast<float>(c[1] - kQ) * s[1];
+  o.z = static_cast<float>(c[2] - kQ) * s[2];
+  o.w = static_cast<float>(c[3] - kQ) * s[3];
+  *reinterpret_cast<float4*>(out + (bh * L.N + n) * static_cast<long long>(L.D) + d) = o;
 }
 
 inline unsigned grid_for(long long threads) {
@@ -659,21 +710,46 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scales, int B, int 
                           int bits, int group, bool k_style, float* out, hipStream_t stream) {
   const long long BH = static_cast<long long>(B) * H;
   const Layout L = make_layout(N, D, bits, group);
-  const unsigned grid = grid_for(BH * N * static_cast<long long>(D));
+  // heads over y (at most 65535) and z
+  const unsigned hy = static_cast<unsigned>(BH < 65535 ? BH : 65535);
+  const unsigned hz = static_cast<unsigned>((BH + hy - 1) / hy);
+  const bool quad = D % 4 == 0 && reinterpret_cast<uintptr_t>(codes) % 4 == 0 &&
+                    reinterpret_cast<uintptr_t>(scales) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(out) % 16 == 0;
+  if (quad) {
+    const dim3 g4(grid_for(static_cast<long long>(N) * (D / 4)), hy, hz);
+    if (k_style) {
+      if (bits == 4)
+        hipLaunchKernelGGL((dequant4_kernel<4, true>), g4, dim3(256), 0, stream, codes, scales,
+                           BH, L, out);
+      else
+        hipLaunchKernelGGL((dequant4_kernel<8, true>), g4, dim3(256), 0, stream, codes, scales,
+                           BH, L, out);
+    } else {
+      if (bits == 4)
+        hipLaunchKernelGGL((dequant4_kernel<4, false>), g4, dim3(256), 0, stream, codes, scales,
+                           BH, L, out);
+      else
+        hipLaunchKernelGGL((dequant4_kernel<8, false>), g4, dim3(256), 0, stream, codes, scales,
+                           BH, L, out);
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid(grid_for(static_cast<long long>(N) * D), hy, hz);
   if (k_style) {
     if (bits == 4)
-      hipLaunchKernelGGL((dequant_kernel<4, true>), dim3(grid), dim3(256), 0, stream, codes,
-                         scales, BH, L, out);
+      hipLaunchKernelGGL((dequant_kernel<4, true>), grid, dim3(256), 0, stream, codes, scales, BH,
+                         L, out);
     else
-      hipLaunchKernelGGL((dequant_kernel<8, true>), dim3(grid), dim3(256), 0, stream, codes,
-                         scales, BH, L, out);
+      hipLaunchKernelGGL((dequant_kernel<8, true>), grid, dim3(256), 0, stream, codes, scales, BH,
+                         L, out);
   } else {
     if (bits == 4)
-      hipLaunchKernelGGL((dequant_kernel<4, false>), dim3(grid), dim3(256), 0, stream, codes,
-                         scales, BH, L, out);
+      hipLaunchKernelGGL((dequant_kernel<4, false>), grid, dim3(256), 0, stream, codes, scales,
+                         BH, L, out);
     else
-      hipLaunchKernelGGL((dequant_kernel<8, false>), dim3(grid), dim3(256), 0, stream, codes,
-                         scales, BH, L, out);
+      hipLaunchKernelGGL((dequant_kernel<8, false>), grid, dim3(256), 0, stream, codes, scales,
+                         BH, L, out);
   }
   return hipGetLastError();
 }

@@ -122,6 +122,9 @@ def test_codec_rejects_before_launch():
     for fn in (lib.kvq_dequant_k, lib.kvq_dequant_v):
         assert fn(FAKE, None, 1, 1, 8, 8, 4, 8, FAKE2, None) == kvq.KVQ_ERR_INVALID
         assert fn(FAKE, FAKE2, 1, 1, 8, 8, 6, 8, FAKE2, None) == kvq.KVQ_ERR_INVALID
+        # 32-bit element index per head
+        assert fn(FAKE, FAKE2, 1, 1, 1 << 25, 128, 4, 32, ctypes.c_void_p(1 << 44),
+                  None) == kvq.KVQ_ERR_UNSUPPORTED
 
 
 def test_attend_f32_rejects_before_launch():

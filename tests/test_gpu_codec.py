@@ -97,3 +97,14 @@ def test_pack_full_gqa_n32768_sampled_heads():
         assert np.array_equal(host(gks[b:b + 1, h:h + 1]), ks)
         assert np.array_equal(host(gvc[b:b + 1, h:h + 1]), vc)
         assert np.array_equal(host(gvs[b:b + 1, h:h + 1]), vs)
+
+
+@pytest.mark.parametrize("D", [8, 6])    # four-feature and one-element dequant kernels
+def test_pack_dequant_more_heads_than_a_grid_row(D):
+    """66,000 (batch, head) pairs, more than one grid dimension holds: the
+    dequant grid spreads heads over two dimensions; every byte and float
+    against the oracle."""
+    rng = np.random.default_rng(90 + D)
+    k = rng.standard_normal((1100, 60, 3, D), dtype=np.float32)
+    v = rng.standard_normal((1100, 60, 3, D), dtype=np.float32)
+    _check_pack_dequant(k, v, 4, 2, f"heads=66000 D={D}")

@@ -234,6 +234,25 @@ def test_attend_mfma_ragged_and_gqa_shapes(hq, hkv, r, n):
         assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("hq,hkv,r", [(8, 1, 1), (5, 1, 1), (6, 3, 4), (7, 1, 1), (4, 1, 2)])
+@pytest.mark.parametrize("n", [1, 35, 1021, 4097])
+def test_attend_mfma_five_to_eight_rows(hq, hkv, r, n, bits):
+    """5..8 query rows per KV head (a GQA group of 8 with one query, or 4
+    heads x 2 queries) on the matrix-core path, ragged token counts, against
+    the oracle and the general kernel."""
+    w = Workload("rg2", 2, hq, hkv, r, n, 128, ((bits, 32),))
+    q, k, v = make_qkv(w, 9)
+    announce(f"attend mfma 5-8 rows hq={hq} hkv={hkv} r={r} n={n} {bits}b")
+    want = _oracle(q, k, v, bits, 32)
+    cache = _gpu_cache(k, v, bits, 32)
+    general = _run(q, cache, n, bits, 32, num_splits=3, variant="valu")
+    for splits in (1, 3, 0, 64):
+        got = _run(q, cache, n, bits, 32, num_splits=splits, variant="mfma")
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
+        assert max_abs(got, general) <= SPLIT_TOL, (splits, max_abs(got, general))
+
+
 @pytest.mark.parametrize("dist", ["clean", "early", "late"])
 @pytest.mark.parametrize("scale_k", [False, True])
 def test_attend_mfma_peaky_and_channel_scaled(dist, scale_k):

@@ -18,7 +18,7 @@ kvq = pytest.importorskip("quantized_kv_cache_attend_amd")
 TOL = 1e-4
 
 
-MFMA_OK = {(4, 32, 128)}   # (bits, group, D) the matrix-core kernels take (<= 32 rows)
+MFMA_OK = {(4, 32, 128), (8, 32, 128)}   # (bits, group, D) the matrix-core kernels take (<= 32 rows)
 
 
 @pytest.mark.parametrize("variant", ["valu", "mfma", "auto"])
@@ -31,6 +31,7 @@ MFMA_OK = {(4, 32, 128)}   # (bits, group, D) the matrix-core kernels take (<= 3
     (1, 2, 2, 4, 3, 128, 4, 32),        # 4-row kernel, N < R
     (2, 4, 1, 8, 70, 128, 4, 32),       # 32 rows, the mask spans two 32-token blocks
     (1, 4, 2, 2, 33, 128, 4, 32),       # 4 rows, tokens 32.. in a second block
+    (2, 4, 1, 2, 70, 128, 4, 32),       # 8 rows per KV head
 ])
 def test_causal_chunk(B, hq, hkv, r, n, d, bits, group, variant):
     if variant == "mfma" and (bits, group, d) not in MFMA_OK:

@@ -44,7 +44,8 @@ def test_attend_window(B, hq, hkv, r, n, w, d, bits, group, causal):
         assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
 
 
-@pytest.mark.parametrize("hq,hkv,r,causal", [(32, 8, 1, False), (16, 2, 2, True), (8, 8, 4, True)])
+@pytest.mark.parametrize("hq,hkv,r,causal", [(32, 8, 1, False), (16, 2, 2, True), (8, 8, 4, True),
+                                             (8, 1, 1, False), (4, 2, 4, True)])
 def test_fused_window_equals_general_kernel(hq, hkv, r, causal):
     """The fused form (window partials + matrix-core combine; the 48-token
     window in two parts, or in one when the workspace has a single extra

@@ -87,9 +87,16 @@ typedef enum kvq_attend_flags {
                             query r (position N-R+r) reads tokens j <= N-R+r */
 } kvq_attend_flags;
 
+/* ---- size limits (every call) -------------------------------------------------
+ * N (and capacity) <= 2^31 - 1 - 2^16 tokens, D <= 2^24 and group <= 2^16:
+ * larger values make the 32-bit layout arithmetic overflow and are rejected
+ * with KVQ_ERR_INVALID (the sizing calls return 0). */
+
 /* ---- host-only sizing (no device work, never fails) ------------------------
- * Byte / element counts of the packed arrays; 0 if an argument is invalid
- * (size < 1, bits not 4 or 8, group odd or < 2). */
+ * Byte / element counts of the packed arrays ([KPG] "how to know the file
+ * really stores 4-bit": codes plus one float32 scale per group, in the
+ * layouts above); 0 if an argument is invalid (size < 1, bits not 4 or 8,
+ * group odd or < 2, a size past the limits above). */
 size_t kvq_k_code_bytes(int B, int H, int N, int D, int bits, int group);  /* B*H*nblocks*D8*32*bits */
 size_t kvq_k_scale_count(int B, int H, int N, int D, int bits, int group); /* B*H*ceil(N/group)*D */
 size_t kvq_v_code_bytes(int B, int H, int N, int D, int bits, int group);  /* B*H*nblocks*32*Dpad*bits/8 */
@@ -109,7 +116,12 @@ int kvq_attend_auto_splits(int B, int Hkv, int N);
  * split count: ZERO-FILL a workspace once before its first use, and again
  * before a call with more (batch, KV head) pairs than any earlier call on it
  * (its counters would reach into earlier partials).  Calls that run at the
- * same time must use different workspaces. */
+ * same time must use different workspaces.  A call that finds a head's
+ * counter already at or above its split count (a workspace that was not
+ * zero-filled as required) cannot trust any ticket: it writes NaN to that
+ * head's output rows instead of a merge, and leaves the counter non-zero, so
+ * the error shows until the workspace is zero-filled.  (A counter left at a
+ * small non-zero value below the split count cannot be told from a live one.) */
 size_t kvq_attend_workspace_bytes(int B, int Hq, int Hkv, int R, int N, int D, int num_splits);
 
 /* ---- kvq_pack_k / kvq_pack_v ------------------------------------------------
@@ -234,7 +246,8 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
  * conditions with capacity for N) and the workspace holds S + P split slots,
  * 1 <= P <= ceil(W / 32) (kvq_attend_workspace_bytes(B, Hq, Hkv, R, N + W, D,
  * S + P); S = num_splits, or the matrix-core kernel's own automatic count, at
- * most kvq_attend_auto_splits(B, Hkv, N)), the call is fused into one
+ * most kvq_attend_auto_splits(B, Hkv, N)), and k_win and v_win are 16-byte
+ * aligned (the window rows are read with 16-byte loads), the call is fused into one
  * matrix-core launch: per KV head, S workgroups attend the packed tokens and
  * P more the window tokens (P the largest count the workspace holds: one
  * workgroup per 32 window tokens at P = ceil(W / 32)), and the split combine
@@ -261,8 +274,10 @@ kvq_status kvq_attend_f32(const float* q, const float* k, const float* v,
 
 /* ---- kvq_stream_read ------------------------------------------------------------------
  * Measurement aid, not part of the method: reads `bytes` (a positive multiple
- * of 16) at device pointer `data` (16-byte aligned) once, with 16-byte loads
- * spread over the whole chip, and discards them (`sink`: a device word that is
+ * of 16) at device pointer `data` (16-byte aligned) once, one contiguous chunk
+ * per workgroup with 16-byte nontemporal loads spread over the whole chip
+ * (the fastest plain read shape measured on MI355X), and discards them
+ * (`sink`: a device word that is
  * written only if the XOR of all the data equals an arbitrary constant).  The
  * fused attend reads every KV byte once ([BKD] "every position is still
  * read"), so this plain read of the same byte count is its measured HBM

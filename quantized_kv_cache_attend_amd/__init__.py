@@ -134,7 +134,51 @@ def new_workspace(B, Hq, Hkv, R, N, D, num_splits=0, device="cuda"):
     """A zero-filled workspace (the library requires zeros before first use)."""
     torch = _torch()
     n = workspace_bytes(B, Hq, Hkv, R, N, D, num_splits)
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    ws = torch.zeros(n, dtype=torch.uint8, device=device)
+    ws._kvq_clean = n  # every byte is zero: any call's counters start at 0
+    return ws
+
+
+# Bytes between two arrival counters at the start of a workspace (one counter
+# per (batch, KV head); include/kvq.h, kvq_attend_workspace_bytes).
+_COUNTER_STRIDE = 256
+
+
+def _prepare_workspace(ws, heads, name="workspace"):
+    """Check a caller's workspace and return its size in bytes.  The library
+    keeps one arrival counter per (batch, KV head) at the start of the
+    workspace and needs them zero when a call starts; every completed call
+    leaves its counters zero.  A workspace that served calls with fewer
+    (batch, KV head) pairs holds split partials where a larger call's counters
+    go, so that range is zero-filled here (a fill kernel on the current
+    stream) before the first call that needs it.  A workspace this binding has
+    not seen before is taken to be zero-filled, as the C contract requires."""
+    torch = _torch()
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not ws.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    nbytes = ws.numel() * ws.element_size()
+    need = min(_COUNTER_STRIDE * heads, nbytes)
+    clean = getattr(ws, "_kvq_clean", None)
+    if clean is None:
+        clean = need
+    elif clean < need:
+        ws.view(torch.uint8)[clean:need].zero_()
+        clean = need
+    ws._kvq_clean = clean
+    return nbytes
+
+
+def _check_out(out, shape, device):
+    torch = _torch()
+    _need(out, torch.float32, "out")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    if out.device != device:
+        raise ValueError("out must be on the same device as q")
 
 
 # --- calls -----------------------------------------------------------------------------
@@ -217,19 +261,23 @@ def attend(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scal
         _check_cache((k_codes, k_scales, v_codes, v_scales), B, Hkv, cap, D, bits, group)
     if workspace is None:
         workspace = new_workspace(B, Hq, Hkv, R, N, D, num_splits, device=q.device)
+    ws_bytes = _prepare_workspace(workspace, B * Hkv)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q.shape, q.device)
+    if variant not in VARIANTS:
+        raise ValueError(f"variant must be one of {sorted(VARIANTS)}")
     if capacity is None and not causal:
         _check(lib.kvq_attend_variant(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                       _ptr(v_scales), B, Hq, Hkv, R, N, D, bits, group,
-                                      float(sm_scale), num_splits, _ptr(workspace),
-                                      workspace.numel(), _ptr(out), VARIANTS[variant],
-                                      _stream(q.device)), "kvq_attend")
+                                      float(sm_scale), num_splits, _ptr(workspace), ws_bytes,
+                                      _ptr(out), VARIANTS[variant], _stream(q.device)),
+               "kvq_attend")
     else:
         _check(lib.kvq_attend_cache(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                     _ptr(v_scales), B, Hq, Hkv, R, N, cap, D, bits, group,
-                                    float(sm_scale), num_splits, _ptr(workspace),
-                                    workspace.numel(), _ptr(out), VARIANTS[variant],
+                                    float(sm_scale), num_splits, _ptr(workspace), ws_bytes,
+                                    _ptr(out), VARIANTS[variant],
                                     KVQ_ATTEND_CAUSAL if causal else 0, _stream(q.device)),
                "kvq_attend_cache")
     return out
@@ -256,12 +304,14 @@ def attend_window(q, k_codes, k_scales, v_codes, v_scales, k_win, v_win, N, bits
     if workspace is None:  # a slot per 32 window tokens beyond the splits: the fused form
         slots = (num_splits or auto_splits(B, Hkv, N + W)) + (W + 31) // 32
         workspace = new_workspace(B, Hq, Hkv, R, N + W, D, slots, device=q.device)
+    ws_bytes = _prepare_workspace(workspace, B * Hkv)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q.shape, q.device)
     _check(lib.kvq_attend_window(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                  _ptr(v_scales), _ptr(k_win), _ptr(v_win), B, Hq, Hkv, R, N, W,
                                  cap, D, bits, group, float(sm_scale), num_splits,
-                                 _ptr(workspace), workspace.numel(), _ptr(out),
+                                 _ptr(workspace), ws_bytes, _ptr(out),
                                  KVQ_ATTEND_CAUSAL if causal else 0, _stream(q.device)),
            "kvq_attend_window")
     return out
@@ -312,14 +362,24 @@ def attend_f32(q, k, v, sm_scale=0.0, num_splits=0, workspace=None, out=None):
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, torch.float32, n)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, R, D] and k, v [B, Hkv, N, D]")
     B, Hq, R, D = q.shape
     Hkv, N = k.shape[1], k.shape[2]
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v must have k's shape {tuple(k.shape)}, got {tuple(v.shape)}")
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k must be [B={B}, Hkv, N, D={D}], got {tuple(k.shape)}")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
     if workspace is None:
         workspace = new_workspace(B, Hq, Hkv, R, N, D, num_splits, device=q.device)
+    ws_bytes = _prepare_workspace(workspace, B * Hkv)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q.shape, q.device)
     _check(lib.kvq_attend_f32(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, R, N, D, float(sm_scale),
-                              num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
+                              num_splits, _ptr(workspace), ws_bytes, _ptr(out),
                               _stream(q.device)), "kvq_attend_f32")
     return out
 

@@ -28,9 +28,18 @@ kvq_status ok() {
   return KVQ_OK;
 }
 
+// Size limits that keep the layout arithmetic (32-bit ints in make_layout)
+// from overflowing: tokens + group and D rounded up to the group stay below
+// 2^31, and D * bits / 8 well below it.
+constexpr int kMaxGroup = 1 << 16;
+constexpr int kMaxTokens = 0x7fffffff - (1 << 16);
+constexpr int kMaxDim = 1 << 24;
+
 bool format_ok(int bits, int group) {
-  return (bits == 4 || bits == 8) && group >= 2 && group % 2 == 0;
+  return (bits == 4 || bits == 8) && group >= 2 && group % 2 == 0 && group <= kMaxGroup;
 }
+
+bool sizes_in_range(int N, int D) { return N <= kMaxTokens && D <= kMaxDim; }
 
 long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
 
@@ -97,12 +106,15 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   if (B < 1 || Hq < 1 || Hkv < 1 || R < 1 || N < 1 || D < 1)
     return fail(KVQ_ERR_INVALID, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d R=%d N=%d D=%d)", B, Hq,
                 Hkv, R, N, D);
+  if (!sizes_in_range(N, D) || cap > kMaxTokens)
+    return fail(KVQ_ERR_INVALID, "N=%d / capacity=%d above %d tokens or D=%d above %d", N, cap,
+                kMaxTokens, D, kMaxDim);
   if (Hq % Hkv) return fail(KVQ_ERR_INVALID, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (cap < n_packed || cap < 1)
     return fail(KVQ_ERR_INVALID, "capacity=%d < %d packed tokens", cap, n_packed);
   if (bits != 32 && !format_ok(bits, group))
-    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
-                group);
+    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group in [2, %d])",
+                bits, group, kMaxGroup);
   if (num_splits < 0) return fail(KVQ_ERR_INVALID, "num_splits=%d < 0", num_splits);
   if (!(std::isfinite(sm_scale)) || sm_scale < 0.0f)
     return fail(KVQ_ERR_INVALID, "sm_scale must be finite and >= 0");
@@ -241,8 +253,11 @@ kvq_status codec_check(const void* a, const void* b, const void* c, int B, int H
   if (B < 1 || H < 1 || N < 1 || D < 1)
     return fail(KVQ_ERR_INVALID, "sizes must be >= 1 (B=%d H=%d N=%d D=%d)", B, H, N, D);
   if (!format_ok(bits, group))
-    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
-                group);
+    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group in [2, %d])",
+                bits, group, kMaxGroup);
+  if (!sizes_in_range(N, D))
+    return fail(KVQ_ERR_INVALID, "N=%d above %d tokens or D=%d above %d", N, kMaxTokens, D,
+                kMaxDim);
   return KVQ_OK;
 }
 
@@ -251,19 +266,23 @@ kvq_status codec_check(const void* a, const void* b, const void* c, int B, int H
 extern "C" {
 
 size_t kvq_k_code_bytes(int B, int H, int N, int D, int bits, int group) {
-  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
+  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group) || !sizes_in_range(N, D))
+    return 0;
   return static_cast<size_t>(B) * H * k_code_bytes_per_head(make_layout(N, D, bits, group));
 }
 size_t kvq_k_scale_count(int B, int H, int N, int D, int bits, int group) {
-  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
+  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group) || !sizes_in_range(N, D))
+    return 0;
   return static_cast<size_t>(B) * H * k_scales_per_head(make_layout(N, D, bits, group));
 }
 size_t kvq_v_code_bytes(int B, int H, int N, int D, int bits, int group) {
-  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
+  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group) || !sizes_in_range(N, D))
+    return 0;
   return static_cast<size_t>(B) * H * v_code_bytes_per_head(make_layout(N, D, bits, group));
 }
 size_t kvq_v_scale_count(int B, int H, int N, int D, int bits, int group) {
-  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group)) return 0;
+  if (B < 1 || H < 1 || N < 1 || D < 1 || !format_ok(bits, group) || !sizes_in_range(N, D))
+    return 0;
   return static_cast<size_t>(B) * H * v_scales_per_head(make_layout(N, D, bits, group));
 }
 
@@ -326,9 +345,12 @@ kvq_status kvq_cache_clear(int B, int H, int capacity, int D, int bits, int grou
   if (B < 1 || H < 1 || capacity < 1 || D < 1)
     return fail(KVQ_ERR_INVALID, "sizes must be >= 1 (B=%d H=%d capacity=%d D=%d)", B, H,
                 capacity, D);
+  if (!sizes_in_range(capacity, D))
+    return fail(KVQ_ERR_INVALID, "capacity=%d above %d tokens or D=%d above %d", capacity,
+                kMaxTokens, D, kMaxDim);
   if (!format_ok(bits, group))
-    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
-                group);
+    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group in [2, %d])",
+                bits, group, kMaxGroup);
   if (!aligned(k_scales, 4) || !aligned(v_scales, 4))
     return fail(KVQ_ERR_INVALID, "float arrays must be 4-byte aligned");
   return hip_status(launch_cache_clear(B, H, capacity, D, bits, group, k_codes, k_scales, v_codes,
@@ -347,9 +369,12 @@ kvq_status kvq_append(const float* k_new, const float* v_new, int B, int H, int 
   if (capacity < 1 || static_cast<long long>(N) + T > capacity)
     return fail(KVQ_ERR_INVALID, "N + T = %lld exceeds capacity=%d",
                 static_cast<long long>(N) + T, capacity);
+  if (!sizes_in_range(capacity, D))
+    return fail(KVQ_ERR_INVALID, "capacity=%d above %d tokens or D=%d above %d", capacity,
+                kMaxTokens, D, kMaxDim);
   if (!format_ok(bits, group))
-    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group >= 2)", bits,
-                group);
+    return fail(KVQ_ERR_INVALID, "format bits=%d group=%d (need bits 4|8, even group in [2, %d])",
+                bits, group, kMaxGroup);
   if (!aligned(k_new, 4) || !aligned(v_new, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4) ||
       !aligned(k_tail, 4))
     return fail(KVQ_ERR_INVALID, "float arrays must be 4-byte aligned");
@@ -440,7 +465,8 @@ kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float
   // attend the packed tokens and P more attend the W float32 window tokens
   // (one per 32 tokens when the workspace has the slots); the fused combine
   // merges all S + P partials.
-  if (N >= 1) {
+  // (The fused form reads the window rows with 16-byte loads.)
+  if (N >= 1 && aligned(k_win, 16) && aligned(v_win, 16)) {
     AttendProblem pm = p;
     pm.N = N;
     pm.pos_end = N + W;

@@ -417,10 +417,19 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
   if (tid == 0) {
     const unsigned prev =
         __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sLast = prev == static_cast<unsigned>(p.splits - 1);
+    sLast = ticket_outcome(prev, p.splits);
   }
   __syncthreads();
-  if (!sLast) return;
+  if (sLast == kTicketWait) return;
+  if (sLast == kTicketStale) {  // the counter was not zero at the start: make it visible
+#pragma unroll
+    for (int i = 0; i < kAcc; ++i) {
+      if (i * kThreads >= rows * D) break;
+      const int idx = tid + i * kThreads;
+      if (idx < rows * D) p.out[row0 * D + idx] = __builtin_nanf("");
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kAcc; ++i) {
     if (i * kThreads >= rows * D) break;

@@ -56,6 +56,19 @@ struct AttendProblem {
 // for one memory line.
 constexpr int kCounterStride = 64;
 
+// What a workgroup's ticket (the counter's value before its increment) says:
+// wait (other splits are still running), merge (it is the last of `splits`),
+// or stale (the counter was not zero when the call started, so no ticket can
+// be trusted: the workspace was not zero-filled as required).  A stale head's
+// output is written as NaN by every workgroup that sees it, and its counter
+// is left non-zero, so the failure shows in this call and in every later one
+// until the workspace is zero-filled again.
+constexpr int kTicketWait = 0, kTicketMerge = 1, kTicketStale = 2;
+__host__ __device__ inline int ticket_outcome(unsigned prev, int splits) {
+  const unsigned s = static_cast<unsigned>(splits);
+  return prev == s - 1 ? kTicketMerge : (prev >= s ? kTicketStale : kTicketWait);
+}
+
 // Workspace carving, shared by the sizing call and the launchers.
 struct WorkspaceLayout {
   size_t m_off, z_off, u_off, cnt_off, total;

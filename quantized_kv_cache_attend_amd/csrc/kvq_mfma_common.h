@@ -302,10 +302,18 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
   if (threadIdx.x == 0) {
     const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-    *last = prev == static_cast<unsigned>(p.splits - 1);
+    *last = ticket_outcome(prev, p.splits);
   }
   __syncthreads();
-  if (!*last) return;
+  if (*last == kTicketWait) return;
+  if (*last == kTicketStale) {  // the counter was not zero at the start: make it visible
+    if (mine) {
+#pragma unroll
+      for (int i = 0; i < kF; ++i)
+        p.out[row * p.D + slot_feature<kRun, kStride>(f0, i)] = __builtin_nanf("");
+    }
+    return;
+  }
   if (mine) {
     // Online merge over the splits, four at a time so a batch's loads are in
     // flight together.

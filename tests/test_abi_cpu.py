@@ -212,3 +212,53 @@ def _attend_window(**kw):
 def test_attend_window_rejects_before_launch(kw):
     assert _attend_window(**kw) == kvq.KVQ_ERR_INVALID
     assert lib.kvq_last_error()
+
+
+# --- size bounds that keep the 32-bit layout arithmetic from overflowing ---------------------
+
+BIG_N = 0x7fffffff - (1 << 16) + 1     # one past the largest token count
+BIG_D = (1 << 24) + 1                  # one past the largest head dimension
+
+
+def test_sizes_reject_out_of_range():
+    assert lib.kvq_k_code_bytes(1, 1, 128, 32, 4, 1 << 17) == 0           # group > 2^16
+    assert lib.kvq_v_code_bytes(1, 1, 128, 32, 4, (1 << 16) + 2) == 0
+    assert lib.kvq_k_code_bytes(1, 1, 128, 32, 4, 1 << 16) > 0            # group 2^16 is fine
+    for fn in (lib.kvq_k_code_bytes, lib.kvq_k_scale_count, lib.kvq_v_code_bytes,
+               lib.kvq_v_scale_count):
+        assert fn(1, 1, BIG_N, 32, 4, 32) == 0
+        assert fn(1, 1, 128, BIG_D, 4, 32) == 0
+        assert fn(1, 1, BIG_N - 1, 8, 4, 32) > 0
+
+
+def test_codec_and_cache_reject_out_of_range():
+    for fn in (lib.kvq_pack_k, lib.kvq_pack_v):
+        assert fn(FAKE, 1, 1, 8, 8, 4, 1 << 17, FAKE, FAKE2, None) == kvq.KVQ_ERR_INVALID
+        assert fn(FAKE, 1, 1, BIG_N, 8, 4, 8, FAKE, FAKE2, None) == kvq.KVQ_ERR_INVALID
+        assert fn(FAKE, 1, 1, 8, BIG_D, 4, 8, FAKE, FAKE2, None) == kvq.KVQ_ERR_INVALID
+    for fn in (lib.kvq_dequant_k, lib.kvq_dequant_v):
+        assert fn(FAKE, FAKE2, 1, 1, BIG_N, 8, 4, 8, ctypes.c_void_p(1 << 44),
+                  None) == kvq.KVQ_ERR_INVALID
+    ptrs = [ctypes.c_void_p(i << 30) for i in (1, 2, 3, 4)]
+    assert lib.kvq_cache_clear(1, 1, BIG_N, 8, 4, 8, *ptrs, None) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_cache_clear(1, 1, 16, 8, 4, 1 << 17, *ptrs, None) == kvq.KVQ_ERR_INVALID
+    assert _append(cap=BIG_N, N=BIG_N - 4) == kvq.KVQ_ERR_INVALID
+    assert _append(group=1 << 17) == kvq.KVQ_ERR_INVALID
+
+
+def test_attend_rejects_out_of_range():
+    assert _attend(N=BIG_N) == kvq.KVQ_ERR_INVALID
+    assert _attend(group=1 << 17) == kvq.KVQ_ERR_INVALID
+    assert _attend_cache(64, BIG_N) == kvq.KVQ_ERR_INVALID
+    assert _attend_window(N=BIG_N - 16, cap=BIG_N) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_last_error()
+
+
+def test_study_rel_l2_closed_form():
+    """The GPU study's per-input error is the page's ||O_q - O_f32||_F /
+    ||O_f32||_F: on the hand-worked case (reference rows (3, 4, 0) and
+    (0, 0, 12), one entry off by 5) it is 5/13, not a per-row mean (1/2)."""
+    from quantized_kv_cache_attend_amd import accuracy
+    ref = np.array([[3.0, 4.0, 0.0], [0.0, 0.0, 12.0]])
+    approx = np.array([[3.0, 4.0, 5.0], [0.0, 0.0, 12.0]])
+    assert accuracy.rel_l2(approx, ref) == pytest.approx(5.0 / 13.0, rel=1e-15)

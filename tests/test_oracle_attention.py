@@ -253,3 +253,31 @@ def test_error_table_plausible(golden):
         assert abs(got[key] - want) < 0.15 * want, (key, got[key], want)
     # the ordering the page reports
     assert got["8_8"] < got["8_32"] < got["4_8"] < got["4_32"]
+
+
+# --- relative L2 error of one input: closed form ------------------------------------------
+
+def test_rel_l2_closed_form():
+    """[KPG] "accuracy and space on the same input": the error of one input is
+    ||O_q - O_f32||_F / ||O_f32||_F over that input's whole output, and the
+    table averages it over inputs.  Worked by hand: reference rows (3, 4, 0)
+    and (0, 0, 12) have ||ref||_F = 13; the approximation adds 5 to one entry,
+    so the error is 5/13.  Plausible slips all give other values: the mean of
+    per-row errors (5/5 + 0/12)/2 = 1/2, dividing by ||approx||_F = sqrt(194)
+    gives 5/sqrt(194), the squared ratio 25/169, the max-abs ratio 5/12."""
+    ref = np.array([[3.0, 4.0, 0.0], [0.0, 0.0, 12.0]])
+    approx = np.array([[3.0, 4.0, 5.0], [0.0, 0.0, 12.0]])
+    got = O.rel_l2(approx, ref)
+    assert got == pytest.approx(5.0 / 13.0, rel=1e-15)
+    for wrong in (0.5, 5.0 / math.sqrt(194.0), 25.0 / 169.0, 5.0 / 12.0):
+        assert abs(got - wrong) > 1e-3
+    # the same output shaped [B, Hq, R, D] (one input) gives the same number
+    assert O.rel_l2(approx.reshape(1, 2, 1, 3), ref.reshape(1, 2, 1, 3)) == pytest.approx(5.0 / 13.0)
+    # an exact output has error 0; scaling both by the same factor changes nothing
+    assert O.rel_l2(ref, ref) == 0.0
+    assert O.rel_l2(4.0 * approx, 4.0 * ref) == pytest.approx(5.0 / 13.0, rel=1e-15)
+    # the mean over two inputs (5/13 and 0) is 5/26, not the error of the pooled arrays
+    errs = [O.rel_l2(approx, ref), O.rel_l2(ref, ref)]
+    assert float(np.mean(errs)) == pytest.approx(5.0 / 26.0, rel=1e-15)
+    pooled = O.rel_l2(np.stack([approx, ref]), np.stack([ref, ref]))
+    assert abs(pooled - 5.0 / 26.0) > 1e-3

@@ -148,11 +148,12 @@ def _prepare_workspace(ws, heads, name="workspace"):
     """Check a caller's workspace and return its size in bytes.  The library
     keeps one arrival counter per (batch, KV head) at the start of the
     workspace and needs them zero when a call starts; every completed call
-    leaves its counters zero.  A workspace that served calls with fewer
-    (batch, KV head) pairs holds split partials where a larger call's counters
-    go, so that range is zero-filled here (a fill kernel on the current
-    stream) before the first call that needs it.  A workspace this binding has
-    not seen before is taken to be zero-filled, as the C contract requires."""
+    leaves its own counters zero and may write split partials right after
+    them.  So after a call on `heads` pairs only the first 256 * heads bytes
+    are known to be zero: a later call on more pairs would find partials where
+    its extra counters go, and that range is zero-filled here (a fill kernel
+    on the current stream) before it runs.  A workspace this binding has not
+    seen before is taken to be zero-filled, as the C contract requires."""
     torch = _torch()
     if not isinstance(ws, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -162,13 +163,10 @@ def _prepare_workspace(ws, heads, name="workspace"):
         raise ValueError(f"{name} must be contiguous")
     nbytes = ws.numel() * ws.element_size()
     need = min(_COUNTER_STRIDE * heads, nbytes)
-    clean = getattr(ws, "_kvq_clean", None)
-    if clean is None:
-        clean = need
-    elif clean < need:
+    clean = getattr(ws, "_kvq_clean", need)
+    if clean < need:
         ws.view(torch.uint8)[clean:need].zero_()
-        clean = need
-    ws._kvq_clean = clean
+    ws._kvq_clean = need  # what the call leaves known-zero (its partials follow)
     return nbytes
 
 

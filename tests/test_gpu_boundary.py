@@ -254,6 +254,11 @@ def test_workspace_reused_for_more_heads():
     kvq.attend(dev(qs), *cs, small.N, num_splits=splits, workspace=ws)
     got = host(kvq.attend(dev(qb), *cb, big.N, num_splits=splits, workspace=ws))
     assert max_abs(got, want) <= TOL
+    # and large, small, large again: the small call's partials land on the
+    # large call's counters of heads 1..7, which are cleared before its next call
+    kvq.attend(dev(qs), *cs, small.N, num_splits=splits, workspace=ws)
+    got2 = host(kvq.attend(dev(qb), *cb, big.N, num_splits=splits, workspace=ws))
+    assert np.array_equal(got2, got)
 
     # C ABI: the same history without the clearing
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")

@@ -233,6 +233,25 @@ kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const floa
                               float sm_scale, int num_splits, void* workspace,
                               size_t workspace_bytes, float* out, int variant, void* stream);
 
+/* ---- kvq_attend_noalloc --------------------------------------------------------------
+ * For callers that cannot allocate memory: code under stream capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  kvq_attend with the same
+ * arguments except the workspace: the split partials and arrival counters go
+ * to a scratch array of 16 MiB that the library keeps in device memory (one
+ * copy per GPU, held until the process ends; its address is looked up once
+ * per device, on the device's first call).  The call allocates nothing.  It
+ * fails with KVQ_ERR_WORKSPACE, before enqueuing anything, when the splits
+ * need more than 16 MiB (kvq_attend_workspace_bytes(...) > 16 MiB, e.g. 16
+ * splits of 4096 query rows of D = 128).  When the call has more (batch, KV
+ * head) pairs than the previous call on this GPU, a small kernel first zeroes
+ * the counters that the previous call's partials overwrote.  All calls on one
+ * GPU share the scratch: calls that can overlap on one GPU (other streams,
+ * other host threads) race and must not be issued. */
+kvq_status kvq_attend_noalloc(const float* q, const uint8_t* k_codes, const float* k_scales,
+                              const uint8_t* v_codes, const float* v_scales,
+                              int B, int Hq, int Hkv, int R, int N, int D, int bits, int group,
+                              float sm_scale, int num_splits, float* out, void* stream);
+
 /* ---- kvq_attend_window ------------------------------------------------------------
  * Attention over a mixed cache: N >= 0 packed tokens (the first N tokens of
  * a cache laid out for `capacity` >= max(N, 1) tokens, as kvq_attend_cache

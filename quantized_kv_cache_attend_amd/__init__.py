@@ -49,6 +49,8 @@ _SIGNATURES = {
                                                          _c_vp, _c_vp]),
     "kvq_attend_variant": (_c_int, [_c_vp] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_vp,
                                                                  _c_size, _c_vp, _c_int, _c_vp]),
+    "kvq_attend_noalloc": (_c_int, [_c_vp] * 5 + [_c_int] * 8 + [_c_float, _c_int, _c_vp,
+                                                                 _c_vp]),
     "kvq_cache_clear": (_c_int, [_c_int] * 6 + [_c_vp] * 5),
     "kvq_append": (_c_int, [_c_vp] * 2 + [_c_int] * 8 + [_c_vp] * 6),
     "kvq_attend_cache": (_c_int, [_c_vp] * 5 + [_c_int] * 9 + [_c_float, _c_int, _c_vp, _c_size,
@@ -278,6 +280,30 @@ def attend(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scal
                                     _ptr(out), VARIANTS[variant],
                                     KVQ_ATTEND_CAUSAL if causal else 0, _stream(q.device)),
                "kvq_attend_cache")
+    return out
+
+
+def attend_noalloc(q, k_codes, k_scales, v_codes, v_scales, N, bits=4, group=32, sm_scale=0.0,
+                   num_splits=0, out=None):
+    """kvq_attend_noalloc: kvq_attend with the library's own scratch as the
+    workspace (no workspace argument, nothing allocated by the call when `out`
+    is given)."""
+    torch = _torch()
+    _need(q, torch.float32, "q")
+    for t, n, dt in ((k_codes, "k_codes", torch.uint8), (k_scales, "k_scales", torch.float32),
+                     (v_codes, "v_codes", torch.uint8), (v_scales, "v_scales", torch.float32)):
+        _need(t, dt, n)
+    B, Hq, R, D = q.shape
+    Hkv = k_codes.shape[1]
+    if bits in (4, 8) and group >= 2 and N >= 1:
+        _check_cache((k_codes, k_scales, v_codes, v_scales), B, Hkv, N, D, bits, group)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, q.shape, q.device)
+    _check(lib.kvq_attend_noalloc(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                  _ptr(v_scales), B, Hq, Hkv, R, N, D, bits, group,
+                                  float(sm_scale), num_splits, _ptr(out), _stream(q.device)),
+           "kvq_attend_noalloc")
     return out
 
 

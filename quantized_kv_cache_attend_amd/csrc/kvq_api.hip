@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 namespace kvq {
 namespace {
@@ -259,6 +260,62 @@ kvq_status codec_check(const void* a, const void* b, const void* c, int B, int H
     return fail(KVQ_ERR_INVALID, "N=%d above %d tokens or D=%d above %d", N, kMaxTokens, D,
                 kMaxDim);
   return KVQ_OK;
+}
+
+// ---- the library's own scratch memory (kvq_attend_noalloc) -------------------
+// For callers that cannot allocate (code under stream capture, tight serving
+// loops, harnesses that forbid hipMalloc): a workspace in a file-scope device
+// array that each GPU holds until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address of each GPU's copy comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+// Bytes at the start of each device's scratch known to be zero: after a call
+// on H (batch, KV head) pairs, its 256 * H bytes of arrival counters (the
+// partials that follow are garbage to a later call's counters).
+size_t g_scratch_clean[kMaxDevices] = {};
+
+__global__ void zero_bytes_kernel(unsigned char* p, size_t n) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    p[i] = 0;
+}
+
+// This device's scratch address, looked up on the device's first call.
+kvq_status scratch_address(int* dev_out, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KVQ_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KVQ_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+    g_scratch_clean[dev] = 0;  // the first call clears its counters itself
+  }
+  *dev_out = dev;
+  *ptr = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+
+// Start of the range [from, need) of a device's scratch that must be zeroed
+// before a call whose counters take `need` bytes; afterwards exactly `need`
+// bytes are known to be zero.
+size_t scratch_claim(int dev, size_t need) {
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  const size_t from = g_scratch_clean[dev] < need ? g_scratch_clean[dev] : need;
+  g_scratch_clean[dev] = need;
+  return from;
 }
 
 }  // namespace
@@ -522,6 +579,47 @@ kvq_status kvq_attend(const float* q, const uint8_t* k_codes, const float* k_sca
                             KVQ_VARIANT_AUTO, stream);
 }
 
+kvq_status kvq_attend_noalloc(const float* q, const uint8_t* k_codes, const float* k_scales,
+                              const uint8_t* v_codes, const float* v_scales, int B, int Hq,
+                              int Hkv, int R, int N, int D, int bits, int group, float sm_scale,
+                              int num_splits, float* out, void* stream) {
+  int dev = 0;
+  void* ws = nullptr;
+  kvq_status st = scratch_address(&dev, &ws);
+  if (st != KVQ_OK) return st;
+  // The same checks as kvq_attend with the scratch as its workspace: a call
+  // whose splits need more than the scratch holds fails with
+  // KVQ_ERR_WORKSPACE before anything is enqueued.
+  AttendProblem p;
+  st = check_attend(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N, N, D, bits, group,
+                    sm_scale, num_splits, ws, kScratchBytes, out, &p);
+  if (st != KVQ_OK) {
+    if (st == KVQ_ERR_WORKSPACE)
+      return fail(KVQ_ERR_WORKSPACE,
+                  "kvq_attend_noalloc: the call needs %zu workspace bytes, the library's "
+                  "scratch holds %zu (use kvq_attend with a caller workspace, or fewer splits)",
+                  kvq_attend_workspace_bytes(B, Hq, Hkv, R, N, D, num_splits), kScratchBytes);
+    return st;
+  }
+  // Counters of this call that an earlier call with fewer (batch, KV head)
+  // pairs overwrote with its partials: zero them first, on the same stream.
+  const size_t counters = static_cast<size_t>(256) * B * Hkv;
+  const size_t from = scratch_claim(dev, counters);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (from < counters) {
+    const size_t n = counters - from;
+    const size_t blocks = (n + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(blocks < 1024 ? blocks : 1024);
+    hipLaunchKernelGGL(zero_bytes_kernel, dim3(grid), dim3(256), 0, s,
+                       static_cast<unsigned char*>(ws) + from, n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(KVQ_ERR_HIP, "scratch clear launch: %s", hipGetErrorString(e));
+  }
+  return kvq_attend(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N, D, bits, group,
+                    sm_scale, num_splits, ws, kScratchBytes, out, stream);
+}
+
 kvq_status kvq_attend_f32(const float* q, const float* k, const float* v, int B, int Hq, int Hkv,
                           int R, int N, int D, float sm_scale, int num_splits, void* workspace,
                           size_t workspace_bytes, float* out, void* stream) {
@@ -558,6 +656,6 @@ const char* kvq_status_string(int status) {
 
 const char* kvq_last_error(void) { return g_last_error; }
 
-int kvq_abi_version(void) { return 6; }
+int kvq_abi_version(void) { return 7; }
 
 }  // extern "C"

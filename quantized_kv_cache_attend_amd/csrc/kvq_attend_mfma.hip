@@ -30,13 +30,15 @@
 //     row of the low nibble above, the next 8 the other);
 //   K scales of the block's group: 128 floats, channel order;
 //   V scales of the block: [value group][32 tokens].
-// Every load is a contiguous, coalesced buffer load into VGPRs; no LDS
-// staging, no barriers before the final merge.  Each wave streams its own
-// blocks through a ring of kDepth register sets: a part of a set is reloaded
-// with the block kDepth ahead as soon as the block in it has consumed that
-// part.  One set is the default: with about one block per wave in flight the
-// whole chip already keeps ~10 MB of loads outstanding, and deeper rings
-// (more registers, a burst of loads at the start) measured slower.
+// Streaming: each wave owns the blocks w, w + kWaves, ... of its split and
+// keeps kDepth of them in flight in its own LDS slots: the four parts of a
+// block (K codes, V codes, K scales, V scales) are copied from HBM straight
+// into LDS by buffer loads with the LDS-destination form and the nontemporal
+// cache policy (no VGPRs held while the load is in flight).  When a block's
+// loads have landed (vmcnt), every lane reads its operand bytes from the slot
+// (contiguous, conflict-free 8- or 16-byte LDS reads in matrix-core operand
+// order), and the slot is refilled with the block kDepth ahead before the
+// block's math starts.  No barrier is needed before the final merge.
 //
 // Exact code operands.  Each stored nibble c is turned into the fp16 value
 // c - 7 exactly: OR-ing it into the mantissa of 0x6400 gives 1024 + c (low
@@ -78,7 +80,7 @@ namespace {
 #define KVQ_MFMA_DEPTH 1
 #endif
 constexpr int kWaves = KVQ_MFMA_WAVES;   // waves per workgroup, one KV head split each
-constexpr int kDepth = KVQ_MFMA_DEPTH;   // blocks in flight per wave
+constexpr int kDepth = KVQ_MFMA_DEPTH;   // blocks in flight per wave (LDS slots)
 constexpr int kThreads = kWaves * 64;
 constexpr int kOut = 4 * 128;            // outputs of one KV head: 4 rows x D
 constexpr int kSlots = kOut / kThreads > 0 ? kOut / kThreads : 1;  // outputs per thread
@@ -95,15 +97,41 @@ constexpr int kSvLow = 2;
 constexpr int kQTop = 10;           // q rows prescaled to max |.| in [2^9, 2^10)
 constexpr float kSkMax = 32.0f;     // K scales below this need no block rescale
 
-struct alignas(16) Smem {
-  union {
-    _Float16 qt[kWaves][4][2][4][4][8];  // per wave: q~ [kstep][hi|lo][row][kblock][8]
-    float wu[kWaves][4][kD];             // per-wave u for the final merge
-    WinSmem<4> win;                      // a recent-token window part
-  } u;
+// One LDS slot holds a whole block: K codes, V codes, K scales, V scales.
+template <int kBits>
+constexpr int kSlotBytes = 2 * kBB<kBits> + 2 * kBS * 4;
+// Buffer loads with the LDS destination per block: 1 KB per instruction for
+// the codes (64 lanes x 16 bytes), half a wave for each 512-byte scale row.
+template <int kBits>
+constexpr int kDmaPerBlock = 2 * kBB<kBits> / 1024 + 2;
+constexpr int kNontemporal = 2;  // cache policy of the block loads (gfx9 "nt")
+
+// LDS of one workgroup.  The merge area and a window part's tiles reuse the
+// ring once every block load has landed (8-bit at 8 waves x 2 slots: exactly
+// the 160 KB of a compute unit).
+struct MergeSmem {
+  float wu[kWaves][4][kD];  // per-wave u for the final merge
   float wm[kWaves][4];
   float wz[kWaves][4];
   int last;
+};
+// Slots per wave: kDepth, or as many as fit in LDS beside the q~ staging
+// (8-bit blocks are 9 KB).
+constexpr int kQtBytes = kWaves * 4 * 2 * 4 * 4 * 8 * 2;
+template <int kBits>
+constexpr int kRing = kDepth < (163840 - kQtBytes) / (kWaves * kSlotBytes<kBits>)
+                          ? kDepth
+                          : (163840 - kQtBytes) / (kWaves * kSlotBytes<kBits>);
+static_assert(kRing<8> >= 1, "an 8-bit block must fit in each wave's LDS");
+
+template <int kBits>
+struct alignas(16) Smem {
+  union {
+    unsigned char ring[kWaves][kRing<kBits>][kSlotBytes<kBits>];  // per wave: blocks in flight
+    MergeSmem m;
+    WinSmem<4> win;                      // a recent-token window part
+  } u;
+  _Float16 qt[kWaves][4][2][4][4][8];    // per wave: q~ [kstep][hi|lo][row][kblock][8]
 };
 
 // One block's operands, as loaded by one lane.
@@ -140,34 +168,64 @@ __device__ __forceinline__ Lanes lane_offsets(int lane) {
           static_cast<unsigned>(((n >> 2) * 32 + q * 8) * 4)};
 }
 
-// Byte offset of block blk in an array of `bytes`-sized blocks, or kNoBlock.
-__device__ __forceinline__ unsigned block_base(int blk, bool valid, unsigned bytes) {
-  return valid ? static_cast<unsigned>(blk) * bytes : kNoBlock;
+#define KVQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Copy block `blk` of a head into an LDS slot (asynchronous; counted by
+// vmcnt, kDmaPerBlock<kBits> loads per block).  The scale rows take lanes
+// 0..31 (16 bytes each), so each lane's LDS destination is the same whether
+// the hardware places data by lane id or by active lane.
+// valid == false issues the same loads at an offset past the arrays: they
+// return zeros without a memory access (keeping the count of loads in flight
+// independent of the path taken).
+template <int kBits>
+__device__ __forceinline__ void dma_block(unsigned char* slot, const Head& h, int blk, int lane,
+                                          bool valid = true) {
+  const unsigned cb = valid ? static_cast<unsigned>(blk) * kBB<kBits> : kNoBlock;
+#pragma unroll
+  for (int c = 0; c < kBB<kBits> / 1024; ++c) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(h.kc, KVQ_LDS(slot + c * 1024), 16,
+                                             cb + c * 1024 + lane * 16, 0, 0, kNontemporal);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(h.vc, KVQ_LDS(slot + kBB<kBits> + c * 1024), 16,
+                                             cb + c * 1024 + lane * 16, 0, 0, kNontemporal);
+  }
+  if (lane < 32) {
+    const unsigned sb = (valid ? static_cast<unsigned>(blk) * kBS * 4 : kNoBlock) + lane * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(h.ksc, KVQ_LDS(slot + 2 * kBB<kBits>), 16, sb, 0, 0,
+                                             kNontemporal);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(h.vsc, KVQ_LDS(slot + 2 * kBB<kBits> + kBS * 4), 16,
+                                             sb, 0, 0, kNontemporal);
+  }
 }
 
-// Loaders of the four parts of one block (base: block_base of that array).
+// Wait until at most `pending` blocks' loads (issued after the one needed
+// now) are still in flight.
 template <int kBits>
-__device__ __forceinline__ void load_ks(BlockRegs<kBits>& r, const Head& h, unsigned base,
-                                        const Lanes& o) {
-  r.ks[0] = buf_f4(h.ksc, base + o.ks, 0);
-  r.ks[1] = buf_f4(h.ksc, base + o.ks + 16, 0);
+__device__ __forceinline__ void wait_blocks(int pending) {
+  constexpr int n = kDmaPerBlock<kBits>;
+  // s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their maxima
+#define KVQ_VMCNT(x) (((x) & 15) | (((x) >> 4) << 14) | 0x0F70)
+  if (pending <= 0) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(0));
+  else if (pending == 1) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(n));
+  else if (pending == 2) __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(2 * n));
+  else __builtin_amdgcn_s_waitcnt(KVQ_VMCNT(3 * n));
+#undef KVQ_VMCNT
 }
+
+// This lane's operands of the block in `slot`.
 template <int kBits>
-__device__ __forceinline__ void load_vs(BlockRegs<kBits>& r, const Head& h, unsigned base,
-                                        const Lanes& o) {
-  r.vs[0] = buf_f4(h.vsc, base + o.vs, 0);
-  r.vs[1] = buf_f4(h.vsc, base + o.vs + 16, 0);
-}
-template <int kBits>
-__device__ __forceinline__ void load_block(BlockRegs<kBits>& r, const Head& h, int blk, bool valid,
+__device__ __forceinline__ void read_block(BlockRegs<kBits>& r, const unsigned char* slot,
                                            const Lanes& o) {
-  load_ks(r, h, block_base(blk, valid, kBS * 4), o);
-  const unsigned cb = block_base(blk, valid, kBB<kBits>);
+  typedef typename CodeOps<kBits>::words W;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r.k[i] = CodeOps<kBits>::load(h.kc, cb + o.k + i * kKStep<kBits>, 0);
-  load_vs(r, h, block_base(blk, valid, kBS * 4), o);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = CodeOps<kBits>::load(h.vc, cb + o.v + i * kVStep<kBits>, 0);
+  for (int i = 0; i < 4; ++i) {
+    r.k[i] = *reinterpret_cast<const W*>(slot + o.k + i * kKStep<kBits>);
+    r.v[i] = *reinterpret_cast<const W*>(slot + kBB<kBits> + o.v + i * kVStep<kBits>);
+  }
+  const unsigned char* sc = slot + 2 * kBB<kBits>;
+  r.ks[0] = *reinterpret_cast<const f32x4*>(sc + o.ks);
+  r.ks[1] = *reinterpret_cast<const f32x4*>(sc + o.ks + 16);
+  r.vs[0] = *reinterpret_cast<const f32x4*>(sc + kBS * 4 + o.vs);
+  r.vs[1] = *reinterpret_cast<const f32x4*>(sc + kBS * 4 + o.vs + 16);
 }
 
 // Running state of one wave.  Lane (n, q) tracks query row n & 3: m is the
@@ -186,20 +244,18 @@ struct WaveState {
 };
 
 // Attend one 32-token block (tokens tok0 .. tok0+31, those >= t_end masked
-// out) held in br, then reload br's parts with block `next` (if has_next;
-// otherwise the loads return zeros without touching memory).
+// out) whose operands are in br.
 // qv: this lane's prescaled q values (precompute slot, channel order);
 // us_row: 2^-Sq of score row n & 3.  kCausal: also mask the tokens after
 // lim, the position of score row n & 3's query; a row that has seen no
 // legal key keeps m = -inf and its exponents are taken against 0, so
 // (-inf) - (-inf) is never formed.
 template <int kBits, bool kCausal>
-__device__ __forceinline__ void attend_block(Smem& sm, BlockRegs<kBits>& br, int tok0, int t_end,
+__device__ __forceinline__ void attend_block(Smem<kBits>& sm, const BlockRegs<kBits>& br,
+                                             int tok0, int t_end,
                                              const typename CodeOps<kBits>::consts& cc,
-                                             WaveState& ws, const Head& h,
-                                             int next, bool has_next, const Lanes& lo_,
-                                             const float (&qv)[8], float us_row, int lim,
-                                             int lim_lo) {
+                                             WaveState& ws, const float (&qv)[8], float us_row,
+                                             int lim, int lim_lo) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
@@ -236,22 +292,19 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs<kBits>& br, int
     for (int j = 0; j < 8; ++j) xs[j] = x[kSlotByte[j]];
     half8_t hi, lo;
     split_hilo(xs, hi, lo);
-    *reinterpret_cast<half8_t*>(&sm.u.qt[wave][ksq][0][rq][kbq][0]) = hi;
-    *reinterpret_cast<half8_t*>(&sm.u.qt[wave][ksq][1][rq][kbq][0]) = lo;
+    *reinterpret_cast<half8_t*>(&sm.qt[wave][ksq][0][rq][kbq][0]) = hi;
+    *reinterpret_cast<half8_t*>(&sm.qt[wave][ksq][1][rq][kbq][0]) = lo;
   }
-  load_ks(br, h, block_base(next, has_next, kBS * 4), lo_);
 
   // S^T = codes^T * q~^T over 4 k-steps of 32 channels.
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 se = zero4, so = zero4;
   const int part = n >> 3, row = n & 3;
-  const unsigned kb = block_base(next, has_next, kBB<kBits>);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     half8_t alo, ahi;  // tokens 2n and 2n + 1
     CodeOps<kBits>::to_half(br.k[ks], cc, alo, ahi);
-    br.k[ks] = CodeOps<kBits>::load(h.kc, kb + lo_.k + ks * kKStep<kBits>, 0);  // next block's k-step
-    const half8_t b = *reinterpret_cast<const half8_t*>(&sm.u.qt[wave][ks][part][row][q][0]);
+    const half8_t b = *reinterpret_cast<const half8_t*>(&sm.qt[wave][ks][part][row][q][0]);
     se = mfma(alo, b, se);
     so = mfma(ahi, b, so);
   }
@@ -338,14 +391,12 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs<kBits>& br, int
     for (int j = 0; j < 8; ++j) xv[j] = xt[kSlotByte[j]];
     split_hilo(xv, ah, al);
   }
-  load_vs(br, h, block_base(next, has_next, kBS * 4), lo_);
 
   // u[4G'+r][f] += p~ x V codes, one feature group of 32 at a time
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     half8_t be, bo;  // features 32g + 2n and 32g + 2n + 1
     CodeOps<kBits>::to_half(br.v[g], cc, be, bo);
-    br.v[g] = CodeOps<kBits>::load(h.vc, kb + lo_.v + g * kVStep<kBits>, 0);  // next block's group
     ws.acc[g][0] = mfma(ah, be, ws.acc[g][0]);
     ws.acc[g][0] = mfma(al, be, ws.acc[g][0]);
     ws.acc[g][1] = mfma(ah, bo, ws.acc[g][1]);
@@ -360,7 +411,7 @@ __device__ __forceinline__ void attend_block(Smem& sm, BlockRegs<kBits>& br, int
 template <int kBits, bool kCausal, bool kWindow>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 attend_mfma_r4_kernel(AttendProblem p) {
-  __shared__ Smem sm;
+  __shared__ Smem<kBits> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -391,7 +442,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
     float U[kSlots], M, Z;
     window_part<4, kThreads, kSlots, kSlots, 0>(p, sm.u.win, bh, split - packed_splits, r, f0, U,
                                                 M, Z);
-    split_combine<kSlots, kSlots, 0>(p, split, bh, r, f0, U, M, Z, &sm.last);
+    split_combine<kSlots, kSlots, 0>(p, split, bh, r, f0, U, M, Z, &sm.u.m.last);
     return;
   }
   // Per-head strides follow the layout's capacity; only blocks below N are read.
@@ -414,7 +465,8 @@ attend_mfma_r4_kernel(AttendProblem p) {
   const int cnt = b_first < b_end ? (b_end - 1 - b_first) / kWaves + 1 : 0;  // wave-uniform
 
   // This lane's query values: row rq = lane >> 4, channels d0 .. d0+7 (its
-  // q~ precompute slot).  Loaded first, so the block loads queue behind them.
+  // q~ precompute slot).  Loaded first: the block loads queue behind them,
+  // and waiting for q does not wait for any block.
   const int rq = lane >> 4;
   const int d0 = ((lane >> 2) & 3) * 32 + (lane & 3) * 8;
   f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = qa;
@@ -424,9 +476,12 @@ attend_mfma_r4_kernel(AttendProblem p) {
     qb = *reinterpret_cast<const f32x4*>(src + 4);
   }
   const Lanes lo = lane_offsets<kBits>(lane);
-  BlockRegs<kBits> br[kDepth];
+  // The first kDepth blocks of this wave go out at once (slots past the
+  // wave's last block take zeros).
+  unsigned char* ring = &sm.u.ring[wave][0][0];
 #pragma unroll
-  for (int j = 0; j < kDepth; ++j) load_block(br[j], h, b_first + j * kWaves, j < cnt, lo);
+  for (int j = 0; j < kRing<kBits>; ++j)
+    dma_block<kBits>(ring + j * kSlotBytes<kBits>, h, b_first + j * kWaves, lane, j < cnt);
 
   // q * qscale, prescaled per row by 2^Sq so the row's largest element lies in
   // [2^9, 2^10) (the 16 lanes of a row are one DPP row).
@@ -465,19 +520,19 @@ attend_mfma_r4_kernel(AttendProblem p) {
   // Causal limit of this lane's score row n & 3.
   const int lim = p.pos_end - p.R + (n & 3) % p.R;
 
-  // The ring: block i sits in register set i % kDepth; once attended, the set
-  // is refilled with block i + kDepth.  Every step of a round runs (a step
-  // past the wave's last block attends an all-masked block of zeros), so the
-  // number of loads in flight never depends on the path taken.
-  for (int i0 = 0; i0 < cnt; i0 += kDepth) {
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-      const int i = i0 + j;
-      const int blk = b_first + i * kWaves;
-      attend_block<kBits, kCausal>(sm, br[j], i < cnt ? blk * kBlockTokens : t_end, t_end, cc, ws, h,
-                            blk + kDepth * kWaves, i + kDepth < cnt, lo, qv, us_row, lim,
-                            p.pos_end - p.R);
-    }
+  // The ring: block i sits in slot i % kDepth.  Once its loads have landed
+  // and its operands are in registers, the slot is refilled with block
+  // i + kDepth, which then streams in while block i is attended.
+  for (int i = 0; i < cnt; ++i) {
+    wait_blocks<kBits>(min(kRing<kBits> - 1, cnt - 1 - i));
+    unsigned char* slot = ring + (i % kRing<kBits>) * kSlotBytes<kBits>;
+    BlockRegs<kBits> br;
+    read_block(br, slot, lo);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot has been read
+    if (i + kRing<kBits> < cnt)
+      dma_block<kBits>(slot, h, b_first + (i + kRing<kBits>) * kWaves, lane);
+    attend_block<kBits, kCausal>(sm, br, (b_first + i * kWaves) * kBlockTokens, t_end, cc, ws, qv,
+                                 us_row, lim, p.pos_end - p.R);
   }
   // z of each row: sum this lane's share over the four q-blocks
   ws.z = qblock_sum(ws.z);
@@ -491,16 +546,17 @@ attend_mfma_r4_kernel(AttendProblem p) {
       uo = ws.acc[g][1];
     }
   }
-  __syncthreads();  // every wave is done with its q~ slots (aliased by wu)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no block load still writes this wave's slots
+  __syncthreads();  // every wave is done with its ring (aliased by the merge area)
   const float fu = __builtin_ldexpf(1.0f, -ws.sv);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sm.u.wu[wave][i][q * 32 + 2 * n] = ue[i] * fu;
-    sm.u.wu[wave][i][q * 32 + 2 * n + 1] = uo[i] * fu;
+    sm.u.m.wu[wave][i][q * 32 + 2 * n] = ue[i] * fu;
+    sm.u.m.wu[wave][i][q * 32 + 2 * n + 1] = uo[i] * fu;
   }
   if (lane < 4) {
-    sm.wm[wave][lane] = ws.m;
-    sm.wz[wave][lane] = ws.z;
+    sm.u.m.wm[wave][lane] = ws.m;
+    sm.u.m.wz[wave][lane] = ws.z;
   }
   __syncthreads();
 
@@ -511,16 +567,16 @@ attend_mfma_r4_kernel(AttendProblem p) {
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) U[j] = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][r]);
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.m.wm[w][r]);
   if (M != -INFINITY) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm.wm[w][r];
+      const float mw = sm.u.m.wm[w][r];
       if (mw == -INFINITY) continue;
       const float x = fast_exp2(mw - M);
-      Z = fmaf(x, sm.wz[w][r], Z);
+      Z = fmaf(x, sm.u.m.wz[w][r], Z);
 #pragma unroll
-      for (int j = 0; j < kSlots; ++j) U[j] = fmaf(x, sm.u.wu[w][r][f0 + j], U[j]);
+      for (int j = 0; j < kSlots; ++j) U[j] = fmaf(x, sm.u.m.wu[w][r][f0 + j], U[j]);
     }
   }
   const long long row0 = bh * rows;
@@ -532,7 +588,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
     }
     return;
   }
-  split_combine<kSlots, kSlots, 0>(p, split, bh, r, f0, U, M, Z, &sm.last);
+  split_combine<kSlots, kSlots, 0>(p, split, bh, r, f0, U, M, Z, &sm.u.m.last);
 }
 
 }  // namespace

@@ -426,7 +426,8 @@ __global__ __launch_bounds__(kThreads) void attend_valu_kernel(AttendProblem p) 
     for (int i = 0; i < kAcc; ++i) {
       if (i * kThreads >= rows * D) break;
       const int idx = tid + i * kThreads;
-      if (idx < rows * D) p.out[row0 * D + idx] = __builtin_nanf("");
+      if (idx < rows * D)  // a quiet NaN, stored as its bit pattern
+        reinterpret_cast<unsigned*>(p.out)[row0 * D + idx] = 0x7fc00000u;
     }
     return;
   }

@@ -309,8 +309,9 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
   if (*last == kTicketStale) {  // the counter was not zero at the start: make it visible
     if (mine) {
 #pragma unroll
-      for (int i = 0; i < kF; ++i)
-        p.out[row * p.D + slot_feature<kRun, kStride>(f0, i)] = __builtin_nanf("");
+      for (int i = 0; i < kF; ++i)  // a quiet NaN, stored as its bit pattern
+        reinterpret_cast<unsigned*>(p.out)[row * p.D + slot_feature<kRun, kStride>(f0, i)] =
+            0x7fc00000u;
     }
     return;
   }

@@ -229,13 +229,15 @@ def test_binding_rejects_bad_out_and_workspace():
 # --- one workspace across call shapes ---------------------------------------------------
 
 def test_workspace_reused_for_more_heads():
-    """A workspace that served a call with one (batch, KV head) pair holds
+    """A workspace that served a call with one (batch, KV head) pair may hold
     that call's partial sums where a call with eight pairs keeps its arrival
-    counters.  Through the binding the new counter range is zero-filled first
-    and the larger call is right.  Called through the C ABI on the same dirty
-    workspace, every head whose counter is not zero gets NaN outputs (the
-    stale counter is detected, not silently merged early or never), and heads
-    with a zero counter are right."""
+    counters (here: every byte past the first counter set non-zero, as such
+    partials can leave it).  Through the binding the new counter range is
+    zero-filled first and the larger call is right, also after a smaller call
+    in between.  Called through the C ABI on the same dirty workspace, every
+    head whose counter is not zero gets NaN outputs (the stale counter is
+    detected, not merged early or never), and the head with a zero counter is
+    right."""
     small = Workload("ws1", 1, 4, 1, 1, 2048, 128, ((4, 32),))
     big = Workload("ws8", 2, 16, 4, 1, 2048, 128, ((4, 32),))
     splits = 4
@@ -252,20 +254,21 @@ def test_workspace_reused_for_more_heads():
     # binding: the larger call's counters are cleared before it runs
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     kvq.attend(dev(qs), *cs, small.N, num_splits=splits, workspace=ws)
+    ws[256:].fill_(0x3F)
     got = host(kvq.attend(dev(qb), *cb, big.N, num_splits=splits, workspace=ws))
     assert max_abs(got, want) <= TOL
-    # and large, small, large again: the small call's partials land on the
-    # large call's counters of heads 1..7, which are cleared before its next call
+    # large, small (dirtying the large call's counters of heads 1..7), large again
     kvq.attend(dev(qs), *cs, small.N, num_splits=splits, workspace=ws)
+    ws[256:].fill_(0x3F)
     got2 = host(kvq.attend(dev(qb), *cb, big.N, num_splits=splits, workspace=ws))
     assert np.array_equal(got2, got)
 
-    # C ABI: the same history without the clearing
+    # C ABI: the same dirty workspace without the clearing
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    kvq.attend(dev(qs), *cs, small.N, num_splits=splits, workspace=ws)
+    ws[256:].fill_(0x3F)
     torch.cuda.synchronize()
     counters = host(ws)[:256 * 8].view(np.uint32)[::64].copy()
-    assert counters[0] == 0 and np.count_nonzero(counters) >= 4
+    assert counters[0] == 0 and np.all(counters[1:] >= splits)
     qd = dev(qb)
     out = torch.empty_like(qd)
     st = kvq.lib.kvq_attend_variant(
@@ -276,8 +279,6 @@ def test_workspace_reused_for_more_heads():
     assert st == kvq.KVQ_OK
     got = host(out).reshape(2 * 4, 4, 128)       # [(b, kv head), rows, D]
     ref = want.reshape(2 * 4, 4, 128)
-    for h in range(8):
-        if counters[h] == 0:
-            assert max_abs(got[h], ref[h]) <= TOL, h
-        elif counters[h] >= splits:
-            assert np.all(np.isnan(got[h])), h
+    assert max_abs(got[0], ref[0]) <= TOL
+    for h in range(1, 8):
+        assert np.all(np.isnan(got[h])), h

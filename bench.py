@@ -138,6 +138,99 @@ def cpu_baseline(w, q, k, v, bits, group, seconds):
     }
 
 
+def long_context_line(launch, sink):
+    """The long-context workload (batch 16, 32768 tokens, GQA 64/8, 4 queries
+    per head: 32 query rows per KV head, the 32-row matrix-core kernel) at its
+    16 KV splits: per-call time of the fused attend over rotating cache copies
+    past the Infinity Cache, launched like the main step, beside a streaming
+    read of the same byte count."""
+    import torch
+    import quantized_kv_cache_attend_amd as kvq
+    w = WORKLOADS["gqa_n32768"]
+    bits, group = w.formats[0]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    q, k, v = make_qkv(w, 0)
+    qd = torch.from_numpy(q).to(dev)
+    kd = torch.from_numpy(k).to(dev)
+    del k
+    kc, ks = kvq.pack_k(kd, bits, group)
+    del kd
+    vd = torch.from_numpy(v).to(dev)
+    del v
+    vc, vs = kvq.pack_v(vd, bits, group)
+    del vd
+    nbytes = kv_bytes(w, bits, group)
+    copies = max(2, math.ceil(3 * MALL_BYTES / nbytes))
+    caches = [(kc, ks, vc, vs)] + [tuple(t.clone() for t in (kc, ks, vc, vs))
+                                   for _ in range(copies - 1)]
+    out = torch.empty_like(qd)
+    ws = kvq.new_workspace(w.B, w.Hq, w.Hkv, w.R, w.N, w.D, w.num_splits, device=dev)
+
+    def one_pass():
+        for c in caches:
+            kvq.attend(qd, *c, w.N, bits, group, num_splits=w.num_splits, workspace=ws, out=out)
+    one_pass()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    run = one_pass
+    if launch == "graph":
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_pass()
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError("gqa_n32768 graph replay differs from the eager result")
+        run = g.replay
+
+    def timed_passes(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    n_pass = max(2, 400 // copies)
+    us = timed_passes(run, n_pass) / copies
+    if not torch.equal(out, ref):
+        raise RuntimeError("gqa_n32768 timed calls changed the output")
+    del caches, kc, ks, vc, vs
+
+    rbytes = (nbytes + 15) // 16 * 16
+    bufs = [torch.zeros(rbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+
+    def reads():
+        for b in bufs:
+            kvq.stream_read(b, sink)
+    read_run = reads
+    if launch == "graph":
+        rg = torch.cuda.CUDAGraph()
+        reads()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(rg):
+            reads()
+        read_run = rg.replay
+    read_us = timed_passes(read_run, n_pass) / copies
+    del bufs
+    gbs = nbytes / (us * 1e-6) / 1e9
+    line = {"splits": w.num_splits, "us": round(us, 2), "kv_bytes": nbytes,
+            "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "read_ceiling_us": round(read_us, 2),
+            "attend_over_read_ceiling": round(us / read_us, 3),
+            "cache_copies": copies, "kernel": "32-row matrix-core"}
+    log(f"[bench] gqa_n32768 at {w.num_splits} splits: {us:.1f} us ({gbs:.0f} GB/s, "
+        f"{gbs / HBM_PEAK_GBS:.1%} of peak); streaming read {read_us:.1f} us")
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -600,6 +693,9 @@ def main():
         log("[bench] single-head workloads (us per call): " +
             ", ".join(f"{k} {v:.2f}" for k, v in small.items()))
 
+        if w.name != "gqa_n32768":
+            extra["gqa_n32768"] = long_context_line(args.launch, sink)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host ...")
@@ -619,7 +715,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"u{bits}+f32",
+        "dtype": (f"u{bits} codes + f32 scales; fp16 hi+lo matrix-core operands, "
+                  "f32 accumulate"),
         "data": "synthetic (seeded N(0,1) float32 Q/K/V, packed on the GPU)",
         "config": {"workload": w.name, "batch": w.B, "n_tokens": w.N, "hq": w.Hq, "hkv": w.Hkv,
                    "queries_per_head": w.R, "head_dim": w.D, "bits": bits, "group": group,

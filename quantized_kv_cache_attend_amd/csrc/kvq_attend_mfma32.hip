@@ -16,23 +16,32 @@
 // Packed format: the 32-token block byte order of kvq_layout.h, whose K and V
 // blocks hand each lane its matrix-core operand bytes at consecutive
 // addresses (see the 4-row kernel in kvq_attend_mfma.hip for the byte map).
-// Codes become exact fp16 (c - 7) operands; float32 factors are split into
-// fp16 hi + lo (kvq_mfma_common.h).
+// Codes become exact fp16 (c - 7) operands (kvq_mfma_common.h).
 //
 // Math per 32-token block, one wave, row tile t = 0, 1 (rows 16t .. 16t+15):
 //   S^T[pair][16t + n] = codes^T (A: 16 token pairs x 32 channels, low and
 //     high nibbles as two products) x q~^T (B: 32 channels x 16 rows), with
-//     the hi and lo halves of q~ accumulated into the same tile;
-//   u[16t + m][f] += p~_g (A: 16 rows x 32 tokens, p~ = p * sV[token][g])
-//     x V codes (B: 32 tokens x 16 feature pairs of value group g).
+//     the fp16 hi and lo halves of q~ accumulated into the same tile;
+//   u[16t + m][f] += p (A: 16 rows x 32 tokens, fp16 hi and lo) x the value
+//     operand of group g (B: 32 tokens x 16 feature pairs).
 // The score tile gives lane (n, q) rows 16t + n and tokens 8q .. 8q+7, which
 // is exactly the A operand of the value product: no data moves between the
 // two products.
 //
-// q~ = q * qscale * sK[d][G] is formed per block: q * qscale sits in LDS,
-// prescaled per row by a power of two that puts its largest element in
-// [2^9, 2^10); K scales below 32 then keep every q~ inside the fp16 range
-// (a block whose K scales reach 32 is rescaled by a power of two first).
+// q~ = q * qscale * sK[d][G] * kf, formed per block in packed fp16 from the
+// hi/lo pairs of q (in registers for the whole kernel, each row prescaled by a
+// power of two that puts its largest element in [2^9, 2^10)) and of the
+// block's K scales (split once per block, one pair of them per lane, and
+// shared through LDS).  kf is a power of two that keeps the block's largest
+// K scale in [2^2, 2^5).
+//
+// The value operand (4-bit codes) carries the V scale: (c - 7) * vh, exact,
+// plus (c - 7) * vl, where vh holds the 8 leading bits of the prescaled scale
+// sV[token][g] * 2^sv and vl the rest.  Both are shared by the two row tiles,
+// so the value product costs three matrix-core products per tile and group
+// (ph vh, pl vh, ph vl).  8-bit codes (|c - 127| up to 8 bits) leave no room
+// for an exact scale product; there p~ = p * sV * 2^sv is split into fp16
+// hi + lo instead.
 #include "kvq_internal.h"
 #include "kvq_layout.h"
 #include "kvq_mfma_common.h"
@@ -57,7 +66,8 @@ constexpr float kLazy = 6.0f;    // reference moves only past m + kLazy
 constexpr int kSvTop = 9;        // V prescale: max V scale * 2^Sv in [2^8, 2^9),
 constexpr int kSvLow = 2;        //   kept while it stays in [2^2, 2^9)
 constexpr int kQTop = 10;        // q rows prescaled to max |.| in [2^9, 2^10)
-constexpr float kSkMax = 32.0f;  // K scales below this need no block rescale
+constexpr int kKTop = 5;         // K prescale: max K scale * kf in [2^4, 2^5),
+constexpr int kKLow = 2;         //   kept while it stays in [2^2, 2^5)
 
 struct alignas(16) Smem32 {
   union {
@@ -65,8 +75,18 @@ struct alignas(16) Smem32 {
     float wu[2][kR][kD];         // u of two waves at a time, for the merge
     WinSmem<kR> win;             // a recent-token window part
   } u;
-  float sks[kW][kBS];            // this block's K scales (per wave), channel order
-  float svs[kW][kBS];            // this block's V scales (per wave), [group][token]
+  // This block's scale operands, per wave, in the lane order of the products
+  // that read them (k-slot order within each 8-wide run):
+  //   kops[ks][qb]: fp16 hi (toward zero) and lo of the K scales of channels
+  //     32 ks + 8 qb + (0..7), times the block's power-of-two guard kf;
+  //   vops[g][qb] (4-bit): fp16 head vh (the 8 leading bits) and remainder vl
+  //     of the prescaled V scales of tokens 8 qb + (0..7) in value group g;
+  //   svs (8-bit): the prescaled V scales, [group][token].
+  u32x4 kops[kW][4][4][2];
+  union {
+    u32x4 vops[kW][4][4][2];
+    float svs[kW][kBS];
+  } v;
   float alp[kW][kR];             // rescale factors of a reference move (per wave)
   float qus[kR];                 // 2^-Sq(row)
   float wm[kW][kR];
@@ -78,8 +98,9 @@ template <int kBits>
 struct Regs32 {
   typename CodeOps<kBits>::words k[4];  // K codes, k-step 0..3
   typename CodeOps<kBits>::words v[4];  // V codes, value group 0..3
-  float2 ks;    // K scales 2 lane, 2 lane + 1 of the block
-  float2 vs;    // V scales 2 lane, 2 lane + 1 of the block ([group][token])
+  float2 ks;    // K scales of this lane's k-slot pair (see Lanes32::s_pair)
+  float2 vs;    // V scales: 4-bit the same slot pair of one value group,
+                // 8-bit scales 2 lane and 2 lane + 1 ([group][token] order)
 };
 
 // Buffer descriptors of one KV head's four arrays (kvq_mfma_common.h): the
@@ -88,15 +109,31 @@ struct Head32 {
   __amdgpu_buffer_rsrc_t kc, ksc, vc, vsc;
 };
 
+// Lane (a, qb, j) = (lane / 16, lane / 4 % 4, lane % 4) owns k-slots 2j, 2j + 1
+// of run (a, qb): entries 32 a + 8 qb + kSlotByte[2j] and kSlotByte[2j + 1]
+// = that + 2 of a block's 128 K scales (channel order) or 4-bit V scales
+// ([group][token] order).
 struct Lanes32 {
-  unsigned k_off, v_off, s_off;  // byte offsets of this lane in a block
+  unsigned k_off, v_off;  // byte offsets of this lane's code bytes in a block
+  unsigned s_pair;        // byte offset of its first scale of the slot pair
+  unsigned s_off;         // byte offset of scales 2 lane, 2 lane + 1 (8-bit V)
 };
+
+__device__ __forceinline__ float buf_f1(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
 
 template <int kBits>
 __device__ __forceinline__ void load_scales32(Regs32<kBits>& r, const Head32& h, int blk,
                                               const Lanes32& o) {
-  r.ks = buf_f2(h.ksc, o.s_off, blk * kBS * 4);
-  r.vs = buf_f2(h.vsc, o.s_off, blk * kBS * 4);
+  r.ks.x = buf_f1(h.ksc, o.s_pair, blk * kBS * 4);
+  r.ks.y = buf_f1(h.ksc, o.s_pair + 8, blk * kBS * 4);
+  if constexpr (kBits == 4) {
+    r.vs.x = buf_f1(h.vsc, o.s_pair, blk * kBS * 4);
+    r.vs.y = buf_f1(h.vsc, o.s_pair + 8, blk * kBS * 4);
+  } else {
+    r.vs = buf_f2(h.vsc, o.s_off, blk * kBS * 4);
+  }
 }
 template <int kBits>
 __device__ __forceinline__ void load_block32(Regs32<kBits>& r, const Head32& h, int blk,
@@ -121,6 +158,7 @@ struct State32 {
   f32x4 acc[4][2][2];
   int sv;
   float vscale, vhi, vlo;
+  float kf, kun, khi, klo;  // K prescale and the K scales that keep it valid
   bool live;
 };
 
@@ -166,6 +204,42 @@ __device__ __forceinline__ half2_t pk16(float x, float y) {
   return __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(x, y));
 }
 
+// fp16 lo = a[j] - hi[j] for 8 float32 values a (k-slot order) and their fp16
+// hi: one v_fma_mixlo_f16 / v_fma_mixhi_f16 per value (the fp16 hi widened
+// inside the instruction, the difference rounded once), with the same
+// early-clobber outputs and closing s_nop 1 as product_hilo.
+__device__ __forceinline__ half8_t residual_lo(const float a[8], half8_t hi) {
+  const u32x4 h = __builtin_bit_cast(u32x4, hi);
+  unsigned l0, l1, l2, l3;
+  asm("v_fma_mixlo_f16 %0, %4, 1.0, -%12 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %5, 1.0, -%12 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %1, %6, 1.0, -%13 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %1, %7, 1.0, -%13 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %2, %8, 1.0, -%14 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %2, %9, 1.0, -%14 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %3, %10, 1.0, -%15 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %3, %11, 1.0, -%15 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "s_nop 1"
+      : "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]));
+  const u32x4 l = {l0, l1, l2, l3};
+  return __builtin_bit_cast(half8_t, l);
+}
+
+// q~ = q * s as fp16 hi + lo from the fp16 hi/lo pairs of q (qh, ql) and of
+// the K scales (sh, sl), all packed fp16 arithmetic: hi = qh * sh rounded to
+// nearest, r = qh * sh - hi (exact: the residual of a product of two fp16
+// values fits in fp16 outside the subnormal range), lo = (ql * sh + r) +
+// qh * sl, each fused multiply-add rounded once.  ql * sl (2^-22 of q~) is
+// dropped.
+__device__ __forceinline__ void scaled_q(half8_t qh, half8_t ql, half8_t sh, half8_t sl,
+                                         half8_t& hi, half8_t& lo) {
+  hi = qh * sh;
+  const half8_t r = __builtin_elementwise_fma(qh, sh, -hi);
+  lo = __builtin_elementwise_fma(qh, sl, __builtin_elementwise_fma(ql, sh, r));
+}
+
 // kMasked: mask tokens >= t_end; kCausal (implies kMasked): also mask, for
 // score row 16t + n, the tokens after its query's position lim[t], and keep
 // rows that have seen no legal key at m = -inf (exponents then taken
@@ -175,8 +249,8 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
                                                const typename CodeOps<kBits>::consts& cc,
                                                State32& st,
                                                const Head32& h, int next, const Lanes32& lo,
-                                               const float us_row[2], const float (&qk)[2][4][8],
-                                               const int (&lim)[2]) {
+                                               const float us_row[2], const half8_t (&qh)[2][4],
+                                               const half8_t (&ql)[2][4], const int (&lim)[2]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
@@ -185,19 +259,24 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
   // ---- block set-up: scale guards, then this block's scales into LDS ------
   const float lks = fmaxf(br.ks.x, br.ks.y);
   const float lvs = fmaxf(br.vs.x, br.vs.y);
-  // A block whose K scales reach kSkMax is scaled down by 2^-e (kf) and its
-  // scores back up (kun); otherwise both are 1.
-  float kf = 1.0f, kun = 1.0f;
-  if (__builtin_amdgcn_ballot_w64(lks >= kSkMax) != 0) {
+  // K prescale kf = 2^e (scores scaled back by kun = 2^-e): set so the
+  // block's largest K scale lands in [2^(kKTop-1), 2^kKTop), kept while it
+  // stays in [2^kKLow, 2^kKTop).  The top keeps q~ < 2^15 (q rows below
+  // 2^10); the bottom keeps the fp16 lo of scales within 2^4 of the
+  // largest out of the subnormal range.
+  if (!st.live || __builtin_amdgcn_ballot_w64(!(lks < st.khi)) != 0 ||
+      __builtin_amdgcn_ballot_w64(lks >= st.klo) == 0) {
     float mx = fmaxf(lks, dpp<kRowRor1>(lks));
     mx = fmaxf(mx, dpp<kRowRor2>(mx));
     mx = fmaxf(mx, dpp<kRowRor4>(mx));
-    mx = fmaxf(mx, dpp<kRowRor8>(mx));
-    mx = qblock_max(mx);
-    const int e = __builtin_amdgcn_frexp_expf(mx);
-    kf = __builtin_ldexpf(1.0f, -e);
-    kun = __builtin_ldexpf(1.0f, e);
+    mx = qblock_max(fmaxf(mx, dpp<kRowRor8>(mx)));
+    const int e = prescale_exp(mx, kKTop);
+    st.kf = __builtin_ldexpf(1.0f, e);
+    st.kun = __builtin_ldexpf(1.0f, -e);
+    st.khi = __builtin_ldexpf(1.0f, kKTop - e);
+    st.klo = __builtin_ldexpf(1.0f, kKLow - e);
   }
+  const float kf = st.kf, kun = st.kun;
   // V prescale 2^sv: set so the largest V scale lands in [2^8, 2^9), moved
   // only when the block's largest V scale leaves [2^kSvLow, 2^kSvTop) after
   // scaling (u is rescaled by the change; z does not carry it).
@@ -224,13 +303,30 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
     st.vlo = __builtin_ldexpf(1.0f, kSvLow - sv_new);
   }
   {
-    float2 k2 = br.ks, v2 = br.vs;
-    k2.x *= kf;
-    k2.y *= kf;
-    v2.x *= st.vscale;
-    v2.y *= st.vscale;
-    *reinterpret_cast<float2*>(&sm.sks[wave][2 * lane]) = k2;
-    *reinterpret_cast<float2*>(&sm.svs[wave][2 * lane]) = v2;
+    // This lane's k-slot pair of run (a, qb), written as one word per operand.
+    const int a = lane >> 4, qb = (lane >> 2) & 3, j = lane & 3;
+    const float k0 = br.ks.x * kf, k1 = br.ks.y * kf;
+    const unsigned kh = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(k0, k1));
+    const unsigned kl = __builtin_bit_cast(
+        unsigned, __builtin_amdgcn_cvt_pkrtz(sub_half<0>(k0, kh), sub_half<1>(k1, kh)));
+    unsigned* kw = reinterpret_cast<unsigned*>(&sm.kops[wave][a][qb][0]);
+    kw[j] = kh;
+    kw[4 + j] = kl;
+    if constexpr (kBits == 4) {
+      // vh keeps the 8 leading bits of the prescaled scale (exact in fp16, and
+      // (c - 7) * vh is exact too: |c - 7| has at most 3 significant bits);
+      // vl = the exact float32 remainder, rounded toward zero to fp16.
+      const float v0 = br.vs.x * st.vscale, v1 = br.vs.y * st.vscale;
+      const float h0 = as_f32(as_u32(v0) & 0xFFFF0000u), h1 = as_f32(as_u32(v1) & 0xFFFF0000u);
+      unsigned* vw = reinterpret_cast<unsigned*>(&sm.v.vops[wave][a][qb][0]);
+      vw[j] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(h0, h1));
+      vw[4 + j] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(v0 - h0, v1 - h1));
+    } else {
+      float2 v2 = br.vs;
+      v2.x *= st.vscale;
+      v2.y *= st.vscale;
+      *reinterpret_cast<float2*>(&sm.v.svs[wave][2 * lane]) = v2;
+    }
   }
   load_scales32(br, h, next, lo);  // next block's scales into the same registers
   const float us0 = us_row[0] * kun, us1 = us_row[1] * kun;
@@ -240,23 +336,11 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
   f32x4 se[2] = {zero4, zero4}, so[2] = {zero4, zero4};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int c0 = ks * 32 + q * 8;
-    const f32x4 sa = *reinterpret_cast<const f32x4*>(&sm.sks[wave][c0]);
-    const f32x4 sb = *reinterpret_cast<const f32x4*>(&sm.sks[wave][c0 + 4]);
-    float sk[8];  // k-slot order
-    sk[0] = sa[0]; sk[1] = sa[2]; sk[2] = sa[1]; sk[3] = sa[3];
-    sk[4] = sb[0]; sk[5] = sb[2]; sk[6] = sb[1]; sk[7] = sb[3];
-    half2_t sk16[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sk16[i] = pk16(sk[2 * i], sk[2 * i + 1]);
+    const half8_t sh = __builtin_bit_cast(half8_t, sm.kops[wave][ks][q][0]);
+    const half8_t sl = __builtin_bit_cast(half8_t, sm.kops[wave][ks][q][1]);
     half8_t bh[2], bl[2];
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      half2_t q16[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q16[i] = pk16(qk[t][ks][2 * i], qk[t][ks][2 * i + 1]);
-      product_hilo(qk[t][ks], sk, q16, sk16, bh[t], bl[t]);
-    }
+    for (int t = 0; t < kTiles; ++t) scaled_q(qh[t][ks], ql[t][ks], sh, sl, bh[t], bl[t]);
     half8_t alo, ahi;  // tokens 2n and 2n + 1
     CodeOps<kBits>::to_half(br.k[ks], cc, alo, ahi);
     br.k[ks] = CodeOps<kBits>::load(h.kc, lo.k_off + ks * kKStep<kBits>,
@@ -343,30 +427,65 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
     for (int i = 0; i < 4; ++i) p16[t][i] = pk16(pk[t][2 * i], pk[t][2 * i + 1]);
   }
 
-  // ---- u += p~ x V codes, p~ = p * sV * 2^sv, one value group at a time ---
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 va = *reinterpret_cast<const f32x4*>(&sm.svs[wave][g * 32 + q * 8]);
-    const f32x4 vb = *reinterpret_cast<const f32x4*>(&sm.svs[wave][g * 32 + q * 8 + 4]);
-    float sv[8];  // k-slot order
-    sv[0] = va[0]; sv[1] = va[2]; sv[2] = va[1]; sv[3] = va[3];
-    sv[4] = vb[0]; sv[5] = vb[2]; sv[6] = vb[1]; sv[7] = vb[3];
-    half2_t sv16[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sv16[i] = pk16(sv[2 * i], sv[2 * i + 1]);
-    half8_t ah[2], al[2];
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) product_hilo(pk[t], sv, p16[t], sv16, ah[t], al[t]);
-    half8_t be, bo;  // features 32g + 2n and 32g + 2n + 1
-    CodeOps<kBits>::to_half(br.v[g], cc, be, bo);
-    br.v[g] = CodeOps<kBits>::load(h.vc, lo.v_off + g * kVStep<kBits>,
-                                   next * kBB<kBits>);  // next block's group
+  if constexpr (kBits == 4) {
+    // ---- u += p x ((c - 7) * (vh + vl)), one value group at a time ---------
+    // p = ph + pl (fp16 hi / lo, shared by the four groups), the V side two
+    // fp16 operands per group (shared by both row tiles): (c - 7) * vh exact,
+    // (c - 7) * vl rounded once; pl * (c - 7) * vl (2^-19 of the term) is
+    // dropped.
+    half8_t ph[2], pl[2];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      st.acc[g][t][0] = mfma(ah[t], be, st.acc[g][t][0]);
-      st.acc[g][t][0] = mfma(al[t], be, st.acc[g][t][0]);
-      st.acc[g][t][1] = mfma(ah[t], bo, st.acc[g][t][1]);
-      st.acc[g][t][1] = mfma(al[t], bo, st.acc[g][t][1]);
+      const u32x4 w = {__builtin_bit_cast(unsigned, p16[t][0]), __builtin_bit_cast(unsigned, p16[t][1]),
+                       __builtin_bit_cast(unsigned, p16[t][2]), __builtin_bit_cast(unsigned, p16[t][3])};
+      ph[t] = __builtin_bit_cast(half8_t, w);
+      pl[t] = residual_lo(pk[t], ph[t]);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const half8_t vh = __builtin_bit_cast(half8_t, sm.v.vops[wave][g][q][0]);
+      const half8_t vl = __builtin_bit_cast(half8_t, sm.v.vops[wave][g][q][1]);
+      half8_t ce, co;  // (c - 7) of features 32g + 2n and 32g + 2n + 1
+      CodeOps<kBits>::to_half(br.v[g], cc, ce, co);
+      br.v[g] = CodeOps<kBits>::load(h.vc, lo.v_off + g * kVStep<kBits>,
+                                     next * kBB<kBits>);  // next block's group
+      const half8_t e1 = ce * vh, e2 = ce * vl, o1 = co * vh, o2 = co * vl;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        st.acc[g][t][0] = mfma(ph[t], e1, st.acc[g][t][0]);
+        st.acc[g][t][0] = mfma(pl[t], e1, st.acc[g][t][0]);
+        st.acc[g][t][0] = mfma(ph[t], e2, st.acc[g][t][0]);
+        st.acc[g][t][1] = mfma(ph[t], o1, st.acc[g][t][1]);
+        st.acc[g][t][1] = mfma(pl[t], o1, st.acc[g][t][1]);
+        st.acc[g][t][1] = mfma(ph[t], o2, st.acc[g][t][1]);
+      }
+    }
+  } else {
+    // ---- u += p~ x V codes, p~ = p * sV * 2^sv, one value group at a time -
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 va = *reinterpret_cast<const f32x4*>(&sm.v.svs[wave][g * 32 + q * 8]);
+      const f32x4 vb = *reinterpret_cast<const f32x4*>(&sm.v.svs[wave][g * 32 + q * 8 + 4]);
+      float sv[8];  // k-slot order
+      sv[0] = va[0]; sv[1] = va[2]; sv[2] = va[1]; sv[3] = va[3];
+      sv[4] = vb[0]; sv[5] = vb[2]; sv[6] = vb[1]; sv[7] = vb[3];
+      half2_t sv16[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv16[i] = pk16(sv[2 * i], sv[2 * i + 1]);
+      half8_t ah[2], al[2];
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) product_hilo(pk[t], sv, p16[t], sv16, ah[t], al[t]);
+      half8_t be, bo;  // features 32g + 2n and 32g + 2n + 1
+      CodeOps<kBits>::to_half(br.v[g], cc, be, bo);
+      br.v[g] = CodeOps<kBits>::load(h.vc, lo.v_off + g * kVStep<kBits>,
+                                     next * kBB<kBits>);  // next block's group
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        st.acc[g][t][0] = mfma(ah[t], be, st.acc[g][t][0]);
+        st.acc[g][t][0] = mfma(al[t], be, st.acc[g][t][0]);
+        st.acc[g][t][1] = mfma(ah[t], bo, st.acc[g][t][1]);
+        st.acc[g][t][1] = mfma(al[t], bo, st.acc[g][t][1]);
+      }
     }
   }
 }
@@ -434,8 +553,12 @@ attend_mfma_r32_kernel(AttendProblem p) {
   const int b_last = b_first + (b_end - 1 - b_first) / kW * kW;  // valid if b_first < b_end
   // Code bytes of lane (n, q): K channels 32 ks + 8q .. +7 of tokens 2n, 2n + 1;
   // V tokens 8q .. 8q+7 of features 32 g + 2n, +1 (2 * kBits bytes each).
+  // Scales: the k-slot pair (2j, 2j + 1) of run (lane / 16, lane / 4 % 4),
+  // entries kSlotByte[2j] = (j & 1) + 4 (j >> 1) and that + 2 of the run.
+  const int sj = lane & 3;
   const Lanes32 lo = {static_cast<unsigned>(lane * 2 * kBits),
                       static_cast<unsigned>(q * 128 * kBits + n * 2 * kBits),
+                      static_cast<unsigned>(4 * (8 * (lane >> 2) + (sj & 1) + 4 * (sj >> 1))),
                       static_cast<unsigned>(lane * 8)};
 
   // The block holding token N-1 is masked when N is not a multiple of 32;
@@ -486,8 +609,9 @@ attend_mfma_r32_kernel(AttendProblem p) {
   __syncthreads();
   const float us_row[2] = {sm.qus[n], kTiles > 1 ? sm.qus[16 + n] : 1.0f};
   // This lane's q values for the whole kernel (rows 16t + n, channels
-  // 32 ks + 8q + (0..7), k-slot order), kept in registers.
-  float qk[2][4][8];
+  // 32 ks + 8q + (0..7), k-slot order) as fp16 hi (toward zero) and lo of the
+  // float32 remainder, kept in registers.
+  half8_t qh[2][4], ql[2][4];
 #pragma unroll
   for (int t = 0; t < kTiles; ++t)
 #pragma unroll
@@ -495,8 +619,10 @@ attend_mfma_r32_kernel(AttendProblem p) {
       const float* qrow = &sm.u.qs[16 * t + n][ks * 32 + q * 8];
       const f32x4 qa = *reinterpret_cast<const f32x4*>(qrow);
       const f32x4 qb = *reinterpret_cast<const f32x4*>(qrow + 4);
+      float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qk[t][ks][j] = j < 4 ? qa[kSlotByte[j]] : qb[kSlotByte[j] - 4];
+      for (int j = 0; j < 8; ++j) x[j] = j < 4 ? qa[kSlotByte[j]] : qb[kSlotByte[j] - 4];
+      split_hilo(x, qh[t][ks], ql[t][ks]);
     }
 
   const typename CodeOps<kBits>::consts cc = CodeOps<kBits>::make();
@@ -506,6 +632,8 @@ attend_mfma_r32_kernel(AttendProblem p) {
   st.sv = 0;
   st.vscale = 1.0f;
   st.vhi = st.vlo = 0.0f;
+  st.kf = st.kun = 1.0f;
+  st.khi = st.klo = 0.0f;
   st.live = false;
   {
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -519,11 +647,11 @@ attend_mfma_r32_kernel(AttendProblem p) {
   const int lim[2] = {p.pos_end - p.R + n % p.R, p.pos_end - p.R + (16 + n) % p.R};
   if (active) {
     attend_block32<kBits, kTiles, true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
-                                  loop_begin <= loop_end ? loop_begin : first, lo, us_row, qk,
-                                  lim);
+                                  loop_begin <= loop_end ? loop_begin : first, lo, us_row, qh,
+                                  ql, lim);
     for (int b = loop_begin; b <= loop_end; b += kW)
       attend_block32<kBits, kTiles, false, false>(sm, br, b * kBlockTokens, t_end, cc, st, h,
-                                   min(b + kW, loop_end), lo, us_row, qk, lim);
+                                   min(b + kW, loop_end), lo, us_row, qh, ql, lim);
   }
   st.z[0] = qblock_sum(st.z[0]);
   if (kTiles > 1) st.z[1] = qblock_sum(st.z[1]);

@@ -303,6 +303,27 @@ kvq_status kvq_attend_f32(const float* q, const float* k, const float* v,
  * ceiling.  Allocates nothing; asynchronous on `stream`. */
 kvq_status kvq_stream_read(const void* data, size_t bytes, void* sink, void* stream);
 
+/* ---- kvq_phase_trace_fetch -----------------------------------------------------------
+ * Measurement aid, not part of the method: the timeline of the last
+ * matrix-core attend launch, to split its time into the steps of
+ * [BKD] "Do not average independently normalized blocks" (stream the blocks,
+ * merge partial statistics) and the two stops of [RL] "two stops of the
+ * online accumulation" (waves, then KV splits).  Only a library built with
+ * KVQ_PHASE_TRACE records anything (quantized_kv_cache_attend_amd/build.py
+ * --phase-trace writes it as libkvq_phase.so beside libkvq.so): there every
+ * wave of the 4-row (kernel 0) or 32-row (kernel 1) matrix-core kernel writes
+ * the chip-wide 100 MHz clock at KVQ_PHASE_MARKS fixed points
+ * (start, query ready, first block ready [4-row kernel only], last block done,
+ * workgroup merged, partial stores acknowledged, ticket taken, end) for the
+ * first KVQ_PHASE_WAVES waves in launch order (workgroup, then wave).  This
+ * copies up to `bytes` (a positive multiple of 8) of those uint64 records
+ * into host memory `host`, KVQ_PHASE_MARKS per wave; a mark a wave did not
+ * reach keeps an older value.  Synchronous.  KVQ_ERR_UNSUPPORTED in the normal
+ * build. */
+#define KVQ_PHASE_WAVES 16384
+#define KVQ_PHASE_MARKS 8
+kvq_status kvq_phase_trace_fetch(int kernel, void* host, size_t bytes);
+
 /* ---- diagnostics -------------------------------------------------------------------- */
 const char* kvq_status_string(int status);  /* static string, never NULL */
 const char* kvq_last_error(void);           /* message of this thread's last failed call */

@@ -60,6 +60,7 @@ _SIGNATURES = {
     "kvq_attend_f32": (_c_int, [_c_vp] * 3 + [_c_int] * 6 + [_c_float, _c_int, _c_vp, _c_size,
                                                              _c_vp, _c_vp]),
     "kvq_stream_read": (_c_int, [_c_vp, _c_size, _c_vp, _c_vp]),
+    "kvq_phase_trace_fetch": (_c_int, [_c_int, _c_vp, _c_size]),
     "kvq_status_string": (ctypes.c_char_p, [_c_int]),
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_abi_version": (_c_int, []),

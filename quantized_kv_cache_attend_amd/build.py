@@ -51,34 +51,45 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *EXTRA_CFLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+LIB_PHASE = os.path.join(PKG, "libkvq_phase.so")
+BUILD_PHASE = os.path.join(ROOT, "_build_phase")
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *CFLAGS, *extra, *EXTRA_CFLAGS.get(os.path.basename(src), []), "-c", src, "-o",
+           obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    if os.path.isdir(BUILD):
-        shutil.rmtree(BUILD)
-    os.makedirs(BUILD)
+def build(verbose: bool = False, phase_trace: bool = False) -> str:
+    """Compile every source and link the library.  phase_trace: the
+    diagnostic build with per-wave phase timestamps in the matrix-core attend
+    kernels (-DKVQ_PHASE_TRACE), written to libkvq_phase.so; the package
+    always loads libkvq.so."""
+    build_dir, lib = (BUILD_PHASE, LIB_PHASE) if phase_trace else (BUILD, LIB)
+    extra = ("-DKVQ_PHASE_TRACE",) if phase_trace else ()
+    if os.path.isdir(build_dir):
+        shutil.rmtree(build_dir)
+    os.makedirs(build_dir)
     srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-mcode-object-version=5", "-shared", "-fPIC", *objs,
            "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, phase_trace="--phase-trace" in sys.argv[1:])
     sys.exit(0)

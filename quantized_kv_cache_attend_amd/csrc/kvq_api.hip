@@ -656,6 +656,20 @@ const char* kvq_status_string(int status) {
 
 const char* kvq_last_error(void) { return g_last_error; }
 
-int kvq_abi_version(void) { return 7; }
+int kvq_abi_version(void) { return 8; }
+
+kvq_status kvq_phase_trace_fetch(int kernel, void* host, size_t bytes) {
+  if (host == nullptr || bytes == 0 || bytes % 8 != 0)
+    return fail(KVQ_ERR_INVALID, "phase records: null host buffer or size %zu not a positive "
+                "multiple of 8", bytes);
+  if (kernel != 0 && kernel != 1)
+    return fail(KVQ_ERR_INVALID, "phase records: kernel %d is neither 0 (4-row) nor 1 (32-row)",
+                kernel);
+  const int st = kernel == 0 ? kvq::phase_fetch_r4(host, bytes) : kvq::phase_fetch_r32(host, bytes);
+  if (st == KVQ_ERR_UNSUPPORTED)
+    return fail(KVQ_ERR_UNSUPPORTED, "phase records exist only in a KVQ_PHASE_TRACE build");
+  if (st != KVQ_OK) return fail(KVQ_ERR_HIP, "phase records: copy from the device failed");
+  return KVQ_OK;
+}
 
 }  // extern "C"

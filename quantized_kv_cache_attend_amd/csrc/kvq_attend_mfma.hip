@@ -412,6 +412,7 @@ template <int kBits, bool kCausal, bool kWindow>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 attend_mfma_r4_kernel(AttendProblem p) {
   __shared__ Smem<kBits> sm;
+  phase_mark(kMarkStart);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -503,6 +504,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
   for (int i = 0; i < 8; ++i) qv[i] = __builtin_ldexpf(qv[i], sq);
   // 2^-Sq of score row n & 3 (held by lanes 16 (n & 3) ..)
   const float us_row = __builtin_ldexpf(1.0f, -__shfl(sq, (n & 3) * 16));
+  phase_mark(kMarkQReady);
 
   const typename CodeOps<kBits>::consts cc = CodeOps<kBits>::make();
   WaveState ws;
@@ -529,11 +531,13 @@ attend_mfma_r4_kernel(AttendProblem p) {
     BlockRegs<kBits> br;
     read_block(br, slot, lo);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot has been read
+    if (i == 0) phase_mark(kMarkFirstBlock);
     if (i + kRing<kBits> < cnt)
       dma_block<kBits>(slot, h, b_first + (i + kRing<kBits>) * kWaves, lane);
     attend_block<kBits, kCausal>(sm, br, (b_first + i * kWaves) * kBlockTokens, t_end, cc, ws, qv,
                                  us_row, lim, p.pos_end - p.R);
   }
+  phase_mark(kMarkLoopEnd);
   // z of each row: sum this lane's share over the four q-blocks
   ws.z = qblock_sum(ws.z);
 
@@ -579,6 +583,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
       for (int j = 0; j < kSlots; ++j) U[j] = fmaf(x, sm.u.m.wu[w][r][f0 + j], U[j]);
     }
   }
+  phase_mark(kMarkMerged);
   const long long row0 = bh * rows;
   if (p.splits == 1) {
     if (r < rows) {
@@ -586,12 +591,16 @@ attend_mfma_r4_kernel(AttendProblem p) {
       for (int j = 0; j < kSlots; ++j)  // Z = 0: a causal row with no legal key
         p.out[(row0 + r) * kD + f0 + j] = Z > 0.0f ? U[j] / Z : 0.0f;
     }
+    phase_mark(kMarkEnd);
     return;
   }
   split_combine<kSlots, kSlots, 0>(p, split, bh, r, f0, U, M, Z, &sm.u.m.last);
+  phase_mark(kMarkEnd);
 }
 
 }  // namespace
+
+int phase_fetch_r4(void* host, size_t bytes) { return phase_fetch(host, bytes); }
 
 int mfma_tokens_per_split(int N, int splits) {
   const int per = (N + splits - 1) / splits;

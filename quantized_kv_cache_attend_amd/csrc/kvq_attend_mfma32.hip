@@ -505,6 +505,7 @@ template <int kBits, int kTiles, bool kCausal, bool kWindow>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attend_mfma_r32_kernel(AttendProblem p) {
   __shared__ Smem32 sm;
+  phase_mark(kMarkStart);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -625,6 +626,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
       split_hilo(x, qh[t][ks], ql[t][ks]);
     }
 
+  phase_mark(kMarkQReady);
   const typename CodeOps<kBits>::consts cc = CodeOps<kBits>::make();
   State32 st;
   st.m[0] = st.m[1] = -INFINITY;
@@ -653,6 +655,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
       attend_block32<kBits, kTiles, false, false>(sm, br, b * kBlockTokens, t_end, cc, st, h,
                                    min(b + kW, loop_end), lo, us_row, qh, ql, lim);
   }
+  phase_mark(kMarkLoopEnd);
   st.z[0] = qblock_sum(st.z[0]);
   if (kTiles > 1) st.z[1] = qblock_sum(st.z[1]);
 
@@ -710,6 +713,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
     }
     if (half == 0) __syncthreads();  // the first pair is read before the second overwrites it
   }
+  phase_mark(kMarkMerged);
   const long long row0 = bh * rows;
   if (p.splits == 1) {
     if (r < rows) {
@@ -721,10 +725,12 @@ attend_mfma_r32_kernel(AttendProblem p) {
         *reinterpret_cast<f32x4*>(&p.out[(row0 + r) * kD + f0 + 32 * i]) = o;
       }
     }
+    phase_mark(kMarkEnd);
     return;
   }
 
   split_combine<16, 4, 32>(p, split, bh, r, f0, U, M, Z, &sm.last);
+  phase_mark(kMarkEnd);
 }
 
 }  // namespace
@@ -748,6 +754,8 @@ void launch_r32(const AttendProblem& p, unsigned grid, hipStream_t stream) {
                          dim3(kT), 0, stream, p);
   }
 }
+
+int phase_fetch_r32(void* host, size_t bytes) { return phase_fetch(host, bytes); }
 
 hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;

@@ -10,6 +10,7 @@
 
 #include <cstdint>
 
+#include "kvq.h"
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -229,6 +230,49 @@ __device__ __forceinline__ void split_hilo(const float x[8], half8_t& hi, half8_
   lo = __builtin_bit_cast(half8_t, l);
 }
 
+// ---- phase timestamps (diagnostic build only) -------------------------------
+// Built with KVQ_PHASE_TRACE, every wave of a matrix-core attend launch records
+// the chip-wide constant 100 MHz clock (s_memrealtime) at fixed points of its
+// work into its translation unit's array, one lane per wave, and
+// kvq_phase_trace_fetch copies the array out.  In the normal build phase_mark
+// compiles to nothing and phase_fetch reports the build as unsupported.
+constexpr int kPhaseWaves = 16384;  // waves recorded: the first ones by workgroup, then wave
+constexpr int kPhaseMarks = 8;
+enum PhaseMark {
+  kMarkStart = 0,       // the wave starts
+  kMarkQReady = 1,      // its query rows are in registers
+  kMarkFirstBlock = 2,  // its first block is ready (4-row kernel)
+  kMarkLoopEnd = 3,     // its last block is attended
+  kMarkMerged = 4,      // the workgroup's waves are merged
+  kMarkAcked = 5,       // the split's partial stores are acknowledged
+  kMarkTicket = 6,      // the split took its ticket
+  kMarkEnd = 7,         // the wave ends
+};
+#ifdef KVQ_PHASE_TRACE
+__device__ unsigned long long phase_trace[kPhaseWaves * kPhaseMarks];
+#endif
+__device__ __forceinline__ void phase_mark(int mark) {
+#ifdef KVQ_PHASE_TRACE
+  const unsigned w = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if ((threadIdx.x & 63) == 0 && w < kPhaseWaves)
+    phase_trace[w * kPhaseMarks + mark] = __builtin_amdgcn_s_memrealtime();
+#else
+  (void)mark;
+#endif
+}
+// Host side: copy up to `bytes` of this translation unit's records.
+inline int phase_fetch(void* host, size_t bytes) {
+#ifdef KVQ_PHASE_TRACE
+  if (bytes > sizeof(phase_trace)) bytes = sizeof(phase_trace);
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(phase_trace), bytes) == hipSuccess ? KVQ_OK
+                                                                                : KVQ_ERR_HIP;
+#else
+  (void)host;
+  (void)bytes;
+  return KVQ_ERR_UNSUPPORTED;
+#endif
+}
+
 // ---- split combine -----------------------------------------------------------
 // The KV splits of a head merge their partial (m, z, u) rows with the same
 // rescale as the blocks ("two stops of the online accumulation" on the
@@ -297,6 +341,7 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above are acknowledged
+  phase_mark(kMarkAcked);
   __syncthreads();
   unsigned* counter = &p.counters[head * kCounterStride];
   if (threadIdx.x == 0) {
@@ -305,6 +350,7 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
     *last = ticket_outcome(prev, p.splits);
   }
   __syncthreads();
+  phase_mark(kMarkTicket);
   if (*last == kTicketWait) return;
   if (*last == kTicketStale) {  // the counter was not zero at the start: make it visible
     if (mine) {

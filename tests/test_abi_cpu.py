@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert lib.kvq_abi_version() == 7
+    assert lib.kvq_abi_version() == 8
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.kvq_status_string(st)
 
@@ -262,3 +262,15 @@ def test_study_rel_l2_closed_form():
     ref = np.array([[3.0, 4.0, 0.0], [0.0, 0.0, 12.0]])
     approx = np.array([[3.0, 4.0, 5.0], [0.0, 0.0, 12.0]])
     assert accuracy.rel_l2(approx, ref) == pytest.approx(5.0 / 13.0, rel=1e-15)
+
+
+def test_phase_trace_fetch_only_in_the_trace_build():
+    """kvq_phase_trace_fetch is exported by every build; the normal library
+    records nothing and says so before touching the device, and bad
+    arguments are rejected first."""
+    buf = (ctypes.c_uint64 * 16)()
+    assert lib.kvq_phase_trace_fetch(0, ctypes.cast(buf, ctypes.c_void_p), 128) == kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_phase_trace_fetch(1, ctypes.cast(buf, ctypes.c_void_p), 128) == kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_phase_trace_fetch(2, ctypes.cast(buf, ctypes.c_void_p), 128) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_phase_trace_fetch(0, None, 128) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_phase_trace_fetch(0, ctypes.cast(buf, ctypes.c_void_p), 12) == kvq.KVQ_ERR_INVALID

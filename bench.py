@@ -462,29 +462,36 @@ def main():
             f"({rbytes / (read_us * 1e-6) / 1e9:.0f} GB/s); attend / ceiling = {kernel_us / read_us:.2f}")
 
         # Decode loop on a growing cache laid out for all N tokens: a prompt
-        # of N - 80 tokens in one append, then one-token steps (kvq_append +
-        # kvq_attend_cache over the tokens so far), 16 untimed, 64 timed with
-        # events around each call (eager: each step's N differs).  The last step attends all N tokens and
-        # must equal the full-cache call above bit for bit.
+        # of N - 80 tokens in one append, then one-token steps over the
+        # tokens so far, 16 untimed and 64 timed with one event pair around
+        # the 64 (eager: each step's N differs).  Two forms of the step: one
+        # kvq_append_attend call (one launch where the 4-row matrix-core
+        # kernel serves it), and kvq_append followed by kvq_attend_cache.  The
+        # last step attends all N tokens and must equal the full-cache call
+        # above bit for bit.
         n_warm, n_timed = 16, 64
         prompt = w.N - n_warm - n_timed
         if prompt >= 1:
-            cache = kvq.new_cache(w.B, w.Hkv, w.N, w.D, bits, group, device=dev)
             kp, vp = kd[:, :, :prompt].contiguous(), vd[:, :, :prompt].contiguous()
+            cache = kvq.new_cache(w.B, w.Hkv, w.N, w.D, bits, group, device=dev)
+            cache2 = kvq.new_cache(w.B, w.Hkv, w.N, w.D, bits, group, device=dev)
             p0 = torch.cuda.Event(enable_timing=True)
             p1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             p0.record(stream)
             kvq.append(kp, vp, 0, cache, w.N, bits, group)
             p1.record(stream)
+            kvq.append(kp, vp, 0, cache2, w.N, bits, group)
             torch.cuda.synchronize()
             prompt_us = p0.elapsed_time(p1) * 1e3
             del kp, vp
             k_steps = [kd[:, :, i:i + 1].contiguous() for i in range(prompt, w.N)]
             v_steps = [vd[:, :, i:i + 1].contiguous() for i in range(prompt, w.N)]
             dec_out = torch.empty_like(qd)
+            dec_out2 = torch.empty_like(qd)
+            ws2 = kvq.new_workspace(w.B, w.Hq, w.Hkv, w.R, w.N, w.D, splits, device=dev)
             torch.cuda.synchronize()
-            # Queue the loops behind a few ms of unrelated reads so the host
+            # Queue each loop behind a few ms of unrelated reads so the host
             # enqueues every step before the GPU reaches them: one event pair
             # then times back-to-back GPU work, not the pace of the Python
             # calls (an event pair around one small kernel costs several us).
@@ -493,9 +500,18 @@ def main():
             def queue_blocker():
                 for _ in range(128):
                     kvq.stream_read(blocker, sink)
-            queue_blocker()
             d0 = torch.cuda.Event(enable_timing=True)
             d1 = torch.cuda.Event(enable_timing=True)
+            queue_blocker()
+            for i, n in enumerate(range(prompt, w.N)):
+                if i == n_warm:
+                    d0.record(stream)
+                kvq.append_attend(qd, k_steps[i], v_steps[i], n, cache2, w.N, bits, group,
+                                  num_splits=splits, workspace=ws2, out=dec_out2)
+            d1.record(stream)
+            torch.cuda.synchronize()
+            fused_us = d0.elapsed_time(d1) * 1e3 / n_timed
+            queue_blocker()
             for i, n in enumerate(range(prompt, w.N)):
                 if i == n_warm:
                     d0.record(stream)
@@ -509,6 +525,8 @@ def main():
                               workspace=ws, variant=args.variant)
             torch.cuda.synchronize()
             same = bool(torch.equal(dec_out, full))
+            same_fused = bool(torch.equal(dec_out2, full)) and all(
+                torch.equal(a, b) for a, b in zip(cache, cache2))
             # the same number of back-to-back attends alone (all N tokens)
             queue_blocker()
             d0.record(stream)
@@ -522,15 +540,18 @@ def main():
                 "tokens": f"{w.N - n_timed + 1}..{w.N}",
                 "prompt_append_us": round(prompt_us, 1),
                 "prompt_tokens": prompt,
-                "step_us": round(step_us, 3),
+                "step_us": round(fused_us, 3),
+                "step_form": "kvq_append_attend (append in the attend's launch)",
                 "attend_only_us": round(attend_us, 3),
-                "append_us": round(step_us - attend_us, 3),
-                "last_step_equals_full_cache_attend": same,
+                "append_us": round(fused_us - attend_us, 3),
+                "two_call_step_us": round(step_us, 3),
+                "two_call_append_us": round(step_us - attend_us, 3),
+                "last_step_equals_full_cache_attend": same and same_fused,
             }
-            log(f"[bench] decode steps: {step_us:.2f} us per one-token append + attend, attend "
-                f"alone {attend_us:.2f} us (back to back, {n_timed} steps); last step == "
-                f"full-cache attend: {same}")
-            del cache, blocker
+            log(f"[bench] decode steps: {fused_us:.2f} us per one-call append + attend, "
+                f"{step_us:.2f} us as two calls, attend alone {attend_us:.2f} us (back to back, "
+                f"{n_timed} steps); last step == full-cache attend: {same and same_fused}")
+            del cache, cache2, blocker, ws2
 
         # A causal multi-token step on the same cache: R_c = 4 new queries per
         # head (the last 4 positions; GQA makes 4 * Hq/Hkv rows per KV head),

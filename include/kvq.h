@@ -196,6 +196,30 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
                             size_t workspace_bytes, float* out, int variant, int flags,
                             void* stream);
 
+/* ---- kvq_append_attend: one decode step ---------------------------------------------
+ * A decode step of [RL] "prefill and decode" (read the cached K/V, append the
+ * new position) in one call: kvq_append of one token per KV head (k_new,
+ * v_new [B][Hkv][1][D] float32) after the first N >= 0 tokens of the cache,
+ * then kvq_attend_cache (variant auto, flags 0) of q over the N + 1 tokens.
+ * The cache arrays, k_tail and out end bit for bit as after those two calls.
+ * Argument rules are theirs (N + 1 <= capacity; out must not overlap the new
+ * rows, k_tail or the workspace).  When the 4-row matrix-core kernel serves
+ * the attend (4- or 8-bit, group 32, D = 128, at most 4 query rows per KV
+ * head) and a workspace of kvq_attend_workspace_bytes(B, Hq, Hkv, R, N + 1,
+ * D, num_splits) bytes is given, both run in one launch: B * Hkv extra
+ * workgroups requantize the open K group and pack the token's V with
+ * device-scope stores and then raise a flag in the head's counter slot of the
+ * workspace, which the one wave attending the token's block waits for (a
+ * bounded wait; if it ran out, that head's output would be NaN).  Otherwise
+ * the two launches run back to back.  Workspace rules as for kvq_attend (the
+ * flag is back at zero after every completed call).  Asynchronous on
+ * `stream`. */
+kvq_status kvq_append_attend(const float* q, const float* k_new, const float* v_new, int B,
+                             int Hq, int Hkv, int R, int N, int capacity, int D, int bits,
+                             int group, uint8_t* k_codes, float* k_scales, uint8_t* v_codes,
+                             float* v_scales, float* k_tail, float sm_scale, int num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, void* stream);
+
 /* ---- kvq_attend ---------------------------------------------------------------
  * out[b][hq][r][:] = softmax_j(sm_scale * q[b][hq][r] . k_j) v_j over all N
  * tokens of KV head hq / (Hq/Hkv), with k_j, v_j decoded from the packed

@@ -53,6 +53,8 @@ _SIGNATURES = {
                                                                  _c_vp]),
     "kvq_cache_clear": (_c_int, [_c_int] * 6 + [_c_vp] * 5),
     "kvq_append": (_c_int, [_c_vp] * 2 + [_c_int] * 8 + [_c_vp] * 6),
+    "kvq_append_attend": (_c_int, [_c_vp] * 3 + [_c_int] * 9 + [_c_vp] * 5 + [
+        _c_float, _c_int, _c_vp, _c_size, _c_vp, _c_vp]),
     "kvq_attend_cache": (_c_int, [_c_vp] * 5 + [_c_int] * 9 + [_c_float, _c_int, _c_vp, _c_size,
                                                                _c_vp, _c_int, _c_int, _c_vp]),
     "kvq_attend_window": (_c_int, [_c_vp] * 7 + [_c_int] * 10 + [_c_float, _c_int, _c_vp,
@@ -380,6 +382,44 @@ def append(k_new, v_new, N, cache, capacity, bits=4, group=32):
     _check(lib.kvq_append(_ptr(k_new), _ptr(v_new), B, H, N, T, capacity, D, bits, group,
                           _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs), _ptr(tail),
                           _stream(k_new.device)), "kvq_append")
+
+
+def append_attend(q, k_new, v_new, N, cache, capacity, bits=4, group=32, sm_scale=0.0,
+                  num_splits=0, workspace=None, out=None):
+    """One decode step (kvq_append_attend): append k_new, v_new [B,Hkv,1,D]
+    float32 after the first N tokens of `cache` (the tuple new_cache returns,
+    laid out for `capacity` tokens), then attend q [B,Hq,R,D] over the N + 1
+    tokens.  Same bytes and output as append() followed by attend(...,
+    capacity=capacity); one launch when the 4-row matrix-core kernel serves
+    the step."""
+    torch = _torch()
+    _need(q, torch.float32, "q")
+    _need(k_new, torch.float32, "k_new")
+    _need(v_new, torch.float32, "v_new")
+    kc, ks, vc, vs, tail = cache
+    for t, n, dt in ((kc, "k_codes", torch.uint8), (ks, "k_scales", torch.float32),
+                     (vc, "v_codes", torch.uint8), (vs, "v_scales", torch.float32),
+                     (tail, "k_tail", torch.float32)):
+        _need(t, dt, n)
+    B, Hq, R, D = q.shape
+    Hkv = kc.shape[1]
+    if tuple(k_new.shape) != (B, Hkv, 1, D) or tuple(v_new.shape) != (B, Hkv, 1, D):
+        raise ValueError(f"k_new and v_new must both be [B, Hkv, 1, D] = {(B, Hkv, 1, D)}")
+    if bits in (4, 8) and group >= 2 and capacity >= 1:
+        _check_cache((kc, ks, vc, vs), B, Hkv, capacity, D, bits, group)
+        if tail.numel() < B * Hkv * group * D:
+            raise ValueError(f"k_tail must hold [B, H, group, D] = {(B, Hkv, group, D)}")
+    if workspace is None:
+        workspace = new_workspace(B, Hq, Hkv, R, N + 1, D, num_splits, device=q.device)
+    ws_bytes = _prepare_workspace(workspace, B * Hkv)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, q.shape, q.device)
+    _check(lib.kvq_append_attend(_ptr(q), _ptr(k_new), _ptr(v_new), B, Hq, Hkv, R, N, capacity,
+                                 D, bits, group, _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+                                 _ptr(tail), float(sm_scale), num_splits, _ptr(workspace),
+                                 ws_bytes, _ptr(out), _stream(q.device)), "kvq_append_attend")
+    return out
 
 
 def attend_f32(q, k, v, sm_scale=0.0, num_splits=0, workspace=None, out=None):

@@ -194,6 +194,11 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   p->part_z = splits > 1 ? reinterpret_cast<float*>(ws + wl.z_off) : nullptr;
   p->part_u = splits > 1 ? reinterpret_cast<float*>(ws + wl.u_off) : nullptr;
   p->counters = splits > 1 ? reinterpret_cast<unsigned*>(ws + wl.cnt_off) : nullptr;
+  p->append = 0;
+  p->k_new = p->v_new = nullptr;
+  p->k_tail = nullptr;
+  p->k_codes_w = p->v_codes_w = nullptr;
+  p->k_scales_w = p->v_scales_w = nullptr;
   return KVQ_OK;
 }
 
@@ -415,9 +420,15 @@ kvq_status kvq_cache_clear(int B, int H, int capacity, int D, int bits, int grou
                     "cache_clear launch");
 }
 
-kvq_status kvq_append(const float* k_new, const float* v_new, int B, int H, int N, int T,
-                      int capacity, int D, int bits, int group, uint8_t* k_codes, float* k_scales,
-                      uint8_t* v_codes, float* v_scales, float* k_tail, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of an append of T tokens after the first N (kvq_append).
+kvq_status check_append(const float* k_new, const float* v_new, int B, int H, int N, int T,
+                        int capacity, int D, int bits, int group, const uint8_t* k_codes,
+                        const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                        const float* k_tail) {
   if (!k_new || !v_new || !k_codes || !k_scales || !v_codes || !v_scales || !k_tail)
     return fail(KVQ_ERR_INVALID, "null pointer argument");
   if (B < 1 || H < 1 || T < 1 || D < 1 || N < 0)
@@ -454,12 +465,24 @@ kvq_status kvq_append(const float* k_new, const float* v_new, int B, int H, int 
       if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b]))
         return fail(KVQ_ERR_INVALID, "cache arrays overlap");
   }
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_append(const float* k_new, const float* v_new, int B, int H, int N, int T,
+                      int capacity, int D, int bits, int group, uint8_t* k_codes, float* k_scales,
+                      uint8_t* v_codes, float* v_scales, float* k_tail, void* stream) {
+  const kvq_status st = check_append(k_new, v_new, B, H, N, T, capacity, D, bits, group, k_codes,
+                                     k_scales, v_codes, v_scales, k_tail);
+  if (st != KVQ_OK) return st;
   return hip_status(launch_append(k_new, v_new, B, H, N, T, capacity, D, bits, group, k_codes,
                                   k_scales, v_codes, v_scales, k_tail,
                                   static_cast<hipStream_t>(stream)),
                     "append launch");
 }
-
 kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float* k_scales,
                             const uint8_t* v_codes, const float* v_scales, int B, int Hq, int Hkv,
                             int R, int N, int capacity, int D, int bits, int group,
@@ -491,6 +514,53 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
     default:
       return fail(KVQ_ERR_INVALID, "unknown variant %d", variant);
   }
+}
+
+kvq_status kvq_append_attend(const float* q, const float* k_new, const float* v_new, int B,
+                             int Hq, int Hkv, int R, int N, int capacity, int D, int bits,
+                             int group, uint8_t* k_codes, float* k_scales, uint8_t* v_codes,
+                             float* v_scales, float* k_tail, float sm_scale, int num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  if (Hkv < 1 || N < 0) return fail(KVQ_ERR_INVALID, "Hkv=%d < 1 or N=%d < 0", Hkv, N);
+  kvq_status st = check_append(k_new, v_new, B, Hkv, N, 1, capacity, D, bits, group, k_codes,
+                               k_scales, v_codes, v_scales, k_tail);
+  if (st != KVQ_OK) return st;
+  AttendProblem p;
+  st = check_attend(q, k_codes, k_scales, v_codes, v_scales, B, Hq, Hkv, R, N + 1, capacity, D,
+                    bits, group, sm_scale, num_splits, workspace, workspace_bytes, out, &p);
+  if (st != KVQ_OK) return st;
+  const long long BH = static_cast<long long>(B) * Hkv;
+  const size_t out_bytes = sizeof(float) * static_cast<size_t>(B) * Hq * R * D;
+  if (overlaps(out, out_bytes, k_new, sizeof(float) * BH * D) ||
+      overlaps(out, out_bytes, v_new, sizeof(float) * BH * D) ||
+      overlaps(out, out_bytes, k_tail, sizeof(float) * BH * group * D))
+    return fail(KVQ_ERR_INVALID, "out overlaps the new rows or k_tail");
+  const WorkspaceLayout wl = workspace_layout(B, Hq, Hkv, R, D, p.splits);
+  // One launch when the 4-row matrix-core kernel serves the step and the
+  // workspace holds the heads' counters (the append flags live there).
+  const bool fused = mfma_eligible(p) && p.rows <= kMfmaMaxRows && workspace != nullptr &&
+                     aligned(workspace, 16) && workspace_bytes >= wl.total;
+  if (fused && overlaps(out, out_bytes, workspace, wl.total))
+    return fail(KVQ_ERR_INVALID, "out overlaps the workspace");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!fused) {
+    st = hip_status(launch_append(k_new, v_new, B, Hkv, N, 1, capacity, D, bits, group, k_codes,
+                                  k_scales, v_codes, v_scales, k_tail, s),
+                    "append launch");
+    if (st != KVQ_OK) return st;
+    if (mfma_eligible(p)) return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
+    return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
+  }
+  p.append = 1;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_tail = k_tail;
+  p.k_codes_w = k_codes;
+  p.k_scales_w = k_scales;
+  p.v_codes_w = v_codes;
+  p.v_scales_w = v_scales;
+  p.counters = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + wl.cnt_off);
+  return hip_status(run_mfma(p, num_splits == 0, s), "append + attend (mfma) launch");
 }
 
 kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float* k_scales,
@@ -656,7 +726,7 @@ const char* kvq_status_string(int status) {
 
 const char* kvq_last_error(void) { return g_last_error; }
 
-int kvq_abi_version(void) { return 8; }
+int kvq_abi_version(void) { return 9; }
 
 kvq_status kvq_phase_trace_fetch(int kernel, void* host, size_t bytes) {
   if (host == nullptr || bytes == 0 || bytes % 8 != 0)

@@ -68,6 +68,7 @@
 #include "kvq_internal.h"
 #include "kvq_layout.h"
 #include "kvq_mfma_common.h"
+#include "kvq_quant.h"
 
 
 namespace kvq {
@@ -177,24 +178,124 @@ __device__ __forceinline__ Lanes lane_offsets(int lane) {
 // valid == false issues the same loads at an offset past the arrays: they
 // return zeros without a memory access (keeping the count of loads in flight
 // independent of the path taken).
-template <int kBits>
+template <int kBits, int kPolicy = kNontemporal>
 __device__ __forceinline__ void dma_block(unsigned char* slot, const Head& h, int blk, int lane,
                                           bool valid = true) {
   const unsigned cb = valid ? static_cast<unsigned>(blk) * kBB<kBits> : kNoBlock;
 #pragma unroll
   for (int c = 0; c < kBB<kBits> / 1024; ++c) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(h.kc, KVQ_LDS(slot + c * 1024), 16,
-                                             cb + c * 1024 + lane * 16, 0, 0, kNontemporal);
+                                             cb + c * 1024 + lane * 16, 0, 0, kPolicy);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(h.vc, KVQ_LDS(slot + kBB<kBits> + c * 1024), 16,
-                                             cb + c * 1024 + lane * 16, 0, 0, kNontemporal);
+                                             cb + c * 1024 + lane * 16, 0, 0, kPolicy);
   }
   if (lane < 32) {
     const unsigned sb = (valid ? static_cast<unsigned>(blk) * kBS * 4 : kNoBlock) + lane * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(h.ksc, KVQ_LDS(slot + 2 * kBB<kBits>), 16, sb, 0, 0,
-                                             kNontemporal);
+                                             kPolicy);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(h.vsc, KVQ_LDS(slot + 2 * kBB<kBits> + kBS * 4), 16,
-                                             sb, 0, 0, kNontemporal);
+                                             sb, 0, 0, kPolicy);
   }
+}
+
+// ---- one-token append in the same launch (decode step) ----------------------
+// Workgroup `head` of the grid's front appends token tn = p.N - 1 of that KV
+// head with the bytes kvq_append writes for one token ("KV分组打包", "what a
+// byte holds"; the cache after n tokens is the pack of those n tokens): the
+// open K group (tokens g0 = tn - tn % 32 .. tn of every channel, the earlier
+// ones from k_tail) is requantized with its new scale, the token's V row is
+// quantized per 32-feature group, and the token joins k_tail unless it
+// completes its group.  Every cache store uses the device cache policy
+// (written through to the device coherence point); once they are
+// acknowledged the head's append flag is raised.  The wave that attends the
+// token's block waits for the flag and then loads the block with the same
+// policy, so it reads these bytes whichever XCD either workgroup runs on.
+constexpr int kCoherent = kNontemporal | kCachePolicyDevice;
+constexpr int kAppendSpins = 1 << 16;  // bound on the flag wait (~tens of ms)
+
+template <int kBits>
+__device__ void append_token(const AttendProblem& p, int head, float* amax_lds) {
+  constexpr int kStep = kBits == 4 ? 2 : 1;  // codes per byte
+  constexpr unsigned kZero = Codec<kBits>::kQmaxInt;
+  static_assert(kThreads == 4 * kD, "thread (channel d, quarter) of the open K group");
+  const Layout L = make_layout(p.cap, kD, kBits, kBlockTokens);
+  const int tid = threadIdx.x;
+  const long long bh = head;
+  const int tn = p.N - 1;
+  const int g0 = tn - tn % kBlockTokens;
+  // K: thread (d, part) holds tokens g0 + 8 part .. +7 of channel d.
+  const int d = tid % kD, part = tid / kD;
+  float x[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = g0 + 8 * part + j;
+    x[j] = t < tn ? p.k_tail[(bh * kBlockTokens + (t - g0)) * kD + d]
+                  : (t == tn ? p.k_new[bh * kD + d] : 0.0f);
+    amax = fmaxf(amax, fabsf(x[j]));
+  }
+  amax_lds[part * kD + d] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(amax_lds[d], amax_lds[kD + d]), fmaxf(amax_lds[2 * kD + d], amax_lds[3 * kD + d]));
+  const float s = group_scale<kBits>(amax);
+  const __amdgpu_buffer_rsrc_t kc =
+      head_rsrc(p.k_codes_w + bh * k_code_bytes_per_head(L), k_code_bytes_per_head(L));
+#pragma unroll
+  for (int j = 0; j < 8; j += kStep) {
+    const int t = g0 + 8 * part + j;
+    unsigned byte = t <= tn ? stored_code<kBits>(x[j], s) : kZero;
+    if (kBits == 4) byte |= (t + 1 <= tn ? stored_code<kBits>(x[j + 1], s) : kZero) << 4;
+    __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(byte), kc,
+                                         static_cast<int>(k_code_byte(L, t, d)), 0,
+                                         kCachePolicyDevice);
+  }
+  if (part == 0)
+    __hip_atomic_store(&p.k_scales_w[bh * k_scales_per_head(L) + k_scale_index(L, g0, d)], s,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // The tail is read only by later calls (ordered by the kernel boundary).
+  if (part == (tn - g0) / 8 && (tn + 1) % kBlockTokens != 0)
+    p.k_tail[(bh * kBlockTokens + tn % kBlockTokens) * kD + d] = x[(tn - g0) % 8];
+  // V: thread f0 = kStep * tid of the token's row; 32 / kStep lanes per group.
+  if (tid < kD / kStep) {
+    const int f0 = kStep * tid;
+    const float v0 = p.v_new[bh * kD + f0];
+    const float v1 = kStep == 2 ? p.v_new[bh * kD + f0 + 1] : 0.0f;
+    float va = fabsf(v0);
+    if (kBits == 4) va = fmaxf(va, fabsf(v1));
+#pragma unroll
+    for (int o = kBlockTokens / kStep / 2; o > 0; o >>= 1) va = fmaxf(va, __shfl_xor(va, o, 64));
+    const float sv = group_scale<kBits>(va);
+    unsigned byte = stored_code<kBits>(v0, sv);
+    if (kBits == 4) byte |= stored_code<kBits>(v1, sv) << 4;
+    const __amdgpu_buffer_rsrc_t vc =
+        head_rsrc(p.v_codes_w + bh * v_code_bytes_per_head(L), v_code_bytes_per_head(L));
+    __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(byte), vc,
+                                         static_cast<int>(v_code_byte(L, tn, f0)), 0,
+                                         kCachePolicyDevice);
+    if (f0 % kBlockTokens == 0)
+      __hip_atomic_store(&p.v_scales_w[bh * v_scales_per_head(L) + v_scale_index(L, tn, f0)], sv,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores are acknowledged
+  __syncthreads();
+  if (tid == 0)
+    __hip_atomic_store(&p.counters[bh * kCounterStride + kAppendFlag], 1u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The wave attending the appended token's block: wait (bounded) for the
+// head's append flag, then reset it for the next call.  false: it never came.
+__device__ __forceinline__ bool wait_append(const AttendProblem& p, int head) {
+  unsigned* flag = &p.counters[static_cast<long long>(head) * kCounterStride + kAppendFlag];
+  bool up = false;
+  for (int spin = 0; spin < kAppendSpins && !up; ++spin) {
+    up = __builtin_amdgcn_readfirstlane(
+             __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
+    if (!up) __builtin_amdgcn_s_sleep(2);
+  }
+  if (up && (threadIdx.x & 63) == 0)
+    __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return up;
 }
 
 // Wait until at most `pending` blocks' loads (issued after the one needed
@@ -408,7 +509,9 @@ __device__ __forceinline__ void attend_block(Smem<kBits>& sm, const BlockRegs<kB
 // kWindow: the last p.win_parts workgroups of each head attend recent-token
 // window parts (a separate instantiation, so the plain kernel's block loop
 // is compiled without that path).
-template <int kBits, bool kCausal, bool kWindow>
+// kAppend: the launch also appends token N - 1 (the first B * Hkv workgroups,
+// append_token; a separate instantiation, so the plain kernel is unchanged).
+template <int kBits, bool kCausal, bool kWindow, bool kAppend>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 attend_mfma_r4_kernel(AttendProblem p) {
   __shared__ Smem<kBits> sm;
@@ -424,7 +527,11 @@ attend_mfma_r4_kernel(AttendProblem p) {
   // round-robin; keep all splits of a head on one XCD so the head's partials
   // stay close for the combine.
   const int heads = p.B * p.Hkv;
-  const int L = blockIdx.x;
+  if (kAppend && static_cast<int>(blockIdx.x) < heads) {
+    append_token<kBits>(p, blockIdx.x, reinterpret_cast<float*>(&sm.u.ring[0][0][0]));
+    return;
+  }
+  const int L = blockIdx.x - (kAppend ? heads : 0);  // a multiple of 8 apart: same XCD order
   int head, split;
   if (heads % 8 == 0) {
     const int slot = L >> 3;
@@ -480,9 +587,20 @@ attend_mfma_r4_kernel(AttendProblem p) {
   // The first kDepth blocks of this wave go out at once (slots past the
   // wave's last block take zeros).
   unsigned char* ring = &sm.u.ring[wave][0][0];
+  // With kAppend, the block holding the appended token (the last block of
+  // the last split) is loaded only after the append's flag, coherently.
+  const int b_app = kAppend ? (p.N - 1) / kBlockTokens : -1;
+  bool app_ok = true;
 #pragma unroll
-  for (int j = 0; j < kRing<kBits>; ++j)
-    dma_block<kBits>(ring + j * kSlotBytes<kBits>, h, b_first + j * kWaves, lane, j < cnt);
+  for (int j = 0; j < kRing<kBits>; ++j) {
+    const int blk = b_first + j * kWaves;
+    if (kAppend && j < cnt && blk == b_app) {
+      app_ok = wait_append(p, head);
+      dma_block<kBits, kCoherent>(ring + j * kSlotBytes<kBits>, h, blk, lane);
+    } else {
+      dma_block<kBits>(ring + j * kSlotBytes<kBits>, h, blk, lane, j < cnt);
+    }
+  }
 
   // q * qscale, prescaled per row by 2^Sq so the row's largest element lies in
   // [2^9, 2^10) (the 16 lanes of a row are one DPP row).
@@ -532,12 +650,25 @@ attend_mfma_r4_kernel(AttendProblem p) {
     read_block(br, slot, lo);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slot has been read
     if (i == 0) phase_mark(kMarkFirstBlock);
-    if (i + kRing<kBits> < cnt)
-      dma_block<kBits>(slot, h, b_first + (i + kRing<kBits>) * kWaves, lane);
+    if (i + kRing<kBits> < cnt) {
+      const int blk = b_first + (i + kRing<kBits>) * kWaves;
+      if (kAppend && blk == b_app) {
+        app_ok = wait_append(p, head);
+        dma_block<kBits, kCoherent>(slot, h, blk, lane);
+      } else {
+        dma_block<kBits>(slot, h, blk, lane);
+      }
+    }
     attend_block<kBits, kCausal>(sm, br, (b_first + i * kWaves) * kBlockTokens, t_end, cc, ws, qv,
                                  us_row, lim, p.pos_end - p.R);
   }
   phase_mark(kMarkLoopEnd);
+  if (kAppend && !app_ok) {  // the append never signalled: make the head's output NaN
+    const f32x4 nan4 = {as_f32(0x7fc00000u), as_f32(0x7fc00000u), as_f32(0x7fc00000u),
+                        as_f32(0x7fc00000u)};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) ws.acc[g][0] = ws.acc[g][1] = nan4;
+  }
   // z of each row: sum this lane's share over the four q-blocks
   ws.z = qblock_sum(ws.z);
 
@@ -610,15 +741,25 @@ int mfma_tokens_per_split(int N, int splits) {
 template <int kBits, bool kWindow>
 void launch_r4(const AttendProblem& p, unsigned grid, hipStream_t stream) {
   if (p.causal)
-    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, true, kWindow>), dim3(grid), dim3(kThreads),
-                       0, stream, p);
+    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, true, kWindow, false>), dim3(grid),
+                       dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, false, kWindow>), dim3(grid), dim3(kThreads),
-                       0, stream, p);
+    hipLaunchKernelGGL((attend_mfma_r4_kernel<kBits, false, kWindow, false>), dim3(grid),
+                       dim3(kThreads), 0, stream, p);
 }
 
 hipError_t launch_attend_mfma(const AttendProblem& p, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
+  if (p.append) {  // plain (no window, not causal) attend with the append workgroups in front
+    const unsigned g = grid + static_cast<unsigned>(p.B) * p.Hkv;
+    if (p.bits == 8)
+      hipLaunchKernelGGL((attend_mfma_r4_kernel<8, false, false, true>), dim3(g), dim3(kThreads),
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((attend_mfma_r4_kernel<4, false, false, true>), dim3(g), dim3(kThreads),
+                         0, stream, p);
+    return hipGetLastError();
+  }
   const bool win = p.win_parts > 0;
   if (p.bits == 8)
     win ? launch_r4<8, true>(p, grid, stream) : launch_r4<8, false>(p, grid, stream);

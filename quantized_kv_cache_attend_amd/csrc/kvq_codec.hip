@@ -23,30 +23,10 @@
 // denormals are kept (no flush-to-zero flag), and rintf rounds half to even.
 #include "kvq_internal.h"
 #include "kvq_layout.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
-
-template <int BITS>
-struct Codec {
-  static constexpr float kQmax = BITS == 4 ? 7.0f : 127.0f;
-  static constexpr int kQmaxInt = BITS == 4 ? 7 : 127;
-};
-
-// Scale of one group from its largest magnitude.
-template <int BITS>
-__device__ __forceinline__ float group_scale(float amax) {
-  float s = amax / Codec<BITS>::kQmax;
-  return s == 0.0f ? 1.0f : s;
-}
-
-// Stored (offset) code of one element.
-template <int BITS>
-__device__ __forceinline__ unsigned stored_code(float x, float s) {
-  float c = rintf(x / s);
-  c = fminf(fmaxf(c, -Codec<BITS>::kQmax), Codec<BITS>::kQmax);
-  return static_cast<unsigned>(static_cast<int>(c) + Codec<BITS>::kQmaxInt);
-}
 
 // K scales: one thread per (head, token group G, channel d), d fastest so
 // both the token-row reads and the group-major scale writes coalesce.

@@ -50,7 +50,24 @@ struct AttendProblem {
   float* part_z;           // [splits][B*Hkv*rows]
   float* part_u;           // [splits][B*Hkv*rows][D]
   unsigned* counters;      // [B*Hkv][kCounterStride], one arrival counter per KV head
+  // One-token append in the same launch (4-row matrix-core kernel): token
+  // N - 1 of every KV head is appended by B * Hkv extra workgroups at the
+  // front of the grid, exactly as kvq_append appends one token; the wave that
+  // attends the token's block waits for the head's append flag first.
+  int append;              // 1: this launch appends token N - 1
+  const float* k_new;      // [B*Hkv][D] float32 K and V of the new token
+  const float* v_new;
+  float* k_tail;           // [B*Hkv][group][D], as kvq_append reads and writes it
+  uint8_t* k_codes_w;      // the cache arrays again, written by the append
+  float* k_scales_w;
+  uint8_t* v_codes_w;
+  float* v_scales_w;
 };
+
+// Append flag of a KV head: word 32 of the head's counter slot (its own
+// memory line).  The append raises it to 1 once its stores are acknowledged;
+// the waiting wave resets it to 0, so every completed call leaves it zero.
+constexpr int kAppendFlag = 32;
 
 // Arrival counters sit 256 bytes apart, so the heads' tickets never contend
 // for one memory line.

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert lib.kvq_abi_version() == 8
+    assert lib.kvq_abi_version() == 9
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.kvq_status_string(st)
 

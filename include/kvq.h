@@ -77,8 +77,10 @@ typedef enum kvq_status {
 typedef enum kvq_variant {
   KVQ_VARIANT_AUTO = 0,  /* what kvq_attend uses */
   KVQ_VARIANT_VALU = 1,  /* any supported format: decode a tile to float32 in LDS */
-  KVQ_VARIANT_MFMA = 2   /* 4- or 8-bit, group 32, D = 128, <= 32 query rows per KV
+  KVQ_VARIANT_MFMA = 2,  /* 4- or 8-bit, group 32, D = 128, <= 32 query rows per KV
                             head: fp16 matrix cores on exact codes */
+  KVQ_VARIANT_STREAM = 3 /* 4- or 8-bit, group 8/16/32/64/128, D = 128, <= 8 query rows
+                            per KV head: float32 registers, each block read once */
 } kvq_variant;
 
 /* Flags of kvq_attend_cache. */
@@ -250,7 +252,12 @@ kvq_status kvq_attend(const float* q, const uint8_t* k_codes, const float* k_sca
  * KVQ_VARIANT_MFMA returns KVQ_ERR_UNSUPPORTED unless bits is 4 or 8,
  * group == 32, D == 128, (Hq/Hkv)*R <= 32, N <= 2^25 - 32 (4-bit) or
  * N <= 2^24 - 32 (8-bit) and q and all four cache arrays are 16-byte
- * aligned; KVQ_VARIANT_AUTO picks it whenever those hold. */
+ * aligned; KVQ_VARIANT_AUTO picks it whenever those hold.
+ * KVQ_VARIANT_STREAM returns KVQ_ERR_UNSUPPORTED unless bits is 4 or 8,
+ * group is 8, 16, 32, 64 or 128, D == 128, (Hq/Hkv)*R <= 8, the same N
+ * limits hold and the same arrays are 16-byte aligned; KVQ_VARIANT_AUTO
+ * picks it where those hold and the matrix-core kernels do not apply.
+ * Every other case runs KVQ_VARIANT_VALU. */
 kvq_status kvq_attend_variant(const float* q, const uint8_t* k_codes, const float* k_scales,
                               const uint8_t* v_codes, const float* v_scales,
                               int B, int Hq, int Hkv, int R, int N, int D, int bits, int group,
@@ -329,15 +336,16 @@ kvq_status kvq_stream_read(const void* data, size_t bytes, void* sink, void* str
 
 /* ---- kvq_phase_trace_fetch -----------------------------------------------------------
  * Measurement aid, not part of the method: the timeline of the last
- * matrix-core attend launch, to split its time into the steps of
+ * launch of a fused attend kernel, to split its time into the steps of
  * [BKD] "Do not average independently normalized blocks" (stream the blocks,
  * merge partial statistics) and the two stops of [RL] "two stops of the
  * online accumulation" (waves, then KV splits).  Only a library built with
  * KVQ_PHASE_TRACE records anything (quantized_kv_cache_attend_amd/build.py
  * --phase-trace writes it as libkvq_phase.so beside libkvq.so): there every
- * wave of the 4-row (kernel 0) or 32-row (kernel 1) matrix-core kernel writes
- * the chip-wide 100 MHz clock at KVQ_PHASE_MARKS fixed points
- * (start, query ready, first block ready [4-row kernel only], last block done,
+ * wave of the 4-row (kernel 0) or 32-row (kernel 1) matrix-core kernel or of
+ * the streaming kernel (kernel 2) writes the chip-wide 100 MHz clock at
+ * KVQ_PHASE_MARKS fixed points
+ * (start, query ready, first block ready [not the 32-row kernel], last block done,
  * workgroup merged, partial stores acknowledged, ticket taken, end) for the
  * first KVQ_PHASE_WAVES waves in launch order (workgroup, then wave).  This
  * copies up to `bytes` (a positive multiple of 8) of those uint64 records

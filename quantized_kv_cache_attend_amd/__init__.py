@@ -73,7 +73,7 @@ for _name, (_res, _args) in _SIGNATURES.items():
     _fn.argtypes = _args
 
 KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP, KVQ_ERR_WORKSPACE = 0, -1, -2, -3, -4
-VARIANTS = {"auto": 0, "valu": 1, "mfma": 2}
+VARIANTS = {"auto": 0, "valu": 1, "mfma": 2, "stream": 3}
 KVQ_ATTEND_CAUSAL = 1
 
 

@@ -44,6 +44,7 @@ CFLAGS = [
 EXTRA_CFLAGS = {
     "kvq_attend_mfma.hip": ["-fno-honor-nans"],
     "kvq_attend_mfma32.hip": ["-fno-honor-nans"],
+    "kvq_attend_stream.hip": ["-fno-honor-nans"],
 }
 
 

@@ -253,6 +253,28 @@ hipError_t run_mfma(AttendProblem p, bool auto_split, hipStream_t s) {
   return wide ? launch_attend_mfma32(p, s) : launch_attend_mfma(p, s);
 }
 
+// The streaming kernel takes D = 128 and power-of-two groups from 8 to 128
+// (a token octet then lies in one K group, and a feature pair in one V
+// group; dpad = 128), up to 8 rows, no causal rule, with the matrix-core
+// kernels' size and alignment conditions (32-bit buffer offsets per head:
+// group-8 scales take 64 bytes per token and head).
+bool stream_eligible(const AttendProblem& p) {
+  const int g = p.group;
+  return (p.bits == 4 || p.bits == 8) && g >= 8 && g <= 128 && (g & (g - 1)) == 0 &&
+         p.D == 128 && p.rows <= kStreamMaxRows && !p.causal && p.W == 0 &&
+         p.cap <= (p.bits == 8 ? kMfmaMaxN8 : kMfmaMaxN) && aligned(p.q, 16) &&
+         aligned(p.k_codes, 16) && aligned(p.v_codes, 16) && aligned(p.k_scales, 16) &&
+         aligned(p.v_scales, 16);
+}
+
+// The automatic choice over the packed cache: matrix cores, else the
+// streaming kernel, else the general one.
+hipError_t run_packed(const AttendProblem& p, bool auto_split, hipStream_t s) {
+  if (mfma_eligible(p)) return run_mfma(p, auto_split, s);
+  if (stream_eligible(p)) return launch_attend_stream(p, s);
+  return launch_attend_valu(p, s);
+}
+
 kvq_status codec_check(const void* a, const void* b, const void* c, int B, int H, int N, int D,
                        int bits, int group) {
   if (!a || !b || !c) return fail(KVQ_ERR_INVALID, "null pointer argument");
@@ -500,8 +522,7 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
   const hipStream_t s = static_cast<hipStream_t>(stream);
   switch (variant) {
     case KVQ_VARIANT_AUTO:
-      if (mfma_eligible(p)) return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
-      return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
+      return hip_status(run_packed(p, num_splits == 0, s), "attend launch");
     case KVQ_VARIANT_VALU:
       return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
     case KVQ_VARIANT_MFMA:
@@ -511,6 +532,13 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
                     "KV head, N <= %d (4-bit) or %d (8-bit) and 16-byte aligned q and cache "
                     "arrays", kMfma32MaxRows, kMfmaMaxN, kMfmaMaxN8);
       return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
+    case KVQ_VARIANT_STREAM:
+      if (!stream_eligible(p))
+        return fail(KVQ_ERR_UNSUPPORTED,
+                    "the streaming kernel needs bits=4|8, group 8|16|32|64|128, D=128, <= %d "
+                    "query rows per KV head, no causal rule, N <= %d (4-bit) or %d (8-bit) and "
+                    "16-byte aligned q and cache arrays", kStreamMaxRows, kMfmaMaxN, kMfmaMaxN8);
+      return hip_status(launch_attend_stream(p, s), "attend (stream) launch");
     default:
       return fail(KVQ_ERR_INVALID, "unknown variant %d", variant);
   }
@@ -548,8 +576,7 @@ kvq_status kvq_append_attend(const float* q, const float* k_new, const float* v_
                                   k_scales, v_codes, v_scales, k_tail, s),
                     "append launch");
     if (st != KVQ_OK) return st;
-    if (mfma_eligible(p)) return hip_status(run_mfma(p, num_splits == 0, s), "attend (mfma) launch");
-    return hip_status(launch_attend_valu(p, s), "attend (valu) launch");
+    return hip_status(run_packed(p, num_splits == 0, s), "attend launch");
   }
   p.append = 1;
   p.k_new = k_new;
@@ -726,16 +753,18 @@ const char* kvq_status_string(int status) {
 
 const char* kvq_last_error(void) { return g_last_error; }
 
-int kvq_abi_version(void) { return 9; }
+int kvq_abi_version(void) { return 10; }
 
 kvq_status kvq_phase_trace_fetch(int kernel, void* host, size_t bytes) {
   if (host == nullptr || bytes == 0 || bytes % 8 != 0)
     return fail(KVQ_ERR_INVALID, "phase records: null host buffer or size %zu not a positive "
                 "multiple of 8", bytes);
-  if (kernel != 0 && kernel != 1)
-    return fail(KVQ_ERR_INVALID, "phase records: kernel %d is neither 0 (4-row) nor 1 (32-row)",
-                kernel);
-  const int st = kernel == 0 ? kvq::phase_fetch_r4(host, bytes) : kvq::phase_fetch_r32(host, bytes);
+  if (kernel < 0 || kernel > 2)
+    return fail(KVQ_ERR_INVALID,
+                "phase records: kernel %d is not 0 (4-row), 1 (32-row) or 2 (streaming)", kernel);
+  const int st = kernel == 0   ? kvq::phase_fetch_r4(host, bytes)
+                 : kernel == 1 ? kvq::phase_fetch_r32(host, bytes)
+                               : kvq::phase_fetch_stream(host, bytes);
   if (st == KVQ_ERR_UNSUPPORTED)
     return fail(KVQ_ERR_UNSUPPORTED, "phase records exist only in a KVQ_PHASE_TRACE build");
   if (st != KVQ_OK) return fail(KVQ_ERR_HIP, "phase records: copy from the device failed");

@@ -1,0 +1,488 @@
+// Streaming float32 attention over the packed cache for D = 128 in formats
+// the matrix-core kernels do not take: 4- or 8-bit codes with a
+// power-of-two group from 8 to 128, up to 8 query rows per KV head, no
+// causal rule, no float32 window.
+//
+// Method: the blocked online softmax of "Block KV decoding: less workspace,
+// more time" (huhohoo.com/en/docs/llm/kv-block-decode-cost), section "Do not
+// average independently normalized blocks", and of "给长前缀列一张有单位的资源账本"
+// (codingai-lec05.pages.dev resource-ledger), section "why FlashAttention need
+// not keep the whole heat map": per query row a reference max m, an
+// exponential sum z and an unnormalized value sum u relative to 2^m, both
+// rescaled when the reference moves (lazily: only when a block's max passes
+// it by more than kSLazy).  Waves and KV splits merge with the same rescale
+// ("two stops of the online accumulation" on the same page).  The dequant
+// is that of "KV分组打包：4-bit到底省了多少？" (huhohoo.com/docs/llm/kv-packed-groups):
+// code c of a group with scale s stands for (c - qmax) * s, here one fused
+// multiply-add c * s + fl32(-qmax * s) (within 2^-21 s of the exact
+// product).  Plain float32 arithmetic throughout.
+//
+// Work split: one workgroup of 4 waves per (KV head, split), with the
+// matrix-core kernels' XCD-aware mapping; wave w attends blocks w, w + 4, ...
+// of its split.  Lane (n, q) = (lane & 15, lane >> 4) owns channel octet n
+// (channels 8n .. 8n + 7), feature octet n (features 8n .. 8n + 7) and token
+// octet q (tokens 8q .. 8q + 7 of each 32-token block).  In the block layout
+// of kvq_layout.h each of these is one contiguous run of code bytes (32 at
+// 4-bit, 64 at 8-bit), and the lane's K scales (8 channels of the token
+// octet's group) and V scales (8 tokens of the feature octet's group) are
+// two 16-byte runs each:
+//   scores: the lane's partial dot products over its 8 channels, with the
+//     query rows read from LDS, are summed over the 16 lanes of its DPP row,
+//     which then all hold the token octet's scores;
+//   values: the lane accumulates u for its 8 features over its 8 tokens for
+//     the whole split; the 4 token octets are summed once, at the end.
+// Streaming: each wave keeps its next block in flight in an LDS slot, copied
+// from HBM by LDS-destination buffer loads (no VGPRs held in flight), in two
+// parts: the K part (codes and scales) is refilled as soon as the block's K
+// pieces are in registers, the V part as soon as its V pieces are, so each
+// part has a whole block's time to land and only one part is held in
+// registers at a time.
+#include "kvq_internal.h"
+#include "kvq_layout.h"
+#include "kvq_mfma_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kSWaves = 4;
+constexpr int kSThreads = kSWaves * 64;
+constexpr int kSD = 128;
+constexpr float kSLazy = 6.0f;  // the reference moves only past m + kSLazy
+
+struct SHead {
+  __amdgpu_buffer_rsrc_t kc, ksc, vc, vsc;
+  long long kblock, vblock;  // code bytes per block
+  int vcols;                 // V byte columns per token octet
+  int vgroups;               // V scale groups per token
+  int gshift;                // log2(group)
+};
+
+// One part (K or V) of a block, this lane's share: code pieces, then the two
+// scale pieces.
+template <int kBits>
+constexpr int kSPart = kBits / 2 + 2;  // 16-byte pieces per lane and part
+template <int kBits>
+struct SPart {
+  u32x4 c[kBits / 2];
+  f32x4 s[2];
+};
+
+// LDS slot of one wave: part x (0 = K, 1 = V), piece j at
+// slot + 1024 (x kSPart + j) + 16 lane.
+template <int kBits>
+constexpr int kSSlotBytes = 2 * 1024 * kSPart<kBits>;
+
+#define KVQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with vmcnt(x) (bits 3:0 and 15:14), expcnt and lgkmcnt at maximum.
+#define KVQ_SVMCNT(x) ((((x) & 15) | (((x) >> 4) << 14)) | 0x0F70)
+
+// Start copying one part of a block into LDS (asynchronous, counted by
+// vmcnt: kSPart loads).  codes / scales: the lane's byte offsets.
+template <int kBits>
+__device__ __forceinline__ void dma_part(unsigned char* part, __amdgpu_buffer_rsrc_t rc,
+                                         unsigned codes, __amdgpu_buffer_rsrc_t rs,
+                                         unsigned scales) {
+  constexpr int kNt = 2;  // nontemporal cache policy: the cache is read once per call
+#pragma unroll
+  for (int i = 0; i < kBits / 2; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, KVQ_LDS(part + 1024 * i), 16, codes + 16 * i, 0,
+                                             0, kNt);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, KVQ_LDS(part + 1024 * (kBits / 2 + i)), 16,
+                                             scales + 16 * i, 0, 0, kNt);
+}
+
+// K part of block blk: channel octet n of tokens 8q .. 8q + 7 and the scales
+// of those channels in the token octet's group.
+template <int kBits>
+__device__ __forceinline__ void dma_k(unsigned char* slot, const SHead& h, int blk, int n, int q) {
+  const unsigned co = static_cast<unsigned>(blk * h.kblock) +
+                      static_cast<unsigned>((n * 4 * kBits + kBits * q) * 8);
+  const int tok = blk * kBlockTokens + 8 * q;
+  const unsigned so = static_cast<unsigned>(((tok >> h.gshift) * kSD + 8 * n) * 4);
+  dma_part<kBits>(slot, h.kc, co, h.ksc, so);
+}
+
+// V part of block blk: feature octet n of tokens 8q .. 8q + 7 and the scales
+// of those tokens in the feature octet's group.
+template <int kBits>
+__device__ __forceinline__ void dma_v(unsigned char* slot, const SHead& h, int blk, int n, int q) {
+  const unsigned co = static_cast<unsigned>(blk * h.vblock) +
+                      static_cast<unsigned>((q * h.vcols + kBits * n) * 8);
+  const unsigned so = static_cast<unsigned>(
+      ((blk * h.vgroups + ((8 * n) >> h.gshift)) * kBlockTokens + 8 * q) * 4);
+  dma_part<kBits>(slot + 1024 * kSPart<kBits>, h.vc, co, h.vsc, so);
+}
+
+template <int kBits>
+__device__ __forceinline__ void read_part(SPart<kBits>& r, const unsigned char* part, int lane) {
+  const unsigned char* b = part + 16 * lane;
+#pragma unroll
+  for (int i = 0; i < kBits / 2; ++i) r.c[i] = *reinterpret_cast<const u32x4*>(b + 1024 * i);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    r.s[i] = *reinterpret_cast<const f32x4*>(b + 1024 * (kBits / 2 + i));
+}
+
+// Codes e = 0..3 of a 4-byte word as float: its bytes (8-bit) or their low
+// or high nibbles (4-bit).  The nibble mask is applied in an asm statement so
+// that the compiler cannot merge it into per-code bit-field extracts: the
+// masked word's bytes then convert with one v_cvt_f32_ubyteN each.
+template <int kBits>
+__device__ __forceinline__ void codes4(unsigned w, bool hi, float c[4]) {
+  unsigned x = w;
+  if (kBits == 4) {
+    const unsigned y = hi ? w >> 4 : w;
+    asm("v_and_b32_e32 %0, 0x0f0f0f0f, %1" : "=v"(x) : "v"(y));
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c[e] = static_cast<float>((x >> (8 * e)) & 0xFFu);
+}
+
+// x summed over the 16 lanes of its DPP row (every lane gets the sum).
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<kRowRor8>(x);
+  x += dpp<kRowRor4>(x);
+  x += dpp<kRowRor2>(x);
+  x += dpp<kRowRor1>(x);
+  return x;
+}
+
+// Query rows in LDS, times sm_scale * log2 e: qs[r][hf][n] holds channels
+// 8n + 4hf .. 8n + 4hf + 3 of row r, so the 16 lanes of a token octet read
+// 256 contiguous bytes (rows past `rows` are zero).
+template <int kRows>
+struct SQuery {
+  f32x4 qs[kRows][2][16];
+};
+
+template <int kBits, int kRows>
+struct SSmem {
+  union {
+    unsigned char ring[kSWaves][kSSlotBytes<kBits>];  // one block slot per wave
+    float wu[kSWaves][kRows][kSD];                     // the merge (after the loop)
+  } u;
+  SQuery<kRows> q;
+  float wm[kSWaves][kRows];
+  float wz[kSWaves][kRows];
+  int last;
+};
+
+// Scores of the lane's token octet in one block: s[r][t] for token 8q + t
+// (summed over all 128 channels; every lane of the DPP row holds them).
+template <int kBits, int kRows>
+__device__ __forceinline__ void block_scores(const SPart<kBits>& kp, const SQuery<kRows>& sq,
+                                             int n, float (&s)[kRows][8]) {
+  constexpr float kQmax = kBits == 4 ? 7.0f : 127.0f;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s[r][t] = 0.0f;
+  // channel quad hf = channels 8n + 4hf .. 8n + 4hf + 3; its codes sit in
+  // dword 2j + hf: token pair j (low nibbles token 2j, high 2j + 1) at 4-bit,
+  // token j at 8-bit.
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x4 qh[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) qh[r] = sq.qs[r][hf][n];
+    const f32x4 ks = kp.s[hf];
+    float kb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kb[e] = -kQmax * ks[e];
+#pragma unroll
+    for (int j = 0; j < kBits; ++j) {
+      const int d = 2 * j + hf;
+      const unsigned w = kp.c[d / 4][d % 4];
+#pragma unroll
+      for (int part = 0; part < (kBits == 4 ? 2 : 1); ++part) {
+        const int t = kBits == 4 ? 2 * j + part : j;
+        float c[4];
+        codes4<kBits>(w, part == 1, c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float kv = fmaf(c[e], ks[e], kb[e]);  // (c - qmax) s
+#pragma unroll
+          for (int r = 0; r < kRows; ++r) s[r][t] = fmaf(qh[r][e], kv, s[r][t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s[r][t] = row_sum16(s[r][t]);
+}
+
+// The lazy online-softmax update for one block; s becomes p = 2^(s - m).
+// ntok: how many of the lane's 8 tokens are in the split (the rest, past
+// the cache's end, take no part).  Every lane of the wave calls it.
+template <int kRows>
+__device__ __forceinline__ void block_softmax(float (&s)[kRows][8], int ntok, float (&m)[kRows],
+                                              float (&z)[kRows], float (&u)[kRows][8],
+                                              bool& live) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const bool ok = t < ntok;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) s[r][t] = ok ? s[r][t] : -INFINITY;
+  }
+  float bm[kRows];
+  bool move = !live;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    float x = s[r][0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) x = fmaxf(x, s[r][t]);
+    bm[r] = qblock_max(x);  // the block's max of row r (every lane)
+    move = move || bm[r] > m[r] + kSLazy;
+  }
+  if (__builtin_amdgcn_readfirstlane(move ? 1 : 0)) {  // wave-uniform
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const float mn = live ? (bm[r] > m[r] + kSLazy ? bm[r] : m[r]) : bm[r];
+      const float a = live ? fast_exp2(m[r] - mn) : 0.0f;
+      z[r] *= a;
+#pragma unroll
+      for (int f = 0; f < 8; ++f) u[r][f] *= a;
+      m[r] = mn;
+    }
+    live = true;
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    float zs = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      s[r][t] = fast_exp2(s[r][t] - m[r]);
+      zs += s[r][t];
+    }
+    z[r] += zs;
+  }
+}
+
+// u[r][f] += sum over the lane's tokens t of p[r][t] (c - qmax) sV, feature
+// 8n + f.  4-bit: dword 2j + hh holds tokens 4hh .. 4hh + 3 of features 2j
+// (low nibbles) and 2j + 1 (high); 8-bit: dword 2f + hh holds them for
+// feature f.
+template <int kBits, int kRows>
+__device__ __forceinline__ void block_values(const SPart<kBits>& vp, const float (&p)[kRows][8],
+                                             float (&u)[kRows][8]) {
+  constexpr float kQmax = kBits == 4 ? 7.0f : 127.0f;
+  float vs[8], vb[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vs[e] = vp.s[0][e];
+    vs[e + 4] = vp.s[1][e];
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) vb[t] = -kQmax * vs[t];
+#pragma unroll
+  for (int d = 0; d < 2 * kBits; ++d) {
+    const unsigned w = vp.c[d / 4][d % 4];
+    const int hh = d & 1;
+#pragma unroll
+    for (int part = 0; part < (kBits == 4 ? 2 : 1); ++part) {
+      const int f = kBits == 4 ? 2 * (d >> 1) + part : d >> 1;
+      float c[4];
+      codes4<kBits>(w, part == 1, c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 4 * hh + e;
+        const float vv = fmaf(c[e], vs[t], vb[t]);  // (c - qmax) s
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) u[r][f] = fmaf(p[r][t], vv, u[r][f]);
+      }
+    }
+  }
+}
+
+template <int kBits, int kRows>
+__global__ __launch_bounds__(kSThreads) void attend_stream_kernel(AttendProblem p) {
+  __shared__ SSmem<kBits, kRows> sm;
+  phase_mark(kMarkStart);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;  // channel / feature octet
+  const int q = lane >> 4;  // token octet
+
+  const int heads = p.B * p.Hkv;
+  const int L = blockIdx.x;
+  int head, split;
+  if (heads % 8 == 0) {
+    const int slot = L >> 3;
+    head = (L & 7) + 8 * (slot / p.splits);
+    split = slot % p.splits;
+  } else {
+    head = L / p.splits;
+    split = L % p.splits;
+  }
+  const long long bh = head;
+  const int rows = p.rows;
+  const Layout lay = make_layout(p.cap, kSD, kBits, p.group);
+  SHead h;
+  h.kblock = lay.kblock_bytes;
+  h.vblock = lay.vblock_bytes;
+  h.vcols = lay.vcols;
+  h.vgroups = lay.vgroups;
+  h.gshift = __builtin_ctz(p.group);
+  h.kc = head_rsrc(p.k_codes + bh * k_code_bytes_per_head(lay), k_code_bytes_per_head(lay));
+  h.ksc = head_rsrc(p.k_scales + bh * k_scales_per_head(lay), k_scales_per_head(lay) * 4);
+  h.vc = head_rsrc(p.v_codes + bh * v_code_bytes_per_head(lay), v_code_bytes_per_head(lay));
+  h.vsc = head_rsrc(p.v_scales + bh * v_scales_per_head(lay), v_scales_per_head(lay) * 4);
+
+  const int t_begin = split * p.tokens_per_split;
+  const int t_end = min(p.N, t_begin + p.tokens_per_split);
+  const int b_begin = t_begin / kBlockTokens;
+  const int b_end = t_end > t_begin ? (t_end + kBlockTokens - 1) / kBlockTokens : b_begin;
+  const int b_first = b_begin + wave;
+  const int cnt = b_first < b_end ? (b_end - 1 - b_first) / kSWaves + 1 : 0;  // wave-uniform
+
+  unsigned char* slot = sm.u.ring[wave];
+  if (cnt > 0) {
+    dma_k<kBits>(slot, h, b_first, n, q);
+    dma_v<kBits>(slot, h, b_first, n, q);
+  }
+
+  // the query rows into LDS (one 16-byte piece per thread)
+  for (int i = tid; i < kRows * 32; i += kSThreads) {
+    const int r = i >> 5, hf = (i >> 4) & 1, o = i & 15;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (r < rows) {
+      x = *reinterpret_cast<const f32x4*>(p.q + (bh * rows + r) * kSD + 8 * o + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] *= p.qscale;
+    }
+    sm.q.qs[r][hf][o] = x;
+  }
+  __syncthreads();
+  phase_mark(kMarkQReady);
+
+  float m[kRows], z[kRows], u[kRows][8];  // u: features 8n .. 8n + 7
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    m[r] = -INFINITY;
+    z[r] = 0.0f;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) u[r][f] = 0.0f;
+  }
+  bool live = false;
+
+  // Loads in flight at each wait, in issue order: K(i) V(i) | K(i + 1) V(i + 1) ...
+  // so K(i) has landed once at most one part (V(i)) is pending, and V(i)
+  // once at most K(i + 1) is.
+  for (int i = 0; i < cnt; ++i) {
+    const int blk = b_first + i * kSWaves;
+    const bool more = i + 1 < cnt;
+    float s[kRows][8];
+    {
+      __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(kSPart<kBits>));  // K(i) in the slot
+      if (i == 0) phase_mark(kMarkFirstBlock);
+      SPart<kBits> kp;
+      read_part<kBits>(kp, slot, lane);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the K part has been read
+      if (more) dma_k<kBits>(slot, h, blk + kSWaves, n, q);
+      block_scores<kBits, kRows>(kp, sm.q, n, s);
+    }
+    block_softmax<kRows>(s, t_end - (blk * kBlockTokens + 8 * q), m, z, u, live);
+    {
+      if (more) __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(kSPart<kBits>));  // V(i) in the slot
+      else __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(0));
+      SPart<kBits> vp;
+      read_part<kBits>(vp, slot + 1024 * kSPart<kBits>, lane);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the V part has been read
+      if (more) dma_v<kBits>(slot, h, blk + kSWaves, n, q);
+      block_values<kBits, kRows>(vp, s, u);
+    }
+  }
+
+  phase_mark(kMarkLoopEnd);
+
+  // ---- merge: the 4 token octets, then the waves through LDS ---------------
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    z[r] = qblock_sum(z[r]);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) u[r][f] = qblock_sum(u[r][f]);
+  }
+  __syncthreads();  // every wave is done with its slot (aliased by the merge area)
+  if (q == 0) {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      f32x4 a, b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = u[r][e];
+        b[e] = u[r][e + 4];
+      }
+      *reinterpret_cast<f32x4*>(&sm.u.wu[wave][r][8 * n]) = a;
+      *reinterpret_cast<f32x4*>(&sm.u.wu[wave][r][8 * n + 4]) = b;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      sm.wm[wave][r] = m[r];
+      sm.wz[wave][r] = z[r];
+    }
+  }
+  __syncthreads();
+  constexpr int kF = kRows * kSD / kSThreads;  // outputs per thread: row r, features f0 ..
+  const int r = tid * kF / kSD;
+  const int f0 = (tid * kF) % kSD;
+  float M = -INFINITY, Z = 0.0f, U[kF];
+#pragma unroll
+  for (int j = 0; j < kF; ++j) U[j] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kSWaves; ++w) M = fmaxf(M, sm.wm[w][r]);
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kSWaves; ++w) {
+      const float mw = sm.wm[w][r];
+      if (mw == -INFINITY) continue;
+      const float x = fast_exp2(mw - M);
+      Z = fmaf(x, sm.wz[w][r], Z);
+#pragma unroll
+      for (int j = 0; j < kF; ++j) U[j] = fmaf(x, sm.u.wu[w][r][f0 + j], U[j]);
+    }
+  }
+  phase_mark(kMarkMerged);
+  if (p.splits == 1) {
+    if (r < rows) {
+#pragma unroll
+      for (int j = 0; j < kF; ++j) p.out[(bh * rows + r) * kSD + f0 + j] = U[j] / Z;
+    }
+    phase_mark(kMarkEnd);
+    return;
+  }
+  split_combine<kF, kF, 0>(p, split, bh, r, f0, U, M, Z, &sm.last);
+  phase_mark(kMarkEnd);
+}
+
+#undef KVQ_SVMCNT
+
+}  // namespace
+
+int phase_fetch_stream(void* host, size_t bytes) { return phase_fetch(host, bytes); }
+
+hipError_t launch_attend_stream(const AttendProblem& p, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
+  const bool r8 = p.rows > 4;
+  if (p.bits == 8) {
+    if (r8)
+      hipLaunchKernelGGL((attend_stream_kernel<8, 8>), dim3(grid), dim3(kSThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attend_stream_kernel<8, 4>), dim3(grid), dim3(kSThreads), 0, stream, p);
+  } else {
+    if (r8)
+      hipLaunchKernelGGL((attend_stream_kernel<4, 8>), dim3(grid), dim3(kSThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attend_stream_kernel<4, 4>), dim3(grid), dim3(kSThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -116,10 +116,16 @@ constexpr int kMfmaMaxRows = 4;
 constexpr int kMfma32MaxRows = 32;
 int mfma_tokens_per_split(int N, int splits);
 hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream);
-// Phase records of the 4-row / 32-row kernels (a kvq_status; KVQ_ERR_UNSUPPORTED
-// unless built with KVQ_PHASE_TRACE).
+// Streaming float32 kernel: 4- or 8-bit, power-of-two group in [8, 128],
+// D = 128, up to kStreamMaxRows query rows per KV head, no causal rule and no
+// float32 window.
+constexpr int kStreamMaxRows = 8;
+hipError_t launch_attend_stream(const AttendProblem& p, hipStream_t stream);
+// Phase records of the 4-row / 32-row / streaming kernels (a kvq_status;
+// KVQ_ERR_UNSUPPORTED unless built with KVQ_PHASE_TRACE).
 int phase_fetch_r4(void* host, size_t bytes);
 int phase_fetch_r32(void* host, size_t bytes);
+int phase_fetch_stream(void* host, size_t bytes);
 hipError_t launch_stream_read(const void* data, long long bytes, unsigned* sink,
                               hipStream_t stream);
 

@@ -1,10 +1,14 @@
-"""Phase timeline of the matrix-core attend kernels (a measurement aid).
+"""Phase timeline of the fused attend kernels (a measurement aid).
 
 Build the diagnostic library first (the same kernels, with per-wave phase
 timestamps; see kvq_phase_trace_fetch in include/kvq.h):
 
     python quantized_kv_cache_attend_amd/build.py --phase-trace
     python -m quantized_kv_cache_attend_amd.phase_trace --workload gqa_n4096
+    python -m quantized_kv_cache_attend_amd.phase_trace --format 4,8 --splits 8
+
+The workload's own format (group 32) runs a matrix-core kernel; another
+group (--format bits,group) runs the streaming kernel.
 
 The workload's synthetic cache is packed with the library and copied until the
 copies exceed the Infinity Cache, as in bench.py.  The diagnostic library's
@@ -50,12 +54,18 @@ def load_phase_lib():
     return lib
 
 
-def run(workload: str, splits: int, batches: int, per_batch: int):
+KERNELS = {0: "4-row", 1: "32-row", 2: "streaming"}
+
+
+def run(workload: str, splits: int, batches: int, per_batch: int, fmt=None):
     import torch
     w = WORKLOADS[workload]
-    bits, group = w.formats[0]
+    bits, group = fmt if fmt else w.formats[0]
     rows = w.Hq // w.Hkv * w.R
-    kernel = 0 if rows <= 4 else 1
+    if group == 32:
+        kernel = 0 if rows <= 4 else 1
+    else:
+        kernel = 2
     splits = w.num_splits if splits < 0 else splits
     lib = load_phase_lib()
     q, k, v = make_qkv(w, 0)
@@ -107,7 +117,7 @@ def run(workload: str, splits: int, batches: int, per_batch: int):
         rec.append(x)
         spans.append(np.nanmax(x[:, 7]))
     x = np.concatenate(rec)
-    print(f"# {workload}: kernel {'4-row' if kernel == 0 else '32-row'}, "
+    print(f"# {workload} {bits}-bit g{group}: kernel {KERNELS[kernel]}, "
           f"{splits if splits else 'automatic'} splits, {recorded // waves_per_wg} workgroups x "
           f"{waves_per_wg} waves recorded; {batches} batches of {per_batch} back-to-back launches "
           f"over {copies} cache copies, the last launch of each batch recorded")
@@ -146,8 +156,10 @@ def main():
     ap.add_argument("--splits", type=int, default=-1, help="-1: the workload's default, 0: auto")
     ap.add_argument("--batches", type=int, default=12)
     ap.add_argument("--per-batch", type=int, default=20)
+    ap.add_argument("--format", default="", help="bits,group (default: the workload's own)")
     args = ap.parse_args()
-    run(args.workload, args.splits, args.batches, args.per_batch)
+    fmt = tuple(int(x) for x in args.format.split(",")) if args.format else None
+    run(args.workload, args.splits, args.batches, args.per_batch, fmt)
 
 
 if __name__ == "__main__":

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_strings():
-    assert lib.kvq_abi_version() == 9
+    assert lib.kvq_abi_version() == 10
     for st in (0, -1, -2, -3, -4, 7):
         assert lib.kvq_status_string(st)
 
@@ -271,6 +271,8 @@ def test_phase_trace_fetch_only_in_the_trace_build():
     buf = (ctypes.c_uint64 * 16)()
     assert lib.kvq_phase_trace_fetch(0, ctypes.cast(buf, ctypes.c_void_p), 128) == kvq.KVQ_ERR_UNSUPPORTED
     assert lib.kvq_phase_trace_fetch(1, ctypes.cast(buf, ctypes.c_void_p), 128) == kvq.KVQ_ERR_UNSUPPORTED
-    assert lib.kvq_phase_trace_fetch(2, ctypes.cast(buf, ctypes.c_void_p), 128) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_phase_trace_fetch(2, ctypes.cast(buf, ctypes.c_void_p), 128) == kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_phase_trace_fetch(3, ctypes.cast(buf, ctypes.c_void_p), 128) == kvq.KVQ_ERR_INVALID
+    assert lib.kvq_phase_trace_fetch(-1, ctypes.cast(buf, ctypes.c_void_p), 128) == kvq.KVQ_ERR_INVALID
     assert lib.kvq_phase_trace_fetch(0, None, 128) == kvq.KVQ_ERR_INVALID
     assert lib.kvq_phase_trace_fetch(0, ctypes.cast(buf, ctypes.c_void_p), 12) == kvq.KVQ_ERR_INVALID

@@ -622,11 +622,12 @@ def main():
         del blocker, kpre, vpre, kw, vw, ws_w
 
         # The other formats on the same cache shape: 8-bit group 32 (the
-        # matrix-core kernels) and 4-bit group 8 (the general kernel), KV GB/s
-        # of their own byte counts, timed like the main step (rotating cache
-        # copies past the Infinity Cache, launched the same way).
+        # matrix-core kernels), 4-bit and 8-bit group 8 (the streaming kernel)
+        # and 4-bit group 8 on the general kernel, KV GB/s of their own byte
+        # counts, timed like the main step (rotating cache copies past the
+        # Infinity Cache, launched the same way).
         fmt = {}
-        for fb, fg in ((8, 32), (4, 8)):
+        for fb, fg, fvar in ((8, 32, "auto"), (4, 8, "auto"), (8, 8, "auto"), (4, 8, "valu")):
             fbytes = kv_bytes(w, fb, fg)
             fcopies = max(2, math.ceil(3 * MALL_BYTES / fbytes))
             fk0, fks0 = kvq.pack_k(kd, fb, fg)
@@ -637,7 +638,8 @@ def main():
 
             def fpass():
                 for c in fcaches:
-                    kvq.attend(qd, *c, w.N, fb, fg, workspace=ws, out=fout, num_splits=splits)
+                    kvq.attend(qd, *c, w.N, fb, fg, workspace=ws, out=fout, num_splits=splits,
+                               variant=fvar)
             fpass()
             torch.cuda.synchronize()
             fref = fout.clone()
@@ -662,11 +664,13 @@ def main():
             f1.record(stream)
             torch.cuda.synchronize()
             fus = f0.elapsed_time(f1) * 1e3 / (n_f * fcopies)
-            fmt[f"{fb}bit_g{fg}"] = {"us": round(fus, 2), "kv_bytes": fbytes,
-                                     "kv_gbs": round(fbytes / (fus * 1e-6) / 1e9, 1),
-                                     "hbm_frac": round(fbytes / (fus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                     "kernel": "matrix-core" if (fb, fg) == (8, 32) else "general",
-                                     "cache_copies": fcopies}
+            key = f"{fb}bit_g{fg}" + ("_general_kernel" if fvar == "valu" else "")
+            fmt[key] = {"us": round(fus, 2), "kv_bytes": fbytes,
+                        "kv_gbs": round(fbytes / (fus * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(fbytes / (fus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "kernel": ("general" if fvar == "valu" else
+                                   "matrix-core" if fg == 32 else "streaming"),
+                        "cache_copies": fcopies}
             del fcaches, fk0, fks0, fv0, fvs0, fout
             if args.launch == "graph":
                 del fgraph

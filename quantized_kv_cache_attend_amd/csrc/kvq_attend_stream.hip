@@ -44,8 +44,6 @@
 namespace kvq {
 namespace {
 
-constexpr int kSWaves = 4;
-constexpr int kSThreads = kSWaves * 64;
 constexpr int kSD = 128;
 constexpr float kSLazy = 6.0f;  // the reference moves only past m + kSLazy
 
@@ -150,31 +148,48 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// Query rows in LDS, times sm_scale * log2 e: qs[r][hf][n] holds channels
-// 8n + 4hf .. 8n + 4hf + 3 of row r, so the 16 lanes of a token octet read
-// 256 contiguous bytes (rows past `rows` are zero).
+// Query rows in LDS: qs[r][hf][n] holds channels 8n + 4hf .. 8n + 4hf + 3 of
+// row r, so the 16 lanes of a token octet read 256 contiguous bytes (rows
+// past `rows` are zero).
 template <int kRows>
 struct SQuery {
   f32x4 qs[kRows][2][16];
 };
 
-template <int kBits, int kRows>
+// Where a lane's query values come from: registers (up to 4 rows: 32 VGPRs)
+// or the LDS copy above (8 rows), read per channel quad and block.
+template <int kRows, bool kInRegs>
+struct QSource;
+template <int kRows>
+struct QSource<kRows, true> {
+  f32x4 q[kRows][2];
+  __device__ __forceinline__ f32x4 get(int r, int hf) const { return q[r][hf]; }
+};
+template <int kRows>
+struct QSource<kRows, false> {
+  const SQuery<kRows>* sq;
+  int n;
+  __device__ __forceinline__ f32x4 get(int r, int hf) const { return sq->qs[r][hf][n]; }
+};
+
+template <int kBits, int kRows, int kWaves>
 struct SSmem {
   union {
-    unsigned char ring[kSWaves][kSSlotBytes<kBits>];  // one block slot per wave
-    float wu[kSWaves][kRows][kSD];                     // the merge (after the loop)
+    unsigned char ring[kWaves][kSSlotBytes<kBits>];  // one block slot per wave
+    float wu[kWaves][kRows][kSD];                     // the merge (after the loop)
   } u;
   SQuery<kRows> q;
-  float wm[kSWaves][kRows];
-  float wz[kSWaves][kRows];
+  float wm[kWaves][kRows];
+  float wz[kWaves][kRows];
   int last;
 };
 
 // Scores of the lane's token octet in one block: s[r][t] for token 8q + t
 // (summed over all 128 channels; every lane of the DPP row holds them).
-template <int kBits, int kRows>
-__device__ __forceinline__ void block_scores(const SPart<kBits>& kp, const SQuery<kRows>& sq,
-                                             int n, float (&s)[kRows][8]) {
+// qscale: sm_scale * log2 e, folded into the K scales (scores in base-2 units).
+template <int kBits, int kRows, typename QS>
+__device__ __forceinline__ void block_scores(const SPart<kBits>& kp, const QS& qsrc,
+                                             float qscale, float (&s)[kRows][8]) {
   constexpr float kQmax = kBits == 4 ? 7.0f : 127.0f;
 #pragma unroll
   for (int r = 0; r < kRows; ++r)
@@ -187,11 +202,13 @@ __device__ __forceinline__ void block_scores(const SPart<kBits>& kp, const SQuer
   for (int hf = 0; hf < 2; ++hf) {
     f32x4 qh[kRows];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) qh[r] = sq.qs[r][hf][n];
-    const f32x4 ks = kp.s[hf];
-    float kb[4];
+    for (int r = 0; r < kRows; ++r) qh[r] = qsrc.get(r, hf);
+    float ks[4], kb[4];  // K scale times qscale, and -qmax times that
 #pragma unroll
-    for (int e = 0; e < 4; ++e) kb[e] = -kQmax * ks[e];
+    for (int e = 0; e < 4; ++e) {
+      ks[e] = kp.s[hf][e] * qscale;
+      kb[e] = -kQmax * ks[e];
+    }
 #pragma unroll
     for (int j = 0; j < kBits; ++j) {
       const int d = 2 * j + hf;
@@ -203,7 +220,7 @@ __device__ __forceinline__ void block_scores(const SPart<kBits>& kp, const SQuer
         codes4<kBits>(w, part == 1, c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float kv = fmaf(c[e], ks[e], kb[e]);  // (c - qmax) s
+          const float kv = fmaf(c[e], ks[e], kb[e]);  // (c - qmax) s qscale
 #pragma unroll
           for (int r = 0; r < kRows; ++r) s[r][t] = fmaf(qh[r][e], kv, s[r][t]);
         }
@@ -299,9 +316,24 @@ __device__ __forceinline__ void block_values(const SPart<kBits>& vp, const float
   }
 }
 
-template <int kBits, int kRows>
-__global__ __launch_bounds__(kSThreads) void attend_stream_kernel(AttendProblem p) {
-  __shared__ SSmem<kBits, kRows> sm;
+// Issue priority of this wave among the waves sharing its SIMD: the share of
+// its blocks still ahead, in 4 levels.  The SIMD prefers the wave furthest
+// behind, so waves that share it finish their (equal) block counts together
+// instead of the older one first (without it the younger wave of a pair took
+// up to 1.7 times as long).
+__device__ __forceinline__ void set_priority(int level) {
+  switch (level) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
+template <int kBits, int kRows, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProblem p) {
+  constexpr int kThreads = kWaves * 64;
+  __shared__ SSmem<kBits, kRows, kWaves> sm;
   phase_mark(kMarkStart);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -339,26 +371,37 @@ __global__ __launch_bounds__(kSThreads) void attend_stream_kernel(AttendProblem 
   const int b_begin = t_begin / kBlockTokens;
   const int b_end = t_end > t_begin ? (t_end + kBlockTokens - 1) / kBlockTokens : b_begin;
   const int b_first = b_begin + wave;
-  const int cnt = b_first < b_end ? (b_end - 1 - b_first) / kSWaves + 1 : 0;  // wave-uniform
+  const int cnt = b_first < b_end ? (b_end - 1 - b_first) / kWaves + 1 : 0;  // wave-uniform
 
+  // The query rows: in registers (loaded ahead of the first block, first
+  // used once it has landed) or, for 8 rows, in LDS (stored before any block
+  // copy is in flight, since an LDS store is ordered after every
+  // LDS-destination load issued before it).
+  // (A descriptor over the head's `rows` rows reads zeros past them.)
+  constexpr bool kQRegs = kRows <= 4;
+  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(p.q + bh * rows * kSD, rows * kSD * 4);
+  QSource<kRows, kQRegs> qsrc;
+  if constexpr (kQRegs) {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        qsrc.q[r][hf] = buf_f4(qrs, static_cast<unsigned>((r * kSD + 8 * n + 4 * hf) * 4), 0);
+  } else {
+    static_assert(kRows * 32 <= kThreads, "one query piece per thread");
+    const int qr = tid >> 5, qhf = (tid >> 4) & 1, qo = tid & 15;
+    if (qr < kRows)
+      sm.q.qs[qr][qhf][qo] =
+          buf_f4(qrs, static_cast<unsigned>((qr * kSD + 8 * qo + 4 * qhf) * 4), 0);
+    __syncthreads();
+    qsrc.sq = &sm.q;
+    qsrc.n = n;
+  }
   unsigned char* slot = sm.u.ring[wave];
   if (cnt > 0) {
     dma_k<kBits>(slot, h, b_first, n, q);
     dma_v<kBits>(slot, h, b_first, n, q);
   }
-
-  // the query rows into LDS (one 16-byte piece per thread)
-  for (int i = tid; i < kRows * 32; i += kSThreads) {
-    const int r = i >> 5, hf = (i >> 4) & 1, o = i & 15;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (r < rows) {
-      x = *reinterpret_cast<const f32x4*>(p.q + (bh * rows + r) * kSD + 8 * o + 4 * hf);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] *= p.qscale;
-    }
-    sm.q.qs[r][hf][o] = x;
-  }
-  __syncthreads();
   phase_mark(kMarkQReady);
 
   float m[kRows], z[kRows], u[kRows][8];  // u: features 8n .. 8n + 7
@@ -375,8 +418,9 @@ __global__ __launch_bounds__(kSThreads) void attend_stream_kernel(AttendProblem 
   // so K(i) has landed once at most one part (V(i)) is pending, and V(i)
   // once at most K(i + 1) is.
   for (int i = 0; i < cnt; ++i) {
-    const int blk = b_first + i * kSWaves;
+    const int blk = b_first + i * kWaves;
     const bool more = i + 1 < cnt;
+    set_priority((cnt - 1 - i) * 4 / cnt);
     float s[kRows][8];
     {
       __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(kSPart<kBits>));  // K(i) in the slot
@@ -384,8 +428,8 @@ __global__ __launch_bounds__(kSThreads) void attend_stream_kernel(AttendProblem 
       SPart<kBits> kp;
       read_part<kBits>(kp, slot, lane);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the K part has been read
-      if (more) dma_k<kBits>(slot, h, blk + kSWaves, n, q);
-      block_scores<kBits, kRows>(kp, sm.q, n, s);
+      if (more) dma_k<kBits>(slot, h, blk + kWaves, n, q);
+      block_scores<kBits, kRows>(kp, qsrc, p.qscale, s);
     }
     block_softmax<kRows>(s, t_end - (blk * kBlockTokens + 8 * q), m, z, u, live);
     {
@@ -394,11 +438,12 @@ __global__ __launch_bounds__(kSThreads) void attend_stream_kernel(AttendProblem 
       SPart<kBits> vp;
       read_part<kBits>(vp, slot + 1024 * kSPart<kBits>, lane);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the V part has been read
-      if (more) dma_v<kBits>(slot, h, blk + kSWaves, n, q);
+      if (more) dma_v<kBits>(slot, h, blk + kWaves, n, q);
       block_values<kBits, kRows>(vp, s, u);
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   phase_mark(kMarkLoopEnd);
 
   // ---- merge: the 4 token octets, then the waves through LDS ---------------
@@ -430,23 +475,27 @@ __global__ __launch_bounds__(kSThreads) void attend_stream_kernel(AttendProblem 
     }
   }
   __syncthreads();
-  constexpr int kF = kRows * kSD / kSThreads;  // outputs per thread: row r, features f0 ..
+  // outputs per thread: row r, features f0 .. f0 + kF - 1 (threads past the
+  // kRows rows take no part)
+  constexpr int kF = (kRows * kSD + kThreads - 1) / kThreads;
+  static_assert(kSD % kF == 0, "whole rows per thread group");
   const int r = tid * kF / kSD;
   const int f0 = (tid * kF) % kSD;
+  const int rr = r < kRows ? r : kRows - 1;  // in-range row for the LDS reads
   float M = -INFINITY, Z = 0.0f, U[kF];
 #pragma unroll
   for (int j = 0; j < kF; ++j) U[j] = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kSWaves; ++w) M = fmaxf(M, sm.wm[w][r]);
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][rr]);
   if (M != -INFINITY) {
 #pragma unroll
-    for (int w = 0; w < kSWaves; ++w) {
-      const float mw = sm.wm[w][r];
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm.wm[w][rr];
       if (mw == -INFINITY) continue;
       const float x = fast_exp2(mw - M);
-      Z = fmaf(x, sm.wz[w][r], Z);
+      Z = fmaf(x, sm.wz[w][rr], Z);
 #pragma unroll
-      for (int j = 0; j < kF; ++j) U[j] = fmaf(x, sm.u.wu[w][r][f0 + j], U[j]);
+      for (int j = 0; j < kF; ++j) U[j] = fmaf(x, sm.u.wu[w][rr][f0 + j], U[j]);
     }
   }
   phase_mark(kMarkMerged);
@@ -468,21 +517,29 @@ __global__ __launch_bounds__(kSThreads) void attend_stream_kernel(AttendProblem 
 
 int phase_fetch_stream(void* host, size_t bytes) { return phase_fetch(host, bytes); }
 
-hipError_t launch_attend_stream(const AttendProblem& p, hipStream_t stream) {
+// Waves per workgroup: 8 (two per SIMD) up to 4 rows, where the kernel holds
+// 240 VGPRs; 4 for 8 rows (251-261 VGPRs: one or two workgroups per compute
+// unit).  The automatic split count aims at two waves per SIMD either way.
+static constexpr int waves_for(int rows) { return rows <= 4 ? 8 : 4; }
+
+int stream_waves(int bits, int rows) {
+  (void)bits;
+  return waves_for(rows > 4 ? 8 : 4);
+}
+
+template <int kBits, int kRows>
+static hipError_t launch_stream(const AttendProblem& p, hipStream_t stream) {
+  constexpr int kWaves = waves_for(kRows);
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
-  const bool r8 = p.rows > 4;
-  if (p.bits == 8) {
-    if (r8)
-      hipLaunchKernelGGL((attend_stream_kernel<8, 8>), dim3(grid), dim3(kSThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attend_stream_kernel<8, 4>), dim3(grid), dim3(kSThreads), 0, stream, p);
-  } else {
-    if (r8)
-      hipLaunchKernelGGL((attend_stream_kernel<4, 8>), dim3(grid), dim3(kSThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attend_stream_kernel<4, 4>), dim3(grid), dim3(kSThreads), 0, stream, p);
-  }
+  hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves>), dim3(grid), dim3(kWaves * 64),
+                     0, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_attend_stream(const AttendProblem& p, hipStream_t stream) {
+  const bool r8 = p.rows > 4;
+  if (p.bits == 8) return r8 ? launch_stream<8, 8>(p, stream) : launch_stream<8, 4>(p, stream);
+  return r8 ? launch_stream<4, 8>(p, stream) : launch_stream<4, 4>(p, stream);
 }
 
 }  // namespace kvq

@@ -121,6 +121,7 @@ hipError_t launch_attend_mfma32(const AttendProblem& p, hipStream_t stream);
 // float32 window.
 constexpr int kStreamMaxRows = 8;
 hipError_t launch_attend_stream(const AttendProblem& p, hipStream_t stream);
+int stream_waves(int bits, int rows);  // waves per workgroup of that launch
 // Phase records of the 4-row / 32-row / streaming kernels (a kvq_status;
 // KVQ_ERR_UNSUPPORTED unless built with KVQ_PHASE_TRACE).
 int phase_fetch_r4(void* host, size_t bytes);

@@ -91,8 +91,8 @@ def run(workload: str, splits: int, batches: int, per_batch: int, fmt=None):
             raise RuntimeError(f"kvq_attend: status {st}")
 
     heads = w.B * w.Hkv
-    grid = (splits or lib_auto_splits(w)) * heads
-    waves_per_wg = 8 if kernel == 0 else 4
+    grid = (splits or lib_auto_splits(w)) * heads  # an upper bound: rows a launch wrote are kept
+    waves_per_wg = 8 if kernel in (0, 2) else 4
     nw = min(PHASE_WAVES, grid * waves_per_wg)
     buf = np.zeros(PHASE_WAVES * PHASE_MARKS, np.uint64)
     for i in range(2 * copies):

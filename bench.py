@@ -73,6 +73,15 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 
+def dtype_label(bits, group, variant):
+    """What the timed kernel computes in: the matrix-core kernels (group 32)
+    take exact fp16 code operands and fp16 hi + lo float32 factors; the
+    streaming and general kernels decode to float32."""
+    if variant in ("auto", "mfma") and group == 32:
+        return f"u{bits} codes + f32 scales; fp16 hi+lo matrix-core operands, f32 accumulate"
+    return f"u{bits} codes + f32 scales; f32 decode and arithmetic"
+
+
 def measured_traffic():
     """HBM bytes per launch of the matrix-core attend kernel from the committed
     counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same
@@ -240,7 +249,7 @@ def main():
                     help="timed steps replayed from a HIP graph (one step per cache copy) "
                          "or launched one by one from Python")
     ap.add_argument("--workload", default="gqa_n4096", choices=["gqa_n4096", "gqa_n32768"])
-    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma", "stream"])
     ap.add_argument("--splits", type=int, default=-1, help="-1: workload default, 0: auto")
     ap.add_argument("--bits", type=int, default=0, choices=[0, 4, 8],
                     help="code width of the timed cache (0: the workload's, 4)")
@@ -740,8 +749,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (f"u{bits} codes + f32 scales; fp16 hi+lo matrix-core operands, "
-                  "f32 accumulate"),
+        "dtype": dtype_label(bits, group, args.variant),
         "data": "synthetic (seeded N(0,1) float32 Q/K/V, packed on the GPU)",
         "config": {"workload": w.name, "batch": w.B, "n_tokens": w.N, "hq": w.Hq, "hkv": w.Hkv,
                    "queries_per_head": w.R, "head_dim": w.D, "bits": bits, "group": group,

@@ -644,6 +644,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
   // and its operands are in registers, the slot is refilled with block
   // i + kDepth, which then streams in while block i is attended.
   for (int i = 0; i < cnt; ++i) {
+    priority_by_blocks_left(i, cnt);  // waves that share a SIMD finish together
     wait_blocks<kBits>(min(kRing<kBits> - 1, cnt - 1 - i));
     unsigned char* slot = ring + (i % kRing<kBits>) * kSlotBytes<kBits>;
     BlockRegs<kBits> br;
@@ -662,6 +663,7 @@ attend_mfma_r4_kernel(AttendProblem p) {
     attend_block<kBits, kCausal>(sm, br, (b_first + i * kWaves) * kBlockTokens, t_end, cc, ws, qv,
                                  us_row, lim, p.pos_end - p.R);
   }
+  __builtin_amdgcn_s_setprio(0);
   phase_mark(kMarkLoopEnd);
   if (kAppend && !app_ok) {  // the append never signalled: make the head's output NaN
     const f32x4 nan4 = {as_f32(0x7fc00000u), as_f32(0x7fc00000u), as_f32(0x7fc00000u),

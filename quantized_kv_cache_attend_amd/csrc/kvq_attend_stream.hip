@@ -316,20 +316,6 @@ __device__ __forceinline__ void block_values(const SPart<kBits>& vp, const float
   }
 }
 
-// Issue priority of this wave among the waves sharing its SIMD: the share of
-// its blocks still ahead, in 4 levels.  The SIMD prefers the wave furthest
-// behind, so waves that share it finish their (equal) block counts together
-// instead of the older one first (without it the younger wave of a pair took
-// up to 1.7 times as long).
-__device__ __forceinline__ void set_priority(int level) {
-  switch (level) {
-    case 0: __builtin_amdgcn_s_setprio(0); break;
-    case 1: __builtin_amdgcn_s_setprio(1); break;
-    case 2: __builtin_amdgcn_s_setprio(2); break;
-    default: __builtin_amdgcn_s_setprio(3); break;
-  }
-}
-
 template <int kBits, int kRows, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProblem p) {
   constexpr int kThreads = kWaves * 64;
@@ -420,7 +406,7 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
   for (int i = 0; i < cnt; ++i) {
     const int blk = b_first + i * kWaves;
     const bool more = i + 1 < cnt;
-    set_priority((cnt - 1 - i) * 4 / cnt);
+    priority_by_blocks_left(i, cnt);  // waves that share a SIMD finish together
     float s[kRows][8];
     {
       __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(kSPart<kBits>));  // K(i) in the slot

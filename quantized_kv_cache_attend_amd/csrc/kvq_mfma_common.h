@@ -273,6 +273,21 @@ inline int phase_fetch(void* host, size_t bytes) {
 #endif
 }
 
+// ---- issue priority ------------------------------------------------------------
+// Priority of this wave among the waves sharing its SIMD before its block i of
+// cnt: the share of its blocks still ahead, in the 4 levels of s_setprio.  The
+// SIMD then prefers the wave furthest behind, so waves with equal block counts
+// finish together instead of the oldest first (which left its workgroup waiting
+// at the merge barrier for the youngest).  The caller drops to 0 after its loop.
+__device__ __forceinline__ void priority_by_blocks_left(int i, int cnt) {
+  switch ((cnt - 1 - i) * 4 / cnt) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
 // ---- split combine -----------------------------------------------------------
 // The KV splits of a head merge their partial (m, z, u) rows with the same
 // rescale as the blocks ("two stops of the online accumulation" on the

@@ -17,20 +17,25 @@
 // multiply-add c * s + fl32(-qmax * s) (within 2^-21 s of the exact
 // product).  Plain float32 arithmetic throughout.
 //
-// Work split: one workgroup of 4 waves per (KV head, split), with the
-// matrix-core kernels' XCD-aware mapping; wave w attends blocks w, w + 4, ...
-// of its split.  Lane (n, q) = (lane & 15, lane >> 4) owns channel octet n
-// (channels 8n .. 8n + 7), feature octet n (features 8n .. 8n + 7) and token
-// octet q (tokens 8q .. 8q + 7 of each 32-token block).  In the block layout
-// of kvq_layout.h each of these is one contiguous run of code bytes (32 at
-// 4-bit, 64 at 8-bit), and the lane's K scales (8 channels of the token
-// octet's group) and V scales (8 tokens of the feature octet's group) are
-// two 16-byte runs each:
-//   scores: the lane's partial dot products over its 8 channels, with the
-//     query rows read from LDS, are summed over the 16 lanes of its DPP row,
-//     which then all hold the token octet's scores;
+// Work split: one workgroup of 8 waves (4 for 8 rows) per (KV head, split),
+// with the matrix-core kernels' XCD-aware mapping; wave w attends blocks
+// w, w + waves, ... of its split.  Lane (n, q) = (lane >> 2, lane & 3) owns
+// channel octet n (channels 8n .. 8n + 7), feature octet n (features 8n ..
+// 8n + 7) and token octet q (tokens 8q .. 8q + 7 of each 32-token block).  In
+// the block layout of kvq_layout.h each of these is one contiguous run of
+// code bytes (32 at 4-bit, 64 at 8-bit), and the lane's K scales (8 channels
+// of the token octet's group) and V scales (8 tokens of the feature octet's
+// group) are two 16-byte runs each:
+//   scores: the lane's partial dot products over its 8 channels, for every
+//     query row, are summed over the 16 lanes of its token octet by a
+//     reduce-scatter (two lane-swap halvings across the wave's 16-lane rows,
+//     then a sum over the 4 lanes of the row), which leaves each lane the full
+//     scores of R/4 rows for its 8 tokens;
+//   softmax: on those scores only, the row max over the 4 token octets of a
+//     quad; the probabilities go back to every lane (two lane-swap stages);
 //   values: the lane accumulates u for its 8 features over its 8 tokens for
-//     the whole split; the 4 token octets are summed once, at the end.
+//     the whole split; the 4 token octets of a quad are summed once, at the
+//     end.
 // Streaming: each wave keeps its next block in flight in an LDS slot, copied
 // from HBM by LDS-destination buffer loads (no VGPRs held in flight), in two
 // parts: the K part (codes and scales) is refilled as soon as the block's K
@@ -69,11 +74,30 @@ struct SPart {
 // slot + 1024 (x kSPart + j) + 16 lane.
 template <int kBits>
 constexpr int kSSlotBytes = 2 * 1024 * kSPart<kBits>;
+// Slots per wave (blocks in flight).  One: a second slot (tried where it fits
+// in LDS) doubles the burst of loads at the start, which delays every
+// wave's first block and its query copy, and made the calls slower (4-bit
+// group 8 on the 8 x 4096 cache 26.0 vs 22.3 us; 8 rows 33.2 vs 28.7 us).
+template <int kBits, int kWaves>
+constexpr int kSDepth = 1;
 
 #define KVQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // s_waitcnt with vmcnt(x) (bits 3:0 and 15:14), expcnt and lgkmcnt at maximum.
 #define KVQ_SVMCNT(x) ((((x) & 15) | (((x) >> 4) << 14)) | 0x0F70)
+
+// Wait until at most `parts` (0 to 4) block parts (kSPart loads each) are in
+// flight.
+template <int kBits>
+__device__ __forceinline__ void wait_parts(int parts) {
+  switch (parts) {
+    case 0: __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(kSPart<kBits>)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(2 * kSPart<kBits>)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(3 * kSPart<kBits>)); break;
+    default: __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(4 * kSPart<kBits>)); break;
+  }
+}
 
 // Start copying one part of a block into LDS (asynchronous, counted by
 // vmcnt: kSPart loads).  codes / scales: the lane's byte offsets.
@@ -139,13 +163,44 @@ __device__ __forceinline__ void codes4(unsigned w, bool hi, float c[4]) {
   for (int e = 0; e < 4; ++e) c[e] = static_cast<float>((x >> (8 * e)) & 0xFFu);
 }
 
-// x summed over the 16 lanes of its DPP row (every lane gets the sum).
-__device__ __forceinline__ float row_sum16(float x) {
+// ---- cross-lane steps (lane = 4 n + q) -----------------------------------------
+// Reduce-scatter halves: lanes below 32 (bit 4 clear) get x summed with the
+// lane 32 (16) away, the others y summed likewise; one swap and one add.
+__device__ __forceinline__ float scatter32(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(y), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+__device__ __forceinline__ float scatter16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(y), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+// x summed over the 4 lanes of its DPP row with the same q (lanes 4 apart).
+__device__ __forceinline__ float sum_over_n4(float x) {
   x += dpp<kRowRor8>(x);
-  x += dpp<kRowRor4>(x);
-  x += dpp<kRowRor2>(x);
-  x += dpp<kRowRor1>(x);
-  return x;
+  return x + dpp<kRowRor4>(x);
+}
+// Sum / max over the 4 lanes of a quad (its 4 token octets).
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;  // quad_perm [1,0,3,2], [2,3,0,1]
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp<kQuadXor1>(x);
+  return x + dpp<kQuadXor2>(x);
+}
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, dpp<kQuadXor1>(x));
+  return fmaxf(x, dpp<kQuadXor2>(x));
+}
+// Values of the rows held by other lanes: v[j] (row (R/2) b5 + (R/4) b4 + j,
+// b5 / b4 the lane's bits 5 / 4) from every lane of the same quad position, in
+// absolute row order: out[r] for r < R.
+template <int kRows>
+__device__ __forceinline__ void gather_rows(const float (&v)[kRows / 4], float (&out)[kRows]) {
+#pragma unroll
+  for (int j = 0; j < kRows / 4; ++j) {
+    float lo, hi;  // the value of the lane with bit 4 clear / set
+    swap16(v[j], lo, hi);
+    swap32(lo, out[j], out[kRows / 2 + j]);
+    swap32(hi, out[kRows / 4 + j], out[kRows / 2 + kRows / 4 + j]);
+  }
 }
 
 // Query rows in LDS: qs[r][hf][n] holds channels 8n + 4hf .. 8n + 4hf + 3 of
@@ -174,8 +229,10 @@ struct QSource<kRows, false> {
 
 template <int kBits, int kRows, int kWaves>
 struct SSmem {
+  // up to 4 rows: each wave's own copy of the query rows, as SQuery
+  f32x4 wq[kRows <= 4 ? kWaves : 1][kRows <= 4 ? kRows * 32 : 1];
   union {
-    unsigned char ring[kWaves][kSSlotBytes<kBits>];  // one block slot per wave
+    unsigned char ring[kWaves][kSDepth<kBits, kWaves>][kSSlotBytes<kBits>];  // block slots
     float wu[kWaves][kRows][kSD];                     // the merge (after the loop)
   } u;
   SQuery<kRows> q;
@@ -184,12 +241,16 @@ struct SSmem {
   int last;
 };
 
-// Scores of the lane's token octet in one block: s[r][t] for token 8q + t
-// (summed over all 128 channels; every lane of the DPP row holds them).
+// Scores of the lane's token octet in one block.  Each lane first forms its
+// partial dot products over its 8 channels for every row and token; a
+// reduce-scatter then leaves it the full scores of R/4 rows: out[j][t] is
+// row (R/2) b5 + (R/4) b4 + j, token 8q + t (b5 / b4: lane bits 5 / 4; the
+// 4 lanes of a DPP row with the same q hold the same values).
 // qscale: sm_scale * log2 e, folded into the K scales (scores in base-2 units).
 template <int kBits, int kRows, typename QS>
 __device__ __forceinline__ void block_scores(const SPart<kBits>& kp, const QS& qsrc,
-                                             float qscale, float (&s)[kRows][8]) {
+                                             float qscale, float (&out)[kRows / 4][8]) {
+  float s[kRows][8];
   constexpr float kQmax = kBits == 4 ? 7.0f : 127.0f;
 #pragma unroll
   for (int r = 0; r < kRows; ++r)
@@ -227,56 +288,71 @@ __device__ __forceinline__ void block_scores(const SPart<kBits>& kp, const QS& q
       }
     }
   }
+  // Reduce over the 16 lanes of each token octet (lanes 4 apart): halve the
+  // rows across lane bit 5, then bit 4, then sum over the 4 lanes in the row.
+  float h[kRows / 2][8];
 #pragma unroll
-  for (int r = 0; r < kRows; ++r)
+  for (int r = 0; r < kRows / 2; ++r)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) s[r][t] = row_sum16(s[r][t]);
+    for (int t = 0; t < 8; ++t) h[r][t] = scatter32(s[r][t], s[r + kRows / 2][t]);
+#pragma unroll
+  for (int j = 0; j < kRows / 4; ++j)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) out[j][t] = sum_over_n4(scatter16(h[j][t], h[j + kRows / 4][t]));
 }
 
-// The lazy online-softmax update for one block; s becomes p = 2^(s - m).
-// ntok: how many of the lane's 8 tokens are in the split (the rest, past
-// the cache's end, take no part).  Every lane of the wave calls it.
+// The lazy online-softmax update for one block on the lane's R/4 rows (as
+// block_scores leaves them); s becomes p = 2^(s - m).  m, z: the lane's rows
+// (z over its token octet only); u: every row.  ntok: how many of the lane's
+// 8 tokens are in the split (the rest, past the cache's end, take no part).
+// Every lane of the wave calls it.
 template <int kRows>
-__device__ __forceinline__ void block_softmax(float (&s)[kRows][8], int ntok, float (&m)[kRows],
-                                              float (&z)[kRows], float (&u)[kRows][8],
-                                              bool& live) {
+__device__ __forceinline__ void block_softmax(float (&s)[kRows / 4][8], int ntok,
+                                              float (&m)[kRows / 4], float (&z)[kRows / 4],
+                                              float (&u)[kRows][8], bool& live) {
+  constexpr int kL = kRows / 4;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const bool ok = t < ntok;
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) s[r][t] = ok ? s[r][t] : -INFINITY;
+    for (int j = 0; j < kL; ++j) s[j][t] = ok ? s[j][t] : -INFINITY;
   }
-  float bm[kRows];
-  bool move = !live;
+  float bm[kL];
+  bool up = false;
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    float x = s[r][0];
+  for (int j = 0; j < kL; ++j) {
+    float x = s[j][0];
 #pragma unroll
-    for (int t = 1; t < 8; ++t) x = fmaxf(x, s[r][t]);
-    bm[r] = qblock_max(x);  // the block's max of row r (every lane)
-    move = move || bm[r] > m[r] + kSLazy;
+    for (int t = 1; t < 8; ++t) x = fmaxf(x, s[j][t]);
+    bm[j] = quad_max(x);  // the block's max of the row (all 32 tokens)
+    up = up || bm[j] > m[j] + kSLazy;
   }
-  if (__builtin_amdgcn_readfirstlane(move ? 1 : 0)) {  // wave-uniform
+  if (!live || __builtin_amdgcn_ballot_w64(up) != 0) {  // wave-uniform
+    float a[kL];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const float mn = live ? (bm[r] > m[r] + kSLazy ? bm[r] : m[r]) : bm[r];
-      const float a = live ? fast_exp2(m[r] - mn) : 0.0f;
-      z[r] *= a;
-#pragma unroll
-      for (int f = 0; f < 8; ++f) u[r][f] *= a;
-      m[r] = mn;
+    for (int j = 0; j < kL; ++j) {
+      const float mn = live ? (bm[j] > m[j] + kSLazy ? bm[j] : m[j]) : bm[j];
+      a[j] = live ? fast_exp2(m[j] - mn) : 0.0f;
+      z[j] *= a[j];
+      m[j] = mn;
     }
+    float ar[kRows];
+    gather_rows<kRows>(a, ar);
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int f = 0; f < 8; ++f) u[r][f] *= ar[r];
     live = true;
   }
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
+  for (int j = 0; j < kL; ++j) {
     float zs = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      s[r][t] = fast_exp2(s[r][t] - m[r]);
-      zs += s[r][t];
+      s[j][t] = fast_exp2(s[j][t] - m[j]);
+      zs += s[j][t];
     }
-    z[r] += zs;
+    z[j] += zs;
   }
 }
 
@@ -324,8 +400,8 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15;  // channel / feature octet
-  const int q = lane >> 4;  // token octet
+  const int n = lane >> 2;  // channel / feature octet
+  const int q = lane & 3;   // token octet
 
   const int heads = p.B * p.Hkv;
   const int L = blockIdx.x;
@@ -363,16 +439,28 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
   // used once it has landed) or, for 8 rows, in LDS (stored before any block
   // copy is in flight, since an LDS store is ordered after every
   // LDS-destination load issued before it).
-  // (A descriptor over the head's `rows` rows reads zeros past them.)
+  // The query rows (a descriptor over the head's `rows` rows reads zeros past
+  // them).  Up to 4 rows each wave copies them into its own LDS area with
+  // LDS-destination loads issued ahead of its first blocks, then reads its
+  // lanes' values into registers: no register is loaded from memory before
+  // the loop, which would make the compiler wait for every block copy in
+  // flight at the loop's entry.  For 8 rows they stay in LDS (stored before
+  // any block copy is in flight, since an LDS store is ordered after every
+  // LDS-destination load issued before it) and are read per block.
   constexpr bool kQRegs = kRows <= 4;
   const __amdgpu_buffer_rsrc_t qrs = head_rsrc(p.q + bh * rows * kSD, rows * kSD * 4);
   QSource<kRows, kQRegs> qsrc;
+  constexpr int kDepth = kSDepth<kBits, kWaves>;
   if constexpr (kQRegs) {
+    // piece i = (r * 2 + hf) * 16 + o of the copy holds channels 8o + 4hf ..
+    // 8o + 4hf + 3 of row r; lane ell of copy step c loads piece 64 c + ell
 #pragma unroll
-    for (int r = 0; r < kRows; ++r)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        qsrc.q[r][hf] = buf_f4(qrs, static_cast<unsigned>((r * kSD + 8 * n + 4 * hf) * 4), 0);
+    for (int c = 0; c < kRows * 32 / 64; ++c) {
+      const int i = 64 * c + lane, r = i >> 5, hf = (i >> 4) & 1, o = i & 15;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qrs, KVQ_LDS(&sm.wq[wave][64 * c]), 16,
+          static_cast<unsigned>((r * kSD + 8 * o + 4 * hf) * 4), 0, 0, 0);
+    }
   } else {
     static_assert(kRows * 32 <= kThreads, "one query piece per thread");
     const int qr = tid >> 5, qhf = (tid >> 4) & 1, qo = tid & 15;
@@ -383,49 +471,78 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
     qsrc.sq = &sm.q;
     qsrc.n = n;
   }
-  unsigned char* slot = sm.u.ring[wave];
-  if (cnt > 0) {
-    dma_k<kBits>(slot, h, b_first, n, q);
-    dma_v<kBits>(slot, h, b_first, n, q);
+  // Block i of the wave sits in slot i % kDepth; the first kDepth blocks go
+  // out at once, in the order K(0) V(0) K(1) V(1) ...
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    if (d < cnt) {
+      dma_k<kBits>(sm.u.ring[wave][d], h, b_first + d * kWaves, n, q);
+      dma_v<kBits>(sm.u.ring[wave][d], h, b_first + d * kWaves, n, q);
+    }
+  }
+  if constexpr (kQRegs) {
+    wait_parts<kBits>(2 * min(kDepth, cnt));  // the query copy has landed
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) qsrc.q[r][hf] = sm.wq[wave][(r * 2 + hf) * 16 + n];
   }
   phase_mark(kMarkQReady);
 
-  float m[kRows], z[kRows], u[kRows][8];  // u: features 8n .. 8n + 7
+  // m, z: the lane's R/4 rows (row (R/2) b5 + (R/4) b4 + j); u: every row,
+  // features 8n .. 8n + 7, over the lane's token octet.
+  constexpr int kL = kRows / 4;
+  float m[kL], z[kL], u[kRows][8];
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    m[r] = -INFINITY;
-    z[r] = 0.0f;
+  for (int j = 0; j < kL; ++j) {
+    m[j] = -INFINITY;
+    z[j] = 0.0f;
+  }
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
 #pragma unroll
     for (int f = 0; f < 8; ++f) u[r][f] = 0.0f;
-  }
   bool live = false;
 
-  // Loads in flight at each wait, in issue order: K(i) V(i) | K(i + 1) V(i + 1) ...
-  // so K(i) has landed once at most one part (V(i)) is pending, and V(i)
-  // once at most K(i + 1) is.
+  // Parts are issued in the order K(0) V(0) K(1) V(1) ...: K(i + kDepth) once
+  // K(i) is in registers, V(i + kDepth) once V(i) is.  So K(i) has landed
+  // once no more than the parts issued after it (V(i), then K and V of the
+  // blocks up to i + kDepth - 1) are pending, and V(i) once no more than the
+  // parts after it (K and V up to block i + kDepth - 1, then K(i + kDepth)).
   for (int i = 0; i < cnt; ++i) {
     const int blk = b_first + i * kWaves;
-    const bool more = i + 1 < cnt;
+    unsigned char* slot = sm.u.ring[wave][i % kDepth];
+    const int ahead = min(kDepth - 1, cnt - 1 - i);  // blocks already issued past i
+    const bool more = i + kDepth < cnt;              // block i + kDepth exists
     priority_by_blocks_left(i, cnt);  // waves that share a SIMD finish together
-    float s[kRows][8];
+    float s[kL][8];
     {
-      __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(kSPart<kBits>));  // K(i) in the slot
+      wait_parts<kBits>(1 + 2 * ahead);  // K(i) in the slot
       if (i == 0) phase_mark(kMarkFirstBlock);
       SPart<kBits> kp;
       read_part<kBits>(kp, slot, lane);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the K part has been read
-      if (more) dma_k<kBits>(slot, h, blk + kWaves, n, q);
+      if (more) dma_k<kBits>(slot, h, blk + kDepth * kWaves, n, q);
       block_scores<kBits, kRows>(kp, qsrc, p.qscale, s);
     }
     block_softmax<kRows>(s, t_end - (blk * kBlockTokens + 8 * q), m, z, u, live);
     {
-      if (more) __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(kSPart<kBits>));  // V(i) in the slot
-      else __builtin_amdgcn_s_waitcnt(KVQ_SVMCNT(0));
+      wait_parts<kBits>(2 * ahead + (more ? 1 : 0));  // V(i) in the slot
       SPart<kBits> vp;
       read_part<kBits>(vp, slot + 1024 * kSPart<kBits>, lane);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the V part has been read
-      if (more) dma_v<kBits>(slot, h, blk + kWaves, n, q);
-      block_values<kBits, kRows>(vp, s, u);
+      if (more) dma_v<kBits>(slot, h, blk + kDepth * kWaves, n, q);
+      float pr[kRows][8];  // p of every row for the lane's tokens
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        float pj[kL], pa[kRows];
+#pragma unroll
+        for (int j = 0; j < kL; ++j) pj[j] = s[j][t];
+        gather_rows<kRows>(pj, pa);
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) pr[r][t] = pa[r];
+      }
+      block_values<kBits, kRows>(vp, pr, u);
     }
   }
 
@@ -434,11 +551,11 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
 
   // ---- merge: the 4 token octets, then the waves through LDS ---------------
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    z[r] = qblock_sum(z[r]);
+  for (int j = 0; j < kL; ++j) z[j] = quad_sum(z[j]);
 #pragma unroll
-    for (int f = 0; f < 8; ++f) u[r][f] = qblock_sum(u[r][f]);
-  }
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int f = 0; f < 8; ++f) u[r][f] = quad_sum(u[r][f]);
   __syncthreads();  // every wave is done with its slot (aliased by the merge area)
   if (q == 0) {
 #pragma unroll
@@ -453,11 +570,12 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
       *reinterpret_cast<f32x4*>(&sm.u.wu[wave][r][8 * n + 4]) = b;
     }
   }
-  if (lane == 0) {
+  if ((lane & 15) == 0) {  // one lane per (bit 5, bit 4): rows (R/2) b5 + (R/4) b4 + j
+    const int r0 = (kRows / 2) * (lane >> 5) + (kRows / 4) * ((lane >> 4) & 1);
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      sm.wm[wave][r] = m[r];
-      sm.wz[wave][r] = z[r];
+    for (int j = 0; j < kL; ++j) {
+      sm.wm[wave][r0 + j] = m[j];
+      sm.wz[wave][r0 + j] = z[j];
     }
   }
   __syncthreads();
@@ -503,9 +621,10 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
 
 int phase_fetch_stream(void* host, size_t bytes) { return phase_fetch(host, bytes); }
 
-// Waves per workgroup: 8 (two per SIMD) up to 4 rows, where the kernel holds
-// 240 VGPRs; 4 for 8 rows (251-261 VGPRs: one or two workgroups per compute
-// unit).  The automatic split count aims at two waves per SIMD either way.
+// Waves per workgroup: 8 up to 4 rows (138-144 VGPRs), 4 for 8 rows (222-225
+// VGPRs, two workgroups per compute unit).  The automatic split count aims at
+// two waves per SIMD either way.  (8 waves for 8 rows measured the same at
+// the automatic split count; 12 waves up to 4 rows were slower.)
 static constexpr int waves_for(int rows) { return rows <= 4 ? 8 : 4; }
 
 int stream_waves(int bits, int rows) {

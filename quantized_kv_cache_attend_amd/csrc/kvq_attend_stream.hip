@@ -164,8 +164,9 @@ __device__ __forceinline__ void codes4(unsigned w, bool hi, float c[4]) {
 }
 
 // ---- cross-lane steps (lane = 4 n + q) -----------------------------------------
-// Reduce-scatter halves: lanes below 32 (bit 4 clear) get x summed with the
-// lane 32 (16) away, the others y summed likewise; one swap and one add.
+// Reduce-scatter halves, one swap and one add each: scatter32 gives the lanes
+// below 32 (bit 5 clear) x summed with the lane 32 away and the others y
+// summed likewise; scatter16 does the same across lanes 16 apart (bit 4).
 __device__ __forceinline__ float scatter32(float x, float y) {
   const auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(y), false, false);
   return as_f32(r[0]) + as_f32(r[1]);
@@ -435,10 +436,6 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
   const int b_first = b_begin + wave;
   const int cnt = b_first < b_end ? (b_end - 1 - b_first) / kWaves + 1 : 0;  // wave-uniform
 
-  // The query rows: in registers (loaded ahead of the first block, first
-  // used once it has landed) or, for 8 rows, in LDS (stored before any block
-  // copy is in flight, since an LDS store is ordered after every
-  // LDS-destination load issued before it).
   // The query rows (a descriptor over the head's `rows` rows reads zeros past
   // them).  Up to 4 rows each wave copies them into its own LDS area with
   // LDS-destination loads issued ahead of its first blocks, then reads its

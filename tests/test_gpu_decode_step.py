@@ -28,7 +28,8 @@ CASES = [
     (1, 4, 1, 1, 8, 32, 1, 29, 6),      # 8-bit, one split (no combine), across token 32
     (2, 4, 2, 1, 8, 32, 0, 60, 10),     # 8-bit, automatic splits
     (2, 8, 2, 2, 4, 32, 0, 60, 10),     # 8 rows per KV head: the 32-row kernel, two launches
-    (2, 8, 2, 1, 4, 8, 2, 60, 10),      # group 8: the general kernel, two launches
+    (2, 8, 2, 1, 4, 8, 2, 60, 10),      # group 8: append, then the streaming kernel (two launches)
+    (1, 8, 1, 1, 8, 16, 0, 5, 40),      # 8-bit group 16, 8 rows: the streaming kernel, auto splits
 ]
 
 

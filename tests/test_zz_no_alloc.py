@@ -35,13 +35,15 @@ def _noalloc(qd, cache, w, bits, group, splits, out):
 
 # (workload, bits, group, splits): the 8 x 4096-token cache, then smaller
 # calls (fewer (batch, KV head) pairs: their partials overwrite counters of the
-# larger one), a 32-row GQA shape, the general kernel, and the large one again.
+# larger one), a 32-row GQA shape, the general kernel, the streaming kernel
+# (group 8, automatic splits), and the large one again.
 SEQUENCE = [
     (WORKLOADS["gqa_n4096"], 4, 32, 0),
     (Workload("small", 1, 4, 1, 1, 1000, 128, ((4, 32),)), 4, 32, 3),
     (Workload("rows32", 2, 16, 2, 4, 3000, 128, ((4, 32),)), 4, 32, 0),
     (Workload("valu", 1, 4, 2, 2, 700, 32, ((4, 8),)), 4, 8, 5),
     (Workload("r4_8bit", 4, 8, 4, 1, 2000, 128, ((8, 32),)), 8, 32, 4),
+    (Workload("stream", 2, 8, 2, 1, 1500, 128, ((4, 8),)), 4, 8, 0),
     (WORKLOADS["gqa_n4096"], 4, 32, 8),
 ]
 

@@ -60,7 +60,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_mfma_gqa_n4096_traffic.md"
 # The sources the measured kernel is compiled from (its file, the shared header
 # and the build script with its flags).
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_kv_cache_attend_amd", "csrc", f)
-                  for f in ("kvq_attend_mfma.hip", "kvq_mfma_common.h")] + [
+                  for f in ("kvq_attend_mfma.hip", "kvq_mfma_common.h", "kvq_internal.h")] + [
                       os.path.join(ROOT, "quantized_kv_cache_attend_amd", "build.py")]
 
 

@@ -186,6 +186,7 @@ kvq_status check_attend(const float* q, const void* k, const void* ks, const voi
   const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(static_cast<float>(D));
   p->qscale = scale * kLog2e;
   p->splits = splits;
+  p->spw = 1;
   p->tokens_per_split =
       static_cast<int>(round_up((static_cast<long long>(N) + splits - 1) / splits, kBlockTokens));
   p->codes_aligned = bits != 32 && aligned(k, 4) && aligned(v, 4);
@@ -245,11 +246,27 @@ int mfma32_auto_splits(int B, int Hkv, int N) {
   return static_cast<int>(s < general ? s : general);
 }
 
+// Splits per workgroup of the 32-row kernel: when a head's splits would need
+// more than one round of its 4-wave workgroups (512: two per compute unit),
+// each workgroup takes several consecutive splits of its head, one after
+// another, writing each split's partial as before; the query rows are staged
+// once and the rounds' start-up and tail are paid once.  Not with window
+// parts, and only where that instantiation keeps its registers (the 2-tile
+// 8-bit and 2-tile causal 4-bit forms would spill and are not compiled).
+int mfma32_splits_per_wg(const AttendProblem& p) {
+  const bool fits = p.rows <= 16 || (p.bits == 4 && !p.causal);
+  if (p.win_parts > 0 || !fits) return 1;
+  const long long wgs = static_cast<long long>(p.B) * p.Hkv * p.splits;
+  const long long per = (wgs + 511) / 512;
+  return static_cast<int>(per < p.splits ? per : p.splits);
+}
+
 hipError_t run_mfma(AttendProblem p, bool auto_split, hipStream_t s) {
   const bool wide = p.rows > kMfmaMaxRows;
   if (auto_split)
     p.splits = wide ? mfma32_auto_splits(p.B, p.Hkv, p.N) : mfma_auto_splits(p.B, p.Hkv, p.N);
   p.tokens_per_split = mfma_tokens_per_split(p.N, p.splits);
+  if (wide) p.spw = mfma32_splits_per_wg(p);
   return wide ? launch_attend_mfma32(p, s) : launch_attend_mfma(p, s);
 }
 

@@ -62,6 +62,7 @@ struct AttendProblem {
   float* k_scales_w;
   uint8_t* v_codes_w;
   float* v_scales_w;
+  int spw;                 // splits per workgroup (32-row kernel; 1 in every other kernel)
 };
 
 // Append flag of a KV head: word 32 of the head's counter slot (its own
@@ -80,10 +81,13 @@ constexpr int kCounterStride = 64;
 // output is written as NaN by every workgroup that sees it, and its counter
 // is left non-zero, so the failure shows in this call and in every later one
 // until the workspace is zero-filled again.
+// A workgroup that completes `arrivals` splits at once (one fetch-add of
+// `arrivals`) is the last when its ticket reaches `splits` exactly.
 constexpr int kTicketWait = 0, kTicketMerge = 1, kTicketStale = 2;
-__host__ __device__ inline int ticket_outcome(unsigned prev, int splits) {
+__host__ __device__ inline int ticket_outcome(unsigned prev, int splits, int arrivals = 1) {
   const unsigned s = static_cast<unsigned>(splits);
-  return prev == s - 1 ? kTicketMerge : (prev >= s ? kTicketStale : kTicketWait);
+  const unsigned a = static_cast<unsigned>(arrivals);  // 1 <= arrivals <= splits
+  return prev == s - a ? kTicketMerge : (prev >= s - a + 1 ? kTicketStale : kTicketWait);
 }
 
 // Workspace carving, shared by the sizing call and the launchers.

@@ -324,13 +324,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t split_rows(const AttendProblem
 // merged partial U / M / Z; the thread with f0 == 0 also owns the row's m and
 // z.  last: an int of LDS.  Every thread of the workgroup calls this (it
 // holds barriers).
+// split_store writes one split's partial rows (no wait); split_ticket_merge
+// waits for every partial store of the workgroup, takes its ticket for
+// `arrivals` splits and, if it is the last, merges.  split_combine is the two
+// for one split.
+// A thread's row of the combine: it takes part (mine) when r < p.rows; row
+// is the row's index among all B * Hkv * rows query rows.
+struct SplitRow {
+  bool mine;
+  long long total_rows, row;
+};
+__device__ __forceinline__ SplitRow split_row(const AttendProblem& p, long long head, int r) {
+  return {r < p.rows, static_cast<long long>(p.B) * p.Hkv * p.rows, head * p.rows + r};
+}
+
 template <int kF, int kRun, int kStride>
-__device__ __forceinline__ void split_combine(const AttendProblem& p, int split, long long head,
-                                              int r, int f0, const float (&U)[kF], float M,
-                                              float Z, int* last) {
-  const bool mine = r < p.rows;
-  const long long total_rows = static_cast<long long>(p.B) * p.Hkv * p.rows;
-  const long long row = head * p.rows + r;
+__device__ __forceinline__ void split_store(const AttendProblem& p, int split, long long head,
+                                            int r, int f0, const float (&U)[kF], float M,
+                                            float Z, const SplitRow& sr) {
+  const bool mine = sr.mine;
+  const long long total_rows = sr.total_rows;
+  const long long row = sr.row;
   if (mine) {
     const long long pr = static_cast<long long>(split) * total_rows + row;
     if constexpr (kRun % 4 == 0) {
@@ -355,14 +369,23 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
       __hip_atomic_store(&p.part_z[pr], Z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores above are acknowledged
+}
+
+template <int kF, int kRun, int kStride>
+__device__ __forceinline__ void split_ticket_merge(const AttendProblem& p, long long head, int r,
+                                                   int f0, int arrivals, int* last,
+                                                   const SplitRow& sr) {
+  const bool mine = sr.mine;
+  const long long total_rows = sr.total_rows;
+  const long long row = sr.row;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial stores are acknowledged
   phase_mark(kMarkAcked);
   __syncthreads();
   unsigned* counter = &p.counters[head * kCounterStride];
   if (threadIdx.x == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    *last = ticket_outcome(prev, p.splits);
+    const unsigned prev = __hip_atomic_fetch_add(counter, static_cast<unsigned>(arrivals),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last = ticket_outcome(prev, p.splits, arrivals);
   }
   __syncthreads();
   phase_mark(kMarkTicket);
@@ -436,6 +459,15 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int kF, int kRun, int kStride>
+__device__ __forceinline__ void split_combine(const AttendProblem& p, int split, long long head,
+                                              int r, int f0, const float (&U)[kF], float M,
+                                              float Z, int* last) {
+  const SplitRow sr = split_row(p, head, r);
+  split_store<kF, kRun, kStride>(p, split, head, r, f0, U, M, Z, sr);
+  split_ticket_merge<kF, kRun, kStride>(p, head, r, f0, 1, last, sr);
 }
 
 // ---- recent-token window parts -------------------------------------------------

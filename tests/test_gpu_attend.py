@@ -307,6 +307,40 @@ def test_attend_mfma32_peaky_and_channel_scaled(dist, scale_k):
         assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
 
 
+# (B, Hq, Hkv, R, N, bits, causal, splits): KV heads x splits above 512, so
+# each workgroup of the 32-row kernel attends ceil(heads x splits / 512)
+# consecutive splits of its head.  The split counts leave a shorter last run,
+# and splits past the last token hold no key.
+MULTI_SPLIT = [
+    (2, 8, 1, 4, 5000, 4, False, 700),     # 32 rows (2 tiles), 3 per workgroup, last run 1
+    (1, 12, 1, 1, 4097, 8, False, 1030),   # 8-bit, 12 rows, 3 per workgroup
+    (3, 16, 2, 1, 3001, 4, False, 302),    # 8 rows, 6 heads, 4 per workgroup, last run 2
+    (2, 4, 1, 4, 2100, 4, True, 601),      # causal, 16 rows
+    (2, 32, 1, 1, 20000, 4, False, 301),   # 2 per workgroup, 3 blocks per split
+]
+
+
+@pytest.mark.parametrize("shape", MULTI_SPLIT,
+                         ids=["B{}-Hq{}-Hkv{}-R{}-N{}-{}b-causal{}-s{}".format(*c)
+                              for c in MULTI_SPLIT])
+def test_attend_mfma32_several_splits_per_workgroup(shape):
+    B, hq, hkv, r, n, bits, causal, splits = shape
+    w = Workload("multi_split", B, hq, hkv, r, n, 128, ((bits, 32),))
+    q, k, v = make_qkv(w, 9)
+    announce(f"attend mfma32 several splits per workgroup {shape}")
+    kc, ks, vc, vs = oracle_pack(k, v, bits, 32)
+    want = O.attend_packed(q, kc, ks, vc, vs, n, bits, 32, causal=causal)
+    cache = _gpu_cache(k, v, bits, 32)
+    got = _run(q, cache, n, bits, 32, num_splits=splits, variant="mfma", causal=causal)
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= TOL, max_abs(got, want)
+    if causal:
+        empty = O.causal_mask(n, r).sum(axis=1) == 0
+        assert (got[:, :, empty] == 0).all()
+    one = _run(q, cache, n, bits, 32, num_splits=1, variant="mfma", causal=causal)
+    assert max_abs(got, one) <= SPLIT_TOL
+
+
 @pytest.mark.parametrize("hq,r", [(4, 1), (16, 2)])
 def test_attend_mfma_large_k_scales(hq, r):
     """K magnitudes large enough that K scales reach 32 (the 32-row kernel

@@ -246,19 +246,25 @@ int mfma32_auto_splits(int B, int Hkv, int N) {
   return static_cast<int>(s < general ? s : general);
 }
 
-// Splits per workgroup of the 32-row kernel: when a head's splits would need
-// more than one round of its 4-wave workgroups (512: two per compute unit),
-// each workgroup takes several consecutive splits of its head, one after
-// another, writing each split's partial as before; the query rows are staged
-// once and the rounds' start-up and tail are paid once.  Not with window
-// parts, and only where that instantiation keeps its registers (the 2-tile
-// 8-bit and 2-tile causal 4-bit forms would spill and are not compiled).
+// Splits per workgroup of the 32-row kernel.  When a head's splits would
+// fill at least 4 rounds of its 4-wave workgroups (512 a round: two per
+// compute unit), each workgroup takes a run of consecutive splits of its head
+// and each wave attends whole splits of that run (a multiple of 4 splits, so
+// the waves get equal shares), storing each split's partial as before; the
+// rounds' start-up and tail are paid once and no split needs a merge of its
+// waves.  With fewer, one split per workgroup.  Not with window parts or the
+// causal rule, nor for 8-bit codes with more than 16 rows (that form would
+// spill and is not compiled).
 int mfma32_splits_per_wg(const AttendProblem& p) {
-  const bool fits = p.rows <= 16 || (p.bits == 4 && !p.causal);
-  if (p.win_parts > 0 || !fits) return 1;
+  constexpr int kWaves = 4;
+  const bool fits = !p.causal && (p.rows <= 16 || p.bits == 4);
+  if (p.win_parts > 0 || !fits || p.splits < kWaves) return 1;
   const long long wgs = static_cast<long long>(p.B) * p.Hkv * p.splits;
   const long long per = (wgs + 511) / 512;
-  return static_cast<int>(per < p.splits ? per : p.splits);
+  if (per < kWaves) return 1;
+  const long long spw = (per + kWaves - 1) / kWaves * kWaves;
+  const long long all = (static_cast<long long>(p.splits) + kWaves - 1) / kWaves * kWaves;
+  return static_cast<int>(spw < all ? spw : all);
 }
 
 hipError_t run_mfma(AttendProblem p, bool auto_split, hipStream_t s) {

@@ -69,10 +69,9 @@ constexpr int kQTop = 10;        // q rows prescaled to max |.| in [2^9, 2^10)
 constexpr int kKTop = 5;         // K prescale: max K scale * kf in [2^4, 2^5),
 constexpr int kKLow = 2;         //   kept while it stays in [2^2, 2^5)
 
-template <bool kMulti>
 struct alignas(16) Smem32 {
   union {
-    float qs[kR][kQStride];      // q * qscale * 2^Sq(row) (single split)
+    float qs[kR][kQStride];      // q * qscale * 2^Sq(row)
     float wu[2][kR][kD];         // u of two waves at a time, for the merge
     WinSmem<kR> win;             // a recent-token window part
   } u;
@@ -93,12 +92,6 @@ struct alignas(16) Smem32 {
   float wm[kW][kR];
   float wz[kW][kR];
   int last;
-  // kMulti (several splits per workgroup): the query rows outlive each
-  // split's merge, so they get an area of their own (last, so that the
-  // members above keep their offsets and 16-byte alignment either way);
-  // otherwise they share the merge's.
-  alignas(16) float qsep[kMulti ? kR : 1][kMulti ? kQStride : 1];
-  __device__ __forceinline__ float* qrow(int r) { return kMulti ? qsep[r] : u.qs[r]; }
 };
 
 template <int kBits>
@@ -251,8 +244,8 @@ __device__ __forceinline__ void scaled_q(half8_t qh, half8_t ql, half8_t sh, hal
 // score row 16t + n, the tokens after its query's position lim[t], and keep
 // rows that have seen no legal key at m = -inf (exponents then taken
 // against 0, so (-inf) - (-inf) is never formed).
-template <int kBits, int kTiles, bool kMasked, bool kCausal, typename SM>
-__device__ __forceinline__ void attend_block32(SM& sm, Regs32<kBits>& br, int tok0, int t_end,
+template <int kBits, int kTiles, bool kMasked, bool kCausal>
+__device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, int tok0, int t_end,
                                                const typename CodeOps<kBits>::consts& cc,
                                                State32& st,
                                                const Head32& h, int next, const Lanes32& lo,
@@ -497,6 +490,71 @@ __device__ __forceinline__ void attend_block32(SM& sm, Regs32<kBits>& br, int to
   }
 }
 
+// Several splits per workgroup (kMulti; no causal rule, no window parts).
+// Workgroup g of a head takes splits [s0, s1) = [g spw, min(splits, (g + 1)
+// spw)); wave w attends splits s0 + w, s0 + w + kW, ... below s1, each one
+// whole: its blocks in order (the block holding token N-1 first when N is not
+// a multiple of 32: the only masked block without the causal rule).  The
+// wave's running (m, z, u) goes on from one of its splits to the next (the
+// online merge of their partials); the workgroup then merges its waves as
+// for one split and stores one partial, in slot g.  The last arriver merges
+// the head's ceil(splits / spw) partials: a two-level combine, with a
+// quarter of the partial rows of one partial per split or fewer.
+struct WaveSplit {
+  int t_end;
+  bool active;                    // the split holds a token
+  int first;                      // attended first (masked if needed)
+  int loop_begin, loop_end;       // then these, in order (inclusive)
+};
+__device__ __forceinline__ WaveSplit wave_split(const AttendProblem& p, int split) {
+  WaveSplit s;
+  const int t_begin = split * p.tokens_per_split;
+  s.t_end = min(p.N, t_begin + p.tokens_per_split);
+  s.active = s.t_end > t_begin;
+  const int b_begin = t_begin / kBlockTokens;
+  const int b_last = (s.t_end - 1) / kBlockTokens;  // valid if active
+  const bool partial = (p.N % kBlockTokens) != 0 && b_last == (p.N - 1) / kBlockTokens;
+  s.first = partial ? b_last : b_begin;
+  s.loop_begin = partial ? b_begin : b_begin + 1;
+  s.loop_end = partial ? b_last - 1 : b_last;
+  return s;
+}
+
+// The wave's splits s, s + kW, ... below s_end into st; br holds split s's
+// first block (loaded by the caller when that split is active).
+template <int kBits, int kTiles>
+__device__ __forceinline__ void attend_wave_splits(
+    const AttendProblem& p, Smem32& sm, Regs32<kBits>& br, const Head32& h, const Lanes32& lo,
+    const typename CodeOps<kBits>::consts& cc, State32& st, const float (&us_row)[2],
+    const half8_t (&qh)[2][4], const half8_t (&ql)[2][4], const int (&lim)[2], int s,
+    int s_end) {
+  WaveSplit sp = wave_split(p, s);
+  for (; s < s_end; s += kW) {
+    // The block loaded after this split's last one: the wave's next split's first.
+    WaveSplit nx = sp;
+    int tail_next = -1;
+    if (s + kW < s_end) {
+      nx = wave_split(p, s + kW);
+      if (nx.active) tail_next = nx.first;
+    }
+    if (sp.active) {
+      const bool loop = sp.loop_begin <= sp.loop_end;
+      attend_block32<kBits, kTiles, true, false>(
+          sm, br, sp.first * kBlockTokens, sp.t_end, cc, st, h,
+          loop ? sp.loop_begin : (tail_next >= 0 ? tail_next : sp.first), lo, us_row, qh, ql,
+          lim);
+      for (int b = sp.loop_begin; b <= sp.loop_end; ++b)
+        attend_block32<kBits, kTiles, false, false>(
+            sm, br, b * kBlockTokens, sp.t_end, cc, st, h,
+            b < sp.loop_end ? b + 1 : (tail_next >= 0 ? tail_next : b), lo, us_row, qh, ql,
+            lim);
+    } else if (tail_next >= 0) {
+      load_block32(br, h, tail_next, lo);
+    }
+    sp = nx;
+  }
+}
+
 // kTiles: 16-row tiles of query rows (1 for up to 16 rows per KV head, 2
 // for up to 32).  kCausal: a causal chunk (row r is query r % R at position pos_end - R +
 // r % R).  Only tokens past pos_end - R can be masked; they lie in at most
@@ -508,42 +566,13 @@ __device__ __forceinline__ void attend_block32(SM& sm, Regs32<kBits>& br, int to
 // kWindow: the last p.win_parts workgroups of each head attend recent-token
 // window parts (a separate instantiation, so the plain kernel's block loop is
 // compiled without that path).
-// One split's blocks for wave `wave`: b_first + i kW up to the split's end.
-// The block holding token N-1 is masked when N is not a multiple of 32 (and,
-// causal, a block past position pos_end - R); the wave that owns it attends
-// it first, then the rest in order.
-struct SplitPlan {
-  int t_end;
-  bool active;                    // the wave has a block in this split
-  int first;                      // attended first (masked if needed)
-  int loop_begin, loop_end;       // then these, kW apart (inclusive)
-};
-template <bool kCausal>
-__device__ __forceinline__ SplitPlan plan_split(const AttendProblem& p, int split, int wave) {
-  SplitPlan s;
-  const int t_begin = split * p.tokens_per_split;
-  s.t_end = min(p.N, t_begin + p.tokens_per_split);
-  const int b_begin = t_begin / kBlockTokens;
-  const int b_end = s.t_end > t_begin ? (s.t_end + kBlockTokens - 1) / kBlockTokens : b_begin;
-  const int b_first = b_begin + wave;
-  const int b_last = b_first + (b_end - 1 - b_first) / kW * kW;  // valid if b_first < b_end
-  s.active = b_first < b_end;
-  const bool partial = ((p.N % kBlockTokens) != 0 && b_last == (p.N - 1) / kBlockTokens) ||
-                       (kCausal && (b_last + 1) * kBlockTokens - 1 > p.pos_end - p.R);
-  s.first = partial ? b_last : b_first;
-  s.loop_begin = partial ? b_first : b_first + kW;
-  s.loop_end = partial ? b_last - kW : b_last;
-  return s;
-}
-
-// kMulti: the workgroup attends p.spw consecutive splits of its head, one
-// after another, each with its own partial rows, and takes one ticket for
-// all of them (a separate instantiation: the loop over splits costs up to
-// ten more VGPRs, and p.spw = 1 needs none of it).
+// kMulti: the workgroup takes p.spw consecutive splits of its head, whole
+// splits per wave (attend_wave_splits), stores one partial for all of them
+// and takes one ticket for them.
 template <int kBits, int kTiles, bool kCausal, bool kWindow, bool kMulti>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 attend_mfma_r32_kernel(AttendProblem p) {
-  __shared__ Smem32<kMulti> sm;
+  __shared__ Smem32 sm;
   phase_mark(kMarkStart);
 
   const int tid = threadIdx.x;
@@ -552,25 +581,24 @@ attend_mfma_r32_kernel(AttendProblem p) {
   const int n = lane & 15;
   const int q = lane >> 4;
 
-  // Workgroup -> (KV head, its run of p.spw consecutive splits); all of a
-  // head's workgroups on one XCD when the head count allows (workgroups are
+  // Workgroup -> (KV head, split); with kMulti, `split` is the workgroup's
+  // index g in its head, and its run is splits [g spw, (g + 1) spw).  All of
+  // a head's workgroups on one XCD when the head count allows (workgroups are
   // dealt to the 8 XCDs round-robin).
   const int heads = p.B * p.Hkv;
-  const int spw = kMulti ? p.spw : 1;
-  const int wph = (p.splits + spw - 1) / spw;  // workgroups per head
+  const int wph = kMulti ? (p.splits + p.spw - 1) / p.spw : p.splits;  // workgroups per head
   const int L = blockIdx.x;
-  int head, g;
+  int head, split;
   if (heads % 8 == 0) {
     const int slot = L >> 3;
     head = (L & 7) + 8 * (slot / wph);
-    g = slot % wph;
+    split = slot % wph;
   } else {
     head = L / wph;
-    g = L % wph;
+    split = L % wph;
   }
-  const int s_first = g * spw;
-  const int s_count = kMulti ? min(spw, p.splits - s_first) : 1;
-  const int split = s_first;  // window parts run one split per workgroup
+  const int s_first = kMulti ? split * p.spw : split;
+  const int s_end = kMulti ? min(p.splits, s_first + p.spw) : split + 1;
   const long long bh = head;
   const int rows = p.rows;
   const int packed_splits = p.splits - p.win_parts;
@@ -591,6 +619,12 @@ attend_mfma_r32_kernel(AttendProblem p) {
                    static_cast<long long>(nblocks) * kBB<kBits>);
   h.vsc = head_rsrc(p.v_scales + bh * nblocks * kBS, static_cast<long long>(nblocks) * kBS * 4);
 
+  const int t_begin = split * p.tokens_per_split;
+  const int t_end = min(p.N, t_begin + p.tokens_per_split);
+  const int b_begin = t_begin / kBlockTokens;
+  const int b_end = t_end > t_begin ? (t_end + kBlockTokens - 1) / kBlockTokens : b_begin;
+  const int b_first = b_begin + wave;
+  const int b_last = b_first + (b_end - 1 - b_first) / kW * kW;  // valid if b_first < b_end
   // Code bytes of lane (n, q): K channels 32 ks + 8q .. +7 of tokens 2n, 2n + 1;
   // V tokens 8q .. 8q+7 of features 32 g + 2n, +1 (2 * kBits bytes each).
   // Scales: the k-slot pair (2j, 2j + 1) of run (lane / 16, lane / 4 % 4),
@@ -601,12 +635,24 @@ attend_mfma_r32_kernel(AttendProblem p) {
                       static_cast<unsigned>(4 * (8 * (lane >> 2) + (sj & 1) + 4 * (sj >> 1))),
                       static_cast<unsigned>(lane * 8)};
 
-  // The first block of each of the workgroup's splits goes out before the
-  // previous split's last block is attended (the first split's before the
-  // query rows are staged).
+  // The block holding token N-1 is masked when N is not a multiple of 32;
+  // the wave that owns it attends it first.  Its loads go out before the
+  // query rows are staged.
+  const bool active = b_first < b_end;
+  const bool partial = ((p.N % kBlockTokens) != 0 && b_last == (p.N - 1) / kBlockTokens) ||
+                       (kCausal && (b_last + 1) * kBlockTokens - 1 > p.pos_end - p.R);
+  const int first = partial ? b_last : b_first;
+  const int loop_begin = partial ? b_first : b_first + kW;
+  const int loop_end = partial ? b_last - kW : b_last;  // inclusive
   Regs32<kBits> br;
-  const SplitPlan sp0 = plan_split<kCausal>(p, s_first, wave);
-  if (sp0.active) load_block32(br, h, sp0.first, lo);
+  if constexpr (kMulti) {
+    if (s_first + wave < s_end) {
+      const WaveSplit w0 = wave_split(p, s_first + wave);
+      if (w0.active) load_block32(br, h, w0.first, lo);
+    }
+  } else if (active) {
+    load_block32(br, h, first, lo);
+  }
 
   // q * qscale into LDS, each row prescaled by 2^Sq so its largest element
   // lies in [2^9, 2^10): thread -> (row tid >> 3, channels 16 (tid & 7) ..
@@ -637,164 +683,153 @@ attend_mfma_r32_kernel(AttendProblem p) {
       f32x4 a;
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[j] = __builtin_ldexpf(v[4 * i + j], sq);
-      *reinterpret_cast<f32x4*>(sm.qrow(r) + c0 + 4 * i) = a;
+      *reinterpret_cast<f32x4*>(&sm.u.qs[r][c0 + 4 * i]) = a;
     }
     if ((tid & 7) == 0) sm.qus[r] = __builtin_ldexpf(1.0f, -sq);
   }
   __syncthreads();
   const float us_row[2] = {sm.qus[n], kTiles > 1 ? sm.qus[16 + n] : 1.0f};
+  // This lane's q values for the whole kernel (rows 16t + n, channels
+  // 32 ks + 8q + (0..7), k-slot order) as fp16 hi (toward zero) and lo of the
+  // float32 remainder, kept in registers.
+  half8_t qh[2][4], ql[2][4];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float* qrow = &sm.u.qs[16 * t + n][ks * 32 + q * 8];
+      const f32x4 qa = *reinterpret_cast<const f32x4*>(qrow);
+      const f32x4 qb = *reinterpret_cast<const f32x4*>(qrow + 4);
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = j < 4 ? qa[kSlotByte[j]] : qb[kSlotByte[j] - 4];
+      split_hilo(x, qh[t][ks], ql[t][ks]);
+    }
+
   phase_mark(kMarkQReady);
   const typename CodeOps<kBits>::consts cc = CodeOps<kBits>::make();
+  State32 st;
+  st.m[0] = st.m[1] = -INFINITY;
+  st.z[0] = st.z[1] = 0.0f;
+  st.sv = 0;
+  st.vscale = 1.0f;
+  st.vhi = st.vlo = 0.0f;
+  st.kf = st.kun = 1.0f;
+  st.khi = st.klo = 0.0f;
+  st.live = false;
+  {
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) st.acc[g][t][0] = st.acc[g][t][1] = zero4;
+  }
+
   // Causal limit of this lane's score rows 16t + n.
   const int lim[2] = {p.pos_end - p.R + n % p.R, p.pos_end - p.R + (16 + n) % p.R};
-  half8_t qh[2][4], ql[2][4];
+  if constexpr (kMulti) {
+    attend_wave_splits<kBits, kTiles>(p, sm, br, h, lo, cc, st, us_row, qh, ql, lim,
+                                      s_first + wave, s_end);
+  } else if (active) {
+    attend_block32<kBits, kTiles, true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
+                                  loop_begin <= loop_end ? loop_begin : first, lo, us_row, qh,
+                                  ql, lim);
+    for (int b = loop_begin; b <= loop_end; b += kW)
+      attend_block32<kBits, kTiles, false, false>(sm, br, b * kBlockTokens, t_end, cc, st, h,
+                                   min(b + kW, loop_end), lo, us_row, qh, ql, lim);
+  }
+  phase_mark(kMarkLoopEnd);
+  st.z[0] = qblock_sum(st.z[0]);
+  if (kTiles > 1) st.z[1] = qblock_sum(st.z[1]);
 
-  // The workgroup's splits one after another, each with its own (m, z, u)
-  // from a fresh state and its own partial rows in the workspace.
-  SplitPlan sp = sp0;
-  for (int si = 0; si < s_count; ++si) {
-    const int split_i = s_first + si;
-    int tail_next = -1;  // the block loaded after this split's last one: the next split's first
-    if (si + 1 < s_count) {
-      const SplitPlan nx = plan_split<kCausal>(p, split_i + 1, wave);
-      if (nx.active) tail_next = nx.first;
-    }
-    if (kMulti || si == 0) {
-      // This lane's q values (rows 16t + n, channels 32 ks + 8q + (0..7),
-      // k-slot order) as fp16 hi (toward zero) and lo of the float32
-      // remainder, from the LDS rows; rebuilt per split with kMulti, so that
-      // they are not held through the merges.
+  // ---- merge the waves: two at a time through LDS -------------------------
+  // thread -> (row r = tid >> 3, features f0 + 32 i + (0..3), f0 = 4 (tid & 7))
+  const int r = tid >> 3;
+  const int f0 = (tid & 7) * 4;
+  const float fu = __builtin_ldexpf(1.0f, -st.sv);
+  __syncthreads();  // every wave is done with q (aliased by wu)
+  if (q == 0) {
+    sm.wm[wave][n] = st.m[0];
+    sm.wm[wave][16 + n] = kTiles > 1 ? st.m[1] : -INFINITY;  // rows 16..31: none with one tile
+    sm.wz[wave][n] = st.z[0];
+    sm.wz[wave][16 + n] = kTiles > 1 ? st.z[1] : 0.0f;
+  }
+  float M = -INFINITY, Z = 0.0f;
+  float U[16];
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t)
+  for (int i = 0; i < 16; ++i) U[i] = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const float* qrow = sm.qrow(16 * t + n) + ks * 32 + q * 8;
-          const f32x4 qa = *reinterpret_cast<const f32x4*>(qrow);
-          const f32x4 qb = *reinterpret_cast<const f32x4*>(qrow + 4);
-          float x[8];
+  for (int half = 0; half < 2; ++half) {
+    if ((wave >> 1) == half) {  // waves 2 half, 2 half + 1 park their u
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = j < 4 ? qa[kSlotByte[j]] : qb[kSlotByte[j] - 4];
-          split_hilo(x, qh[t][ks], ql[t][ks]);
-        }
-    }
-    State32 st;
-    st.m[0] = st.m[1] = -INFINITY;
-    st.z[0] = st.z[1] = 0.0f;
-    st.sv = 0;
-    st.vscale = 1.0f;
-    st.vhi = st.vlo = 0.0f;
-    st.kf = st.kun = 1.0f;
-    st.khi = st.klo = 0.0f;
-    st.live = false;
-    {
-      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) st.acc[gg][t][0] = st.acc[gg][t][1] = zero4;
-    }
-    if (sp.active) {
-      const bool loop = sp.loop_begin <= sp.loop_end;
-      attend_block32<kBits, kTiles, true, kCausal>(
-          sm, br, sp.first * kBlockTokens, sp.t_end, cc, st, h,
-          loop ? sp.loop_begin : (tail_next >= 0 ? tail_next : sp.first), lo, us_row, qh, ql,
-          lim);
-      for (int b = sp.loop_begin; b <= sp.loop_end; b += kW) {
-        const int next = b + kW <= sp.loop_end ? b + kW : (tail_next >= 0 ? tail_next : b);
-        attend_block32<kBits, kTiles, false, false>(sm, br, b * kBlockTokens, sp.t_end, cc, st,
-                                                    h, next, lo, us_row, qh, ql, lim);
-      }
-    } else if (tail_next >= 0) {
-      load_block32(br, h, tail_next, lo);
-    }
-    phase_mark(kMarkLoopEnd);
-    st.z[0] = qblock_sum(st.z[0]);
-    if (kTiles > 1) st.z[1] = qblock_sum(st.z[1]);
-
-    // ---- merge the waves: two at a time through LDS -----------------------
-    // thread -> (row r = tid >> 3, features f0 + 32 i + (0..3), f0 = 4 (tid & 7))
-    const int r = tid >> 3;
-    const int f0 = (tid & 7) * 4;
-    const float fu = __builtin_ldexpf(1.0f, -st.sv);
-    __syncthreads();  // every wave is done with q (single split: aliased by wu) and the previous merge
-    if (q == 0) {
-      sm.wm[wave][n] = st.m[0];
-      sm.wm[wave][16 + n] = kTiles > 1 ? st.m[1] : -INFINITY;  // rows 16..31: none with one tile
-      sm.wz[wave][n] = st.z[0];
-      sm.wz[wave][16 + n] = kTiles > 1 ? st.z[1] : 0.0f;
-    }
-    float M = -INFINITY, Z = 0.0f;
-    float U[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) U[i] = 0.0f;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if ((wave >> 1) == half) {  // waves 2 half, 2 half + 1 park their u
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-          for (int t = 0; t < kTiles; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float2 u2;
-              u2.x = st.acc[gg][t][0][i] * fu;
-              u2.y = st.acc[gg][t][1][i] * fu;
-              *reinterpret_cast<float2*>(
-                  &sm.u.wu[wave & 1][16 * t + 4 * q + i][32 * gg + 2 * n]) = u2;
-            }
-      }
-      __syncthreads();
-      if (half == 0) {
-#pragma unroll
-        for (int w = 0; w < kW; ++w) M = fmaxf(M, sm.wm[w][r]);
-      }
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w2 = 0; w2 < 2; ++w2) {
-          const float mw = sm.wm[2 * half + w2][r];
-          if (mw == -INFINITY) continue;
-          const float e = fast_exp2(mw - M);
-          Z = fmaf(e, sm.wz[2 * half + w2][r], Z);
+        for (int t = 0; t < kTiles; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.u.wu[w2][r][f0 + 32 * i]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) U[4 * i + j] = fmaf(e, a[j], U[4 * i + j]);
+            float2 u2;
+            u2.x = st.acc[g][t][0][i] * fu;
+            u2.y = st.acc[g][t][1][i] * fu;
+            *reinterpret_cast<float2*>(
+                &sm.u.wu[wave & 1][16 * t + 4 * q + i][32 * g + 2 * n]) = u2;
           }
-        }
-      }
-      if (half == 0) __syncthreads();  // the first pair is read before the second overwrites it
     }
-    phase_mark(kMarkMerged);
-    if (p.splits == 1) {
-      const long long row0 = bh * rows;
-      if (r < rows) {
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) M = fmaxf(M, sm.wm[w][r]);
+    }
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) {
+        const float mw = sm.wm[2 * half + w2][r];
+        if (mw == -INFINITY) continue;
+        const float e = fast_exp2(mw - M);
+        Z = fmaf(e, sm.wz[2 * half + w2][r], Z);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f32x4 o;
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.u.wu[w2][r][f0 + 32 * i]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = Z > 0.0f ? U[4 * i + j] / Z : 0.0f;  // Z = 0: no key
-          *reinterpret_cast<f32x4*>(&p.out[(row0 + r) * kD + f0 + 32 * i]) = o;
+          for (int j = 0; j < 4; ++j) U[4 * i + j] = fmaf(e, a[j], U[4 * i + j]);
         }
       }
-      phase_mark(kMarkEnd);
-      return;
     }
-    split_store<16, 4, 32>(p, split_i, bh, r, f0, U, M, Z, split_row(p, bh, r));
-    if (si + 1 < s_count) sp = plan_split<kCausal>(p, split_i + 1, wave);
+    if (half == 0) __syncthreads();  // the first pair is read before the second overwrites it
   }
-  split_ticket_merge<16, 4, 32>(p, bh, tid >> 3, (tid & 7) * 4, s_count, &sm.last,
-                                split_row(p, bh, tid >> 3));
+  phase_mark(kMarkMerged);
+  const long long row0 = bh * rows;
+  if (p.splits == 1) {
+    if (r < rows) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = Z > 0.0f ? U[4 * i + j] / Z : 0.0f;  // Z = 0: no key
+        *reinterpret_cast<f32x4*>(&p.out[(row0 + r) * kD + f0 + 32 * i]) = o;
+      }
+    }
+    phase_mark(kMarkEnd);
+    return;
+  }
+
+  if constexpr (kMulti) {  // slot `split` (the workgroup's index in its head)
+    const SplitRow sr = split_row(p, bh, r);
+    split_store<16, 4, 32>(p, split, bh, r, f0, U, M, Z, sr);
+    split_ticket_merge<16, 4, 32>(p, bh, r, f0, s_end - s_first, &sm.last, sr, wph);
+  } else {
+    split_combine<16, 4, 32>(p, split, bh, r, f0, U, M, Z, &sm.last);
+  }
   phase_mark(kMarkEnd);
 }
 
 }  // namespace
 
-// Several splits per workgroup only in the instantiations that keep their
-// registers: one tile, or two tiles of 4-bit codes without the causal rule
-// (the others are not compiled; mfma32_splits_per_wg keeps spw = 1 there).
+// Several splits per workgroup (whole splits per wave): not with the causal
+// rule (the two blocks that can hold masked tokens may fall in one wave's
+// split, and a wave attends only its first block masked), nor for 2 tiles of
+// 8-bit codes (that form would spill).
 template <int kBits, int kTiles, bool kCausal>
-constexpr bool kMultiFits = kTiles == 1 || (kBits == 4 && !kCausal);
+constexpr bool kMultiFits = !kCausal && (kTiles == 1 || kBits == 4);
 
 template <int kBits, int kTiles, bool kCausal>
 hipError_t launch_r32c(const AttendProblem& p, unsigned grid, hipStream_t stream) {

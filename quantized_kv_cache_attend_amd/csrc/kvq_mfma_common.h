@@ -326,8 +326,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t split_rows(const AttendProblem
 // holds barriers).
 // split_store writes one split's partial rows (no wait); split_ticket_merge
 // waits for every partial store of the workgroup, takes its ticket for
-// `arrivals` splits and, if it is the last, merges.  split_combine is the two
-// for one split.
+// `arrivals` splits and, if it is the last, merges the partials in slots
+// 0 .. parts - 1.  split_combine is the two for one split (parts = splits).
 // A thread's row of the combine: it takes part (mine) when r < p.rows; row
 // is the row's index among all B * Hkv * rows query rows.
 struct SplitRow {
@@ -374,7 +374,7 @@ __device__ __forceinline__ void split_store(const AttendProblem& p, int split, l
 template <int kF, int kRun, int kStride>
 __device__ __forceinline__ void split_ticket_merge(const AttendProblem& p, long long head, int r,
                                                    int f0, int arrivals, int* last,
-                                                   const SplitRow& sr) {
+                                                   const SplitRow& sr, int parts) {
   const bool mine = sr.mine;
   const long long total_rows = sr.total_rows;
   const long long row = sr.row;
@@ -400,13 +400,12 @@ __device__ __forceinline__ void split_ticket_merge(const AttendProblem& p, long 
     return;
   }
   if (mine) {
-    // Online merge over the splits, four at a time so a batch's loads are in
-    // flight together.
+    // Online merge over the partials, four at a time so a batch's loads are
+    // in flight together.
     constexpr int kBatch = 4;
     float Mg = -INFINITY, Zg = 0.0f, V[kF];
 #pragma unroll
     for (int i = 0; i < kF; ++i) V[i] = 0.0f;
-    const int parts = p.splits;
     for (int s0 = 0; s0 < parts; s0 += kBatch) {
       float ms[kBatch], zs[kBatch], us[kBatch][kF];
 #pragma unroll
@@ -467,7 +466,7 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
                                               float Z, int* last) {
   const SplitRow sr = split_row(p, head, r);
   split_store<kF, kRun, kStride>(p, split, head, r, f0, U, M, Z, sr);
-  split_ticket_merge<kF, kRun, kStride>(p, head, r, f0, 1, last, sr);
+  split_ticket_merge<kF, kRun, kStride>(p, head, r, f0, 1, last, sr, p.splits);
 }
 
 // ---- recent-token window parts -------------------------------------------------

@@ -307,16 +307,22 @@ def test_attend_mfma32_peaky_and_channel_scaled(dist, scale_k):
         assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
 
 
-# (B, Hq, Hkv, R, N, bits, causal, splits): KV heads x splits above 512, so
-# each workgroup of the 32-row kernel attends ceil(heads x splits / 512)
-# consecutive splits of its head.  The split counts leave a shorter last run,
-# and splits past the last token hold no key.
+# (B, Hq, Hkv, R, N, bits, causal, splits).  Where KV heads x splits fill at
+# least 4 rounds of 512 workgroups, each workgroup of the 32-row kernel takes
+# a run of 4 ceil(heads x splits / 2048) consecutive splits, each wave
+# attends whole splits of it, and the workgroup stores one partial for the
+# run (a two-level combine).  The split counts leave a shorter last run
+# (some waves without a split), splits past the last token hold no key, and
+# the masked block is a split's first.  The causal and the 8-bit 32-row
+# shapes keep one split per workgroup.
 MULTI_SPLIT = [
-    (2, 8, 1, 4, 5000, 4, False, 700),     # 32 rows (2 tiles), 3 per workgroup, last run 1
-    (1, 12, 1, 1, 4097, 8, False, 1030),   # 8-bit, 12 rows, 3 per workgroup
-    (3, 16, 2, 1, 3001, 4, False, 302),    # 8 rows, 6 heads, 4 per workgroup, last run 2
-    (2, 4, 1, 4, 2100, 4, True, 601),      # causal, 16 rows
-    (2, 32, 1, 1, 20000, 4, False, 301),   # 2 per workgroup, 3 blocks per split
+    (2, 8, 1, 4, 5000, 4, False, 1001),     # 32 rows, runs of 4, last run 1
+    (1, 12, 1, 1, 4097, 8, False, 2050),    # 8-bit, 12 rows, runs of 8 (2 per wave), last 2
+    (3, 16, 2, 1, 3001, 4, False, 302),     # 8 rows, 6 heads, runs of 4, last run 2
+    (2, 32, 1, 1, 100000, 4, False, 1030),  # 4 blocks per split, runs of 8, last run 6
+    (64, 64, 8, 1, 256, 4, False, 4),       # 512 heads: one workgroup per head, a split per wave
+    (2, 4, 1, 4, 2100, 4, True, 1201),      # causal: one split per workgroup
+    (1, 32, 1, 1, 5000, 8, False, 2000),    # 8-bit 32 rows: one split per workgroup
 ]
 
 

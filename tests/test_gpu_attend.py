@@ -96,11 +96,17 @@ def test_attend_gqa_n32768_sampled(variant, seed):
     announce(f"attend gqa_n32768 full seed={seed} {variant}")
     cache = _gpu_cache(k, v, 4, 32)
     got = _run(q, cache, w.N, 4, 32, num_splits=w.num_splits, variant=variant)
+    # 64 splits: runs of 16 splits per workgroup, 4 whole splits per wave
+    more = _run(q, cache, w.N, 4, 32, num_splits=64, variant=variant) if seed == 0 else None
     rep = w.Hq // w.Hkv
     for b, h in ((0, 0), (5, 6), (15, 7)):
         qs = q[b:b + 1, h * rep:(h + 1) * rep]
         want = _oracle(qs, k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], 4, 32)
         assert max_abs(got[b:b + 1, h * rep:(h + 1) * rep], want) <= TOL
+        if more is not None:
+            assert max_abs(more[b:b + 1, h * rep:(h + 1) * rep], want) <= TOL
+    if more is not None:
+        assert max_abs(more, got) <= SPLIT_TOL
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -321,6 +327,7 @@ MULTI_SPLIT = [
     (3, 16, 2, 1, 3001, 4, False, 302),     # 8 rows, 6 heads, runs of 4, last run 2
     (2, 32, 1, 1, 100000, 4, False, 1030),  # 4 blocks per split, runs of 8, last run 6
     (64, 64, 8, 1, 256, 4, False, 4),       # 512 heads: one workgroup per head, a split per wave
+    (1, 8, 1, 1, 4097, 4, False, 65535),    # the most splits: runs of 128 (32 per wave), last run 127
     (2, 4, 1, 4, 2100, 4, True, 1201),      # causal: one split per workgroup
     (1, 32, 1, 1, 5000, 8, False, 2000),    # 8-bit 32 rows: one split per workgroup
 ]

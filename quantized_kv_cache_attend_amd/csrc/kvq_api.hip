@@ -253,12 +253,10 @@ int mfma32_auto_splits(int B, int Hkv, int N) {
 // the waves get equal shares), storing each split's partial as before; the
 // rounds' start-up and tail are paid once and no split needs a merge of its
 // waves.  With fewer, one split per workgroup.  Not with window parts or the
-// causal rule, nor for 8-bit codes with more than 16 rows (that form would
-// spill and is not compiled).
+// causal rule (that form is not compiled).
 int mfma32_splits_per_wg(const AttendProblem& p) {
   constexpr int kWaves = 4;
-  const bool fits = !p.causal && (p.rows <= 16 || p.bits == 4);
-  if (p.win_parts > 0 || !fits || p.splits < kWaves) return 1;
+  if (p.win_parts > 0 || p.causal || p.splits < kWaves) return 1;
   const long long wgs = static_cast<long long>(p.B) * p.Hkv * p.splits;
   const long long per = (wgs + 511) / 512;
   if (per < kWaves) return 1;

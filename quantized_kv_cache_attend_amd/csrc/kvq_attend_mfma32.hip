@@ -826,10 +826,11 @@ attend_mfma_r32_kernel(AttendProblem p) {
 
 // Several splits per workgroup (whole splits per wave): not with the causal
 // rule (the two blocks that can hold masked tokens may fall in one wave's
-// split, and a wave attends only its first block masked), nor for 2 tiles of
-// 8-bit codes (that form would spill).
+// split, and a wave attends only its first block masked).  The 2-tile 8-bit
+// form spills 16 bytes per lane, saved before the block loops and reloaded
+// after them.
 template <int kBits, int kTiles, bool kCausal>
-constexpr bool kMultiFits = !kCausal && (kTiles == 1 || kBits == 4);
+constexpr bool kMultiFits = !kCausal;
 
 template <int kBits, int kTiles, bool kCausal>
 hipError_t launch_r32c(const AttendProblem& p, unsigned grid, hipStream_t stream) {

@@ -109,6 +109,21 @@ def test_attend_gqa_n32768_sampled(variant, seed):
         assert max_abs(more, got) <= SPLIT_TOL
 
 
+def test_attend_gqa_n32768_8bit_sampled():
+    """The long-context workload in 8-bit group 32 at its 16 splits (4 splits
+    per workgroup, two row tiles): sampled KV heads against the oracle."""
+    w = WORKLOADS["gqa_n32768"]
+    q, k, v = make_qkv(w, 2)
+    announce("attend gqa_n32768 8-bit full")
+    cache = _gpu_cache(k, v, 8, 32)
+    got = _run(q, cache, w.N, 8, 32, num_splits=w.num_splits)
+    rep = w.Hq // w.Hkv
+    for b, h in ((0, 0), (9, 3), (15, 7)):
+        qs = q[b:b + 1, h * rep:(h + 1) * rep]
+        want = _oracle(qs, k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], 8, 32)
+        assert max_abs(got[b:b + 1, h * rep:(h + 1) * rep], want) <= TOL
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("n", [1, 7, 35, 1021, 4097])
 @pytest.mark.parametrize("d", [32, 64, 128])
@@ -319,8 +334,8 @@ def test_attend_mfma32_peaky_and_channel_scaled(dist, scale_k):
 # attends whole splits of it, and the workgroup stores one partial for the
 # run (a two-level combine).  The split counts leave a shorter last run
 # (some waves without a split), splits past the last token hold no key, and
-# the masked block is a split's first.  The causal and the 8-bit 32-row
-# shapes keep one split per workgroup.
+# the masked block is a split's first.  The causal shape keeps one split per
+# workgroup.
 MULTI_SPLIT = [
     (2, 8, 1, 4, 5000, 4, False, 1001),     # 32 rows, runs of 4, last run 1
     (1, 12, 1, 1, 4097, 8, False, 2050),    # 8-bit, 12 rows, runs of 8 (2 per wave), last 2
@@ -329,7 +344,7 @@ MULTI_SPLIT = [
     (64, 64, 8, 1, 256, 4, False, 4),       # 512 heads: one workgroup per head, a split per wave
     (1, 8, 1, 1, 4097, 4, False, 65535),    # the most splits: runs of 128 (32 per wave), last run 127
     (2, 4, 1, 4, 2100, 4, True, 1201),      # causal: one split per workgroup
-    (1, 32, 1, 1, 5000, 8, False, 2000),    # 8-bit 32 rows: one split per workgroup
+    (1, 32, 1, 1, 5000, 8, False, 2000),    # 8-bit, 32 rows (2 tiles), runs of 4
 ]
 
 

@@ -252,11 +252,14 @@ int mfma32_auto_splits(int B, int Hkv, int N) {
 // and each wave attends whole splits of that run (a multiple of 4 splits, so
 // the waves get equal shares), storing each split's partial as before; the
 // rounds' start-up and tail are paid once and no split needs a merge of its
-// waves.  With fewer, one split per workgroup.  Not with window parts or the
-// causal rule (that form is not compiled).
+// waves.  With fewer, one split per workgroup.  Not with window parts (the
+// whole-split waves take at most two masked blocks, which holds while the
+// queries end at N), nor for causal calls with 8-bit codes and more than 16
+// rows (that form is not compiled).
 int mfma32_splits_per_wg(const AttendProblem& p) {
   constexpr int kWaves = 4;
-  if (p.win_parts > 0 || p.causal || p.splits < kWaves) return 1;
+  if (p.win_parts > 0 || p.pos_end != p.N || p.splits < kWaves) return 1;
+  if (p.causal && p.bits == 8 && p.rows > 16) return 1;
   const long long wgs = static_cast<long long>(p.B) * p.Hkv * p.splits;
   const long long per = (wgs + 511) / 512;
   if (per < kWaves) return 1;

@@ -490,22 +490,27 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
   }
 }
 
-// Several splits per workgroup (kMulti; no causal rule, no window parts).
-// Workgroup g of a head takes splits [s0, s1) = [g spw, min(splits, (g + 1)
-// spw)); wave w attends splits s0 + w, s0 + w + kW, ... below s1, each one
-// whole: its blocks in order (the block holding token N-1 first when N is not
-// a multiple of 32: the only masked block without the causal rule).  The
-// wave's running (m, z, u) goes on from one of its splits to the next (the
-// online merge of their partials); the workgroup then merges its waves as
-// for one split and stores one partial, in slot g.  The last arriver merges
-// the head's ceil(splits / spw) partials: a two-level combine, with a
-// quarter of the partial rows of one partial per split or fewer.
+// Several splits per workgroup (kMulti; no window parts).  Workgroup g of a
+// head takes splits [s0, s1) = [g spw, min(splits, (g + 1) spw)); wave w
+// attends splits s0 + w, s0 + w + kW, ... below s1, each one whole: first
+// its masked blocks (the block holding token N-1 when N is not a multiple of
+// 32, and with the causal rule the blocks holding tokens past N - R: at most
+// two, both at the end of the split), then the others in order.  The wave's
+// running (m, z, u) goes on from one of its splits to the next (the online
+// merge of their partials; a split of earlier tokens gives every row a legal
+// key, so a masked block never meets a row that still needs one after an
+// unmasked block); the workgroup then merges its waves as for one split and
+// stores one partial, in slot g.  The last arriver merges the head's
+// ceil(splits / spw) partials: a two-level combine, with a quarter of the
+// partial rows of one partial per split or fewer.
 struct WaveSplit {
   int t_end;
   bool active;                    // the split holds a token
   int first;                      // attended first (masked if needed)
+  int second;                     // a second masked block, or -1
   int loop_begin, loop_end;       // then these, in order (inclusive)
 };
+template <bool kCausal>
 __device__ __forceinline__ WaveSplit wave_split(const AttendProblem& p, int split) {
   WaveSplit s;
   const int t_begin = split * p.tokens_per_split;
@@ -513,36 +518,45 @@ __device__ __forceinline__ WaveSplit wave_split(const AttendProblem& p, int spli
   s.active = s.t_end > t_begin;
   const int b_begin = t_begin / kBlockTokens;
   const int b_last = (s.t_end - 1) / kBlockTokens;  // valid if active
-  const bool partial = (p.N % kBlockTokens) != 0 && b_last == (p.N - 1) / kBlockTokens;
-  s.first = partial ? b_last : b_begin;
-  s.loop_begin = partial ? b_begin : b_begin + 1;
-  s.loop_end = partial ? b_last - 1 : b_last;
+  // First block holding a masked token: the causal limit of row 0 (the
+  // lowest) is pos_end - R; without the rule only the ragged last block.
+  const int b_ragged = (p.N % kBlockTokens) != 0 ? (p.N - 1) / kBlockTokens : INT_MAX;
+  const int b_mask = kCausal ? min(b_ragged, (p.pos_end - p.R + 1) / kBlockTokens) : b_ragged;
+  const int b_lo = max(b_begin, b_mask);
+  const int masked = b_lo <= b_last ? b_last - b_lo + 1 : 0;  // 0, 1 or 2 (pos_end = N)
+  s.first = masked > 0 ? b_last : b_begin;
+  s.second = kCausal && masked > 1 ? b_last - 1 : -1;
+  s.loop_begin = masked > 0 ? b_begin : b_begin + 1;
+  s.loop_end = b_last - masked;
   return s;
 }
 
 // The wave's splits s, s + kW, ... below s_end into st; br holds split s's
 // first block (loaded by the caller when that split is active).
-template <int kBits, int kTiles>
+template <int kBits, int kTiles, bool kCausal>
 __device__ __forceinline__ void attend_wave_splits(
     const AttendProblem& p, Smem32& sm, Regs32<kBits>& br, const Head32& h, const Lanes32& lo,
     const typename CodeOps<kBits>::consts& cc, State32& st, const float (&us_row)[2],
     const half8_t (&qh)[2][4], const half8_t (&ql)[2][4], const int (&lim)[2], int s,
     int s_end) {
-  WaveSplit sp = wave_split(p, s);
+  WaveSplit sp = wave_split<kCausal>(p, s);
   for (; s < s_end; s += kW) {
     // The block loaded after this split's last one: the wave's next split's first.
     WaveSplit nx = sp;
     int tail_next = -1;
     if (s + kW < s_end) {
-      nx = wave_split(p, s + kW);
+      nx = wave_split<kCausal>(p, s + kW);
       if (nx.active) tail_next = nx.first;
     }
     if (sp.active) {
       const bool loop = sp.loop_begin <= sp.loop_end;
-      attend_block32<kBits, kTiles, true, false>(
+      const int after = loop ? sp.loop_begin : (tail_next >= 0 ? tail_next : sp.first);
+      attend_block32<kBits, kTiles, true, kCausal>(
           sm, br, sp.first * kBlockTokens, sp.t_end, cc, st, h,
-          loop ? sp.loop_begin : (tail_next >= 0 ? tail_next : sp.first), lo, us_row, qh, ql,
-          lim);
+          sp.second >= 0 ? sp.second : after, lo, us_row, qh, ql, lim);
+      if (sp.second >= 0)
+        attend_block32<kBits, kTiles, true, kCausal>(sm, br, sp.second * kBlockTokens, sp.t_end,
+                                                     cc, st, h, after, lo, us_row, qh, ql, lim);
       for (int b = sp.loop_begin; b <= sp.loop_end; ++b)
         attend_block32<kBits, kTiles, false, false>(
             sm, br, b * kBlockTokens, sp.t_end, cc, st, h,
@@ -647,7 +661,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
   Regs32<kBits> br;
   if constexpr (kMulti) {
     if (s_first + wave < s_end) {
-      const WaveSplit w0 = wave_split(p, s_first + wave);
+      const WaveSplit w0 = wave_split<kCausal>(p, s_first + wave);
       if (w0.active) load_block32(br, h, w0.first, lo);
     }
   } else if (active) {
@@ -728,7 +742,7 @@ attend_mfma_r32_kernel(AttendProblem p) {
   // Causal limit of this lane's score rows 16t + n.
   const int lim[2] = {p.pos_end - p.R + n % p.R, p.pos_end - p.R + (16 + n) % p.R};
   if constexpr (kMulti) {
-    attend_wave_splits<kBits, kTiles>(p, sm, br, h, lo, cc, st, us_row, qh, ql, lim,
+    attend_wave_splits<kBits, kTiles, kCausal>(p, sm, br, h, lo, cc, st, us_row, qh, ql, lim,
                                       s_first + wave, s_end);
   } else if (active) {
     attend_block32<kBits, kTiles, true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
@@ -824,13 +838,12 @@ attend_mfma_r32_kernel(AttendProblem p) {
 
 }  // namespace
 
-// Several splits per workgroup (whole splits per wave): not with the causal
-// rule (the two blocks that can hold masked tokens may fall in one wave's
-// split, and a wave attends only its first block masked).  The 2-tile 8-bit
-// form spills 16 bytes per lane, saved before the block loops and reloaded
-// after them.
+// Several splits per workgroup in every form but the causal one with 2 tiles
+// of 8-bit codes, whose spills would reach the block loop.  The non-causal
+// 2-tile 8-bit form spills 16 bytes per lane, saved before the block loops
+// and reloaded after them.
 template <int kBits, int kTiles, bool kCausal>
-constexpr bool kMultiFits = !kCausal;
+constexpr bool kMultiFits = !(kCausal && kTiles == 2 && kBits == 8);
 
 template <int kBits, int kTiles, bool kCausal>
 hipError_t launch_r32c(const AttendProblem& p, unsigned grid, hipStream_t stream) {

@@ -334,8 +334,7 @@ def test_attend_mfma32_peaky_and_channel_scaled(dist, scale_k):
 # attends whole splits of it, and the workgroup stores one partial for the
 # run (a two-level combine).  The split counts leave a shorter last run
 # (some waves without a split), splits past the last token hold no key, and
-# the masked block is a split's first.  The causal shape keeps one split per
-# workgroup.
+# the masked block is a split's first.
 MULTI_SPLIT = [
     (2, 8, 1, 4, 5000, 4, False, 1001),     # 32 rows, runs of 4, last run 1
     (1, 12, 1, 1, 4097, 8, False, 2050),    # 8-bit, 12 rows, runs of 8 (2 per wave), last 2
@@ -343,8 +342,16 @@ MULTI_SPLIT = [
     (2, 32, 1, 1, 100000, 4, False, 1030),  # 4 blocks per split, runs of 8, last run 6
     (64, 64, 8, 1, 256, 4, False, 4),       # 512 heads: one workgroup per head, a split per wave
     (1, 8, 1, 1, 4097, 4, False, 65535),    # the most splits: runs of 128 (32 per wave), last run 127
-    (2, 4, 1, 4, 2100, 4, True, 1201),      # causal: one split per workgroup
     (1, 32, 1, 1, 5000, 8, False, 2000),    # 8-bit, 32 rows (2 tiles), runs of 4
+    # Causal (queries at N - R .. N - 1): the tokens past N - R masked for some
+    # rows lie in one block or two; a wave attends its split's masked blocks
+    # first.
+    (2, 4, 1, 4, 2100, 4, True, 1201),      # one masked block, runs of 8
+    (16, 16, 4, 8, 2084, 4, True, 40),      # 32 rows: blocks 64 and 65 masked, one split
+    (16, 16, 4, 8, 2084, 4, True, 100),     # the two masked blocks in adjacent splits
+    (16, 8, 2, 4, 2081, 4, True, 65),       # 16 rows (1 tile): two masked blocks, one split
+    (16, 8, 2, 4, 2081, 8, True, 65),       # the same in 8-bit
+    (16, 16, 4, 8, 2084, 8, True, 40),      # causal 8-bit 32 rows: one split per workgroup
 ]
 
 

@@ -352,6 +352,8 @@ MULTI_SPLIT = [
     (16, 8, 2, 4, 2081, 4, True, 65),       # 16 rows (1 tile): two masked blocks, one split
     (16, 8, 2, 4, 2081, 8, True, 65),       # the same in 8-bit
     (16, 16, 4, 8, 2084, 8, True, 40),      # causal 8-bit 32 rows: one split per workgroup
+    (64, 64, 8, 4, 2, 4, True, 4),          # N < R: queries with no legal key (output 0)
+    (64, 64, 8, 4, 35, 4, True, 4),         # 512 heads, splits past the last token
 ]
 
 

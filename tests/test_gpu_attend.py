@@ -378,6 +378,37 @@ def test_attend_mfma32_several_splits_per_workgroup(shape):
     assert max_abs(got, one) <= SPLIT_TOL
 
 
+# 16 shapes drawn once (seeded) among those where the 32-row kernel takes
+# several splits per workgroup: 4- and 8-bit, causal or not, 5..32 rows per
+# KV head, ragged N up to 3000, split counts with uneven runs.
+MULTI_SPLIT_DRAWN = [
+    (8, 4, 2, 4, 2633, 4, True, 268), (8, 64, 8, 1, 2261, 4, False, 76),
+    (4, 8, 2, 4, 185, 4, True, 397), (2, 32, 8, 2, 2487, 4, False, 374),
+    (16, 8, 2, 2, 503, 8, True, 58), (8, 8, 4, 8, 2357, 8, False, 111),
+    (3, 32, 4, 4, 1869, 4, False, 462), (16, 8, 8, 8, 1467, 4, False, 40),
+    (4, 8, 1, 4, 2540, 8, False, 1053), (4, 8, 2, 2, 2771, 4, True, 214),
+    (4, 4, 1, 2, 1402, 4, False, 412), (16, 4, 1, 8, 2145, 4, True, 143),
+    (16, 2, 1, 4, 1058, 4, False, 292), (2, 8, 4, 4, 2585, 8, False, 376),
+    (8, 8, 8, 8, 2137, 8, False, 85), (8, 8, 1, 2, 1148, 8, True, 259),
+]
+
+
+@pytest.mark.parametrize("shape", MULTI_SPLIT_DRAWN,
+                         ids=["B{}-Hq{}-Hkv{}-R{}-N{}-{}b-causal{}-s{}".format(*c)
+                              for c in MULTI_SPLIT_DRAWN])
+def test_attend_mfma32_several_splits_drawn_shapes(shape):
+    B, hq, hkv, r, n, bits, causal, splits = shape
+    w = Workload("multi_drawn", B, hq, hkv, r, n, 128, ((bits, 32),))
+    q, k, v = make_qkv(w, 10)
+    announce(f"attend mfma32 drawn shape {shape}")
+    kc, ks, vc, vs = oracle_pack(k, v, bits, 32)
+    want = O.attend_packed(q, kc, ks, vc, vs, n, bits, 32, causal=causal)
+    got = _run(q, _gpu_cache(k, v, bits, 32), n, bits, 32, num_splits=splits, variant="mfma",
+               causal=causal)
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= TOL, max_abs(got, want)
+
+
 @pytest.mark.parametrize("hq,r", [(4, 1), (16, 2)])
 def test_attend_mfma_large_k_scales(hq, r):
     """K magnitudes large enough that K scales reach 32 (the 32-row kernel

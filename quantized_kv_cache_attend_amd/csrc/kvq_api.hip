@@ -249,10 +249,12 @@ int mfma32_auto_splits(int B, int Hkv, int N) {
 // Splits per workgroup of the 32-row kernel.  When a head's splits would
 // fill at least 4 rounds of its 4-wave workgroups (512 a round: two per
 // compute unit), each workgroup takes a run of consecutive splits of its head
-// and each wave attends whole splits of that run (a multiple of 4 splits, so
-// the waves get equal shares), storing each split's partial as before; the
-// rounds' start-up and tail are paid once and no split needs a merge of its
-// waves.  With fewer, one split per workgroup.  Not with window parts (the
+// (a multiple of 4 splits, so the waves get equal shares): each wave attends
+// whole splits of the run, the workgroup merges its waves and stores one
+// partial for the run, and the last arriver merges one partial per
+// workgroup.  The rounds' start-up and tail are paid once, and a quarter of
+// the partial rows or fewer go through memory.  With fewer, one split per
+// workgroup.  Not with window parts (the
 // whole-split waves take at most two masked blocks, which holds while the
 // queries end at N), nor for causal calls with 8-bit codes and more than 16
 // rows (that form is not compiled).

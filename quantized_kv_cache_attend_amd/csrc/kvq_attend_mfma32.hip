@@ -9,7 +9,7 @@
 // not keep the whole heat map": per query row a reference max m, an
 // exponential sum z and an unnormalized value sum u relative to 2^m, both
 // rescaled by 2^(m_old - m_new) when the reference moves (lazily: only when a
-// block's max exceeds it by more than 2^kLazy, which bounds p = 2^(s - m)).
+// block's max exceeds it by more than kLazy, so p = 2^(s - m) <= 2^kLazy).
 // Waves and KV splits are merged with the same rescale ("two stops of the
 // online accumulation" on the same page).
 //
@@ -62,7 +62,13 @@ constexpr int kVStep = 32 * kBits;   //   and V value-group stride
 constexpr int kBS = 128;         // K or V scales of one block
 constexpr int kQStride = 132;    // LDS row of q: 4 words of padding keep the
                                  // 16 rows read by a quarter-wave on distinct banks
-constexpr float kLazy = 6.0f;    // reference moves only past m + kLazy
+// The reference moves only past m + kLazy (base-2 units), so p <= 2^kLazy.
+// 4-bit codes: p goes to the value product as fp16 hi + lo, exact in range up
+// to 2^15; 12 makes a move rare even for peaky rows (score spread of several
+// units), and each move rescales all of a wave's u.  8-bit codes: p~ = p * sV
+// * 2^sv stays below 2^(kLazy + kSvTop) = 2^15.
+template <int kBits>
+constexpr float kLazy = kBits == 4 ? 12.0f : 6.0f;
 constexpr int kSvTop = 9;        // V prescale: max V scale * 2^Sv in [2^8, 2^9),
 constexpr int kSvLow = 2;        //   kept while it stays in [2^2, 2^9)
 constexpr int kQTop = 10;        // q rows prescaled to max |.| in [2^9, 2^10)
@@ -379,13 +385,13 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
 
   // Move the reference of rows that overshoot it by more than kLazy (a
   // wave-uniform decision).
-  if (!st.live || __builtin_amdgcn_ballot_w64(lmx[0] > st.m[0] + kLazy ||
-                                              (kTiles > 1 && lmx[1] > st.m[1] + kLazy)) != 0) {
+  if (!st.live || __builtin_amdgcn_ballot_w64(lmx[0] > st.m[0] + kLazy<kBits> ||
+                                              (kTiles > 1 && lmx[1] > st.m[1] + kLazy<kBits>)) != 0) {
     float alpha[2];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const float mx = qblock_max(lmx[t]);  // row max over the block (finite unless kCausal)
-      const float m_new = st.live ? (mx > st.m[t] + kLazy ? mx : st.m[t]) : mx;
+      const float m_new = st.live ? (mx > st.m[t] + kLazy<kBits> ? mx : st.m[t]) : mx;
       alpha[t] = st.live ? fast_exp2(st.m[t] - m_new) : 0.0f;
       if (kCausal && m_new == -INFINITY) alpha[t] = 0.0f;  // still no legal key: z = u = 0
       st.z[t] *= alpha[t];
@@ -411,7 +417,7 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
     st.live = true;
   }
 
-  // p = 2^(s - m) <= 2^kLazy; z += sum p.  pk holds p in k-slot order.
+  // p = 2^(s - m) <= 2^kLazy<kBits>; z += sum p.  pk holds p in k-slot order.
   float pk[2][8];
   half2_t p16[2][4];
 #pragma unroll

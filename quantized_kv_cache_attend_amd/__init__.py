@@ -22,7 +22,9 @@ import os
 import torch  # noqa: F401  (must precede the CDLL below)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvq.so")
+# KVQ_LIBRARY names another build of the same library (the host-ASan build
+# that a CPU test loads); by default the in-tree libkvq.so.
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -54,6 +54,12 @@ def sources():
 
 LIB_PHASE = os.path.join(PKG, "libkvq_phase.so")
 BUILD_PHASE = os.path.join(ROOT, "_build_phase")
+# Host AddressSanitizer build of the same sources (device code unchanged):
+# the C-ABI layer's argument checks, sizing and error strings run under ASan
+# in a CPU test (the GPU code itself is never built with a sanitizer).
+BUILD_ASAN = os.path.join(ROOT, "_build_asan")
+LIB_ASAN = os.path.join(BUILD_ASAN, "libkvq_asan.so")
+ASAN_CFLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
@@ -66,13 +72,18 @@ def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, phase_trace: bool = False) -> str:
+def build(verbose: bool = False, phase_trace: bool = False, asan: bool = False) -> str:
     """Compile every source and link the library.  phase_trace: the
     diagnostic build with per-wave phase timestamps in the matrix-core attend
-    kernels (-DKVQ_PHASE_TRACE), written to libkvq_phase.so; the package
-    always loads libkvq.so."""
-    build_dir, lib = (BUILD_PHASE, LIB_PHASE) if phase_trace else (BUILD, LIB)
-    extra = ("-DKVQ_PHASE_TRACE",) if phase_trace else ()
+    kernels (-DKVQ_PHASE_TRACE), written to libkvq_phase.so; asan: host code
+    built with AddressSanitizer into _build_asan/libkvq_asan.so (loaded only
+    with the ASan runtime preloaded).  The package loads libkvq.so."""
+    if asan:
+        build_dir, lib, extra = BUILD_ASAN, LIB_ASAN, tuple(ASAN_CFLAGS)
+    elif phase_trace:
+        build_dir, lib, extra = BUILD_PHASE, LIB_PHASE, ("-DKVQ_PHASE_TRACE",)
+    else:
+        build_dir, lib, extra = BUILD, LIB, ()
     if os.path.isdir(build_dir):
         shutil.rmtree(build_dir)
     os.makedirs(build_dir)
@@ -92,5 +103,5 @@ def build(verbose: bool = False, phase_trace: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True, phase_trace="--phase-trace" in sys.argv[1:])
+    build(verbose=True, phase_trace="--phase-trace" in sys.argv[1:], asan="--asan" in sys.argv[1:])
     sys.exit(0)

@@ -597,7 +597,8 @@ def main():
             f"(unmasked {timings[False]:.2f} us)")
 
         # The mixed cache: the 64 most recent tokens in float32, the rest
-        # packed (kvq_attend_window, general kernel), same queries.
+        # packed (kvq_attend_window: window parts in the matrix-core launch),
+        # same queries.
         win = 64
         kpre = kvq.pack_k(kd[:, :, :w.N - win].contiguous(), bits, group)
         vpre = kvq.pack_v(vd[:, :, :w.N - win].contiguous(), bits, group)
@@ -625,8 +626,8 @@ def main():
         torch.cuda.synchronize()
         win_us = w0.elapsed_time(w1) * 1e3 / n_w
         extra["window_step"] = {"float32_window_tokens": win, "us": round(win_us, 2),
-                                "form": "window partial (general kernel) + matrix-core attend "
-                                        "merging it in its combine"}
+                                "form": "one matrix-core launch: packed splits, then window "
+                                        "parts, merged in its split combine"}
         log(f"[bench] mixed cache (last {win} tokens float32): {win_us:.1f} us")
         del blocker, kpre, vpre, kw, vw, ws_w
 

@@ -523,24 +523,16 @@ attend_mfma_r4_kernel(AttendProblem p) {
   const int n = lane & 15;  // MFMA column / A row
   const int q = lane >> 4;  // MFMA k-block / output row quad
 
-  // Workgroup -> (KV head, split).  Workgroups are dealt to the 8 XCDs
-  // round-robin; keep all splits of a head on one XCD so the head's partials
-  // stay close for the combine.
+  // Workgroup -> (KV head, split): all splits of a head on one XCD, window
+  // parts after every packed split (wg_slot).
   const int heads = p.B * p.Hkv;
   if (kAppend && static_cast<int>(blockIdx.x) < heads) {
     append_token<kBits>(p, blockIdx.x, reinterpret_cast<float*>(&sm.u.ring[0][0][0]));
     return;
   }
   const int L = blockIdx.x - (kAppend ? heads : 0);  // a multiple of 8 apart: same XCD order
-  int head, split;
-  if (heads % 8 == 0) {
-    const int slot = L >> 3;
-    head = (L & 7) + 8 * (slot / p.splits);
-    split = slot % p.splits;
-  } else {
-    head = L / p.splits;
-    split = L % p.splits;
-  }
+  const WgSlot ws_slot = wg_slot(L, heads, p.splits, kWindow ? p.win_parts : 0);
+  const int head = ws_slot.head, split = ws_slot.split;
   const long long bh = head;
   const int rows = p.rows;
   const int packed_splits = p.splits - p.win_parts;

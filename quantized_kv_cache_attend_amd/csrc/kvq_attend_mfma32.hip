@@ -607,16 +607,11 @@ attend_mfma_r32_kernel(AttendProblem p) {
   // dealt to the 8 XCDs round-robin).
   const int heads = p.B * p.Hkv;
   const int wph = kMulti ? (p.splits + p.spw - 1) / p.spw : p.splits;  // workgroups per head
-  const int L = blockIdx.x;
-  int head, split;
-  if (heads % 8 == 0) {
-    const int slot = L >> 3;
-    head = (L & 7) + 8 * (slot / wph);
-    split = slot % wph;
-  } else {
-    head = L / wph;
-    split = L % wph;
-  }
+  // Window parts stay among their head's splits here: this kernel's grid
+  // often needs more than one round of workgroups, and window parts placed
+  // after every packed split would wait for the second.
+  const WgSlot wslot = wg_slot(blockIdx.x, heads, wph, 0);
+  const int head = wslot.head, split = wslot.split;
   const int s_first = kMulti ? split * p.spw : split;
   const int s_end = kMulti ? min(p.splits, s_first + p.spw) : split + 1;
   const long long bh = head;

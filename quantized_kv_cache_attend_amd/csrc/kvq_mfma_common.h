@@ -469,6 +469,41 @@ __device__ __forceinline__ void split_combine(const AttendProblem& p, int split,
   split_ticket_merge<kF, kRun, kStride>(p, head, r, f0, 1, last, sr, p.splits);
 }
 
+// Workgroup L of a launch -> (KV head, split).  Workgroups are dealt to the 8
+// XCDs round-robin; when the head count is a multiple of 8, the workgroups of
+// a head are a multiple of 8 apart, so all of them run on one XCD and their
+// partials meet in one L2.  With window parts (the last `win` of a head's
+// `per_head` splits), the packed splits of every head come first in the grid
+// and the window parts after them: the packed splits then take one compute
+// unit each before any second workgroup lands on one, and what shares a
+// compute unit is a short window part, not a packed split.
+struct WgSlot {
+  int head, split;
+};
+__device__ __forceinline__ WgSlot wg_slot(int L, int heads, int per_head, int win) {
+  int count = per_head, base = 0;
+  if (win > 0) {
+    const int packed = per_head - win;
+    if (L < packed * heads) {
+      count = packed;
+    } else {
+      L -= packed * heads;
+      count = win;
+      base = packed;
+    }
+  }
+  WgSlot s;
+  if (heads % 8 == 0) {
+    const int slot = L >> 3;
+    s.head = (L & 7) + 8 * (slot / count);
+    s.split = base + slot % count;
+  } else {
+    s.head = L / count;
+    s.split = base + L % count;
+  }
+  return s;
+}
+
 // ---- recent-token window parts -------------------------------------------------
 // A mixed cache ([RL] "prefill and decode": the newest tokens kept in
 // float32 beside the packed ones) attended in one launch: the last

@@ -496,6 +496,23 @@ __device__ __forceinline__ void attend_block32(Smem32& sm, Regs32<kBits>& br, in
   }
 }
 
+// Issue priority of a wave before its block i of cnt, from the blocks still
+// ahead, by a ladder that narrows toward the end: level 3 while more than a
+// quarter is ahead, then 2, 1 and 0 below a quarter, an eighth and a
+// sixteenth.  The two waves sharing a SIMD (one from each of the compute
+// unit's two workgroups) start together with equal runs; the older one gets
+// the SIMD's issue slots when their levels tie, so the one behind gets them as
+// soon as it falls a level back, and near the end, where the levels are a few
+// blocks wide, the two finish within a few blocks of each other instead of the
+// younger one running its last third alone at one wave's issue rate.
+__device__ __forceinline__ void priority_by_blocks_ahead(int i, int cnt) {
+  const int r = cnt - 1 - i;
+  if (r * 16 < cnt) __builtin_amdgcn_s_setprio(0);
+  else if (r * 8 < cnt) __builtin_amdgcn_s_setprio(1);
+  else if (r * 4 < cnt) __builtin_amdgcn_s_setprio(2);
+  else __builtin_amdgcn_s_setprio(3);
+}
+
 // Several splits per workgroup (kMulti; no window parts).  Workgroup g of a
 // head takes splits [s0, s1) = [g spw, min(splits, (g + 1) spw)); wave w
 // attends splits s0 + w, s0 + w + kW, ... below s1, each one whole: first
@@ -545,6 +562,13 @@ __device__ __forceinline__ void attend_wave_splits(
     const typename CodeOps<kBits>::consts& cc, State32& st, const float (&us_row)[2],
     const half8_t (&qh)[2][4], const half8_t (&ql)[2][4], const int (&lim)[2], int s,
     int s_end) {
+  // The wave's blocks over all its splits, for its issue priority.
+  int cnt = 0;
+  for (int t = s; t < s_end; t += kW) {
+    const WaveSplit w = wave_split<kCausal>(p, t);
+    if (w.active) cnt += 1 + (w.second >= 0) + max(0, w.loop_end - w.loop_begin + 1);
+  }
+  int done = 0;
   WaveSplit sp = wave_split<kCausal>(p, s);
   for (; s < s_end; s += kW) {
     // The block loaded after this split's last one: the wave's next split's first.
@@ -557,17 +581,22 @@ __device__ __forceinline__ void attend_wave_splits(
     if (sp.active) {
       const bool loop = sp.loop_begin <= sp.loop_end;
       const int after = loop ? sp.loop_begin : (tail_next >= 0 ? tail_next : sp.first);
+      priority_by_blocks_ahead(done++, cnt);
       attend_block32<kBits, kTiles, true, kCausal>(
           sm, br, sp.first * kBlockTokens, sp.t_end, cc, st, h,
           sp.second >= 0 ? sp.second : after, lo, us_row, qh, ql, lim);
-      if (sp.second >= 0)
+      if (sp.second >= 0) {
+        priority_by_blocks_ahead(done++, cnt);
         attend_block32<kBits, kTiles, true, kCausal>(sm, br, sp.second * kBlockTokens, sp.t_end,
                                                      cc, st, h, after, lo, us_row, qh, ql, lim);
-      for (int b = sp.loop_begin; b <= sp.loop_end; ++b)
+      }
+      for (int b = sp.loop_begin; b <= sp.loop_end; ++b) {
+        priority_by_blocks_ahead(done++, cnt);
         attend_block32<kBits, kTiles, false, false>(
             sm, br, b * kBlockTokens, sp.t_end, cc, st, h,
             b < sp.loop_end ? b + 1 : (tail_next >= 0 ? tail_next : b), lo, us_row, qh, ql,
             lim);
+      }
     } else if (tail_next >= 0) {
       load_block32(br, h, tail_next, lo);
     }
@@ -746,13 +775,18 @@ attend_mfma_r32_kernel(AttendProblem p) {
     attend_wave_splits<kBits, kTiles, kCausal>(p, sm, br, h, lo, cc, st, us_row, qh, ql, lim,
                                       s_first + wave, s_end);
   } else if (active) {
+    const int cnt = 1 + (loop_begin <= loop_end ? (loop_end - loop_begin) / kW + 1 : 0);
+    priority_by_blocks_ahead(0, cnt);
     attend_block32<kBits, kTiles, true, kCausal>(sm, br, first * kBlockTokens, t_end, cc, st, h,
                                   loop_begin <= loop_end ? loop_begin : first, lo, us_row, qh,
                                   ql, lim);
-    for (int b = loop_begin; b <= loop_end; b += kW)
+    for (int b = loop_begin, i = 1; b <= loop_end; b += kW, ++i) {
+      priority_by_blocks_ahead(i, cnt);
       attend_block32<kBits, kTiles, false, false>(sm, br, b * kBlockTokens, t_end, cc, st, h,
                                    min(b + kW, loop_end), lo, us_row, qh, ql, lim);
+    }
   }
+  __builtin_amdgcn_s_setprio(0);
   phase_mark(kMarkLoopEnd);
   st.z[0] = qblock_sum(st.z[0]);
   if (kTiles > 1) st.z[1] = qblock_sum(st.z[1]);

@@ -23,6 +23,10 @@ TOL = 1e-4
     (1, 2, 2, 8, 300, 33, 64, 8, 8, True),
     (2, 4, 2, 4, 0, 40, 128, 4, 32, False),     # no packed token at all
     (1, 2, 1, 2, 4096, 1, 128, 4, 32, True),
+    # 8 KV heads (the 4-row kernel places window parts after every head's
+    # packed splits) with four window parts, 8-bit and 4-bit
+    (1, 32, 8, 1, 700, 100, 128, 8, 32, False),
+    (3, 24, 8, 1, 1500, 97, 128, 4, 32, True),
 ])
 def test_attend_window(B, hq, hkv, r, n, w, d, bits, group, causal):
     wl = Workload("win", B, hq, hkv, r, n + w, d, ((bits, group),))

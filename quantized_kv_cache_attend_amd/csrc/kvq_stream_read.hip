@@ -2,12 +2,14 @@
 // kernels' throughput is compared with (every KV byte is read exactly once,
 // so a plain read of the same number of bytes bounds the fused path).
 //
-// Shape: one contiguous chunk per workgroup, 16-byte nontemporal loads, four
+// Shape: one contiguous chunk per workgroup, 16-byte nontemporal loads, eight
 // in flight per lane.  Among the read shapes measured on MI355X (grid-stride
 // and chunked loops, 64 to 4096 workgroups of 256 to 1024 threads, one to
 // eight loads in flight, global-to-LDS DMA, with and without the
 // nontemporal hint) this one was at or near the fastest for both a 42 MB and
-// a 671 MB read; the nontemporal hint alone was worth 8 % (42 MB) to 12 %
+// a 671 MB read (interleaved with 256-2048 workgroups and 4 or 8 loads in
+// flight: 7.68 us for 42 MB, 96.9 us for 671 MB, against 7.65-8.29 us and
+// 98.1-111.1 us); the nontemporal hint alone was worth 8 % (42 MB) to 12 %
 // (671 MB) over plain loads.
 #include "kvq_internal.h"
 
@@ -17,7 +19,7 @@ namespace {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kReadThreads = 512;
-constexpr int kInFlight = 4;          // 16-byte loads in flight per lane
+constexpr int kInFlight = 8;          // 16-byte loads in flight per lane
 constexpr unsigned kReadGrid = 1024;  // at most 4 workgroups per CU
 
 // Each workgroup reads words [blk * chunk, min(n, (blk + 1) * chunk)) and

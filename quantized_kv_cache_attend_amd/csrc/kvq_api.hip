@@ -281,13 +281,13 @@ hipError_t run_mfma(AttendProblem p, bool auto_split, hipStream_t s) {
 
 // The streaming kernel takes D = 128 and power-of-two groups from 8 to 128
 // (a token octet then lies in one K group, and a feature pair in one V
-// group; dpad = 128), up to 8 rows, no causal rule, with the matrix-core
+// group; dpad = 128), up to 8 rows, causal or not, no float32 window, with the matrix-core
 // kernels' size and alignment conditions (32-bit buffer offsets per head:
 // group-8 scales take 64 bytes per token and head).
 bool stream_eligible(const AttendProblem& p) {
   const int g = p.group;
   return (p.bits == 4 || p.bits == 8) && g >= 8 && g <= 128 && (g & (g - 1)) == 0 &&
-         p.D == 128 && p.rows <= kStreamMaxRows && !p.causal && p.W == 0 &&
+         p.D == 128 && p.rows <= kStreamMaxRows && p.W == 0 &&
          p.cap <= (p.bits == 8 ? kMfmaMaxN8 : kMfmaMaxN) && aligned(p.q, 16) &&
          aligned(p.k_codes, 16) && aligned(p.v_codes, 16) && aligned(p.k_scales, 16) &&
          aligned(p.v_scales, 16);
@@ -589,7 +589,7 @@ kvq_status kvq_attend_cache(const float* q, const uint8_t* k_codes, const float*
       if (!stream_eligible(p))
         return fail(KVQ_ERR_UNSUPPORTED,
                     "the streaming kernel needs bits=4|8, group 8|16|32|64|128, D=128, <= %d "
-                    "query rows per KV head, no causal rule, N <= %d (4-bit) or %d (8-bit) and "
+                    "query rows per KV head, no float32 window, N <= %d (4-bit) or %d (8-bit) and "
                     "16-byte aligned q and cache arrays", kStreamMaxRows, kMfmaMaxN, kMfmaMaxN8);
       return hip_status(run_stream(p, num_splits == 0, s), "attend (stream) launch");
     default:

@@ -1,7 +1,7 @@
 // Streaming float32 attention over the packed cache for D = 128 in formats
 // the matrix-core kernels do not take: 4- or 8-bit codes with a
-// power-of-two group from 8 to 128, up to 8 query rows per KV head, no
-// causal rule, no float32 window.
+// power-of-two group from 8 to 128, up to 8 query rows per KV head, with or
+// without the causal rule (a separate instantiation), no float32 window.
 //
 // Method: the blocked online softmax of "Block KV decoding: less workspace,
 // more time" (huhohoo.com/en/docs/llm/kv-block-decode-cost), section "Do not
@@ -306,9 +306,13 @@ __device__ __forceinline__ void block_scores(const SPart<kBits>& kp, const QS& q
 // block_scores leaves them); s becomes p = 2^(s - m).  m, z: the lane's rows
 // (z over its token octet only); u: every row.  ntok: how many of the lane's
 // 8 tokens are in the split (the rest, past the cache's end, take no part).
+// kCausal: nrow[j] more bounds row j's tokens (its query's position), and a
+// row that has seen no legal key yet keeps m = -inf, its exponents taken
+// against 0 (so (-inf) - (-inf) is never formed) and z = u = 0.
 // Every lane of the wave calls it.
-template <int kRows>
+template <int kRows, bool kCausal>
 __device__ __forceinline__ void block_softmax(float (&s)[kRows / 4][8], int ntok,
+                                              const int (&nrow)[kRows / 4],
                                               float (&m)[kRows / 4], float (&z)[kRows / 4],
                                               float (&u)[kRows][8], bool& live) {
   constexpr int kL = kRows / 4;
@@ -316,7 +320,8 @@ __device__ __forceinline__ void block_softmax(float (&s)[kRows / 4][8], int ntok
   for (int t = 0; t < 8; ++t) {
     const bool ok = t < ntok;
 #pragma unroll
-    for (int j = 0; j < kL; ++j) s[j][t] = ok ? s[j][t] : -INFINITY;
+    for (int j = 0; j < kL; ++j)
+      s[j][t] = ok && (!kCausal || t < nrow[j]) ? s[j][t] : -INFINITY;
   }
   float bm[kL];
   bool up = false;
@@ -333,7 +338,7 @@ __device__ __forceinline__ void block_softmax(float (&s)[kRows / 4][8], int ntok
 #pragma unroll
     for (int j = 0; j < kL; ++j) {
       const float mn = live ? (bm[j] > m[j] + kSLazy ? bm[j] : m[j]) : bm[j];
-      a[j] = live ? fast_exp2(m[j] - mn) : 0.0f;
+      a[j] = live && (!kCausal || m[j] != -INFINITY) ? fast_exp2(m[j] - mn) : 0.0f;
       z[j] *= a[j];
       m[j] = mn;
     }
@@ -347,10 +352,11 @@ __device__ __forceinline__ void block_softmax(float (&s)[kRows / 4][8], int ntok
   }
 #pragma unroll
   for (int j = 0; j < kL; ++j) {
+    const float ref = kCausal && m[j] == -INFINITY ? 0.0f : m[j];
     float zs = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      s[j][t] = fast_exp2(s[j][t] - m[j]);
+      s[j][t] = fast_exp2(s[j][t] - ref);
       zs += s[j][t];
     }
     z[j] += zs;
@@ -393,7 +399,10 @@ __device__ __forceinline__ void block_values(const SPart<kBits>& vp, const float
   }
 }
 
-template <int kBits, int kRows, int kWaves>
+// kCausal: a causal chunk (row r is query r % R at position pos_end - R +
+// r % R and reads tokens up to its own); only tokens past pos_end - R can be
+// masked, and a row with no legal key in the split returns m = -inf, z = 0.
+template <int kBits, int kRows, int kWaves, bool kCausal>
 __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProblem p) {
   constexpr int kThreads = kWaves * 64;
   __shared__ SSmem<kBits, kRows, kWaves> sm;
@@ -500,6 +509,14 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
 #pragma unroll
     for (int f = 0; f < 8; ++f) u[r][f] = 0.0f;
   bool live = false;
+  // Causal limit of the lane's rows (R/2) b5 + (R/4) b4 + j: the last token
+  // each may read.
+  int lim[kL];
+  {
+    const int r0 = (kRows / 2) * (lane >> 5) + (kRows / 4) * ((lane >> 4) & 1);
+#pragma unroll
+    for (int j = 0; j < kL; ++j) lim[j] = kCausal ? p.pos_end - p.R + (r0 + j) % p.R : 0;
+  }
 
   // Parts are issued in the order K(0) V(0) K(1) V(1) ...: K(i + kDepth) once
   // K(i) is in registers, V(i + kDepth) once V(i) is.  So K(i) has landed
@@ -522,7 +539,13 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
       if (more) dma_k<kBits>(slot, h, blk + kDepth * kWaves, n, q);
       block_scores<kBits, kRows>(kp, qsrc, p.qscale, s);
     }
-    block_softmax<kRows>(s, t_end - (blk * kBlockTokens + 8 * q), m, z, u, live);
+    {
+      const int tok0 = blk * kBlockTokens + 8 * q;
+      int nrow[kL];
+#pragma unroll
+      for (int j = 0; j < kL; ++j) nrow[j] = lim[j] - tok0 + 1;
+      block_softmax<kRows, kCausal>(s, t_end - tok0, nrow, m, z, u, live);
+    }
     {
       wait_parts<kBits>(2 * ahead + (more ? 1 : 0));  // V(i) in the slot
       SPart<kBits> vp;
@@ -603,7 +626,8 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
   if (p.splits == 1) {
     if (r < rows) {
 #pragma unroll
-      for (int j = 0; j < kF; ++j) p.out[(bh * rows + r) * kSD + f0 + j] = U[j] / Z;
+      for (int j = 0; j < kF; ++j)  // causal: Z = 0 for a row with no legal key
+        p.out[(bh * rows + r) * kSD + f0 + j] = !kCausal || Z > 0.0f ? U[j] / Z : 0.0f;
     }
     phase_mark(kMarkEnd);
     return;
@@ -633,8 +657,12 @@ template <int kBits, int kRows>
 static hipError_t launch_stream(const AttendProblem& p, hipStream_t stream) {
   constexpr int kWaves = waves_for(kRows);
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
-  hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves>), dim3(grid), dim3(kWaves * 64),
-                     0, stream, p);
+  if (p.causal)
+    hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves, true>), dim3(grid),
+                       dim3(kWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves, false>), dim3(grid),
+                       dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 

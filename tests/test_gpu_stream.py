@@ -156,7 +156,7 @@ def test_stream_deterministic_back_to_back():
     assert bool(same.all())
 
 
-@pytest.mark.parametrize("what", ["group2", "group12", "rows9", "d64", "causal", "group256"])
+@pytest.mark.parametrize("what", ["group2", "group12", "rows9", "d64", "group256"])
 def test_stream_variant_rejects_what_it_does_not_take(what):
     B, Hq, Hkv, R, N, D, bits, group = 1, 4, 1, 1, 64, 128, 4, 8
     if what == "group2":
@@ -169,14 +169,49 @@ def test_stream_variant_rejects_what_it_does_not_take(what):
         Hq = 9
     elif what == "d64":
         D = 64
-    q = torch.zeros((B, Hq, 2 if what == "causal" else R, D), dtype=torch.float32, device="cuda")
+    q = torch.zeros((B, Hq, R, D), dtype=torch.float32, device="cuda")
     x = torch.zeros((B, Hkv, N, D), dtype=torch.float32, device="cuda")
     kc, ks = kvq.pack_k(x, bits, group)
     vc, vs = kvq.pack_v(x, bits, group)
     with pytest.raises(kvq.KvqError) as e:
-        if what == "causal":
-            kvq.attend(q, kc, ks, vc, vs, N, bits, group, capacity=N, causal=True,
-                       variant="stream")
-        else:
-            kvq.attend(q, kc, ks, vc, vs, N, bits, group, variant="stream")
+        kvq.attend(q, kc, ks, vc, vs, N, bits, group, variant="stream")
     assert e.value.status == -2  # KVQ_ERR_UNSUPPORTED
+
+
+# Causal chunks on the streaming kernel: (B, Hq, Hkv, R, N), the R queries of
+# each head at the last R positions.
+CAUSAL_SHAPES = [
+    (1, 4, 1, 2, 100),      # 8 rows, the mask inside one block
+    (2, 8, 2, 2, 33),       # 8 rows, masked tokens 31 and 32 in two blocks
+    (1, 4, 2, 2, 1),        # N < R: query 0 of every head has no legal key
+    (2, 2, 2, 4, 1057),     # 4 rows: one head x 4 queries
+    (1, 2, 1, 3, 70),       # 6 rows
+    (8, 32, 8, 1, 1000),    # R = 1: the unmasked call
+]
+
+
+@pytest.mark.parametrize("shape", CAUSAL_SHAPES, ids=[_ids(s) for s in CAUSAL_SHAPES])
+@pytest.mark.parametrize("bits,group", [(4, 8), (8, 16), (4, 64), (8, 128)],
+                         ids=["4b-g8", "8b-g16", "4b-g64", "8b-g128"])
+def test_stream_causal_matches_oracle(shape, bits, group):
+    """Per-row causal limits, rows without a legal key (zeros), masks across two
+    blocks and splits past the last token, against the oracle and the general
+    kernel; the automatic choice runs the streaming kernel."""
+    B, Hq, Hkv, R, N = shape
+    w = Workload("stream_causal", B, Hq, Hkv, R, N, 128, ((bits, group),))
+    q, k, v = make_qkv(w, 21)
+    announce(f"stream causal {_ids(shape)} {bits}b g{group}")
+    kc, ks, vc, vs = oracle_pack(k, v, bits, group)
+    want = O.attend_packed(q, kc, ks, vc, vs, N, bits, group, causal=True)
+    empty = O.causal_mask(N, R).sum(axis=1) == 0       # queries with no legal key
+    cache = _cache(k, v, bits, group)
+    for splits in (1, 3, 0, 64):
+        got = _attend(q, cache, N, bits, group, num_splits=splits, variant="stream", causal=True)
+        assert np.isfinite(got).all(), splits
+        assert max_abs(got, want) <= TOL, (splits, max_abs(got, want))
+        assert (got[:, :, empty] == 0).all(), splits
+        gen = _attend(q, cache, N, bits, group, num_splits=splits, variant="valu", causal=True)
+        assert max_abs(got, gen) <= KERNEL_TOL, (splits, max_abs(got, gen))
+    auto = _attend(q, cache, N, bits, group, causal=True)
+    stream = _attend(q, cache, N, bits, group, variant="stream", causal=True)
+    assert np.array_equal(auto, stream)

@@ -668,18 +668,20 @@ kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float
   p.causal = (flags & KVQ_ATTEND_CAUSAL) && R > 1;
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
-  // Fused form, one launch of a matrix-core kernel: S workgroups per head
-  // attend the packed tokens and P more attend the W float32 window tokens
-  // (one per 32 tokens when the workspace has the slots); the fused combine
-  // merges all S + P partials.
-  // (The fused form reads the window rows with 16-byte loads.)
+  // Fused form, one launch of a matrix-core kernel (or, for the formats it
+  // takes, of the streaming kernel): S workgroups per head attend the packed
+  // tokens and P more attend the W float32 window tokens (one per 32 tokens
+  // when the workspace has the slots); the fused combine merges all S + P
+  // partials.  (The fused form reads the window rows with 16-byte loads.)
   if (N >= 1 && aligned(k_win, 16) && aligned(v_win, 16)) {
     AttendProblem pm = p;
     pm.N = N;
     pm.pos_end = N + W;
-    if (mfma_eligible(pm)) {
+    const bool mfma = mfma_eligible(pm);
+    if (mfma || stream_eligible(pm)) {  // (pm.W is still 0: the packed part alone)
       const bool wide = pm.rows > kMfmaMaxRows;
       const int S = num_splits ? num_splits
+                    : !mfma    ? stream_auto_splits(B, Hkv, N, stream_waves(bits, pm.rows))
                                : (wide ? mfma32_auto_splits(B, Hkv, N) : mfma_auto_splits(B, Hkv, N));
       int P = (W + kBlockTokens - 1) / kBlockTokens;  // window parts wanted
       while (P > 1 && (S + P > 65535 || !workspace ||
@@ -699,7 +701,8 @@ kvq_status kvq_attend_window(const float* q, const uint8_t* k_codes, const float
         pm.part_z = reinterpret_cast<float*>(ws + wl.z_off);
         pm.part_u = reinterpret_cast<float*>(ws + wl.u_off);
         pm.counters = reinterpret_cast<unsigned*>(ws + wl.cnt_off);
-        const hipError_t e = wide ? launch_attend_mfma32(pm, s) : launch_attend_mfma(pm, s);
+        const hipError_t e = !mfma ? launch_attend_stream(pm, s)
+                             : wide ? launch_attend_mfma32(pm, s) : launch_attend_mfma(pm, s);
         return hip_status(e, "attend_window (fused) launch");
       }
     }

@@ -235,6 +235,7 @@ struct SSmem {
   union {
     unsigned char ring[kWaves][kSDepth<kBits, kWaves>][kSSlotBytes<kBits>];  // block slots
     float wu[kWaves][kRows][kSD];                     // the merge (after the loop)
+    WinSmem<kRows> win;                               // a recent-token window part
   } u;
   SQuery<kRows> q;
   float wm[kWaves][kRows];
@@ -402,9 +403,16 @@ __device__ __forceinline__ void block_values(const SPart<kBits>& vp, const float
 // kCausal: a causal chunk (row r is query r % R at position pos_end - R +
 // r % R and reads tokens up to its own); only tokens past pos_end - R can be
 // masked, and a row with no legal key in the split returns m = -inf, z = 0.
-template <int kBits, int kRows, int kWaves, bool kCausal>
+// kWindow: the last p.win_parts splits of each head are parts of a float32
+// window of the most recent tokens (window_part, kvq_mfma_common.h), placed
+// after every head's packed splits in the grid (wg_slot).
+template <int kBits, int kRows, int kWaves, bool kCausal, bool kWindow>
 __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProblem p) {
   constexpr int kThreads = kWaves * 64;
+  // Outputs per thread in the merge and the split combine: row r, features
+  // f0 .. f0 + kF - 1 (threads past the kRows rows take no part).
+  constexpr int kF = (kRows * kSD + kThreads - 1) / kThreads;
+  static_assert(kSD % kF == 0, "whole rows per thread group");
   __shared__ SSmem<kBits, kRows, kWaves> sm;
   phase_mark(kMarkStart);
   const int tid = threadIdx.x;
@@ -414,18 +422,18 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
   const int q = lane & 3;   // token octet
 
   const int heads = p.B * p.Hkv;
-  const int L = blockIdx.x;
-  int head, split;
-  if (heads % 8 == 0) {
-    const int slot = L >> 3;
-    head = (L & 7) + 8 * (slot / p.splits);
-    split = slot % p.splits;
-  } else {
-    head = L / p.splits;
-    split = L % p.splits;
-  }
+  const WgSlot wslot = wg_slot(blockIdx.x, heads, p.splits, kWindow ? p.win_parts : 0);
+  const int head = wslot.head, split = wslot.split;
   const long long bh = head;
   const int rows = p.rows;
+  if (kWindow && split >= p.splits - p.win_parts) {  // a window part (the whole workgroup)
+    const int r = tid * kF / kSD, f0 = (tid * kF) % kSD;
+    float U[kF], M, Z;
+    window_part<kRows, kThreads, kF, kF, 0>(p, sm.u.win, bh, split - (p.splits - p.win_parts),
+                                            r, f0, U, M, Z);
+    split_combine<kF, kF, 0>(p, split, bh, r, f0, U, M, Z, &sm.last);
+    return;
+  }
   const Layout lay = make_layout(p.cap, kSD, kBits, p.group);
   SHead h;
   h.kblock = lay.kblock_bytes;
@@ -599,10 +607,7 @@ __global__ __launch_bounds__(kWaves * 64) void attend_stream_kernel(AttendProble
     }
   }
   __syncthreads();
-  // outputs per thread: row r, features f0 .. f0 + kF - 1 (threads past the
-  // kRows rows take no part)
-  constexpr int kF = (kRows * kSD + kThreads - 1) / kThreads;
-  static_assert(kSD % kF == 0, "whole rows per thread group");
+  // outputs per thread: row r, features f0 .. f0 + kF - 1
   const int r = tid * kF / kSD;
   const int f0 = (tid * kF) % kSD;
   const int rr = r < kRows ? r : kRows - 1;  // in-range row for the LDS reads
@@ -657,12 +662,20 @@ template <int kBits, int kRows>
 static hipError_t launch_stream(const AttendProblem& p, hipStream_t stream) {
   constexpr int kWaves = waves_for(kRows);
   const unsigned grid = static_cast<unsigned>(p.splits) * p.B * p.Hkv;
-  if (p.causal)
-    hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves, true>), dim3(grid),
+  if (p.win_parts > 0) {
+    if (p.causal)
+      hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves, true, true>), dim3(grid),
+                         dim3(kWaves * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves, false, true>), dim3(grid),
+                         dim3(kWaves * 64), 0, stream, p);
+  } else if (p.causal) {
+    hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves, true, false>), dim3(grid),
                        dim3(kWaves * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves, false>), dim3(grid),
+  } else {
+    hipLaunchKernelGGL((attend_stream_kernel<kBits, kRows, kWaves, false, false>), dim3(grid),
                        dim3(kWaves * 64), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -125,3 +125,32 @@ def test_window_full_size_sampled():
         qs = q[b:b + 1, h * rep:(h + 1) * rep]
         want = O.attend_window(qs, k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], win, 4, 32)
         assert max_abs(got[b:b + 1, h * rep:(h + 1) * rep], want) <= TOL, (b, h)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 8), (8, 16), (4, 64)], ids=["4b-g8", "8b-g16", "4b-g64"])
+@pytest.mark.parametrize("hq,hkv,r,causal", [(32, 8, 1, False), (16, 2, 2, True), (8, 8, 1, True),
+                                             (4, 1, 2, False)])
+def test_fused_window_on_the_streaming_kernel(bits, group, hq, hkv, r, causal):
+    """Mixed caches in the formats the streaming kernel takes: its launch with
+    window parts after the packed splits, against the oracle and against the
+    general kernel on the same call (a workspace with no extra slot forces
+    the latter)."""
+    B, n, w, D = 2, 1500, 70, 128
+    wl = Workload("stream_win", B, hq, hkv, r, n + w, D, ((bits, group),))
+    q, k, v = make_qkv(wl, 17)
+    announce(f"window on the streaming kernel hq={hq} hkv={hkv} R={r} {bits}b g{group} "
+             f"causal={causal}")
+    want = O.attend_window(q, k, v, w, bits, group, causal=causal)
+    kc, ks = kvq.pack_k(dev(k[:, :, :n]), bits, group)
+    vc, vs = kvq.pack_v(dev(v[:, :, :n]), bits, group)
+    kw, vw, qd = dev(k[:, :, n:]), dev(v[:, :, n:]), dev(q)
+    for splits in (1, 3, 0):
+        fused = host(kvq.attend_window(qd, kc, ks, vc, vs, kw, vw, n, bits, group,
+                                       num_splits=splits, causal=causal))
+        assert np.isfinite(fused).all(), splits
+        assert max_abs(fused, want) <= TOL, (splits, max_abs(fused, want))
+        if splits:
+            small = kvq.new_workspace(B, hq, hkv, r, n + w, D, splits)
+            general = host(kvq.attend_window(qd, kc, ks, vc, vs, kw, vw, n, bits, group,
+                                             num_splits=splits, workspace=small, causal=causal))
+            assert max_abs(fused, general) <= 2e-5, (splits, max_abs(fused, general))

@@ -235,7 +235,8 @@ def test_split_bounds_cover_and_empty_tail():
     assert sum(hi - lo for lo, hi in b) == 5 and b[-1][0] == b[-1][1]
 
 
-# --- quantization error: plausibility only (parity unpinned) -------------------------------
+# --- quantization error: the page's table values come from its own random draws, so this is a
+# --- plausibility check of the study (band and ordering); rel_l2 itself is pinned elsewhere ---
 
 def test_error_table_plausible(golden):
     g = golden("error_table.json")

@@ -689,6 +689,58 @@ def main():
             ", ".join(f"{k} ({v['kernel']}) {v['us']:.1f} us ({v['kv_gbs']:.0f} GB/s)"
                       for k, v in fmt.items()))
 
+        # The streaming kernel's causal and mixed-cache forms on the same cache
+        # shape in 4-bit group 8: a causal chunk of 2 queries per head (8 rows
+        # per KV head) over the whole cache, and the 64 most recent tokens kept
+        # in float32 with the 1-query step; rotating cache copies past the
+        # Infinity Cache, timed with stream events over back-to-back calls.
+        sbits, sgroup, swin = 4, 8, 64
+        sbytes = kv_bytes(w, sbits, sgroup)
+        scopies = max(2, math.ceil(3 * MALL_BYTES / sbytes))
+        sk0 = kvq.pack_k(kd, sbits, sgroup) + kvq.pack_v(vd, sbits, sgroup)
+        scaches = [sk0] + [tuple(t.clone() for t in sk0) for _ in range(scopies - 1)]
+        q2 = torch.from_numpy(make_qkv(dataclasses.replace(w, R=2), 1, n=1)[0]).to(dev)
+        ws2 = kvq.new_workspace(w.B, w.Hq, w.Hkv, 2, w.N, w.D, 0, device=dev)
+        out2 = torch.empty_like(q2)
+        wk0 = (kvq.pack_k(kd[:, :, :w.N - swin].contiguous(), sbits, sgroup) +
+               kvq.pack_v(vd[:, :, :w.N - swin].contiguous(), sbits, sgroup))
+        wcaches = [wk0] + [tuple(t.clone() for t in wk0) for _ in range(scopies - 1)]
+        kwin, vwin = kd[:, :, w.N - swin:].contiguous(), vd[:, :, w.N - swin:].contiguous()
+        ws_sw = kvq.new_workspace(w.B, w.Hq, w.Hkv, w.R, w.N, w.D,
+                                  kvq.auto_splits(w.B, w.Hkv, w.N) + swin // 32, device=dev)
+        outw = torch.empty_like(qd)
+
+        def causal8(c):
+            kvq.attend(q2, *c, w.N, sbits, sgroup, workspace=ws2, out=out2, causal=True)
+
+        def window8(c):
+            kvq.attend_window(qd, *c, kwin, vwin, w.N - swin, sbits, sgroup, workspace=ws_sw,
+                              out=outw)
+
+        sforms = {}
+        for name, fn, cs in (("4bit_g8_causal_2_queries", causal8, scaches),
+                             ("4bit_g8_window_64", window8, wcaches)):
+            for c in cs[:2]:
+                fn(c)
+            torch.cuda.synchronize()
+            n_s = max(2, 200 // len(cs))
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(n_s):
+                for c in cs:
+                    fn(c)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            sforms[name] = {"us": round(s0.elapsed_time(s1) * 1e3 / (n_s * len(cs)), 2),
+                            "kernel": "streaming", "cache_copies": len(cs)}
+        if not (torch.isfinite(out2).all() and torch.isfinite(outw).all()):
+            raise RuntimeError("streaming-kernel forms gave non-finite outputs")
+        extra["streaming_forms"] = sforms
+        log("[bench] streaming kernel, 4-bit g8: " +
+            ", ".join(f"{k} {v['us']:.1f} us" for k, v in sforms.items()))
+        del scaches, wcaches, sk0, wk0, q2, out2, outw, ws2, ws_sw
+
         # The single-head workloads (128 / 512 / 1024 tokens, D = 32, every
         # format they name): per-call time of one fused attend, graph-launched
         # back to back.  These are latency-bound (a few KB of cache).

@@ -293,13 +293,14 @@ kvq_status kvq_attend_noalloc(const float* q, const uint8_t* k_codes, const floa
  * sm_scale, splits, workspace (sized for N + W tokens) and flags
  * (KVQ_ATTEND_CAUSAL: positions counted over N + W) as in kvq_attend_cache.
  * When the packed part suits the matrix-core kernels (KVQ_VARIANT_MFMA's
- * conditions with capacity for N) and the workspace holds S + P split slots,
+ * conditions with capacity for N), or else the streaming kernel
+ * (KVQ_VARIANT_STREAM's), the workspace holds S + P split slots,
  * 1 <= P <= ceil(W / 32) (kvq_attend_workspace_bytes(B, Hq, Hkv, R, N + W, D,
- * S + P); S = num_splits, or the matrix-core kernel's own automatic count, at
- * most kvq_attend_auto_splits(B, Hkv, N)), and k_win and v_win are 16-byte
- * aligned (the window rows are read with 16-byte loads), the call is fused into one
- * matrix-core launch: per KV head, S workgroups attend the packed tokens and
- * P more the window tokens (P the largest count the workspace holds: one
+ * S + P); S = num_splits, or that kernel's own automatic count, at most
+ * kvq_attend_auto_splits(B, Hkv, N)), and k_win and v_win are 16-byte
+ * aligned (the window rows are read with 16-byte loads), the call is fused into
+ * one launch of that kernel: per KV head, S workgroups attend the packed tokens
+ * and P more the window tokens (P the largest count the workspace holds: one
  * workgroup per 32 window tokens at P = ceil(W / 32)), and the split combine
  * merges all S + P partials.  Otherwise the general kernel reads both
  * parts.  A decode

@@ -1,7 +1,8 @@
 // Streaming float32 attention over the packed cache for D = 128 in formats
 // the matrix-core kernels do not take: 4- or 8-bit codes with a
 // power-of-two group from 8 to 128, up to 8 query rows per KV head, with or
-// without the causal rule (a separate instantiation), no float32 window.
+// without the causal rule, and with or without a float32 window of the most
+// recent tokens (each a separate instantiation).
 //
 // Method: the blocked online softmax of "Block KV decoding: less workspace,
 // more time" (huhohoo.com/en/docs/llm/kv-block-decode-cost), section "Do not
